@@ -1,0 +1,334 @@
+"""Pins for the FP64 oracle (CPU only): each check ties the oracle to something other than itself.
+
+* brute force: textbook softmax(q K^T) V on tiny inputs, with every eligible block selected;
+* split invariance: chunk partials for several split counts, merged, equal the unsplit attention;
+* top-k: equal to Python's stable sort on tie-heavy rows, all-equal rows, all -inf rows, k >= width;
+* closed forms: constant V, all-zero K, one dominant cell, q = 0;
+* score identity: (sum of a group's q heads) . (block mean key) = the mean of the per-cell, per-head logits;
+* merge algebra: empty or out-of-range chunks change nothing, bit for bit;
+* the 24-bit split: exact for every integer in range, error of the scaling step within 2^-17.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import brute
+import oracle
+import synth
+
+B = oracle.BLOCK
+
+
+def small_case(seed, n_kv=2, G=3, d=64, cap=300, n_valid=290, rows=3, poison=True):
+    pool = synth.random_pool(seed, n_kv, cap, n_valid, d, poison=poison)
+    q = synth.random_q(seed + 1, rows, n_kv * G, d)
+    pos = np.array([n_valid - rows + r for r in range(rows)], np.int32)
+    return pool, q, pos
+
+
+# ---------------------------------------------------------------------------------------------------------------
+# brute force
+# ---------------------------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("d,n_valid,positions", [
+    (64, 290, [289, 288, 200]),      # ragged last block, a query inside a block
+    (128, 256, [255, 63, 64]),       # exact blocks, queries at a block's last and a block's first cell
+    (64, 70, [0, 5, 69]),            # query at cell 0 sees one cell
+])
+def test_dense_equals_textbook(d, n_valid, positions):
+    pool, q, _ = small_case(11, d=d, cap=n_valid + 17, n_valid=n_valid, rows=len(positions))
+    pos = np.array(positions, np.int32)
+    out, lse = oracle.attn(q, pos, pool, n_kv=2)
+    ref = brute.textbook_attention(q, pos, pool)
+    np.testing.assert_allclose(out, ref, rtol=0, atol=1e-12)
+    assert np.all(np.isfinite(lse))
+
+
+def test_full_selection_equals_textbook():
+    """k >= the number of blocks: the top-k keeps every eligible block, so selection attention is dense attention."""
+    pool, q, pos = small_case(21, d=128, cap=520, n_valid=500, rows=3)
+    nb = -(-pool.n_valid // B)
+    r = oracle.block_index(pool)
+    s = oracle.block_scores(q, pos, r, 2, pool.n_valid, nb)
+    ids, counts = oracle.topk(s.reshape(-1, nb), k=nb + 3)
+    ids = ids.reshape(3, 2, nb + 3)
+    counts = counts.reshape(3, 2)
+    out, _ = oracle.attn(q, pos, pool, 2, ids=ids, counts=counts)
+    ref = brute.textbook_attention(q, pos, pool)
+    np.testing.assert_allclose(out, ref, rtol=0, atol=1e-12)
+
+
+def test_sparse_equals_textbook_on_selected_blocks():
+    pool, q, pos = small_case(31, d=64, cap=600, n_valid=600, rows=2)
+    nb = -(-pool.n_valid // B)
+    r = oracle.block_index(pool)
+    s = oracle.block_scores(q, pos, r, 2, pool.n_valid, nb)
+    ids, counts = oracle.topk(s.reshape(-1, nb), k=3)
+    ids = ids.reshape(2, 2, 3)
+    counts = counts.reshape(2, 2)
+    sel = [[set(int(b) for b in ids[i, g] if b >= 0) for g in range(2)] for i in range(2)]
+    out, _ = oracle.attn(q, pos, pool, 2, ids=ids, counts=counts)
+    ref = brute.textbook_attention(q, pos, pool, selected_blocks=sel)
+    np.testing.assert_allclose(out, ref, rtol=0, atol=1e-12)
+
+
+def test_dense_matches_matrix_form_medium():
+    pool, q, pos = small_case(41, n_kv=2, G=2, d=128, cap=3000, n_valid=2900, rows=5)
+    out, _ = oracle.attn(q, pos, pool, 2)
+    ref = brute.matrix_attention(q, pos, pool)
+    np.testing.assert_allclose(out, ref, rtol=0, atol=1e-12)
+
+
+def test_attn_one_matches_attn():
+    pool, q, pos = small_case(43)
+    out, lse = oracle.attn(q, pos, pool, 2)
+    for i, h in [(0, 0), (2, 5), (1, 3)]:
+        o1, l1 = oracle.attn_one(q, pos, i, h, pool, 2)
+        assert np.array_equal(o1, out[i, h]) and l1 == lse[i, h]
+
+
+def test_lse_is_log_of_partition_function():
+    pool, q, pos = small_case(47, d=64, n_valid=130, cap=140, rows=1)
+    _, lse = oracle.attn(q, pos, pool, 2)
+    K = brute.repeat_kv(brute.dequant(pool.k[:, :130], pool.ks[:, :130]), 6)
+    for h in range(6):
+        t = [float(np.dot(q[0, h].astype(np.float64), K[h, c])) for c in range(pos[0] + 1)]
+        mx = max(t)
+        assert abs(lse[0, h] - (mx + math.log(math.fsum(math.exp(x - mx) for x in t)))) < 1e-12
+
+
+# ---------------------------------------------------------------------------------------------------------------
+# split invariance and merge algebra
+# ---------------------------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("S", [1, 2, 3, 5, 20])
+def test_split_invariance_sparse(S):
+    pool, q, pos = small_case(51, d=64, cap=1300, n_valid=1290, rows=3)
+    nb = -(-pool.n_valid // B)
+    r = oracle.block_index(pool)
+    s = oracle.block_scores(q, pos, r, 2, pool.n_valid, nb)
+    ids, counts = oracle.topk(s.reshape(-1, nb), k=7)
+    ids, counts = ids.reshape(3, 2, 7), counts.reshape(3, 2)
+    ref, ref_lse = oracle.attn(q, pos, pool, 2, ids=ids, counts=counts)
+    m, l, o, e = oracle.chunk_partials(q, pos, pool, 2, S, ids=ids, counts=counts)
+    out, lse = oracle.merge(m, l, o, e)
+    np.testing.assert_allclose(out, ref, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, ref_lse, rtol=0, atol=1e-12)
+    # chunks past the row's selected blocks are empty, the others hold at least one cell here
+    for i in range(3):
+        for h in range(6):
+            n_sel = counts[i, h // 3]
+            assert e[i, h, :n_sel].sum() == 0 or S > n_sel
+            assert np.all(e[i, h, min(S, n_sel):] == 1)
+
+
+def test_split_invariance_one_block_per_chunk():
+    pool, q, pos = small_case(53, d=128, cap=700, n_valid=650, rows=2)
+    nb = -(-pool.n_valid // B)
+    ids, counts = oracle.full_selection(pos, 2, pool.n_valid, nb)
+    ref, _ = oracle.attn(q, pos, pool, 2, ids=ids, counts=counts)
+    m, l, o, e = oracle.chunk_partials(q, pos, pool, 2, nb, ids=ids, counts=counts)
+    out, _ = oracle.merge(m, l, o, e)
+    np.testing.assert_allclose(out, ref, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("bpc", [1, 2, 3])
+def test_split_invariance_dense(bpc):
+    pool, q, pos = small_case(57, d=64, cap=1000, n_valid=700, rows=2)
+    S = -(-1000 // (B * bpc))
+    n_active = np.full(2, -(-700 // (B * bpc)), np.int32)
+    ref, _ = oracle.attn(q, pos, pool, 2)
+    m, l, o, e = oracle.chunk_partials(q, pos, pool, 2, S, bpc=bpc)
+    out, _ = oracle.merge(m, l, o, e, n_active=n_active)
+    np.testing.assert_allclose(out, ref, rtol=0, atol=1e-12)
+    assert np.all(e[:, :, n_active[0]:] == 1)
+
+
+def test_merge_skips_marked_and_inactive_chunks_bitwise():
+    pool, q, pos = small_case(61, d=64, cap=900, n_valid=900, rows=2)
+    m, l, o, e = oracle.chunk_partials(q, pos, pool, 2, 5, bpc=3)
+    out, lse = oracle.merge(m, l, o, e)
+    # interleave garbage chunks that are marked empty, and append unmarked garbage past n_active
+    S2 = 12
+    m2 = np.full(m.shape[:2] + (S2,), 1000.0)    # a max that would swamp every real chunk if it were read
+    l2 = np.full_like(m2, np.nan)
+    o2 = np.full(o.shape[:2] + (S2, o.shape[3]), np.nan)
+    e2 = np.ones(m2.shape, np.uint8)
+    slots = [0, 2, 3, 6, 8]
+    for j, sj in enumerate(slots):
+        m2[..., sj], l2[..., sj], o2[..., sj, :], e2[..., sj] = m[..., j], l[..., j], o[..., j, :], e[..., j]
+    e2[..., 10:] = 0                      # unmarked garbage beyond n_active
+    out2, lse2 = oracle.merge(m2, l2, o2, e2, n_active=np.full(2, 10, np.int32))
+    assert np.array_equal(out, out2) and np.array_equal(lse, lse2)
+
+
+def test_merge_of_disjoint_sets_is_union():
+    """Attention over a union of two disjoint cell sets = LSE merge of the two partial results."""
+    pool, q, pos = small_case(63, d=64, cap=512, n_valid=512, rows=1)
+    ids_a = np.array([[[0, 2, -1]] * 2], np.int32)
+    ids_b = np.array([[[5, 7, -1]] * 2], np.int32)
+    ids_u = np.array([[[0, 2, 5, 7]] * 2], np.int32)
+    cnt2 = np.array([[2, 2]], np.int32)
+    oa, la = oracle.attn(q, pos, pool, 2, ids=ids_a, counts=cnt2)
+    ob, lb = oracle.attn(q, pos, pool, 2, ids=ids_b, counts=cnt2)
+    ou, lu = oracle.attn(q, pos, pool, 2, ids=ids_u, counts=np.array([[4, 4]], np.int32))
+    M = np.maximum(la, lb)
+    wa, wb = np.exp(la - M), np.exp(lb - M)
+    merged = (wa[..., None] * oa + wb[..., None] * ob) / (wa + wb)[..., None]
+    np.testing.assert_allclose(merged, ou, rtol=0, atol=1e-12)
+
+
+def test_all_empty_row():
+    pool, q, _ = small_case(65, d=64, cap=200, n_valid=0, rows=1)
+    pos = np.array([10], np.int32)
+    out, lse = oracle.attn(q, pos, pool, 2)
+    assert np.all(out == 0) and np.all(lse == -np.inf)
+    m, l, o, e = oracle.chunk_partials(q, pos, pool, 2, 3, bpc=1)
+    assert np.all(e == 1) and np.all(m == -np.inf) and np.all(l == 0)
+    out2, lse2 = oracle.merge(m, l, o, e)
+    assert np.all(out2 == 0) and np.all(lse2 == -np.inf)
+
+
+# ---------------------------------------------------------------------------------------------------------------
+# top-k
+# ---------------------------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("width,k,levels,p_ninf", [
+    (16, 8, 0, 0.0), (256, 32, 4, 0.0), (300, 64, 3, 0.3), (97, 97, 0, 0.1), (50, 80, 2, 0.0),
+    (1024, 64, 0, 0.5), (33, 1, 1, 0.0), (64, 5, 0, 1.0),
+])
+def test_topk_equals_stable_sort(width, k, levels, p_ninf):
+    s = synth.random_scores(71 + width, 6, width, levels=levels, p_ninf=p_ninf)
+    ids, counts = oracle.topk(s, k)
+    for r in range(6):
+        exp_ids, exp_n = brute.sorted_topk([float(x) for x in s[r]], k)
+        assert list(ids[r]) == exp_ids and counts[r] == exp_n
+
+
+def test_topk_all_equal_takes_lowest_indices():
+    s = np.zeros((2, 40))
+    s[1, :7] = -np.inf
+    ids, counts = oracle.topk(s, 5)
+    assert list(ids[0]) == [0, 1, 2, 3, 4] and list(ids[1]) == [7, 8, 9, 10, 11]
+    assert list(counts) == [5, 5]
+
+
+def test_topk_negative_zero_ties_positive_zero():
+    s = np.array([[0.0, -0.0, 1.0, -0.0, 0.0]])
+    ids, _ = oracle.topk(s, 3)
+    assert list(ids[0]) == [0, 1, 2]
+
+
+# ---------------------------------------------------------------------------------------------------------------
+# closed forms
+# ---------------------------------------------------------------------------------------------------------------
+def test_constant_v_gives_constant_output():
+    pool, q, pos = small_case(81, d=128, cap=400, n_valid=333, rows=2)
+    pool.v[:, :333] = 37
+    pool.vs[:, :333] = np.float32(0.0125)
+    out, _ = oracle.attn(q, pos, pool, 2)
+    np.testing.assert_allclose(out, 37 * float(np.float32(0.0125)), rtol=1e-14, atol=0)
+
+
+def test_zero_keys_give_uniform_weights():
+    pool, q, pos = small_case(83, d=64, cap=400, n_valid=300, rows=2)
+    pool.k[:, :300] = 0
+    ids = np.array([[[1, 3, -1]] * 2] * 2, np.int32)
+    counts = np.array([[2, 2], [2, 2]], np.int32)
+    out, _ = oracle.attn(q, pos, pool, 2, ids=ids, counts=counts)
+    V = brute.dequant(pool.v[:, :300], pool.vs[:, :300])
+    for i in range(2):
+        cells = [c for c in list(range(64, 128)) + list(range(192, 256)) if c <= pos[i]]
+        for h in range(6):
+            np.testing.assert_allclose(out[i, h], V[h // 3, cells].mean(axis=0), rtol=0, atol=1e-14)
+
+
+def test_one_dominant_cell():
+    pool, _, _ = small_case(85, d=64, cap=200, n_valid=200, rows=1)
+    q = np.zeros((1, 6, 64), np.float32)
+    q[0, :, 0] = 0.5
+    pool.k[:, :200, 0] = 0
+    pool.k[:, 77, 0] = 127
+    pool.ks[:, 77, 0] = 2.0            # logit 127 for cell 77, 0 elsewhere
+    out, _ = oracle.attn(q, np.array([199], np.int32), pool, 2)
+    V = brute.dequant(pool.v[:, :200], pool.vs[:, :200])
+    for h in range(6):
+        np.testing.assert_allclose(out[0, h], V[h // 3, 77], rtol=1e-20, atol=1e-40)
+
+
+def test_zero_query_selects_lowest_blocks_and_averages():
+    pool, _, _ = small_case(87, d=64, cap=700, n_valid=650, rows=1)
+    q = np.zeros((1, 6, 64), np.float32)
+    pos = np.array([649], np.int32)
+    nb = -(-650 // B)
+    s = oracle.block_scores(q, pos, oracle.block_index(pool), 2, 650, nb)
+    assert np.all(s == 0)
+    ids, counts = oracle.topk(s.reshape(-1, nb), 4)
+    assert np.all(ids == [0, 1, 2, 3]) and np.all(counts == 4)
+    out, _ = oracle.attn(q, pos, pool, 2, ids=ids.reshape(1, 2, 4), counts=counts.reshape(1, 2))
+    V = brute.dequant(pool.v[:, :650], pool.vs[:, :650])
+    for h in range(6):
+        np.testing.assert_allclose(out[0, h], V[h // 3, :256].mean(axis=0), rtol=0, atol=1e-14)
+
+
+# ---------------------------------------------------------------------------------------------------------------
+# index and scores
+# ---------------------------------------------------------------------------------------------------------------
+def test_block_index_is_block_mean():
+    pool, _, _ = small_case(91, d=128, cap=500, n_valid=450)
+    r = oracle.block_index(pool)
+    np.testing.assert_allclose(r, brute.block_means(pool), rtol=0, atol=1e-14)
+    r_wide = oracle.block_index(pool, n_blocks=10)       # blocks past n_valid hold zeros
+    assert np.all(r_wide[:, 8:] == 0) and np.array_equal(r_wide[:, :8], r)
+
+
+def test_score_identity_and_causal_eligibility():
+    pool, q, pos = small_case(93, d=64, cap=500, n_valid=450, rows=3)
+    pos = np.array([449, 130, 127], np.int32)
+    nb = 9
+    s = oracle.block_scores(q, pos, oracle.block_index(pool), 2, 450, nb + 2)
+    K = brute.dequant(pool.k[:, :450], pool.ks[:, :450])
+    for i in range(3):
+        for g in range(2):
+            for b in range(nb + 2):
+                if b >= nb or b * B > pos[i]:
+                    assert s[i, g, b] == -np.inf
+                    continue
+                cells = range(b * B, min((b + 1) * B, 450))
+                per_cell = [sum(float(np.dot(q[i, h].astype(np.float64), K[g, c])) for h in range(3 * g, 3 * g + 3))
+                            for c in cells]
+                assert abs(s[i, g, b] - math.fsum(per_cell) / len(per_cell)) < 1e-12
+
+
+def test_oracle_never_reads_poison():
+    pool, q, pos = small_case(95, d=64, cap=400, n_valid=190, rows=2, poison=True)
+    assert np.isnan(pool.ks[0, 190, 0])
+    nb = 3
+    s = oracle.block_scores(q, pos, oracle.block_index(pool), 2, 190, nb)
+    ids, counts = oracle.topk(s.reshape(-1, nb), 3)
+    out, lse = oracle.attn(q, pos, pool, 2, ids=ids.reshape(2, 2, 3), counts=counts.reshape(2, 2))
+    assert np.all(np.isfinite(out)) and np.all(np.isfinite(lse)) and np.all(np.isfinite(s))
+
+
+# ---------------------------------------------------------------------------------------------------------------
+# 24-bit operand split
+# ---------------------------------------------------------------------------------------------------------------
+def test_split24_exact_over_whole_range():
+    X = np.arange(-127 * 65536, 127 * 65536 + 1, dtype=np.int32)
+    h, l, m = oracle.split24(X)
+    for part in (h, l, m):
+        assert part.min() >= -128 and part.max() <= 127
+    rec = 65536 * h.astype(np.int64) + 256 * l.astype(np.int64) + m.astype(np.int64)
+    assert np.array_equal(rec, X.astype(np.int64))
+
+
+def test_quant24_error_bound():
+    rng = np.random.Generator(np.random.PCG64(5))
+    x = rng.standard_normal(200_000)
+    amax = float(np.abs(x).max())
+    X = oracle.quant24(x, amax)
+    assert np.abs(X).max() <= 127 * 65536
+    xs = x * 127.0 / amax
+    assert np.abs(xs - X / 65536.0).max() <= 2.0 ** -17
+    # round half to even at exact halves
+    halves = np.array([0.5, 1.5, 2.5, -0.5, -1.5]) / 65536.0 * 1.0
+    Xh = oracle.quant24(halves, 127.0)
+    assert list(Xh) == [0, 2, 2, 0, -2]
