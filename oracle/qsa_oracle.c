@@ -149,8 +149,9 @@ static int32_t visible_cells(const orc_pool *p, int32_t block, int32_t pos_i, co
     int32_t nb = sel ? n_sel : b_end - b_begin;
     for (int32_t j = 0; j < nb; j++) {
         int32_t b = sel ? sel[j] : b_begin + j;
-        if (b < 0) continue;
-        for (int32_t c = b * block; c < (b + 1) * block; c++)
+        int64_t first = (int64_t)b * block;
+        if (b < 0 || first >= p->n_valid) continue;   /* ids past the valid cells name no cell */
+        for (int32_t c = (int32_t)first; c < first + block; c++)
             if (c < p->n_valid && c <= pos_i) cells[n++] = c;
     }
     return n;

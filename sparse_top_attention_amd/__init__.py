@@ -1,0 +1,240 @@
+"""Python binding of libqsa (QSA attention over an int8 KV cache, MI355X / gfx950).
+
+Argument marshalling only: every function checks dtypes, devices and contiguity of torch tensors, passes their
+device pointers and the current HIP stream to the C ABI declared in include/qsa.h, and raises QSAError on a
+non-zero status. No torch operator runs on the compute path; PyTorch supplies device memory and streams.
+
+The library is the in-tree ``libqsa.so``; importing this package raises if it has not been built (there is no
+fallback implementation).
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+from typing import Optional, Sequence
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqsa.so")
+
+QSA_OK = 0
+STATUS_NAMES = {0: "QSA_OK", -1: "QSA_ERR_NULL", -2: "QSA_ERR_SHAPE", -3: "QSA_ERR_UNSUPPORTED",
+                -4: "QSA_ERR_SCRATCH", -5: "QSA_ERR_RANGE", -6: "QSA_ERR_LAUNCH"}
+BLOCK = 64
+
+
+class QSAError(RuntimeError):
+    def __init__(self, fn, status):
+        self.status = status
+        super().__init__(f"{fn} failed: {STATUS_NAMES.get(status, status)} ({_lib().qsa_status_str(status).decode()})")
+
+
+class _Dims(ctypes.Structure):
+    _fields_ = [("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("block_cells", ctypes.c_int32)]
+
+
+class _Pool(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("k_scale", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("v_scale", ctypes.c_void_p), ("index", ctypes.c_void_p), ("capacity", ctypes.c_int32),
+                ("n_valid", ctypes.c_int32)]
+
+
+class _Partials(ctypes.Structure):
+    _fields_ = [("m", ctypes.c_void_p), ("l", ctypes.c_void_p), ("o", ctypes.c_void_p), ("empty", ctypes.c_void_p),
+                ("max_chunks", ctypes.c_int32)]
+
+
+_L = None
+
+
+def _lib():
+    global _L
+    if _L is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"libqsa.so is not built ({LIB_PATH}); run __graft_entry__.build() or "
+                              f"python -m sparse_top_attention_amd.build")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+        PP, PD, PPart = ctypes.POINTER(_Pool), _Dims, ctypes.POINTER(_Partials)
+        L.qsa_block_index.argtypes = [PP, PD, I32, I32, P, P]
+        L.qsa_block_scores.argtypes = [P, P, I32, PP, PD, I32, P, P]
+        L.qsa_topk_scratch_bytes.argtypes = [I32, I32, I32]
+        L.qsa_topk_scratch_bytes.restype = SZ
+        L.qsa_topk.argtypes = [P, I32, I32, I32, P, P, P, SZ, P]
+        L.qsa_attn_chunk.argtypes = [P, P, I32, PP, I32, P, PD, P, P, I32, I32, I32, ctypes.c_float, PPart, P]
+        L.qsa_attn_merge.argtypes = [PPart, I32, PD, I32, P, P, P, P]
+        L.qsa_prompt_scratch_bytes.argtypes = [I32, PD]
+        L.qsa_prompt_scratch_bytes.restype = SZ
+        L.qsa_prompt_attn.argtypes = [P, I32, I32, PP, PD, ctypes.c_float, P, P, SZ, P]
+        L.qsa_status_str.argtypes = [I32]
+        L.qsa_status_str.restype = ctypes.c_char_p
+        for fn in ("qsa_block_index", "qsa_block_scores", "qsa_topk", "qsa_attn_chunk", "qsa_attn_merge",
+                   "qsa_prompt_attn"):
+            getattr(L, fn).restype = I32
+        _L = L
+    return _L
+
+
+def lib_handle():
+    """The loaded ctypes library (loads it on first use)."""
+    return _lib()
+
+
+# ----------------------------------------------------------------------------------------------- helpers
+def _ptr(t: Optional[torch.Tensor], dtype, name, allow_none=False):
+    if t is None:
+        if allow_none:
+            return None
+        raise ValueError(f"{name} is required")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name}: expected a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: expected a contiguous tensor")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(fn, status):
+    if status != QSA_OK:
+        raise QSAError(fn, status)
+
+
+@dataclasses.dataclass
+class Dims:
+    n_q_heads: int
+    n_kv_heads: int
+    head_dim: int
+    block_cells: int = BLOCK
+
+    def c(self):
+        return _Dims(self.n_q_heads, self.n_kv_heads, self.head_dim, self.block_cells)
+
+
+@dataclasses.dataclass
+class Pool:
+    """Device tensors of one int8 KV pool: k, v int8 [n_kv][cap][d]; k_scale, v_scale f32 [n_kv][cap][d/64];
+    index f32 [n_kv][ceil(cap/64)][d] (optional, needed by qsa_block_scores)."""
+    k: torch.Tensor
+    k_scale: torch.Tensor
+    v: torch.Tensor
+    v_scale: torch.Tensor
+    n_valid: int
+    index: Optional[torch.Tensor] = None
+
+    @property
+    def capacity(self):
+        return self.k.shape[1]
+
+    def c(self):
+        return _Pool(_ptr(self.k, torch.int8, "k"), _ptr(self.k_scale, torch.float32, "k_scale"),
+                     _ptr(self.v, torch.int8, "v"), _ptr(self.v_scale, torch.float32, "v_scale"),
+                     _ptr(self.index, torch.float32, "index", allow_none=True), self.capacity, self.n_valid)
+
+
+@dataclasses.dataclass
+class Partials:
+    """Chunk partials: m, l f32 [n_rows][Hq][max_chunks]; o f32 [n_rows][Hq][max_chunks][d]; empty u8."""
+    m: torch.Tensor
+    l: torch.Tensor
+    o: torch.Tensor
+    empty: torch.Tensor
+
+    @property
+    def max_chunks(self):
+        return self.m.shape[-1]
+
+    @staticmethod
+    def empty_like_shape(n_rows, n_q_heads, max_chunks, head_dim, device="cuda"):
+        return Partials(torch.empty(n_rows, n_q_heads, max_chunks, dtype=torch.float32, device=device),
+                        torch.empty(n_rows, n_q_heads, max_chunks, dtype=torch.float32, device=device),
+                        torch.empty(n_rows, n_q_heads, max_chunks, head_dim, dtype=torch.float32, device=device),
+                        torch.empty(n_rows, n_q_heads, max_chunks, dtype=torch.uint8, device=device))
+
+    def c(self):
+        return _Partials(_ptr(self.m, torch.float32, "m"), _ptr(self.l, torch.float32, "l"),
+                         _ptr(self.o, torch.float32, "o"), _ptr(self.empty, torch.uint8, "empty"), self.max_chunks)
+
+
+# --------------------------------------------------------------------------------------------- the calls
+def qsa_block_index(pool: Pool, dims: Dims, cell_begin: int, cell_end: int, index: torch.Tensor, stream=None):
+    p = pool.c()
+    _check("qsa_block_index", _lib().qsa_block_index(ctypes.byref(p), dims.c(), cell_begin, cell_end,
+                                                     _ptr(index, torch.float32, "index"), _stream(stream)))
+    return index
+
+
+def qsa_block_scores(q, pos, pool: Pool, dims: Dims, n_blocks: int, scores, stream=None):
+    p = pool.c()
+    _check("qsa_block_scores", _lib().qsa_block_scores(_ptr(q, torch.float32, "q"), _ptr(pos, torch.int32, "pos"),
+                                                       q.shape[0], ctypes.byref(p), dims.c(), n_blocks,
+                                                       _ptr(scores, torch.float32, "scores"), _stream(stream)))
+    return scores
+
+
+def qsa_topk_scratch_bytes(n_rows, width, k):
+    return _lib().qsa_topk_scratch_bytes(n_rows, width, k)
+
+
+def qsa_topk(scores, k, ids, counts, scratch=None, stream=None):
+    width = scores.shape[-1]
+    n_rows = scores.numel() // width if width else 0
+    sp = None if scratch is None else _ptr(scratch, torch.uint8, "scratch")
+    nbytes = 0 if scratch is None else scratch.numel()
+    _check("qsa_topk", _lib().qsa_topk(_ptr(scores, torch.float32, "scores"), n_rows, width, k,
+                                       _ptr(ids, torch.int32, "ids"), _ptr(counts, torch.int32, "counts"),
+                                       sp, nbytes, _stream(stream)))
+    return ids, counts
+
+
+def qsa_attn_chunk(q, pos, pools: Sequence[Pool], dims: Dims, out: Partials, n_chunks: int, sm_scale: float = 1.0,
+                   row_pool=None, ids=None, counts=None, blocks_per_chunk: int = 1, stream=None):
+    arr = (_Pool * len(pools))(*[p.c() for p in pools])
+    k = ids.shape[-1] if ids is not None else 0
+    part = out.c()
+    _check("qsa_attn_chunk", _lib().qsa_attn_chunk(
+        _ptr(q, torch.float32, "q"), _ptr(pos, torch.int32, "pos"), q.shape[0], arr, len(pools),
+        _ptr(row_pool, torch.int32, "row_pool", allow_none=True), dims.c(),
+        _ptr(ids, torch.int32, "ids", allow_none=True), _ptr(counts, torch.int32, "counts", allow_none=True), k,
+        blocks_per_chunk, n_chunks, sm_scale, ctypes.byref(part), _stream(stream)))
+    return out
+
+
+def qsa_attn_merge(part: Partials, dims: Dims, n_chunks: int, out, lse=None, n_active=None, stream=None):
+    pc = part.c()
+    _check("qsa_attn_merge", _lib().qsa_attn_merge(
+        ctypes.byref(pc), part.m.shape[0], dims.c(), n_chunks, _ptr(n_active, torch.int32, "n_active", True),
+        _ptr(out, torch.float32, "out"), _ptr(lse, torch.float32, "lse", allow_none=True), _stream(stream)))
+    return out
+
+
+def qsa_prompt_scratch_bytes(n_q, dims: Dims):
+    return _lib().qsa_prompt_scratch_bytes(n_q, dims.c())
+
+
+def qsa_prompt_attn(q, pos0: int, pool: Pool, dims: Dims, out, sm_scale: float = 1.0, scratch=None, stream=None):
+    p = pool.c()
+    sp = None if scratch is None else _ptr(scratch, torch.uint8, "scratch")
+    nbytes = 0 if scratch is None else scratch.numel()
+    _check("qsa_prompt_attn", _lib().qsa_prompt_attn(_ptr(q, torch.float32, "q"), q.shape[0], pos0,
+                                                     ctypes.byref(p), dims.c(), sm_scale,
+                                                     _ptr(out, torch.float32, "out"), sp, nbytes, _stream(stream)))
+    return out
+
+
+def qsa_status_str(status: int) -> str:
+    return _lib().qsa_status_str(status).decode()
+
+
+__all__ = ["Dims", "Pool", "Partials", "QSAError", "qsa_block_index", "qsa_block_scores", "qsa_topk_scratch_bytes",
+           "qsa_topk", "qsa_attn_chunk", "qsa_attn_merge", "qsa_prompt_scratch_bytes", "qsa_prompt_attn",
+           "qsa_status_str", "lib_handle"]

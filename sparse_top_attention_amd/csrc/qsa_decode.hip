@@ -1,0 +1,515 @@
+// Decode-path kernels of libqsa for gfx950: block index, block scores, split-K chunk attention and the
+// log-sum-exp merge. All four stream int8 codes / fp32 rows from HBM with 16-byte coalesced loads and use the
+// VALU only (no matrix cores): per cell the work is a few hundred FMAs against 272 bytes, so HBM and the fp32 VALU
+// are the ceilings.
+//
+// Lane layout shared by the index and chunk kernels ("cell x slice"): a cell's D dims are cut into D/16 slices of
+// 16 dims (one 16-byte load of int8 codes), so a wave covers 64 / (D/16) cells per step; lane = cell_slot * LPC +
+// slice. A slice never straddles a 64-dim scale group. Per-cell dot products are finished by a DPP sum over the
+// LPC lanes of the cell, after which every lane of the cell holds the same logit.
+#include "qsa_internal.h"
+
+#include <math.h>
+
+namespace qsa {
+
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr float LN2 = 0.6931471805599453f;
+
+__device__ __forceinline__ void unpack16(const int4 w, float (&x)[16])
+{
+    const int32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+        x[4 * j + 0] = sbyte_f<0>(ws[j]);
+        x[4 * j + 1] = sbyte_f<1>(ws[j]);
+        x[4 * j + 2] = sbyte_f<2>(ws[j]);
+        x[4 * j + 3] = sbyte_f<3>(ws[j]);
+    }
+}
+
+// --------------------------------------------------------------------------------------------- block index
+// index[g][b][:] = mean of the dequantised keys of block b's valid cells. One wave per (block, KV head).
+template <int D>
+__global__ __launch_bounds__(64) void block_index_kernel(const int8_t *__restrict__ k, const float *__restrict__ ks,
+                                                         int32_t cap, int32_t n_valid, int32_t b_first,
+                                                         int32_t blk_stride, float *__restrict__ index)
+{
+    constexpr int LPC = D / 16, CPS = 64 / LPC, STEPS = QSA_BLOCK / CPS, NG = D / QSA_GROUP;
+    const int lane = threadIdx.x, r = lane / LPC, s = lane % LPC, grp = (16 * s) / QSA_GROUP;
+    const int32_t b = b_first + blockIdx.x, g = blockIdx.y;
+    const int32_t c0 = b * QSA_BLOCK;
+    float acc[16];
+#pragma unroll
+    for (int e = 0; e < 16; e++) acc[e] = 0.f;
+#pragma unroll
+    for (int st = 0; st < STEPS; st++) {
+        const int32_t c = c0 + st * CPS + r;
+        if (c < n_valid) {
+            const int64_t cell = (int64_t)g * cap + c;
+            const int4 w = *reinterpret_cast<const int4 *>(k + cell * D + 16 * s);
+            const float sc = ks[cell * NG + grp];
+            float x[16];
+            unpack16(w, x);
+#pragma unroll
+            for (int e = 0; e < 16; e++) acc[e] = fmaf(sc, x[e], acc[e]);
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < 16; e++) acc[e] = strided_sum<LPC>(acc[e]);
+    int32_t nb = n_valid - c0;
+    nb = nb < 0 ? 0 : (nb > QSA_BLOCK ? QSA_BLOCK : nb);
+    const float inv = nb > 0 ? 1.0f / (float)nb : 0.f;
+    if (r == 0) {
+        float4 *dst = reinterpret_cast<float4 *>(index + ((int64_t)g * blk_stride + b) * D + 16 * s);
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+            dst[j] = make_float4(acc[4 * j] * inv, acc[4 * j + 1] * inv, acc[4 * j + 2] * inv, acc[4 * j + 3] * inv);
+    }
+}
+
+// -------------------------------------------------------------------------------------------- block scores
+// scores[i][g][b] = qsum[i][g] . index[g][b]. Lanes: LPB = D/8 lanes per block (8 dims each), BPS = 64/LPB blocks
+// per step, NSTEP steps per wave; the index rows are loaded once and reused for every query row.
+template <int D>
+__global__ __launch_bounds__(64) void block_scores_kernel(const float *__restrict__ q, const int32_t *__restrict__ pos,
+                                                          int32_t n_rows, int32_t n_qh, int32_t n_kv, int32_t G,
+                                                          const float *__restrict__ index, int32_t blk_stride,
+                                                          int32_t n_valid, int32_t n_blocks,
+                                                          float *__restrict__ scores)
+{
+    constexpr int LPB = D / 8, BPS = 64 / LPB, NSTEP = 4;
+    const int lane = threadIdx.x, rb = lane / LPB, s = lane % LPB;
+    const int32_t g = blockIdx.y;
+    const int32_t bw = blockIdx.x * (BPS * NSTEP);
+    float rv[NSTEP][8];
+    int32_t bidx[NSTEP];
+#pragma unroll
+    for (int st = 0; st < NSTEP; st++) {
+        const int32_t b = bw + st * BPS + rb;
+        bidx[st] = b;
+        if (b < n_blocks && (int64_t)b * QSA_BLOCK < n_valid) {
+            const float4 *src = reinterpret_cast<const float4 *>(index + ((int64_t)g * blk_stride + b) * D + 8 * s);
+            const float4 u = src[0], w = src[1];
+            rv[st][0] = u.x; rv[st][1] = u.y; rv[st][2] = u.z; rv[st][3] = u.w;
+            rv[st][4] = w.x; rv[st][5] = w.y; rv[st][6] = w.z; rv[st][7] = w.w;
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; e++) rv[st][e] = 0.f;
+        }
+    }
+    for (int32_t i = 0; i < n_rows; i++) {
+        float qt[8];
+#pragma unroll
+        for (int e = 0; e < 8; e++) qt[e] = 0.f;
+        for (int32_t h = g * G; h < (g + 1) * G; h++) {
+            const float4 *src = reinterpret_cast<const float4 *>(q + ((int64_t)i * n_qh + h) * D + 8 * s);
+            const float4 u = src[0], w = src[1];
+            qt[0] += u.x; qt[1] += u.y; qt[2] += u.z; qt[3] += u.w;
+            qt[4] += w.x; qt[5] += w.y; qt[6] += w.z; qt[7] += w.w;
+        }
+        const int32_t p = pos[i];
+#pragma unroll
+        for (int st = 0; st < NSTEP; st++) {
+            float dot = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; e++) dot = fmaf(qt[e], rv[st][e], dot);
+            dot = group_sum<LPB>(dot);
+            const int32_t b = bidx[st];
+            const int64_t first = (int64_t)b * QSA_BLOCK;
+            if (s == 0 && b < n_blocks)
+                scores[((int64_t)i * n_kv + g) * n_blocks + b] = (first <= p && first < n_valid) ? dot : -INFINITY;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------------------- chunk attention
+struct ChunkArgs {
+    const float *q;
+    const int32_t *pos;
+    const int32_t *row_pool;
+    const int32_t *ids;
+    const int32_t *counts;
+    float *m_out;
+    float *l_out;
+    float *o_out;
+    uint8_t *empty_out;
+    PoolArg pools[QSA_MAX_POOLS];
+    int32_t n_pools;
+    int32_t n_qh;
+    int32_t n_kv;
+    int32_t G;
+    int32_t n_hsub;
+    int32_t topk;
+    int32_t bpc;
+    int32_t n_chunks;
+    int32_t max_chunks;
+    float qscale;  // sm_scale * log2(e): logits are kept in base-2 units inside the kernel
+};
+
+// One wave per (chunk j, KV head g x head subset, row i). Each lane owns one cell slot r (cells r, r + CPS, ...
+// of every block) and one 16-dim slice s, and keeps a running max / sum / output per q head for its cell slot;
+// the cell slots are merged with a log-sum-exp fold across lanes at the end of the chunk.
+template <int D, int HPW>
+__global__ __launch_bounds__(64) void attn_chunk_kernel(const ChunkArgs a)
+{
+    constexpr int LPC = D / 16, CPS = 64 / LPC, STEPS = QSA_BLOCK / CPS, NG = D / QSA_GROUP;
+    const int lane = threadIdx.x, r = lane / LPC, s = lane % LPC, grp = (16 * s) / QSA_GROUP;
+    const int32_t j = blockIdx.x, i = blockIdx.z;
+    const int32_t g = blockIdx.y / a.n_hsub, h0 = g * a.G + (blockIdx.y % a.n_hsub) * HPW;
+
+    const int32_t pidx = a.row_pool ? a.row_pool[i] : 0;
+    const bool pool_ok = pidx >= 0 && pidx < a.n_pools;
+    PoolArg P = a.pools[pool_ok ? pidx : 0];
+    const int32_t limit = pool_ok ? min(P.n_valid - 1, a.pos[i]) : -1;  // visible cells: c <= limit
+
+    // this chunk's block run
+    int32_t n_blk, first;
+    const int32_t *blist = nullptr;
+    if (a.ids) {
+        int32_t cnt = a.counts[(int64_t)i * a.n_kv + g];
+        cnt = cnt < 0 ? 0 : (cnt > a.topk ? a.topk : cnt);
+        const int32_t base = cnt / a.n_chunks, rem = cnt % a.n_chunks;
+        n_blk = base + (j < rem ? 1 : 0);
+        first = j * base + (j < rem ? j : rem);
+        blist = a.ids + ((int64_t)i * a.n_kv + g) * a.topk;
+    } else {
+        n_blk = a.bpc;
+        first = j * a.bpc;
+    }
+
+    float qv[HPW][16];
+#pragma unroll
+    for (int h = 0; h < HPW; h++) {
+        const float4 *src = reinterpret_cast<const float4 *>(a.q + ((int64_t)i * a.n_qh + h0 + h) * D + 16 * s);
+#pragma unroll
+        for (int jj = 0; jj < 4; jj++) {
+            const float4 u = src[jj];
+            qv[h][4 * jj + 0] = u.x * a.qscale;
+            qv[h][4 * jj + 1] = u.y * a.qscale;
+            qv[h][4 * jj + 2] = u.z * a.qscale;
+            qv[h][4 * jj + 3] = u.w * a.qscale;
+        }
+    }
+    float mrun[HPW], lrun[HPW], o[HPW][16];
+#pragma unroll
+    for (int h = 0; h < HPW; h++) {
+        mrun[h] = -INFINITY;
+        lrun[h] = 0.f;
+#pragma unroll
+        for (int e = 0; e < 16; e++) o[h][e] = 0.f;
+    }
+
+    for (int32_t t = 0; t < n_blk; t++) {
+        const int32_t b = blist ? blist[first + t] : first + t;
+        if (b < 0 || (int64_t)b * QSA_BLOCK > limit) continue;  // negative id, or no visible valid cell
+        const int32_t cb = b * QSA_BLOCK;
+
+        // q . k for this lane's cells of the block
+        float lg[STEPS][HPW];
+#pragma unroll
+        for (int st = 0; st < STEPS; st++) {
+            const int32_t c = cb + st * CPS + r;
+            const bool vis = c <= limit;
+            int4 w = make_int4(0, 0, 0, 0);
+            float sc = 0.f;
+            if (vis) {
+                const int64_t cell = (int64_t)g * P.capacity + c;
+                w = *reinterpret_cast<const int4 *>(P.k + cell * D + 16 * s);
+                sc = P.ks[cell * NG + grp];
+            }
+            float x[16];
+            unpack16(w, x);
+#pragma unroll
+            for (int h = 0; h < HPW; h++) {
+                float dot = 0.f;
+#pragma unroll
+                for (int e = 0; e < 16; e++) dot = fmaf(qv[h][e], x[e], dot);
+                dot = group_sum<LPC>(dot * sc);
+                lg[st][h] = vis ? dot : -INFINITY;
+            }
+        }
+        // running max per (cell slot, head); rescale what was accumulated before
+#pragma unroll
+        for (int h = 0; h < HPW; h++) {
+            float mb = lg[0][h];
+#pragma unroll
+            for (int st = 1; st < STEPS; st++) mb = fmaxf(mb, lg[st][h]);
+            const float mnew = fmaxf(mrun[h], mb);
+            const float alpha = (mnew == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(mrun[h] - mnew);
+            mrun[h] = mnew;
+            lrun[h] *= alpha;
+#pragma unroll
+            for (int e = 0; e < 16; e++) o[h][e] *= alpha;
+        }
+        // p . v
+#pragma unroll
+        for (int st = 0; st < STEPS; st++) {
+            const int32_t c = cb + st * CPS + r;
+            const bool vis = c <= limit;
+            int4 w = make_int4(0, 0, 0, 0);
+            float sc = 0.f;
+            if (vis) {
+                const int64_t cell = (int64_t)g * P.capacity + c;
+                w = *reinterpret_cast<const int4 *>(P.v + cell * D + 16 * s);
+                sc = P.vs[cell * NG + grp];
+            }
+            float x[16];
+            unpack16(w, x);
+#pragma unroll
+            for (int h = 0; h < HPW; h++) {
+                const float p = vis ? __builtin_amdgcn_exp2f(lg[st][h] - mrun[h]) : 0.f;
+                lrun[h] += p;
+                const float wgt = p * sc;
+#pragma unroll
+                for (int e = 0; e < 16; e++) o[h][e] = fmaf(wgt, x[e], o[h][e]);
+            }
+        }
+    }
+
+    // fold the CPS cell slots (lanes LPC apart) into one partial per head
+    float mtot[HPW];
+#pragma unroll
+    for (int h = 0; h < HPW; h++) {
+        const float M = strided_max<LPC>(mrun[h]);
+        mtot[h] = M;
+        const float sc = (mrun[h] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mrun[h] - M);
+        lrun[h] = strided_sum<LPC>(lrun[h] * sc);
+#pragma unroll
+        for (int e = 0; e < 16; e++) o[h][e] = strided_sum<LPC>(o[h][e] * sc);
+    }
+#pragma unroll
+    for (int h = 0; h < HPW; h++) {
+        const int64_t idx = ((int64_t)i * a.n_qh + h0 + h) * a.max_chunks + j;
+        const bool empty = mtot[h] == -INFINITY;
+        if (lane == 0) {
+            a.m_out[idx] = empty ? -INFINITY : mtot[h] * LN2;
+            a.l_out[idx] = empty ? 0.f : lrun[h];
+            a.empty_out[idx] = empty ? 1 : 0;
+        }
+        if (r == h % CPS) {
+            float4 *dst = reinterpret_cast<float4 *>(a.o_out + idx * D + 16 * s);
+#pragma unroll
+            for (int jj = 0; jj < 4; jj++)
+                dst[jj] = empty ? make_float4(0.f, 0.f, 0.f, 0.f)
+                                : make_float4(o[h][4 * jj], o[h][4 * jj + 1], o[h][4 * jj + 2], o[h][4 * jj + 3]);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------------------------------- merge
+// One workgroup of 4 waves per (row, q head). Pass 1 finds the max over the row's non-empty chunks, pass 2 adds
+// e^(m_j - M) l_j and e^(m_j - M) o_j; each wave takes a contiguous quarter of the chunks and the quarters are
+// combined through LDS. Lanes own D/64 consecutive dims.
+template <int D>
+__global__ __launch_bounds__(256) void attn_merge_kernel(const float *__restrict__ m, const float *__restrict__ l,
+                                                         const float *__restrict__ o, const uint8_t *__restrict__ em,
+                                                         int32_t max_chunks, int32_t n_chunks,
+                                                         const int32_t *__restrict__ n_active, int32_t n_qh,
+                                                         float *__restrict__ out, float *__restrict__ lse)
+{
+    constexpr int VPL = D / 64;
+    __shared__ float sM[4], sL[4];
+    __shared__ float sO[4][D];
+    const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
+    const int32_t row = blockIdx.x;               // = i * n_qh + h
+    const int32_t i = row / n_qh;
+    int32_t na = n_active ? n_active[i] : n_chunks;
+    na = na < 0 ? 0 : (na > n_chunks ? n_chunks : na);
+    const int32_t j0 = (int32_t)(((int64_t)na * wave) / 4), j1 = (int32_t)(((int64_t)na * (wave + 1)) / 4);
+    const int64_t base = (int64_t)row * max_chunks;
+
+    float M = -INFINITY;
+    for (int32_t jj = j0; jj < j1; jj++)
+        if (!em[base + jj]) M = fmaxf(M, m[base + jj]);
+    if (lane == 0) sM[wave] = M;
+    __syncthreads();
+    M = fmaxf(fmaxf(sM[0], sM[1]), fmaxf(sM[2], sM[3]));
+
+    float L = 0.f, acc[VPL];
+#pragma unroll
+    for (int e = 0; e < VPL; e++) acc[e] = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll 4
+        for (int32_t jj = j0; jj < j1; jj++) {
+            if (em[base + jj]) continue;
+            const float w = expf(m[base + jj] - M);
+            L = fmaf(w, l[base + jj], L);
+            const float *src = o + (base + jj) * D + VPL * lane;
+#pragma unroll
+            for (int e = 0; e < VPL; e++) acc[e] = fmaf(w, src[e], acc[e]);
+        }
+    }
+    if (lane == 0) sL[wave] = L;
+#pragma unroll
+    for (int e = 0; e < VPL; e++) sO[wave][VPL * lane + e] = acc[e];
+    __syncthreads();
+    if (wave == 0) {
+        const float Lt = (sL[0] + sL[1]) + (sL[2] + sL[3]);
+        const bool none = M == -INFINITY;
+#pragma unroll
+        for (int e = 0; e < VPL; e++) {
+            const int d = VPL * lane + e;
+            const float num = (sO[0][d] + sO[1][d]) + (sO[2][d] + sO[3][d]);
+            out[(int64_t)row * D + d] = none ? 0.f : num / Lt;
+        }
+        if (lse && lane == 0) lse[row] = none ? -INFINITY : M + logf(Lt);
+    }
+}
+
+}  // namespace qsa
+
+using namespace qsa;
+
+// ======================================================================================== C entry points
+extern "C" qsa_status qsa_block_index(const qsa_pool *pool, qsa_dims dims, int32_t cell_begin, int32_t cell_end,
+                                      float *index, qsa_stream_t stream)
+{
+    qsa_status st = check_dims(dims);
+    if (st != QSA_OK) return st;
+    if ((st = check_pool(pool, false)) != QSA_OK) return st;
+    if (!index) return QSA_ERR_NULL;
+    if (cell_begin < 0 || cell_end < cell_begin || cell_end > pool->capacity) return QSA_ERR_RANGE;
+    if (cell_end == cell_begin) return QSA_OK;
+    const int32_t b0 = cell_begin / QSA_BLOCK, b1 = ceil_div(cell_end, QSA_BLOCK);
+    const int32_t stride = ceil_div(pool->capacity, QSA_BLOCK);
+    dim3 grid(b1 - b0, dims.n_kv_heads);
+    hipStream_t s = (hipStream_t)stream;
+    switch (dims.head_dim) {
+    case 64: block_index_kernel<64><<<grid, 64, 0, s>>>(pool->k, pool->k_scale, pool->capacity, pool->n_valid, b0, stride, index); break;
+    case 128: block_index_kernel<128><<<grid, 64, 0, s>>>(pool->k, pool->k_scale, pool->capacity, pool->n_valid, b0, stride, index); break;
+    default: block_index_kernel<256><<<grid, 64, 0, s>>>(pool->k, pool->k_scale, pool->capacity, pool->n_valid, b0, stride, index); break;
+    }
+    return launch_status();
+}
+
+extern "C" qsa_status qsa_block_scores(const float *q, const int32_t *pos, int32_t n_rows, const qsa_pool *pool,
+                                       qsa_dims dims, int32_t n_blocks, float *scores, qsa_stream_t stream)
+{
+    qsa_status st = check_dims(dims);
+    if (st != QSA_OK) return st;
+    if ((st = check_pool(pool, false)) != QSA_OK) return st;
+    if (!q || !pos || !scores || !pool->index) return QSA_ERR_NULL;
+    if (n_rows < 0 || n_blocks < 0) return QSA_ERR_SHAPE;
+    const int32_t stride = ceil_div(pool->capacity, QSA_BLOCK);
+    if (n_blocks > stride) return QSA_ERR_RANGE;
+    if (n_rows == 0 || n_blocks == 0) return QSA_OK;
+    const int32_t G = dims.n_q_heads / dims.n_kv_heads;
+    const int32_t per_wave = (64 / (dims.head_dim / 8)) * 4;
+    dim3 grid(ceil_div(n_blocks, per_wave), dims.n_kv_heads);
+    hipStream_t s = (hipStream_t)stream;
+#define QSA_SCORES(DD) block_scores_kernel<DD><<<grid, 64, 0, s>>>(q, pos, n_rows, dims.n_q_heads, dims.n_kv_heads, G, pool->index, stride, pool->n_valid, n_blocks, scores)
+    switch (dims.head_dim) {
+    case 64: QSA_SCORES(64); break;
+    case 128: QSA_SCORES(128); break;
+    default: QSA_SCORES(256); break;
+    }
+#undef QSA_SCORES
+    return launch_status();
+}
+
+namespace {
+template <int D>
+void launch_chunk(int hpw, dim3 grid, hipStream_t s, const ChunkArgs &a)
+{
+    switch (hpw) {
+    case 1: attn_chunk_kernel<D, 1><<<grid, 64, 0, s>>>(a); break;
+    case 2: attn_chunk_kernel<D, 2><<<grid, 64, 0, s>>>(a); break;
+    case 3: attn_chunk_kernel<D, 3><<<grid, 64, 0, s>>>(a); break;
+    case 4: attn_chunk_kernel<D, 4><<<grid, 64, 0, s>>>(a); break;
+    case 5: attn_chunk_kernel<D, 5><<<grid, 64, 0, s>>>(a); break;
+    default: attn_chunk_kernel<D, 6><<<grid, 64, 0, s>>>(a); break;
+    }
+}
+
+// q heads handled by one wave: the largest divisor of G that is at most 6 (fewer for wide heads).
+int heads_per_wave(int G, int D)
+{
+    const int cap = D == 256 ? 3 : 6;
+    for (int h = cap; h >= 1; h--)
+        if (G % h == 0) return h;
+    return 1;
+}
+}  // namespace
+
+extern "C" qsa_status qsa_attn_chunk(const float *q, const int32_t *pos, int32_t n_rows, const qsa_pool *pools,
+                                     int32_t n_pools, const int32_t *row_pool, qsa_dims dims, const int32_t *ids,
+                                     const int32_t *counts, int32_t k, int32_t blocks_per_chunk, int32_t n_chunks,
+                                     float sm_scale, const qsa_partials *out, qsa_stream_t stream)
+{
+    qsa_status st = check_dims(dims);
+    if (st != QSA_OK) return st;
+    if (!q || !pos || !pools || !out) return QSA_ERR_NULL;
+    if (!out->m || !out->l || !out->o || !out->empty) return QSA_ERR_NULL;
+    if (n_rows < 0 || n_pools <= 0) return QSA_ERR_SHAPE;
+    if (n_pools > QSA_MAX_POOLS) return QSA_ERR_UNSUPPORTED;
+    for (int32_t p = 0; p < n_pools; p++)
+        if ((st = check_pool(&pools[p], true)) != QSA_OK) return st;
+    if (ids) {
+        if (!counts) return QSA_ERR_NULL;
+        if (k <= 0) return QSA_ERR_RANGE;
+    } else if (blocks_per_chunk <= 0) {
+        return QSA_ERR_RANGE;
+    }
+    if (n_chunks <= 0) return QSA_ERR_RANGE;
+    if (n_chunks > out->max_chunks) return QSA_ERR_SCRATCH;
+    if (n_rows == 0) return QSA_OK;
+    if (n_rows > 65535) return QSA_ERR_UNSUPPORTED;
+
+    ChunkArgs a{};
+    a.q = q; a.pos = pos; a.row_pool = row_pool; a.ids = ids; a.counts = counts;
+    a.m_out = out->m; a.l_out = out->l; a.o_out = out->o; a.empty_out = out->empty;
+    for (int32_t p = 0; p < n_pools; p++)
+        a.pools[p] = PoolArg{pools[p].k, pools[p].k_scale, pools[p].v, pools[p].v_scale, pools[p].capacity,
+                             pools[p].n_valid};
+    a.n_pools = row_pool ? n_pools : 1;
+    a.n_qh = dims.n_q_heads; a.n_kv = dims.n_kv_heads; a.G = dims.n_q_heads / dims.n_kv_heads;
+    const int hpw = heads_per_wave(a.G, dims.head_dim);
+    a.n_hsub = a.G / hpw;
+    a.topk = k; a.bpc = blocks_per_chunk; a.n_chunks = n_chunks; a.max_chunks = out->max_chunks;
+    a.qscale = sm_scale * LOG2E;
+    dim3 grid(n_chunks, dims.n_kv_heads * a.n_hsub, n_rows);
+    hipStream_t s = (hipStream_t)stream;
+    switch (dims.head_dim) {
+    case 64: launch_chunk<64>(hpw, grid, s, a); break;
+    case 128: launch_chunk<128>(hpw, grid, s, a); break;
+    default: launch_chunk<256>(hpw, grid, s, a); break;
+    }
+    return launch_status();
+}
+
+extern "C" qsa_status qsa_attn_merge(const qsa_partials *in, int32_t n_rows, qsa_dims dims, int32_t n_chunks,
+                                     const int32_t *n_active, float *out, float *lse, qsa_stream_t stream)
+{
+    qsa_status st = check_dims(dims);
+    if (st != QSA_OK) return st;
+    if (!in || !out) return QSA_ERR_NULL;
+    if (!in->m || !in->l || !in->o || !in->empty) return QSA_ERR_NULL;
+    if (n_rows < 0 || n_chunks < 0) return QSA_ERR_SHAPE;
+    if (n_chunks > in->max_chunks) return QSA_ERR_SCRATCH;
+    if (n_rows == 0) return QSA_OK;
+    dim3 grid((uint32_t)n_rows * (uint32_t)dims.n_q_heads);
+    hipStream_t s = (hipStream_t)stream;
+#define QSA_MERGE(DD) attn_merge_kernel<DD><<<grid, 256, 0, s>>>(in->m, in->l, in->o, in->empty, in->max_chunks, n_chunks, n_active, dims.n_q_heads, out, lse)
+    switch (dims.head_dim) {
+    case 64: QSA_MERGE(64); break;
+    case 128: QSA_MERGE(128); break;
+    default: QSA_MERGE(256); break;
+    }
+#undef QSA_MERGE
+    return launch_status();
+}
+
+extern "C" const char *qsa_status_str(qsa_status status)
+{
+    switch (status) {
+    case QSA_OK: return "ok";
+    case QSA_ERR_NULL: return "null pointer";
+    case QSA_ERR_SHAPE: return "inconsistent shape";
+    case QSA_ERR_UNSUPPORTED: return "unsupported shape";
+    case QSA_ERR_SCRATCH: return "scratch or partials too small";
+    case QSA_ERR_RANGE: return "argument out of range";
+    case QSA_ERR_LAUNCH: return "kernel launch failed";
+    }
+    return "unknown status";
+}

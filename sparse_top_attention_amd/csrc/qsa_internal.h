@@ -1,0 +1,155 @@
+// Internal helpers shared by libqsa's translation units: status plumbing on the host, and wave64 cross-lane
+// primitives (DPP within a row of 16 lanes, permlane swaps across rows) on the device. gfx950 only.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "qsa.h"
+
+#define QSA_BLOCK 64  // cells per selection block
+#define QSA_GROUP 64  // dims per int8 scale group
+#define QSA_MAX_POOLS 8
+
+namespace qsa {
+
+// ------------------------------------------------------------------------------------------------ host side
+inline bool dims_supported(const qsa_dims &d)
+{
+    if (d.block_cells != QSA_BLOCK) return false;
+    if (d.head_dim != 64 && d.head_dim != 128 && d.head_dim != 256) return false;
+    if (d.n_kv_heads <= 0 || d.n_q_heads <= 0 || d.n_q_heads % d.n_kv_heads != 0) return false;
+    if (d.n_q_heads / d.n_kv_heads > 8) return false;
+    return true;
+}
+
+inline qsa_status check_dims(const qsa_dims &d)
+{
+    if (d.n_q_heads <= 0 || d.n_kv_heads <= 0 || d.head_dim <= 0 || d.block_cells <= 0) return QSA_ERR_SHAPE;
+    if (d.n_q_heads % d.n_kv_heads != 0) return QSA_ERR_SHAPE;
+    return dims_supported(d) ? QSA_OK : QSA_ERR_UNSUPPORTED;
+}
+
+inline qsa_status check_pool(const qsa_pool *p, bool need_v)
+{
+    if (!p) return QSA_ERR_NULL;
+    if (!p->k || !p->k_scale) return QSA_ERR_NULL;
+    if (need_v && (!p->v || !p->v_scale)) return QSA_ERR_NULL;
+    if (p->capacity < 0 || p->n_valid < 0) return QSA_ERR_SHAPE;
+    if (p->n_valid > p->capacity) return QSA_ERR_RANGE;
+    return QSA_OK;
+}
+
+inline int32_t ceil_div(int32_t a, int32_t b) { return (a + b - 1) / b; }
+
+inline qsa_status launch_status()
+{
+    return hipGetLastError() == hipSuccess ? QSA_OK : QSA_ERR_LAUNCH;
+}
+
+// Kernel-argument copy of a pool (device pointers only).
+struct PoolArg {
+    const int8_t *k;
+    const float *ks;
+    const int8_t *v;
+    const float *vs;
+    int32_t capacity;
+    int32_t n_valid;
+};
+
+// ---------------------------------------------------------------------------------------------- device side
+// DPP controls (gfx9 encoding).
+constexpr int DPP_QUAD_XOR1 = 0xB1;     // quad_perm [1,0,3,2]
+constexpr int DPP_QUAD_XOR2 = 0x4E;     // quad_perm [2,3,0,1]
+constexpr int DPP_ROW_HALF_MIRROR = 0x141;  // lane i of each 8 -> 7 - i
+constexpr int DPP_ROW_MIRROR = 0x140;       // lane i of each 16 -> 15 - i
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v)
+{
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+
+// Pairwise combine with the lane 16 apart (within each 32) or 32 apart, via the gfx950 permlane swaps. With both
+// operands equal, the swap leaves {own value, partner value} in the two result registers of every lane (which
+// register holds which depends on the half), so a commutative op on the pair gives the same bits in both lanes.
+__device__ __forceinline__ float sum16(float v)
+{
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_int(v), __float_as_int(v), false, false);
+    return __int_as_float(r[0]) + __int_as_float(r[1]);
+}
+__device__ __forceinline__ float max16(float v)
+{
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_int(v), __float_as_int(v), false, false);
+    return fmaxf(__int_as_float(r[0]), __int_as_float(r[1]));
+}
+__device__ __forceinline__ float sum32(float v)
+{
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(v), __float_as_int(v), false, false);
+    return __int_as_float(r[0]) + __int_as_float(r[1]);
+}
+__device__ __forceinline__ float max32(float v)
+{
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(v), __float_as_int(v), false, false);
+    return fmaxf(__int_as_float(r[0]), __int_as_float(r[1]));
+}
+
+// Sum / max over aligned groups of N lanes (N in {2, 4, 8, 16, 32, 64}); every lane of the group gets the result.
+template <int N>
+__device__ __forceinline__ float group_sum(float v)
+{
+    if constexpr (N >= 2) v += dpp_f<DPP_QUAD_XOR1>(v);
+    if constexpr (N >= 4) v += dpp_f<DPP_QUAD_XOR2>(v);
+    if constexpr (N >= 8) v += dpp_f<DPP_ROW_HALF_MIRROR>(v);
+    if constexpr (N >= 16) v += dpp_f<DPP_ROW_MIRROR>(v);
+    if constexpr (N >= 32) v = sum16(v);
+    if constexpr (N >= 64) v = sum32(v);
+    return v;
+}
+
+template <int N>
+__device__ __forceinline__ float group_max(float v)
+{
+    if constexpr (N >= 2) v = fmaxf(v, dpp_f<DPP_QUAD_XOR1>(v));
+    if constexpr (N >= 4) v = fmaxf(v, dpp_f<DPP_QUAD_XOR2>(v));
+    if constexpr (N >= 8) v = fmaxf(v, dpp_f<DPP_ROW_HALF_MIRROR>(v));
+    if constexpr (N >= 16) v = fmaxf(v, dpp_f<DPP_ROW_MIRROR>(v));
+    if constexpr (N >= 32) v = max16(v);
+    if constexpr (N >= 64) v = max32(v);
+    return v;
+}
+
+// Sum over lanes that are STRIDE apart (lanes l, l + STRIDE, l + 2 STRIDE, ... up to 64): every lane gets the
+// sum over its residue class mod STRIDE. STRIDE in {1, 2, 4, 8, 16, 32, 64}.
+template <int STRIDE>
+__device__ __forceinline__ float strided_sum(float v)
+{
+    if constexpr (STRIDE <= 1) v += dpp_f<DPP_QUAD_XOR1>(v);
+    if constexpr (STRIDE <= 2) v += dpp_f<DPP_QUAD_XOR2>(v);
+    if constexpr (STRIDE <= 4) v += __shfl_xor(v, 4);
+    if constexpr (STRIDE <= 8) v += __shfl_xor(v, 8);
+    if constexpr (STRIDE <= 16) v = sum16(v);
+    if constexpr (STRIDE <= 32) v = sum32(v);
+    return v;
+}
+
+template <int STRIDE>
+__device__ __forceinline__ float strided_max(float v)
+{
+    if constexpr (STRIDE <= 1) v = fmaxf(v, dpp_f<DPP_QUAD_XOR1>(v));
+    if constexpr (STRIDE <= 2) v = fmaxf(v, dpp_f<DPP_QUAD_XOR2>(v));
+    if constexpr (STRIDE <= 4) v = fmaxf(v, __shfl_xor(v, 4));
+    if constexpr (STRIDE <= 8) v = fmaxf(v, __shfl_xor(v, 8));
+    if constexpr (STRIDE <= 16) v = max16(v);
+    if constexpr (STRIDE <= 32) v = max32(v);
+    return v;
+}
+
+// Signed byte j of a dword, as float.
+template <int J>
+__device__ __forceinline__ float sbyte_f(int32_t w)
+{
+    return (float)((w << (24 - 8 * J)) >> 24);
+}
+
+}  // namespace qsa

@@ -1,0 +1,155 @@
+"""The C-ABI library (CPU only): it loads, exports every function include/qsa.h declares, and its host-side
+argument checks return the documented status codes. These calls fail validation before any HIP call, so no
+GPU is touched."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import sparse_top_attention_amd as qsa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qsa.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\**\s*(qsa_[a-z0-9_]+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_calls():
+    names = declared_functions()
+    for fn in ["qsa_block_index", "qsa_block_scores", "qsa_topk", "qsa_topk_scratch_bytes", "qsa_attn_chunk",
+               "qsa_attn_merge", "qsa_prompt_attn", "qsa_prompt_scratch_bytes", "qsa_status_str"]:
+        assert fn in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = qsa.lib_handle()
+    for fn in declared_functions():
+        assert hasattr(L, fn), fn
+
+
+def test_no_symbol_from_the_oracle():
+    L = ctypes.CDLL(qsa.LIB_PATH)
+    for fn in ["orc_attn", "orc_topk", "orc_merge", "orc_block_scores"]:
+        assert not hasattr(L, fn)
+
+
+def test_status_strings():
+    for code in range(-6, 1):
+        assert qsa.qsa_status_str(code)
+
+
+D = qsa._Dims
+
+
+def _pool(k=1, ks=1, v=1, vs=1, index=1, cap=1024, n_valid=1024):
+    return qsa._Pool(k, ks, v, vs, index, cap, n_valid)
+
+
+def _parts(max_chunks=8):
+    return qsa._Partials(1, 1, 1, 1, max_chunks)
+
+
+GOOD = D(24, 4, 128, 64)
+
+
+@pytest.mark.parametrize("dims,expect", [
+    (D(24, 4, 96, 64), -3),    # head_dim not supported
+    (D(24, 4, 128, 32), -3),   # block size not 64
+    (D(24, 5, 128, 64), -2),   # q heads not a multiple of KV heads
+    (D(40, 4, 128, 64), -3),   # more than 8 q heads per KV head
+    (D(0, 4, 128, 64), -2),
+])
+def test_dims_validation(dims, expect):
+    L = qsa.lib_handle()
+    p = _pool()
+    assert L.qsa_block_index(ctypes.byref(p), dims, 0, 64, 1, None) == expect
+    assert L.qsa_block_scores(1, 1, 1, ctypes.byref(p), dims, 16, 1, None) == expect
+
+
+def test_block_index_validation():
+    L = qsa.lib_handle()
+    assert L.qsa_block_index(None, GOOD, 0, 64, 1, None) == -1
+    p = _pool()
+    assert L.qsa_block_index(ctypes.byref(p), GOOD, 0, 64, None, None) == -1
+    assert L.qsa_block_index(ctypes.byref(p), GOOD, -1, 64, 1, None) == -5
+    assert L.qsa_block_index(ctypes.byref(p), GOOD, 100, 64, 1, None) == -5
+    assert L.qsa_block_index(ctypes.byref(p), GOOD, 0, 2000, 1, None) == -5
+    assert L.qsa_block_index(ctypes.byref(p), GOOD, 64, 64, 1, None) == 0      # empty range: nothing to do
+    bad = _pool(n_valid=2000)
+    assert L.qsa_block_index(ctypes.byref(bad), GOOD, 0, 64, 1, None) == -5    # n_valid > capacity
+    nok = _pool(k=None)
+    assert L.qsa_block_index(ctypes.byref(nok), GOOD, 0, 64, 1, None) == -1
+
+
+def test_block_scores_validation():
+    L = qsa.lib_handle()
+    p = _pool()
+    assert L.qsa_block_scores(None, 1, 1, ctypes.byref(p), GOOD, 16, 1, None) == -1
+    noidx = _pool(index=None)
+    assert L.qsa_block_scores(1, 1, 1, ctypes.byref(noidx), GOOD, 16, 1, None) == -1
+    assert L.qsa_block_scores(1, 1, 1, ctypes.byref(p), GOOD, 17, 1, None) == -5  # wider than ceil(cap/64)
+    assert L.qsa_block_scores(1, 1, -1, ctypes.byref(p), GOOD, 16, 1, None) == -2
+    assert L.qsa_block_scores(1, 1, 0, ctypes.byref(p), GOOD, 16, 1, None) == 0    # no rows: nothing to do
+
+
+def test_topk_validation():
+    L = qsa.lib_handle()
+    assert L.qsa_topk_scratch_bytes(16, 256, 32) == 0
+    assert L.qsa_topk(None, 1, 16, 8, 1, 1, None, 0, None) == -1
+    assert L.qsa_topk(1, 1, 16, 0, 1, 1, None, 0, None) == -5
+    assert L.qsa_topk(1, 1, 16, 17, 1, 1, None, 0, None) == -5
+    assert L.qsa_topk(1, 1, 20000, 8, 1, 1, None, 0, None) == -3
+    assert L.qsa_topk(1, 0, 16, 8, 1, 1, None, 0, None) == 0
+
+
+def test_chunk_validation():
+    L = qsa.lib_handle()
+    pools = (qsa._Pool * 2)(_pool(), _pool())
+    parts = _parts(8)
+    args = dict(q=1, pos=1, n_rows=4, pools=pools, n_pools=2, row_pool=1, dims=GOOD, ids=1, counts=1, k=32,
+                bpc=1, n_chunks=8, sm=1.0, out=ctypes.byref(parts), stream=None)
+
+    def call(**kw):
+        a = dict(args)
+        a.update(kw)
+        return L.qsa_attn_chunk(a["q"], a["pos"], a["n_rows"], a["pools"], a["n_pools"], a["row_pool"], a["dims"],
+                                a["ids"], a["counts"], a["k"], a["bpc"], a["n_chunks"], a["sm"], a["out"],
+                                a["stream"])
+    assert call(n_chunks=9) == -4                        # partials too small
+    assert call(n_chunks=0) == -5
+    assert call(k=0) == -5
+    assert call(counts=None) == -1
+    assert call(q=None) == -1
+    assert call(n_pools=9) == -3
+    assert call(n_pools=0) == -2
+    assert call(ids=None, bpc=0) == -5
+    bad = (qsa._Pool * 2)(_pool(), _pool(n_valid=5000))
+    assert call(pools=bad) == -5
+    nov = (qsa._Pool * 1)(_pool(v=None))
+    assert call(pools=nov, n_pools=1) == -1
+    noparts = qsa._Partials(1, None, 1, 1, 8)
+    assert call(out=ctypes.byref(noparts)) == -1
+    assert call(n_rows=0) == 0
+
+
+def test_merge_validation():
+    L = qsa.lib_handle()
+    parts = _parts(8)
+    assert L.qsa_attn_merge(ctypes.byref(parts), 4, GOOD, 9, None, 1, None, None) == -4
+    assert L.qsa_attn_merge(None, 4, GOOD, 8, None, 1, None, None) == -1
+    assert L.qsa_attn_merge(ctypes.byref(parts), 4, GOOD, 8, None, None, None, None) == -1
+    assert L.qsa_attn_merge(ctypes.byref(parts), 0, GOOD, 8, None, 1, None, None) == 0
+
+
+def test_prompt_validation():
+    L = qsa.lib_handle()
+    p = _pool()
+    assert L.qsa_prompt_attn(None, 16, 0, ctypes.byref(p), GOOD, 1.0, 1, None, 0, None) == -1
+    assert L.qsa_prompt_attn(1, 16, -1, ctypes.byref(p), GOOD, 1.0, 1, None, 0, None) == -5
+    assert L.qsa_prompt_attn(1, 16, 0, ctypes.byref(p), D(24, 4, 96, 64), 1.0, 1, None, 0, None) == -3
