@@ -1,0 +1,263 @@
+"""Benchmark of the QSA decode layer (block scores -> radix top-k -> split-K chunk attention -> LSE merge) on one
+MI355X, plus the FP64 oracle timed on the host cores as a reported CPU baseline.
+
+A step is one decode layer over one batch: the verify window (4 queries at the last 4 positions of 16,384 valid
+cells in a 200,000-cell int8 pool, 24 q heads over 4 KV heads, head_dim 128, top-32 blocks of 64 cells per
+(query, KV head)). The block index is built beforehand (it is updated when cells are appended, not per query).
+Inputs are resident in HBM before timing. Steps rotate over enough identical pool copies that the bytes they touch
+exceed the 256 MB Infinity Cache, so K/V come from HBM; the layers are replayed from one captured HIP graph.
+
+Prints one JSON line. `value` = algorithmic bytes of a layer / time per layer (GB/s); `roofline` reports the chunk
+kernel (the dominant one): its algorithmic bytes per launch / its average launch duration, timed with HIP events
+around graphs of back-to-back launches on the stream the kernels run on.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+BLOCK = 64
+KV_BYTES_PER_CELL_HEAD = 128 + 128 + 4 + 4     # K and V codes plus two fp32 scales at head_dim 128
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1280)
+    ap.add_argument("--warmup", type=int, default=128)
+    ap.add_argument("--workload", default="verify_window",
+                    choices=["tiny_decode", "verify_window", "drafter"])
+    ap.add_argument("--copies", type=int, default=64, help="pool copies the steps rotate over")
+    ap.add_argument("--chunks", type=int, default=0, help="split count (0 = the library default for the shape)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    return ap.parse_args()
+
+
+def union_cells(ids, counts, pos, n_valid, n_kv):
+    """Number of distinct visible (KV head, cell) pairs the selected blocks of all rows touch."""
+    n = 0
+    for g in range(n_kv):
+        cells = set()
+        for i in range(ids.shape[0]):
+            lim = min(int(pos[i]), n_valid - 1)
+            for b in ids[i, g, :counts[i, g]]:
+                if b < 0:
+                    continue
+                lo = int(b) * BLOCK
+                hi = min(lo + BLOCK - 1, lim)
+                if hi >= lo:
+                    cells.update(range(lo, hi + 1))
+        n += len(cells)
+    return n
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: the QSA path here is single-GPU (sharding by KV head, slot or sequence is "
+              "described in the design notes, not built); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import sparse_top_attention_amd as qsa
+    import synth
+
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    w = synth.workload(args.workload, poison=False)
+    pool_np = w.pools[0]
+    dims = qsa.Dims(w.n_q_heads, w.n_kv_heads, w.head_dim)
+    n_rows, n_kv, D = w.q.shape[0], w.n_kv_heads, w.head_dim
+    dense = w.topk == 0
+    nb = -(-pool_np.n_valid // BLOCK)
+    S = args.chunks or (w.n_chunks if dense else 16)
+
+    def t(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    # ---- inputs resident in HBM: one pool, then identical copies to rotate over
+    base = qsa.Pool(t(pool_np.k), t(pool_np.ks), t(pool_np.v), t(pool_np.vs), pool_np.n_valid)
+    base.index = torch.zeros(n_kv, -(-pool_np.capacity // BLOCK), D, dtype=torch.float32, device=dev)
+    qsa.qsa_block_index(base, dims, 0, pool_np.n_valid, base.index)
+    copies = [base]
+    for _ in range(args.copies - 1):
+        c = qsa.Pool(base.k.clone(), base.k_scale.clone(), base.v.clone(), base.v_scale.clone(), base.n_valid,
+                     base.index.clone())
+        copies.append(c)
+    q = t(w.q)
+    pos = t(w.pos)
+    scores = torch.empty(n_rows, n_kv, max(nb, 1), dtype=torch.float32, device=dev)
+    k = max(w.topk, 1)
+    ids = torch.empty(n_rows, n_kv, k, dtype=torch.int32, device=dev)
+    counts = torch.empty(n_rows, n_kv, dtype=torch.int32, device=dev)
+    part = qsa.Partials.empty_like_shape(n_rows, w.n_q_heads, S, D, device=dev)
+    out = torch.empty(n_rows, w.n_q_heads, D, dtype=torch.float32, device=dev)
+    lse = torch.empty(n_rows, w.n_q_heads, dtype=torch.float32, device=dev)
+    n_active = t(np.full(n_rows, w.n_active, np.int32)) if dense else None
+    torch.cuda.synchronize()
+
+    def select(p):
+        qsa.qsa_block_scores(q, pos, p, dims, nb, scores)
+        qsa.qsa_topk(scores, w.topk, ids, counts)
+
+    def attend(p):
+        if dense:
+            qsa.qsa_attn_chunk(q, pos, [p], dims, part, S, w.sm_scale, blocks_per_chunk=w.blocks_per_chunk)
+        else:
+            qsa.qsa_attn_chunk(q, pos, [p], dims, part, S, w.sm_scale, ids=ids, counts=counts)
+
+    def merge():
+        qsa.qsa_attn_merge(part, dims, S, out, lse, n_active=n_active)
+
+    def layer(p):
+        if not dense:
+            select(p)
+        attend(p)
+        merge()
+
+    stream = torch.cuda.Stream()
+
+    def capture(fn_per_copy, n):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(stream):
+            for c in range(n):               # eager pass so every kernel is loaded before capture
+                fn_per_copy(copies[c % len(copies)])
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=stream):
+            for c in range(n):
+                fn_per_copy(copies[c % len(copies)])
+        torch.cuda.synchronize()
+        return g
+
+    L = len(copies)
+    g_full = capture(layer, L)
+    rem = args.steps % L
+    g_rem = capture(layer, rem) if rem else None
+
+    def run_steps(n_steps):
+        for _ in range(n_steps // L):
+            g_full.replay()
+        if n_steps % L:
+            (g_rem if n_steps % L == rem else capture(layer, n_steps % L)).replay()
+
+    with torch.cuda.stream(stream):
+        run_steps(args.warmup)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        run_steps(args.steps)
+        e1.record(stream)
+        torch.cuda.synchronize()
+    ms_total = e0.elapsed_time(e1)
+    ms_per_step = ms_total / args.steps
+
+    # ---- per-kernel average launch durations: graphs of L back-to-back launches of one kernel, one per copy
+    def kernel_avg_us(fn_per_copy, reps=20):
+        g = capture(fn_per_copy, L)
+        with torch.cuda.stream(stream):
+            g.replay()
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for _ in range(reps):
+                g.replay()
+            b.record(stream)
+            torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / (reps * L)
+
+    breakdown = {}
+    if not dense:
+        breakdown["block_scores+topk"] = kernel_avg_us(select)
+    breakdown["attn_chunk"] = kernel_avg_us(attend)
+    breakdown["attn_merge"] = kernel_avg_us(lambda p: merge())
+
+    # ---- algorithmic bytes
+    ids_h, counts_h = ids.cpu().numpy(), counts.cpu().numpy()
+    if dense:
+        vis = sum(min(pool_np.n_valid, int(p) + 1) for p in w.pos) * n_kv   # one row here
+        kv_cells = vis
+    else:
+        kv_cells = union_cells(ids_h, counts_h, w.pos, pool_np.n_valid, n_kv)
+    kv_bytes = kv_cells * KV_BYTES_PER_CELL_HEAD
+    q_bytes = w.q.nbytes
+    out_bytes = n_rows * w.n_q_heads * D * 4
+    index_bytes = 0 if dense else n_kv * nb * D * 4
+    layer_bytes = index_bytes + q_bytes + kv_bytes + out_bytes
+    chunk_bytes = kv_bytes + q_bytes                       # what the chunk kernel must read, partials not counted
+    chunk_gbs = chunk_bytes / (breakdown["attn_chunk"] * 1e-6) / 1e9
+    value = layer_bytes / (ms_per_step * 1e-3) / 1e9
+
+    result = {
+        "metric": "decode QSA us/layer + HBM GB/s; prompt-chunk ms + int8 MFMA % of peak",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "us_per_layer": round(ms_per_step * 1e3, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "rows": n_rows, "q_heads": w.n_q_heads, "kv_heads": n_kv,
+                   "head_dim": D, "n_valid": pool_np.n_valid, "capacity": pool_np.capacity,
+                   "topk_blocks": w.topk, "chunks": S, "pool_copies": L, "kv_int8": True,
+                   "layer_bytes": int(layer_bytes), "kv_union_cells": int(kv_cells)},
+        "kernels_us": {k2: round(v2, 3) for k2, v2 in breakdown.items()},
+        "roofline": {"bound": "hbm", "kernel": "attn_chunk", "achieved": round(chunk_gbs, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(chunk_gbs / HBM_PEAK_GBS, 4),
+                     "bytes_per_launch": int(chunk_bytes), "traffic": None},
+        "cpu_baseline": None,
+    }
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, layer_bytes, args.cpu_seconds)
+    print(json.dumps(result))
+
+
+def cpu_baseline(w, layer_bytes, budget_s):
+    """The FP64 oracle (single thread) on the same workload: scores, top-k and attention of one layer, repeated
+    for about budget_s seconds; reported in the bench's unit (algorithmic bytes per layer / time per layer)."""
+    import oracle
+    pool = w.pools[0]
+    n_kv = w.n_kv_heads
+    nb = -(-pool.n_valid // BLOCK)
+    r = oracle.block_index(pool)          # append-time step, outside the timed sample as on the GPU
+    dense = w.topk == 0
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        if dense:
+            oracle.attn(w.q, w.pos, pool, n_kv)
+        else:
+            s = oracle.block_scores(w.q, w.pos, r, n_kv, pool.n_valid, nb)
+            ids, cnt = oracle.topk(s.reshape(-1, nb), w.topk)
+            oracle.attn(w.q, w.pos, pool, n_kv, ids=ids.reshape(len(w.pos), n_kv, -1),
+                        counts=cnt.reshape(len(w.pos), n_kv))
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    per_layer = el / n
+    return {"value": round(layer_bytes / per_layer / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n} full {w.name} layers (scores, top-k, attention; FP64, one thread) in {el:.1f} s, "
+                      f"{per_layer * 1e3:.1f} ms per layer", "host_cpus": os.cpu_count()}
+
+
+if __name__ == "__main__":
+    main()

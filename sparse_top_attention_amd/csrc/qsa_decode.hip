@@ -98,27 +98,39 @@ __global__ __launch_bounds__(64) void block_scores_kernel(const float *__restric
             for (int e = 0; e < 8; e++) rv[st][e] = 0.f;
         }
     }
-    for (int32_t i = 0; i < n_rows; i++) {
-        float qt[8];
+    for (int32_t i0 = 0; i0 < n_rows; i0 += 8) {
+        const int nr = min(8, n_rows - i0);
+        float qt[8][8];
 #pragma unroll
-        for (int e = 0; e < 8; e++) qt[e] = 0.f;
-        for (int32_t h = g * G; h < (g + 1) * G; h++) {
-            const float4 *src = reinterpret_cast<const float4 *>(q + ((int64_t)i * n_qh + h) * D + 8 * s);
-            const float4 u = src[0], w = src[1];
-            qt[0] += u.x; qt[1] += u.y; qt[2] += u.z; qt[3] += u.w;
-            qt[4] += w.x; qt[5] += w.y; qt[6] += w.z; qt[7] += w.w;
+        for (int rr = 0; rr < 8; rr++) {
+#pragma unroll
+            for (int e = 0; e < 8; e++) qt[rr][e] = 0.f;
+            if (rr < nr) {
+                for (int32_t h = g * G; h < (g + 1) * G; h++) {
+                    const float4 *src =
+                        reinterpret_cast<const float4 *>(q + ((int64_t)(i0 + rr) * n_qh + h) * D + 8 * s);
+                    const float4 u = src[0], w = src[1];
+                    qt[rr][0] += u.x; qt[rr][1] += u.y; qt[rr][2] += u.z; qt[rr][3] += u.w;
+                    qt[rr][4] += w.x; qt[rr][5] += w.y; qt[rr][6] += w.z; qt[rr][7] += w.w;
+                }
+            }
         }
-        const int32_t p = pos[i];
 #pragma unroll
-        for (int st = 0; st < NSTEP; st++) {
-            float dot = 0.f;
+        for (int rr = 0; rr < 8; rr++) {
+            if (rr >= nr) break;
+            const int32_t i = i0 + rr;
+            const int32_t p = pos[i];
 #pragma unroll
-            for (int e = 0; e < 8; e++) dot = fmaf(qt[e], rv[st][e], dot);
-            dot = group_sum<LPB>(dot);
-            const int32_t b = bidx[st];
-            const int64_t first = (int64_t)b * QSA_BLOCK;
-            if (s == 0 && b < n_blocks)
-                scores[((int64_t)i * n_kv + g) * n_blocks + b] = (first <= p && first < n_valid) ? dot : -INFINITY;
+            for (int st = 0; st < NSTEP; st++) {
+                float dot = 0.f;
+#pragma unroll
+                for (int e = 0; e < 8; e++) dot = fmaf(qt[rr][e], rv[st][e], dot);
+                dot = group_sum<LPB>(dot);
+                const int32_t b = bidx[st];
+                const int64_t first = (int64_t)b * QSA_BLOCK;
+                if (s == 0 && b < n_blocks)
+                    scores[((int64_t)i * n_kv + g) * n_blocks + b] = (first <= p && first < n_valid) ? dot : -INFINITY;
+            }
         }
     }
 }
@@ -147,23 +159,30 @@ struct ChunkArgs {
     float qscale;  // sm_scale * log2(e): logits are kept in base-2 units inside the kernel
 };
 
-// One wave per (chunk j, KV head g x head subset, row i). Each lane owns one cell slot r (cells r, r + CPS, ...
-// of every block) and one 16-dim slice s, and keeps a running max / sum / output per q head for its cell slot;
-// the cell slots are merged with a log-sum-exp fold across lanes at the end of the chunk.
+// One workgroup of CW waves per (chunk j, KV head g x head subset, row i); wave w takes blocks w, w + CW, ... of
+// the chunk's run. In a wave each lane owns one cell slot r (cells r, r + CPS, ... of a block) and one 16-dim
+// slice s. Per block: all K/V loads are issued first (addresses clamped to a visible cell, invisible cells masked
+// afterwards), then q.k for HPW heads, a wave-wide block max per head, then p.v. The running max is shared by
+// the whole wave, so the cell slots are folded with plain sums at the end; the CW waves are combined through LDS
+// with a log-sum-exp rescale.
+constexpr int CW = 4;
+
 template <int D, int HPW>
-__global__ __launch_bounds__(64) void attn_chunk_kernel(const ChunkArgs a)
+__global__ __launch_bounds__(64 * CW) void attn_chunk_kernel(const ChunkArgs a)
 {
     constexpr int LPC = D / 16, CPS = 64 / LPC, STEPS = QSA_BLOCK / CPS, NG = D / QSA_GROUP;
-    const int lane = threadIdx.x, r = lane / LPC, s = lane % LPC, grp = (16 * s) / QSA_GROUP;
+    __shared__ float sm[CW][HPW], sl[CW][HPW];
+    __shared__ float so[CW][HPW][D];
+    const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
+    const int r = lane / LPC, s = lane % LPC, grp = (16 * s) / QSA_GROUP;
     const int32_t j = blockIdx.x, i = blockIdx.z;
     const int32_t g = blockIdx.y / a.n_hsub, h0 = g * a.G + (blockIdx.y % a.n_hsub) * HPW;
 
     const int32_t pidx = a.row_pool ? a.row_pool[i] : 0;
     const bool pool_ok = pidx >= 0 && pidx < a.n_pools;
-    PoolArg P = a.pools[pool_ok ? pidx : 0];
+    const PoolArg P = a.pools[pool_ok ? pidx : 0];
     const int32_t limit = pool_ok ? min(P.n_valid - 1, a.pos[i]) : -1;  // visible cells: c <= limit
 
-    // this chunk's block run
     int32_t n_blk, first;
     const int32_t *blist = nullptr;
     if (a.ids) {
@@ -200,100 +219,126 @@ __global__ __launch_bounds__(64) void attn_chunk_kernel(const ChunkArgs a)
         for (int e = 0; e < 16; e++) o[h][e] = 0.f;
     }
 
-    for (int32_t t = 0; t < n_blk; t++) {
+    const int8_t *kbase = P.k + (int64_t)g * P.capacity * D + 16 * s;
+    const int8_t *vbase = P.v + (int64_t)g * P.capacity * D + 16 * s;
+    const float *ksbase = P.ks + (int64_t)g * P.capacity * NG + grp;
+    const float *vsbase = P.vs + (int64_t)g * P.capacity * NG + grp;
+
+    for (int32_t t = wave; t < n_blk; t += CW) {
         const int32_t b = blist ? blist[first + t] : first + t;
         if (b < 0 || (int64_t)b * QSA_BLOCK > limit) continue;  // negative id, or no visible valid cell
         const int32_t cb = b * QSA_BLOCK;
 
-        // q . k for this lane's cells of the block
+        int4 kw[STEPS], vw[STEPS];
+        float ksc[STEPS], vsc[STEPS];
+#pragma unroll
+        for (int st = 0; st < STEPS; st++) {
+            const int32_t c = min(cb + st * CPS + r, limit);
+            kw[st] = *reinterpret_cast<const int4 *>(kbase + (int64_t)c * D);
+            ksc[st] = ksbase[(int64_t)c * NG];
+        }
+#pragma unroll
+        for (int st = 0; st < STEPS; st++) {
+            const int32_t c = min(cb + st * CPS + r, limit);
+            vw[st] = *reinterpret_cast<const int4 *>(vbase + (int64_t)c * D);
+            vsc[st] = vsbase[(int64_t)c * NG];
+        }
+
         float lg[STEPS][HPW];
 #pragma unroll
         for (int st = 0; st < STEPS; st++) {
-            const int32_t c = cb + st * CPS + r;
-            const bool vis = c <= limit;
-            int4 w = make_int4(0, 0, 0, 0);
-            float sc = 0.f;
-            if (vis) {
-                const int64_t cell = (int64_t)g * P.capacity + c;
-                w = *reinterpret_cast<const int4 *>(P.k + cell * D + 16 * s);
-                sc = P.ks[cell * NG + grp];
-            }
+            const bool vis = cb + st * CPS + r <= limit;
             float x[16];
-            unpack16(w, x);
+            unpack16(kw[st], x);
 #pragma unroll
             for (int h = 0; h < HPW; h++) {
                 float dot = 0.f;
 #pragma unroll
                 for (int e = 0; e < 16; e++) dot = fmaf(qv[h][e], x[e], dot);
-                dot = group_sum<LPC>(dot * sc);
+                dot = group_sum<LPC>(dot * ksc[st]);
                 lg[st][h] = vis ? dot : -INFINITY;
             }
         }
-        // running max per (cell slot, head); rescale what was accumulated before
 #pragma unroll
         for (int h = 0; h < HPW; h++) {
             float mb = lg[0][h];
 #pragma unroll
             for (int st = 1; st < STEPS; st++) mb = fmaxf(mb, lg[st][h]);
+            mb = strided_max<LPC>(mb);            // the block holds a visible cell, so mb is finite
             const float mnew = fmaxf(mrun[h], mb);
-            const float alpha = (mnew == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(mrun[h] - mnew);
+            const float alpha = __builtin_amdgcn_exp2f(mrun[h] - mnew);  // 0 on the first block
             mrun[h] = mnew;
             lrun[h] *= alpha;
 #pragma unroll
             for (int e = 0; e < 16; e++) o[h][e] *= alpha;
         }
-        // p . v
 #pragma unroll
         for (int st = 0; st < STEPS; st++) {
-            const int32_t c = cb + st * CPS + r;
-            const bool vis = c <= limit;
-            int4 w = make_int4(0, 0, 0, 0);
-            float sc = 0.f;
-            if (vis) {
-                const int64_t cell = (int64_t)g * P.capacity + c;
-                w = *reinterpret_cast<const int4 *>(P.v + cell * D + 16 * s);
-                sc = P.vs[cell * NG + grp];
-            }
             float x[16];
-            unpack16(w, x);
+            unpack16(vw[st], x);
 #pragma unroll
             for (int h = 0; h < HPW; h++) {
-                const float p = vis ? __builtin_amdgcn_exp2f(lg[st][h] - mrun[h]) : 0.f;
+                const float p = __builtin_amdgcn_exp2f(lg[st][h] - mrun[h]);   // masked cells: 2^-inf = 0
                 lrun[h] += p;
-                const float wgt = p * sc;
+                const float wgt = p * vsc[st];
 #pragma unroll
                 for (int e = 0; e < 16; e++) o[h][e] = fmaf(wgt, x[e], o[h][e]);
             }
         }
     }
 
-    // fold the CPS cell slots (lanes LPC apart) into one partial per head
-    float mtot[HPW];
+    // fold the cell slots (lanes LPC apart share a slice) and hand the wave's partial to LDS
 #pragma unroll
     for (int h = 0; h < HPW; h++) {
-        const float M = strided_max<LPC>(mrun[h]);
-        mtot[h] = M;
-        const float sc = (mrun[h] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mrun[h] - M);
-        lrun[h] = strided_sum<LPC>(lrun[h] * sc);
+        lrun[h] = strided_sum<LPC>(lrun[h]);
 #pragma unroll
-        for (int e = 0; e < 16; e++) o[h][e] = strided_sum<LPC>(o[h][e] * sc);
+        for (int e = 0; e < 16; e++) o[h][e] = strided_sum<LPC>(o[h][e]);
+    }
+    if (lane == 0) {
+#pragma unroll
+        for (int h = 0; h < HPW; h++) {
+            sm[wave][h] = mrun[h];
+            sl[wave][h] = lrun[h];
+        }
     }
 #pragma unroll
-    for (int h = 0; h < HPW; h++) {
-        const int64_t idx = ((int64_t)i * a.n_qh + h0 + h) * a.max_chunks + j;
-        const bool empty = mtot[h] == -INFINITY;
-        if (lane == 0) {
-            a.m_out[idx] = empty ? -INFINITY : mtot[h] * LN2;
-            a.l_out[idx] = empty ? 0.f : lrun[h];
-            a.empty_out[idx] = empty ? 1 : 0;
-        }
+    for (int h = 0; h < HPW; h++)
         if (r == h % CPS) {
-            float4 *dst = reinterpret_cast<float4 *>(a.o_out + idx * D + 16 * s);
 #pragma unroll
-            for (int jj = 0; jj < 4; jj++)
-                dst[jj] = empty ? make_float4(0.f, 0.f, 0.f, 0.f)
-                                : make_float4(o[h][4 * jj], o[h][4 * jj + 1], o[h][4 * jj + 2], o[h][4 * jj + 3]);
+            for (int e = 0; e < 16; e++) so[wave][h][16 * s + e] = o[h][e];
         }
+    __syncthreads();
+
+    // combine the CW waves: M = max m_w, out = sum e^(m_w - M) o_w (waves without a cell have m_w = -inf)
+    for (int idx = tid; idx < HPW * D; idx += 64 * CW) {
+        const int h = idx / D, d = idx % D;
+        float M = sm[0][h];
+#pragma unroll
+        for (int w = 1; w < CW; w++) M = fmaxf(M, sm[w][h]);
+        float num = 0.f;
+        if (M != -INFINITY) {
+#pragma unroll
+            for (int w = 0; w < CW; w++)
+                if (sm[w][h] != -INFINITY) num = fmaf(__builtin_amdgcn_exp2f(sm[w][h] - M), so[w][h][d], num);
+        }
+        a.o_out[(((int64_t)i * a.n_qh + h0 + h) * a.max_chunks + j) * D + d] = num;
+    }
+    if (tid < HPW) {
+        const int h = tid;
+        float M = sm[0][h];
+#pragma unroll
+        for (int w = 1; w < CW; w++) M = fmaxf(M, sm[w][h]);
+        float L = 0.f;
+        if (M != -INFINITY) {
+#pragma unroll
+            for (int w = 0; w < CW; w++)
+                if (sm[w][h] != -INFINITY) L = fmaf(__builtin_amdgcn_exp2f(sm[w][h] - M), sl[w][h], L);
+        }
+        const int64_t idx = ((int64_t)i * a.n_qh + h0 + h) * a.max_chunks + j;
+        const bool empty = M == -INFINITY;
+        a.m_out[idx] = empty ? -INFINITY : M * LN2;
+        a.l_out[idx] = L;
+        a.empty_out[idx] = empty ? 1 : 0;
     }
 }
 
@@ -412,20 +457,25 @@ namespace {
 template <int D>
 void launch_chunk(int hpw, dim3 grid, hipStream_t s, const ChunkArgs &a)
 {
-    switch (hpw) {
-    case 1: attn_chunk_kernel<D, 1><<<grid, 64, 0, s>>>(a); break;
-    case 2: attn_chunk_kernel<D, 2><<<grid, 64, 0, s>>>(a); break;
-    case 3: attn_chunk_kernel<D, 3><<<grid, 64, 0, s>>>(a); break;
-    case 4: attn_chunk_kernel<D, 4><<<grid, 64, 0, s>>>(a); break;
-    case 5: attn_chunk_kernel<D, 5><<<grid, 64, 0, s>>>(a); break;
-    default: attn_chunk_kernel<D, 6><<<grid, 64, 0, s>>>(a); break;
+    // only the head counts heads_per_wave can pick for this head dim are instantiated
+    if constexpr (D == 256) {
+        attn_chunk_kernel<D, 1><<<grid, 64 * CW, 0, s>>>(a);
+    } else {
+        switch (hpw) {
+        case 1: attn_chunk_kernel<D, 1><<<grid, 64 * CW, 0, s>>>(a); break;
+        case 2: attn_chunk_kernel<D, 2><<<grid, 64 * CW, 0, s>>>(a); break;
+        case 3: attn_chunk_kernel<D, 3><<<grid, 64 * CW, 0, s>>>(a); break;
+        default:
+            if constexpr (D == 64) attn_chunk_kernel<D, 4><<<grid, 64 * CW, 0, s>>>(a);
+            break;
+        }
     }
 }
 
-// q heads handled by one wave: the largest divisor of G that is at most 6 (fewer for wide heads).
+// q heads handled by one wave: the largest divisor of G within the register budget of the head dim.
 int heads_per_wave(int G, int D)
 {
-    const int cap = D == 256 ? 3 : 6;
+    const int cap = D == 64 ? 4 : (D == 128 ? 3 : 1);
     for (int h = cap; h >= 1; h--)
         if (G % h == 0) return h;
     return 1;

@@ -48,6 +48,7 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ sco
     __shared__ uint32_t hist[256];
     __shared__ uint32_t sh_wave[4];
     __shared__ uint32_t sh_digit, sh_remaining;
+    __shared__ bool sh_whole;
     const int tid = threadIdx.x;
     const int64_t row = blockIdx.x;
     const float *src = scores + row * width;
@@ -72,6 +73,7 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ sco
         T = 0u;           // every eligible key is above it
     } else {
         uint32_t prefix = 0, mask = 0, remaining = kk;
+        bool done_early = false;
 #pragma unroll 1
         for (int pass = 0; pass < 4; pass++) {
             const int shift = 24 - 8 * pass;
@@ -88,15 +90,26 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ sco
             if (cum >= remaining && cum - v < remaining) {
                 sh_digit = 255u - (uint32_t)tid;
                 sh_remaining = remaining - (cum - v);
+                sh_whole = (remaining - (cum - v)) == v;   // the whole bin is taken
             }
             __syncthreads();
             prefix |= sh_digit << shift;
             mask |= 255u << shift;
             remaining = sh_remaining;
+            const bool whole = sh_whole;
             __syncthreads();
+            if (whole) {  // every key with this prefix is kept: keep all keys >= prefix, no tie to break
+                done_early = true;
+                break;
+            }
         }
-        T = prefix;
-        take_eq = remaining;
+        if (done_early) {
+            T = prefix == 0u ? 0u : prefix - 1u;
+            take_eq = 0;
+        } else {
+            T = prefix;
+            take_eq = remaining;
+        }
     }
 
     // compaction in index order: keys > T, then the first take_eq keys == T
