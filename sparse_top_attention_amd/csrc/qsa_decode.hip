@@ -528,6 +528,21 @@ extern "C" qsa_status qsa_attn_chunk(const float *q, const int32_t *pos, int32_t
     return launch_status();
 }
 
+qsa_status qsa::merge_launch(const float *m, const float *l, const float *o, const uint8_t *empty, int32_t max_chunks,
+                             int32_t n_chunks, const int32_t *n_active, int32_t n_rows, int32_t n_qh,
+                             int32_t head_dim, float *out, float *lse, hipStream_t s)
+{
+    dim3 grid((uint32_t)n_rows * (uint32_t)n_qh);
+#define QSA_MERGE(DD) attn_merge_kernel<DD><<<grid, 256, 0, s>>>(m, l, o, empty, max_chunks, n_chunks, n_active, n_qh, out, lse)
+    switch (head_dim) {
+    case 64: QSA_MERGE(64); break;
+    case 128: QSA_MERGE(128); break;
+    default: QSA_MERGE(256); break;
+    }
+#undef QSA_MERGE
+    return launch_status();
+}
+
 extern "C" qsa_status qsa_attn_merge(const qsa_partials *in, int32_t n_rows, qsa_dims dims, int32_t n_chunks,
                                      const int32_t *n_active, float *out, float *lse, qsa_stream_t stream)
 {
@@ -538,16 +553,8 @@ extern "C" qsa_status qsa_attn_merge(const qsa_partials *in, int32_t n_rows, qsa
     if (n_rows < 0 || n_chunks < 0) return QSA_ERR_SHAPE;
     if (n_chunks > in->max_chunks) return QSA_ERR_SCRATCH;
     if (n_rows == 0) return QSA_OK;
-    dim3 grid((uint32_t)n_rows * (uint32_t)dims.n_q_heads);
-    hipStream_t s = (hipStream_t)stream;
-#define QSA_MERGE(DD) attn_merge_kernel<DD><<<grid, 256, 0, s>>>(in->m, in->l, in->o, in->empty, in->max_chunks, n_chunks, n_active, dims.n_q_heads, out, lse)
-    switch (dims.head_dim) {
-    case 64: QSA_MERGE(64); break;
-    case 128: QSA_MERGE(128); break;
-    default: QSA_MERGE(256); break;
-    }
-#undef QSA_MERGE
-    return launch_status();
+    return merge_launch(in->m, in->l, in->o, in->empty, in->max_chunks, n_chunks, n_active, n_rows, dims.n_q_heads,
+                        dims.head_dim, out, lse, (hipStream_t)stream);
 }
 
 extern "C" const char *qsa_status_str(qsa_status status)

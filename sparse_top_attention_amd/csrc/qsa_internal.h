@@ -57,6 +57,11 @@ struct PoolArg {
     int32_t n_valid;
 };
 
+// Launches the log-sum-exp merge of chunk partials laid out [n_rows][n_qh][max_chunks] (+[head_dim] for o).
+qsa_status merge_launch(const float *m, const float *l, const float *o, const uint8_t *empty, int32_t max_chunks,
+                        int32_t n_chunks, const int32_t *n_active, int32_t n_rows, int32_t n_qh, int32_t head_dim,
+                        float *out, float *lse, hipStream_t stream);
+
 // ---------------------------------------------------------------------------------------------- device side
 // DPP controls (gfx9 encoding).
 constexpr int DPP_QUAD_XOR1 = 0xB1;     // quad_perm [1,0,3,2]

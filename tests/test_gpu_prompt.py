@@ -1,0 +1,113 @@
+"""Parity of the int8-MFMA prompt-chunk attention against the FP64 oracle (dense causal attention), through the
+C ABI. Bar: max relative error 1e-5 per (query, head) row. Pools carry poison past n_valid."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_top_attention_amd as qsa
+import synth
+from gpu_util import dev, rel_err_rows, to_device
+
+pytestmark = pytest.mark.gpu
+TOL = 1e-5
+
+
+def run_prompt(q, pos0, p_dev, dims, sm_scale=1.0):
+    n_q = q.shape[0]
+    nbytes = qsa.qsa_prompt_scratch_bytes(n_q, dims)
+    scratch = torch.empty(max(nbytes, 1), dtype=torch.uint8, device="cuda")
+    out = torch.full((n_q, dims.n_q_heads, dims.head_dim), float("nan"), dtype=torch.float32, device="cuda")
+    qsa.qsa_prompt_attn(dev(q), pos0, p_dev, dims, out, sm_scale=sm_scale, scratch=scratch)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+@pytest.mark.parametrize("n_kv,G,n_q,pos0,n_valid,cap", [
+    (4, 6, 70, 300, 400, 420),       # 24/4 heads, ragged tile tails, several workgroups
+    (2, 6, 11, 0, 700, 700),         # the first query sees one cell
+    (4, 6, 40, 380, 400, 450),       # queries past n_valid see every valid cell
+    (1, 1, 130, 500, 640, 640),
+    (2, 2, 33, 64, 97, 128),
+    (2, 8, 50, 1000, 1049, 1100),
+])
+def test_prompt_small(n_kv, G, n_q, pos0, n_valid, cap):
+    pool = synth.random_pool(300 + n_q, n_kv, cap, n_valid, 128)
+    q = synth.random_q(301 + n_q, n_q, n_kv * G, 128)
+    dims = qsa.Dims(n_kv * G, n_kv, 128)
+    got = run_prompt(q, pos0, to_device(pool), dims)
+    pos = (pos0 + np.arange(n_q)).astype(np.int32)
+    ref, _ = oracle.attn(q, pos, pool, n_kv)
+    assert np.all(np.isfinite(got))
+    assert rel_err_rows(got, ref).max() <= TOL
+
+
+def test_prompt_sm_scale_and_zero_query():
+    pool = synth.random_pool(311, 2, 300, 260, 128)
+    q = synth.random_q(312, 20, 12, 128)
+    q[3] = 0.0                                            # all-zero rows: uniform weights
+    dims = qsa.Dims(12, 2, 128)
+    got = run_prompt(q, 230, to_device(pool), dims, sm_scale=0.37)
+    pos = (230 + np.arange(20)).astype(np.int32)
+    ref, _ = oracle.attn(q, pos, pool, 2, sm_scale=0.37)
+    assert rel_err_rows(got, ref).max() <= TOL
+
+
+def test_prompt_single_chunk_path():
+    """8 KV heads x 4,096 queries: enough workgroups that the kernel writes the output without split chunks."""
+    n_kv, G, n_q, pos0, n_valid = 8, 1, 4096, 100, 4200
+    dims = qsa.Dims(n_kv * G, n_kv, 128)
+    pool = synth.random_pool(321, n_kv, n_valid, n_valid, 128)
+    q = synth.random_q(322, n_q, n_kv * G, 128)
+    got = run_prompt(q, pos0, to_device(pool), dims)
+    assert np.all(np.isfinite(got))
+    pos = (pos0 + np.arange(n_q)).astype(np.int32)
+    rng = np.random.default_rng(5)
+    for i in list(rng.integers(0, n_q, 10)) + [0, n_q - 1]:
+        for h in (0, 7):
+            ref, _ = oracle.attn_one(q, pos, int(i), h, pool, n_kv)
+            assert rel_err_rows(got[i, h][None], ref[None]).max() <= TOL, (i, h)
+
+
+def test_prompt_chunk_full_size_sampled():
+    """The 2,048-query prompt chunk at the end of a 32,768-cell context, checked on sampled rows."""
+    w = synth.workload("prompt_chunk")
+    pool = w.pools[0]
+    dims = qsa.Dims(w.n_q_heads, w.n_kv_heads, w.head_dim)
+    got = run_prompt(w.q, w.pos0, to_device(pool), dims)
+    assert np.all(np.isfinite(got))
+    rng = np.random.default_rng(7)
+    picks = [(0, 0), (1, 23), (63, 5), (64, 6), (1023, 11), (2047, 17), (2047, 0)]
+    picks += [(int(i), int(h)) for i, h in zip(rng.integers(0, 2048, 8), rng.integers(0, 24, 8))]
+    for i, h in picks:
+        ref, _ = oracle.attn_one(w.q, w.pos, i, h, pool, w.n_kv_heads)
+        assert rel_err_rows(got[i, h][None], ref[None]).max() <= TOL, (i, h)
+
+
+def test_prompt_last_row_equals_dense_decode():
+    """The prompt's last query is an ordinary dense decode over the whole context: compare it with the chunk
+    attention and merge run densely over the same pool."""
+    w = synth.workload("prompt_chunk", n_valid=4096, cap=4096, rows=256)
+    pool = w.pools[0]
+    dims = qsa.Dims(w.n_q_heads, w.n_kv_heads, w.head_dim)
+    p = to_device(pool)
+    got = run_prompt(w.q, w.pos0, p, dims)
+    q_last = dev(w.q[-1:])
+    pos_last = dev(w.pos[-1:])
+    part = qsa.Partials.empty_like_shape(1, w.n_q_heads, 64, 128)
+    qsa.qsa_attn_chunk(q_last, pos_last, [p], dims, part, 64, 1.0, blocks_per_chunk=1)
+    out = torch.empty(1, w.n_q_heads, 128, dtype=torch.float32, device="cuda")
+    qsa.qsa_attn_merge(part, dims, 64, out)
+    torch.cuda.synchronize()
+    assert rel_err_rows(got[-1:], out.cpu().numpy()).max() <= 2 * TOL
+
+
+def test_prompt_scratch_too_small_is_rejected():
+    pool = synth.random_pool(331, 2, 300, 260, 128)
+    dims = qsa.Dims(12, 2, 128)
+    n = qsa.qsa_prompt_scratch_bytes(20, dims)
+    scratch = torch.empty(n - 1, dtype=torch.uint8, device="cuda")
+    out = torch.empty(20, 12, 128, dtype=torch.float32, device="cuda")
+    with pytest.raises(qsa.QSAError) as e:
+        qsa.qsa_prompt_attn(dev(synth.random_q(1, 20, 12, 128)), 230, to_device(pool), dims, out, scratch=scratch)
+    assert e.value.status == -4
