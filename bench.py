@@ -26,6 +26,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+INT8_PEAK_TOPS = 5000.0   # dense int8 matrix-core peak of an MI355X
 BLOCK = 64
 KV_BYTES_PER_CELL_HEAD = 128 + 128 + 4 + 4     # K and V codes plus two fp32 scales at head_dim 128
 
@@ -36,7 +37,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=1280)
     ap.add_argument("--warmup", type=int, default=128)
     ap.add_argument("--workload", default="verify_window",
-                    choices=["tiny_decode", "verify_window", "drafter"])
+                    choices=["tiny_decode", "verify_window", "drafter", "prompt_chunk"])
+    ap.add_argument("--no-prompt", action="store_true", help="skip the prompt-chunk measurement")
+    ap.add_argument("--prompt-steps", type=int, default=20)
     ap.add_argument("--copies", type=int, default=64, help="pool copies the steps rotate over")
     ap.add_argument("--chunks", type=int, default=0, help="split count (0 = the library default for the shape)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -69,7 +72,16 @@ def main():
         print("bench.py measures one GPU: the QSA path here is single-GPU (sharding by KV head, slot or sequence is "
               "described in the design notes, not built); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
+    if args.workload == "prompt_chunk":
+        res = bench_prompt(args, args.steps if args.steps != 1280 else args.prompt_steps, main_line=True)
+    else:
+        res = bench_decode(args)
+        if not args.no_prompt:
+            res["prompt_chunk"] = bench_prompt(args, args.prompt_steps, main_line=False)
+    print(json.dumps(res))
 
+
+def bench_decode(args):
     import torch
 
     import sparse_top_attention_amd as qsa
@@ -83,7 +95,7 @@ def main():
     n_rows, n_kv, D = w.q.shape[0], w.n_kv_heads, w.head_dim
     dense = w.topk == 0
     nb = -(-pool_np.n_valid // BLOCK)
-    S = args.chunks or (w.n_chunks if dense else 16)
+    S = args.chunks or (w.n_chunks if dense else 8)
 
     def t(a):
         return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
@@ -227,7 +239,96 @@ def main():
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, layer_bytes, args.cpu_seconds)
-    print(json.dumps(result))
+    del copies
+    torch.cuda.empty_cache()
+    return result
+
+
+def prompt_ops(w):
+    """Algorithmic int8 ops of one prompt chunk: for every (query, q head) and every visible cell, 128 multiply-adds
+    for q.k and 128 for p.v, each done on three digit planes, 2 ops per multiply-add."""
+    n_valid = w.pools[0].n_valid
+    vis = sum(min(n_valid, int(p) + 1) for p in w.pos)
+    return vis * w.n_q_heads * w.head_dim * 2 * 3 * 2, vis
+
+
+def bench_prompt(args, steps, main_line):
+    """The 2,048-query prompt chunk at the end of a 32,768-cell context: one qsa_prompt_attn call per step, replayed
+    from a HIP graph over pool copies (K/V and q are resident in HBM)."""
+    import torch
+
+    import sparse_top_attention_amd as qsa
+    import synth
+
+    dev = torch.device("cuda:0")
+    w = synth.workload("prompt_chunk", poison=False)
+    pool_np = w.pools[0]
+    dims = qsa.Dims(w.n_q_heads, w.n_kv_heads, w.head_dim)
+    n_q = w.q.shape[0]
+
+    def t(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    n_copies = 8
+    base = qsa.Pool(t(pool_np.k), t(pool_np.ks), t(pool_np.v), t(pool_np.vs), pool_np.n_valid)
+    copies = [base] + [qsa.Pool(base.k.clone(), base.k_scale.clone(), base.v.clone(), base.v_scale.clone(),
+                                base.n_valid) for _ in range(n_copies - 1)]
+    qs = [t(w.q)] + [None] * (n_copies - 1)
+    for c in range(1, n_copies):
+        qs[c] = qs[0].clone()
+    scratch = torch.empty(qsa.qsa_prompt_scratch_bytes(n_q, dims), dtype=torch.uint8, device=dev)
+    out = torch.empty(n_q, w.n_q_heads, w.head_dim, dtype=torch.float32, device=dev)
+    stream = torch.cuda.Stream()
+
+    def call(c):
+        qsa.qsa_prompt_attn(qs[c], w.pos0, copies[c], dims, out, sm_scale=w.sm_scale, scratch=scratch)
+
+    with torch.cuda.stream(stream):
+        for c in range(n_copies):
+            call(c)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for c in range(n_copies):
+            call(c)
+    torch.cuda.synchronize()
+    reps = max(1, -(-steps // n_copies))
+    with torch.cuda.stream(stream):
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+    n_calls = reps * n_copies
+    ms = e0.elapsed_time(e1) / n_calls
+    ops, vis = prompt_ops(w)
+    tops = ops / (ms * 1e-3) / 1e12
+    res = {
+        "workload": "prompt_chunk", "queries": n_q, "pos0": w.pos0, "n_valid": pool_np.n_valid,
+        "q_heads": w.n_q_heads, "kv_heads": w.n_kv_heads, "head_dim": w.head_dim,
+        "ms_per_call": round(ms, 4), "calls_timed": n_calls, "int8_ops_per_call": int(ops),
+        "roofline": {"bound": "mfma", "kernel": "qsa_prompt_attn (q split + attention + chunk merge)",
+                     "achieved": round(tops, 1), "peak": INT8_PEAK_TOPS, "unit": "TOPS",
+                     "frac": round(tops / INT8_PEAK_TOPS, 4), "ops_per_launch": int(ops), "traffic": None},
+    }
+    if main_line:
+        res = {
+            "metric": "decode QSA us/layer + HBM GB/s; prompt-chunk ms + int8 MFMA % of peak",
+            "value": round(tops, 2), "unit": "TOPS", "n_gpus": 1, "steps": n_calls, "warmup": n_copies,
+            "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": "i8", "data": "synthetic",
+            "config": {"workload": "prompt_chunk", "queries": n_q, "q_heads": w.n_q_heads,
+                       "kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "n_valid": pool_np.n_valid,
+                       "pos0": w.pos0, "pool_copies": n_copies},
+            "roofline": res["roofline"], "cpu_baseline": None}
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_prompt(w, ops, vis, args.cpu_seconds)
+    del copies, qs, scratch
+    torch.cuda.empty_cache()
+    return res
 
 
 def cpu_baseline(w, layer_bytes, budget_s):
@@ -257,6 +358,31 @@ def cpu_baseline(w, layer_bytes, budget_s):
     return {"value": round(layer_bytes / per_layer / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"{n} full {w.name} layers (scores, top-k, attention; FP64, one thread) in {el:.1f} s, "
                       f"{per_layer * 1e3:.1f} ms per layer", "host_cpus": os.cpu_count()}
+
+
+def cpu_baseline_prompt(w, ops, vis, budget_s):
+    """The FP64 oracle on sampled (query, head) rows of the prompt chunk for about budget_s seconds, scaled to the
+    whole chunk's algorithmic ops (rows differ only in their causal length)."""
+    import oracle
+    pool = w.pools[0]
+    rng = np.random.default_rng(0)
+    n_q = w.q.shape[0]
+    done_cells, n = 0, 0
+    t0 = time.perf_counter()
+    while True:
+        i, h = int(rng.integers(0, n_q)), int(rng.integers(0, w.n_q_heads))
+        oracle.attn_one(w.q, w.pos, i, h, pool, w.n_kv_heads)
+        done_cells += min(pool.n_valid, int(w.pos[i]) + 1)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    per_cell = el / done_cells
+    full_s = per_cell * vis * w.n_q_heads
+    return {"value": round(ops / full_s / 1e12, 6), "unit": "TOPS", "cores": 1, "kind": "oracle",
+            "sample": f"{n} random (query, head) rows of the prompt chunk (FP64 dense attention, one thread) in "
+                      f"{el:.1f} s; scaled to the chunk's {vis * w.n_q_heads} (row, cell) pairs: {full_s:.0f} s "
+                      f"per chunk", "host_cpus": os.cpu_count()}
 
 
 if __name__ == "__main__":
