@@ -28,7 +28,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 INT8_PEAK_TOPS = 5000.0   # dense int8 matrix-core peak of an MI355X
 BLOCK = 64
-KV_BYTES_PER_CELL_HEAD = 128 + 128 + 4 + 4     # K and V codes plus two fp32 scales at head_dim 128
+KV_BYTES_PER_CELL_HEAD = 128 + 128 + 8 + 8     # K and V codes plus their two fp32 group scales each, head_dim 128
 
 
 def parse():
@@ -40,11 +40,30 @@ def parse():
                     choices=["tiny_decode", "verify_window", "drafter", "prompt_chunk"])
     ap.add_argument("--no-prompt", action="store_true", help="skip the prompt-chunk measurement")
     ap.add_argument("--prompt-steps", type=int, default=20)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain device copy of known size (to scale HBM byte counters)")
     ap.add_argument("--copies", type=int, default=64, help="pool copies the steps rotate over")
     ap.add_argument("--chunks", type=int, default=0, help="split count (0 = the library default for the shape)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     return ap.parse_args()
+
+
+def measured_traffic(key):
+    """Per-launch HBM bytes (read + write) measured with rocprofv3 byte counters for this kernel source, or None
+    once the source has changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        entry = json.load(f).get(key)
+    if not entry:
+        return None
+    with open(os.path.join(ROOT, entry["source"]), "rb") as f:
+        if hashlib.sha256(f.read()).hexdigest()[:16] != entry["sha256_16"]:
+            return None
+    return int(entry["read_bytes"] + entry["write_bytes"])
 
 
 def union_cells(ids, counts, pos, n_valid, n_kv):
@@ -72,6 +91,9 @@ def main():
         print("bench.py measures one GPU: the QSA path here is single-GPU (sharding by KV head, slot or sequence is "
               "described in the design notes, not built); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        print(json.dumps(copy_calibration()))
+        return
     if args.workload == "prompt_chunk":
         res = bench_prompt(args, args.steps if args.steps != 1280 else args.prompt_steps, main_line=True)
     else:
@@ -233,7 +255,8 @@ def bench_decode(args):
         "kernels_us": {k2: round(v2, 3) for k2, v2 in breakdown.items()},
         "roofline": {"bound": "hbm", "kernel": "attn_chunk", "achieved": round(chunk_gbs, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(chunk_gbs / HBM_PEAK_GBS, 4),
-                     "bytes_per_launch": int(chunk_bytes), "traffic": None},
+                     "bytes_per_launch": int(chunk_bytes),
+                     "traffic": measured_traffic(f"attn_chunk_{args.workload}") if S == 8 else None},
         "cpu_baseline": None,
     }
 
@@ -242,6 +265,19 @@ def bench_decode(args):
     del copies
     torch.cuda.empty_cache()
     return result
+
+
+def copy_calibration(nbytes=1 << 28, reps=4):
+    """A plain device-to-device copy of nbytes, reps times: a profiler's byte counters for these dispatches, divided
+    by nbytes read and nbytes written, give the factor that turns counter readings into bytes."""
+    import torch
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    return {"copy_bytes_read": nbytes, "copy_bytes_written": nbytes, "reps": reps}
 
 
 def prompt_ops(w):
@@ -312,7 +348,8 @@ def bench_prompt(args, steps, main_line):
         "ms_per_call": round(ms, 4), "calls_timed": n_calls, "int8_ops_per_call": int(ops),
         "roofline": {"bound": "mfma", "kernel": "qsa_prompt_attn (q split + attention + chunk merge)",
                      "achieved": round(tops, 1), "peak": INT8_PEAK_TOPS, "unit": "TOPS",
-                     "frac": round(tops / INT8_PEAK_TOPS, 4), "ops_per_launch": int(ops), "traffic": None},
+                     "frac": round(tops / INT8_PEAK_TOPS, 4), "ops_per_launch": int(ops),
+                     "traffic": measured_traffic("prompt_attn_prompt_chunk")},
     }
     if main_line:
         res = {
