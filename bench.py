@@ -312,7 +312,7 @@ def bench_prompt(args, steps, main_line):
     qs = [t(w.q)] + [None] * (n_copies - 1)
     for c in range(1, n_copies):
         qs[c] = qs[0].clone()
-    scratch = torch.empty(qsa.qsa_prompt_scratch_bytes(n_q, dims), dtype=torch.uint8, device=dev)
+    scratch = torch.empty(qsa.qsa_prompt_scratch_bytes(n_q, w.pos0, dims), dtype=torch.uint8, device=dev)
     out = torch.empty(n_q, w.n_q_heads, w.head_dim, dtype=torch.float32, device=dev)
     stream = torch.cuda.Stream()
 

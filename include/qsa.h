@@ -140,13 +140,14 @@ qsa_status qsa_attn_chunk(const float *q, const int32_t *pos, int32_t n_rows, co
 qsa_status qsa_attn_merge(const qsa_partials *in, int32_t n_rows, qsa_dims dims, int32_t n_chunks,
                           const int32_t *n_active, float *out, float *lse, qsa_stream_t stream);
 
-/* Scratch bytes qsa_prompt_attn needs for n_q queries. */
-size_t qsa_prompt_scratch_bytes(int32_t n_q, qsa_dims dims);
+/* Scratch bytes qsa_prompt_attn needs for n_q queries starting at position pos0 (0 if the arguments are invalid or
+ * head_dim has no prompt kernel). Covers any pool: the call sees at most pos0 + n_q cells. */
+size_t qsa_prompt_scratch_bytes(int32_t n_q, int32_t pos0, qsa_dims dims);
 
 /* Prompt-chunk attention on int8 matrix cores ([1367] "What it does"): dense causal attention for n_q queries at
  * positions pos0 .. pos0 + n_q - 1 over the pool's cells c <= pos (and c < n_valid). Both products run on the
- * int8 K/V codes as stored; q (per row, head and 64-dim group) and the probabilities times v_scale (per row and
- * 64-cell tile) are split into three exact 8-bit parts so every int32 sum is exact.
+ * int8 K/V codes as stored; q (scaled per query and head) is split into three exact 8-bit parts and the
+ * probabilities times v_scale (scaled per KV head) into four, so every int32 sum is exact.
  * out [n_q][n_q_heads][head_dim]; sm_scale multiplies q . k. Requires pos0 >= 0, head_dim == 128
  * (QSA_ERR_UNSUPPORTED otherwise) and scratch_bytes >= qsa_prompt_scratch_bytes (QSA_ERR_SCRATCH). */
 qsa_status qsa_prompt_attn(const float *q, int32_t n_q, int32_t pos0, const qsa_pool *pool, qsa_dims dims,

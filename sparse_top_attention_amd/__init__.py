@@ -66,7 +66,7 @@ def _lib():
         L.qsa_topk.argtypes = [P, I32, I32, I32, P, P, P, SZ, P]
         L.qsa_attn_chunk.argtypes = [P, P, I32, PP, I32, P, PD, P, P, I32, I32, I32, ctypes.c_float, PPart, P]
         L.qsa_attn_merge.argtypes = [PPart, I32, PD, I32, P, P, P, P]
-        L.qsa_prompt_scratch_bytes.argtypes = [I32, PD]
+        L.qsa_prompt_scratch_bytes.argtypes = [I32, I32, PD]
         L.qsa_prompt_scratch_bytes.restype = SZ
         L.qsa_prompt_attn.argtypes = [P, I32, I32, PP, PD, ctypes.c_float, P, P, SZ, P]
         L.qsa_status_str.argtypes = [I32]
@@ -217,8 +217,8 @@ def qsa_attn_merge(part: Partials, dims: Dims, n_chunks: int, out, lse=None, n_a
     return out
 
 
-def qsa_prompt_scratch_bytes(n_q, dims: Dims):
-    return _lib().qsa_prompt_scratch_bytes(n_q, dims.c())
+def qsa_prompt_scratch_bytes(n_q, pos0, dims: Dims):
+    return _lib().qsa_prompt_scratch_bytes(n_q, pos0, dims.c())
 
 
 def qsa_prompt_attn(q, pos0: int, pool: Pool, dims: Dims, out, sm_scale: float = 1.0, scratch=None, stream=None):

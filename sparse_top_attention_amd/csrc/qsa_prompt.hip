@@ -1,26 +1,38 @@
 // Prompt-chunk attention on gfx950 int8 matrix cores (v_mfma_i32_16x16x64_i8).
 //
-// Both products run on the int8 K/V codes as stored. The other operand of each product is split into three
-// exact signed bytes (X = 65536 h + 256 l + m), so every int32 sum is exact and only the recombination is fp32:
-//   q    : one scale per (query, head) maps max |q| to 127, X = rint(q * 127 * 65536 / max|q|);
-//   p*vs : p = 2^(t - m_ref) <= 1 and vs <= VS[g][grp] (max over the visible cells), X = rint(p vs 127 65536 / VS).
+// Both products run on the int8 K/V codes as stored. The other operand of each product is split into exact signed
+// bytes, so every int32 sum is exact and only the recombination is fp32:
+//   q    : one scale per (query, head) maps max |q| to 127 * 2^16; X = rint(q * scale) = 2^16 h + 2^8 l + m.
+//   p*vs : p = 2^(t - m_ref) <= 1 and w = vs * 127 * 2^24 / VS[g] (VS[g] = max v_scale over the cells the call
+//          sees, w precomputed per cell and group), X = p * w rounded to an integer = 2^24 d3 + 2^16 d2 + 2^8 d1 + d0.
+//          Four bytes (31 bits) rather than three because one scale covers a whole row: most cells sit far below
+//          the row maximum, and with 24 bits their rounding alone reached 1e-5 relative at a 32K context.
 //
 // Orientation. With row = (query, q head) and lane l of a wave owning row l % 16:
 //   S^T[cell][row] = K[cell][:] . Q^T        (A = K codes from LDS, B = q digits from LDS)
-//   O^T[dim][row]  = V^T[dim][cell] . P^T    (A = V^T from LDS,      B = p digits straight from S^T's registers)
+//   O^T[dim][row]  = V^T[dim][cell] . P^T    (A = V^T read from LDS with transposing loads, B = p digits)
 // The 16x16 result of an MFMA puts rows 4*(l/16) + v (v = 0..3) of column l % 16 in lane l. In S^T block b the
 // A-row 4G + v is loaded with cell 16G + 4b + v, so after the four blocks of a 64-cell tile lane l holds the 16
 // cells 16G .. 16G + 15 (G = l / 16) of its row -- exactly the k-slots lane l must supply as the B operand of the
-// PV product, and the same cells V^T's row chunk G holds. P never leaves registers.
+// PV product, and the cells the lane's V^T operand holds. P never leaves registers.
+//
+// Tiles go from HBM straight into LDS (global_load_lds, no staging registers), double-buffered; bank swizzles are
+// applied by choosing which 16-byte chunk each lane fetches. V stays [cell][dim] in LDS; ds_read_b64_tr_b8 (within
+// each 16-lane group, lane j receives byte i of the 8 bytes addressed by lane 2i + (j >= 8), at byte j mod 8) turns
+// two reads per 16-dim block into the V^T operand.
 //
 // The PV int32 sums are accumulated across tiles while the reference max m_ref of a row does not move; when a tile's
 // row max exceeds m_ref, the wave folds the int32 sums into fp32 (rescaled by 2^(m_old - m_new)) and restarts them,
 // with m_ref set DELTA above the new max so that later small increases need no fold.
 #include "qsa_internal.h"
 
+#include <type_traits>
+
 namespace qsa {
 
 typedef int32_t v4i __attribute__((ext_vector_type(4)));
+typedef int32_t v2i __attribute__((ext_vector_type(2)));
+#define QSA_LDS __attribute__((address_space(3)))
 
 constexpr int PD = 128;          // head dim of the prompt kernel
 constexpr int PT = 64;           // cells per tile
@@ -28,18 +40,34 @@ constexpr int PW = 4;            // waves per workgroup
 constexpr int PROWS = 16 * PW;   // rows (query, head) per workgroup
 constexpr float PLOG2E = 1.4426950408889634f;
 constexpr float PLN2 = 0.6931471805599453f;
-constexpr float PDELTA = 2.0f;   // headroom (log2 units) added to the reference max at a fold
-constexpr float MAGIC = 8388608.0f;                 // 2^23: fp32 with ulp 1 on [2^23, 2^24)
-constexpr uint32_t MAGIC_BIAS = 0x4A7F7F80u;        // bits(2^23) - 0x808080
+constexpr float PDELTA = 4.0f;   // headroom (log2 units) added to the reference max at a fold
+constexpr float QMAX = 127.0f * 65536.0f;          // largest q digit value
+constexpr float PMAX = 127.0f * 16777216.0f;       // largest p * w digit value
+// (uint32)(p * w + PBIAS) = X + 0x808080: bytes 0..2 hold d0 + 128, d1 + 128, d2 + 128 and byte 3 holds d3 in
+// [0, 127] (X <= 127 * 2^24 keeps the sum below 2^31). The conversion truncates; below 2^24 the fractional part is
+// dropped, an error of at most one unit in 2^31 of the row's largest term.
+constexpr float PBIAS = 8421504.0f;                // 0x808080
+constexpr int FOLD_EVERY = 1024;                   // tiles between forced folds (int32 sums stay below 2^31)
 constexpr int NCU = 256;                            // compute units of an MI355X
+constexpr int VS_SLICES = 32;
 
-// 16-byte chunk swizzles for the LDS tiles (K rows of 128 B, V^T rows of 64 B)
+// 16-byte chunk swizzles of the LDS tiles (rows of 128 B): K chunks for the plain 16-byte operand reads, V chunks
+// for the 8-byte transposing reads (consecutive cells land on different banks).
 __device__ __forceinline__ int swz_k(int cell) { return (cell & 3) | ((cell >> 2) & 4); }
-__device__ __forceinline__ int swz_v(int dim) { return (dim >> 1) & 3; }
+__device__ __forceinline__ int swz_v(int cell) { return cell & 7; }
 
 __device__ __forceinline__ uint32_t bperm(uint32_t s0, uint32_t s1, uint32_t sel)
 {
     return __builtin_amdgcn_perm(s0, s1, sel);
+}
+
+__device__ __forceinline__ void load_lds16(const void *src, QSA_LDS void *dst)
+{
+    __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
+}
+__device__ __forceinline__ void load_lds4(const void *src, QSA_LDS void *dst)
+{
+    __builtin_amdgcn_global_load_lds(src, dst, 4, 0, 0);
 }
 
 // ---------------------------------------------------------------------------------------------- q digits
@@ -54,7 +82,7 @@ __global__ __launch_bounds__(64) void prompt_qsplit_kernel(const float *__restri
     const int32_t g = h / G, r = qi * G + h % G;
     const float2 x = reinterpret_cast<const float2 *>(q + (int64_t)blockIdx.x * PD)[lane];
     const float amax = group_max<64>(fmaxf(fabsf(x.x), fabsf(x.y)));
-    const float s = amax > 0.f ? (127.0f * 65536.0f) / amax : 0.f;
+    const float s = amax > 0.f ? QMAX / amax : 0.f;
     const int32_t X[2] = {(int32_t)rintf(x.x * s), (int32_t)rintf(x.y * s)};
     int32_t dg[3][2];
 #pragma unroll
@@ -72,32 +100,53 @@ __global__ __launch_bounds__(64) void prompt_qsplit_kernel(const float *__restri
         const uint16_t pair = (uint16_t)((dg[p][0] & 255) | ((dg[p][1] & 255) << 8));
         reinterpret_cast<uint16_t *>(dst + p * PD)[lane] = pair;
     }
-    if (lane == 0) qs[(int64_t)g * R + r] = amax > 0.f ? amax / (127.0f * 65536.0f) * qscale : 0.f;
+    if (lane == 0) qs[(int64_t)g * R + r] = amax > 0.f ? amax / QMAX * qscale : 0.f;
 }
 
 // ------------------------------------------------------------------------------------------ V-scale bound
-// VS[g][grp] = max of v_scale over the cells any query of the call can see (1 when there is none).
+// Partial maxima of v_scale (both 64-dim groups) over the cells any query of the call can see: each workgroup
+// reduces one of VS_SLICES slices of KV head g's cells; the attention kernel folds the slices.
 __global__ __launch_bounds__(256) void prompt_vsmax_kernel(const float *__restrict__ vs, int32_t cap, int32_t n_cells,
-                                                           float *__restrict__ VS)
+                                                           float *__restrict__ VSp)
 {
     __shared__ float red[4];
-    const int32_t g = blockIdx.x / 2, grp = blockIdx.x % 2;
+    const int32_t g = blockIdx.x, sl = blockIdx.y;
+    const int32_t per = (n_cells + VS_SLICES - 1) / VS_SLICES;
+    const int32_t e0 = 2 * min(n_cells, sl * per), e1 = 2 * min(n_cells, (sl + 1) * per);
     float m = 0.f;
-    for (int32_t c = threadIdx.x; c < n_cells; c += 256) m = fmaxf(m, vs[((int64_t)g * cap + c) * 2 + grp]);
+    for (int32_t e = e0 + threadIdx.x; e < e1; e += 256) m = fmaxf(m, vs[(int64_t)g * cap * 2 + e]);
     m = group_max<64>(m);
     if (threadIdx.x % 64 == 0) red[threadIdx.x / 64] = m;
     __syncthreads();
-    if (threadIdx.x == 0) {
-        const float t = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-        VS[blockIdx.x] = t > 0.f ? t : 1.f;
-    }
+    if (threadIdx.x == 0) VSp[g * VS_SLICES + sl] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+
+__device__ __forceinline__ float head_vs(const float *__restrict__ VSp, int32_t g)
+{
+    float VS = 0.f;
+#pragma unroll 4
+    for (int k = 0; k < VS_SLICES; k++) VS = fmaxf(VS, VSp[g * VS_SLICES + k]);
+    return VS > 0.f ? VS : 1.f;
+}
+
+// w[g][c][grp] = v_scale * 127 * 2^24 / VS[g] for the n_cells cells the call sees.
+__global__ __launch_bounds__(256) void prompt_vscale_kernel(const float *__restrict__ vs, int32_t cap, int32_t n_cells,
+                                                            const float *__restrict__ VSp, float *__restrict__ w)
+{
+    const int32_t g = blockIdx.y;
+    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (e >= 2 * (int64_t)n_cells) return;
+    const float sc = PMAX / head_vs(VSp, g);
+    w[(int64_t)g * n_cells * 2 + e] = vs[(int64_t)g * cap * 2 + e] * sc;
 }
 
 // ------------------------------------------------------------------------------------------- main kernel
 struct PromptArgs {
     const int8_t *qd;
     const float *qs;
-    const float *VS;
+    const float *VSp;  // [n_kv][VS_SLICES] partial maxima of v_scale
+    const float *w;    // [n_kv][w_cells][2] scaled v_scale
+    int32_t w_cells;
     PoolArg pool;
     float *m_out;
     float *l_out;
@@ -115,10 +164,10 @@ struct PromptArgs {
 constexpr int QROW = 3 * PD + 16;  // LDS bytes per row of q digits (padded: consecutive rows start 4 banks apart)
 
 struct __align__(16) PromptTile {
-    int8_t k[PT * PD];     // [cell][128], 16-byte chunks swizzled by swz_k(cell)
-    int8_t vt[PD * PT];    // [dim][64],   16-byte chunks swizzled by swz_v(dim)
+    int8_t k[PT * PD];     // [cell][128], 16-byte chunk p of row c holds chunk p ^ swz_k(c)
+    int8_t v[PT * PD];     // [cell][128], 16-byte chunk p of row c holds chunk p ^ swz_v(c)
     float ks[PT * 2];      // [cell][grp]
-    float vs[PT * 2];      // [cell][grp], scaled by 127 * 65536 / VS[grp]
+    float vs[PT * 2];      // [cell][grp], scaled to w
 };
 
 __global__ __launch_bounds__(256, 2) void prompt_attn_kernel(const PromptArgs a)
@@ -156,104 +205,77 @@ __global__ __launch_bounds__(256, 2) void prompt_attn_kernel(const PromptArgs a)
         *reinterpret_cast<int4 *>(sq + rr * QROW + 16 * k16) = v;
     }
     const int8_t *qrow_lds = sq + (16 * wave + n16) * QROW + 16 * G4;
-    const float crow = row_ok ? a.qs[(int64_t)g * a.R + r] : 0.f;
-    const float VS0 = a.VS[2 * g], VS1 = a.VS[2 * g + 1];
-    const float vsc0 = (127.0f * 65536.0f) / VS0, vsc1 = (127.0f * 65536.0f) / VS1;
-    const float sw0 = VS0 / (127.0f * 65536.0f), sw1 = VS1 / (127.0f * 65536.0f);
 
-    v4i accH[8], accL[8], accM[8];
-    float O[8][4];
+    // logit scale of the row; a floor keeps -inf * crow = -inf for all-zero q rows (whose logits are all 0)
+    const float crow = fmaxf(row_ok ? a.qs[(int64_t)g * a.R + r] : 0.f, 1e-30f);
+    const float sw = head_vs(a.VSp, g) / PMAX;  // value of one unit of the p * w digits
+
+    v4i acc[4][8];   // PV int32 sums per digit plane (weights 2^24, 2^16, 2^8, 1)
 #pragma unroll
-    for (int db = 0; db < 8; db++) {
-        accH[db] = accL[db] = accM[db] = v4i{0, 0, 0, 0};
+    for (int db = 0; db < 8; db++) acc[0][db] = acc[1][db] = acc[2][db] = acc[3][db] = v4i{0, 0, 0, 0};
+    // The fp32 sums (the lane's 32 outputs of its row) change only at folds, so they live in the row's output slot
+    // in global memory rather than in registers: the out row itself with one chunk, the chunk's partial otherwise.
+    const int32_t hq = g * a.G + (r % a.G);
+    const int64_t orow_idx = ((int64_t)qi * a.n_qh + hq) * a.S + j;
+    float *const orow = (a.S == 1 ? a.out : a.o_out) + orow_idx * PD + 4 * G4;
+    bool have_o = false;
+    // O = (O + sum_planes acc * 2^(8 plane) * sw) * alpha, restarting the int32 sums
+    auto fold = [&](float alpha, float4 (&o)[8]) {
 #pragma unroll
-        for (int v = 0; v < 4; v++) O[db][v] = 0.f;
-    }
+        for (int db = 0; db < 8; db++)
+            o[db] = have_o ? *reinterpret_cast<const float4 *>(orow + 16 * db) : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int db = 0; db < 8; db++) {
+            float part[4];
+#pragma unroll
+            for (int v = 0; v < 4; v++)
+                part[v] = fmaf((float)acc[0][db][v], 16777216.f,
+                               fmaf((float)acc[1][db][v], 65536.f, fmaf((float)acc[2][db][v], 256.f, (float)acc[3][db][v])));
+            o[db] = make_float4(fmaf(part[0], sw, o[db].x) * alpha, fmaf(part[1], sw, o[db].y) * alpha,
+                                fmaf(part[2], sw, o[db].z) * alpha, fmaf(part[3], sw, o[db].w) * alpha);
+            acc[0][db] = acc[1][db] = acc[2][db] = acc[3][db] = v4i{0, 0, 0, 0};
+        }
+    };
     float lsum = 0.f, mref = -INFINITY;
 
-    // ---- tile staging: registers first (global loads in flight), then LDS
+    // ---- tile staging, straight from HBM into LDS: per 64-cell tile, 8 KB of K codes, 8 KB of V codes and 512 B of
+    // each scale; wave w issues 16-byte slots [128 w, 128 w + 128) of K and of V and one 64-float half of a scale array
     const int8_t *kg = P.k + (int64_t)g * P.capacity * PD;
     const int8_t *vg = P.v + (int64_t)g * P.capacity * PD;
     const float *ksg = P.ks + (int64_t)g * P.capacity * 2;
-    const float *vsg = P.vs + (int64_t)g * P.capacity * 2;
-    int4 kst[2];
-    int2 vst[4];
-    float2 kss, vss;
-    auto stage = [&](int32_t t) {
+    const float *vsg = a.w + (int64_t)g * a.w_cells * 2;
+    auto stage = [&](int32_t t, int buf) {
         const int32_t cb = t * PT;
-        {
-            const int32_t c = min(cb + tid / 4, c_last);
-            const int4 *src = reinterpret_cast<const int4 *>(kg + (int64_t)c * PD + 32 * (tid % 4));
-            kst[0] = src[0];
-            kst[1] = src[1];
-        }
-#pragma unroll
-        for (int k4 = 0; k4 < 4; k4++) {
-            const int32_t c = min(cb + 4 * (tid % 16) + k4, c_last);
-            vst[k4] = *reinterpret_cast<const int2 *>(vg + (int64_t)c * PD + 8 * (tid / 16));
-        }
-        if (tid < PT) {
-            const int32_t c = min(cb + tid, c_last);
-            kss = *reinterpret_cast<const float2 *>(ksg + (int64_t)c * 2);
-            vss = *reinterpret_cast<const float2 *>(vsg + (int64_t)c * 2);
-        }
-    };
-    auto commit = [&](int buf) {
         PromptTile &T = tile[buf];
-        {
-            const int cell = tid / 4;
 #pragma unroll
-            for (int h = 0; h < 2; h++) {
-                const int chunk = 2 * (tid % 4) + h;
-                *reinterpret_cast<int4 *>(T.k + cell * PD + 16 * (chunk ^ swz_k(cell))) = kst[h];
-            }
+        for (int h = 0; h < 2; h++) {
+            const int slot = 128 * wave + 64 * h + lane;
+            const int cell = slot >> 3, pos = slot & 7;
+            const int32_t c = min(cb + cell, c_last);
+            load_lds16(kg + (int64_t)c * PD + 16 * (pos ^ swz_k(cell)),
+                       (QSA_LDS void *)(T.k + 1024 * (2 * wave + h)));
+            load_lds16(vg + (int64_t)c * PD + 16 * (pos ^ swz_v(cell)),
+                       (QSA_LDS void *)(T.v + 1024 * (2 * wave + h)));
         }
-        {
-            // 4 cells x 8 dims -> 8 dwords of 4 cells each (one per dim)
-            uint32_t lo[4], hi[4];
-#pragma unroll
-            for (int k4 = 0; k4 < 4; k4++) {
-                lo[k4] = (uint32_t)vst[k4].x;
-                hi[k4] = (uint32_t)vst[k4].y;
-            }
-            uint32_t dcol[8];
-#pragma unroll
-            for (int half = 0; half < 2; half++) {
-                const uint32_t *w = half ? hi : lo;
-                const uint32_t A01 = bperm(w[1], w[0], 0x05010400u), C01 = bperm(w[1], w[0], 0x07030602u);
-                const uint32_t A23 = bperm(w[3], w[2], 0x05010400u), C23 = bperm(w[3], w[2], 0x07030602u);
-                dcol[4 * half + 0] = bperm(A23, A01, 0x05040100u);
-                dcol[4 * half + 1] = bperm(A23, A01, 0x07060302u);
-                dcol[4 * half + 2] = bperm(C23, C01, 0x05040100u);
-                dcol[4 * half + 3] = bperm(C23, C01, 0x07060302u);
-            }
-            const int cell0 = 4 * (tid % 16), chunk = cell0 / 16, within = cell0 % 16;
-#pragma unroll
-            for (int dd = 0; dd < 8; dd++) {
-                const int dim = 8 * (tid / 16) + dd;
-                *reinterpret_cast<uint32_t *>(T.vt + dim * PT + 16 * (chunk ^ swz_v(dim)) + within) = dcol[dd];
-            }
-        }
-        if (tid < PT) {
-            T.ks[2 * tid] = kss.x;
-            T.ks[2 * tid + 1] = kss.y;
-            T.vs[2 * tid] = vss.x * vsc0;
-            T.vs[2 * tid + 1] = vss.y * vsc1;
-        }
+        const int e = 64 * (wave & 1) + lane;  // float e of the tile's [cell][grp] scales
+        const int32_t c = min(cb + (e >> 1), c_last);
+        if (wave < 2) load_lds4(ksg + (int64_t)c * 2 + (e & 1), (QSA_LDS void *)(T.ks + 64 * (wave & 1)));
+        else load_lds4(vsg + (int64_t)c * 2 + (e & 1), (QSA_LDS void *)(T.vs + 64 * (wave & 1)));
     };
 
-    if (t0 < t1) {
-        stage(t0);
-        commit(0);
-    }
+    if (t0 < t1) stage(t0, 0);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
-    for (int32_t t = t0; t < t1; t++) {
+    // Tiles before t_mask end at or before the wave's smallest limit and need no causal mask; the loop is split so
+    // the mask compares only run on the last tiles. Every iteration has one barrier, so the waves stay matched.
+    const int32_t t_mask = wave_lim < PT - 1 ? 0 : (wave_lim - (PT - 1)) / PT + 1;
+    auto step = [&](int32_t t, auto masked_tag) {
+        constexpr bool masked = decltype(masked_tag)::value;
         const int buf = (t - t0) & 1;
-        if (t + 1 < t1) stage(t + 1);
+        if (t + 1 < t1) stage(t + 1, buf ^ 1);
         const PromptTile &T = tile[buf];
         const int32_t cb = t * PT;
-        const bool masked = cb + PT - 1 > wave_lim;
 
         // ---- S^T = K . Q^T, four 16-cell blocks; lane l ends with cells 16*G4 + 4b + v of row n16
         float t2[4][4];
@@ -281,8 +303,10 @@ __global__ __launch_bounds__(256, 2) void prompt_attn_kernel(const PromptArgs a)
             for (int v = 0; v < 4; v++) {
                 const float a0 = fmaf((float)hacc[0][v], 65536.f, (float)lmacc[0][v]);
                 const float a1 = fmaf((float)hacc[1][v], 65536.f, (float)lmacc[1][v]);
-                float tv = fmaf(a1, k1[v], a0 * k0[v]) * crow;
-                if (masked && cb + cl0 + v > lim) tv = -INFINITY;
+                float tv = fmaf(a1, k1[v], a0 * k0[v]);   // logit / crow
+                if constexpr (masked) {
+                    if (cb + cl0 + v > lim) tv = -INFINITY;
+                }
                 t2[b][v] = tv;
             }
         }
@@ -294,101 +318,97 @@ __global__ __launch_bounds__(256, 2) void prompt_attn_kernel(const PromptArgs a)
 #pragma unroll
             for (int v = 0; v < 4; v++) rm = fmaxf(rm, t2[b][v]);
         rm = max16(rm);
-        rm = max32(rm);
+        rm = max32(rm) * crow;                       // row max in log2 units (crow > 0)
         const bool need = rm > mref;
-        if (__any(need)) {
+        const bool force = ((t - t0) % FOLD_EVERY) == FOLD_EVERY - 1;   // wave-uniform
+        if (__any(need) || force) {
             const float mnew = need ? rm + PDELTA : mref;
-            const float alpha = need ? __builtin_amdgcn_exp2f(mref - mnew) : 1.f;
+            if ((need || force) && row_ok) {   // both sums are relative to the old reference
+                const float alpha = need ? __builtin_amdgcn_exp2f(mref - mnew) : 1.f;
+                float4 o[8];
+                fold(alpha, o);
 #pragma unroll
-            for (int db = 0; db < 8; db++) {
-                const float sw = db < 4 ? sw0 : sw1;
-#pragma unroll
-                for (int v = 0; v < 4; v++) {
-                    const float part = fmaf((float)accH[db][v], 65536.f,
-                                            fmaf((float)accL[db][v], 256.f, (float)accM[db][v]));
-                    O[db][v] = fmaf(part, sw, O[db][v]) * alpha;   // both are relative to the old reference
-                }
-                accH[db] = accL[db] = accM[db] = v4i{0, 0, 0, 0};
+                for (int db = 0; db < 8; db++) *reinterpret_cast<float4 *>(orow + 16 * db) = o[db];
+                have_o = true;
+                lsum *= alpha;
+                mref = mnew;
             }
-            lsum *= alpha;
-            mref = mnew;
         }
         const float mexp = mref == -INFINITY ? 0.f : mref;
 
-        // ---- p, its digits per scale group, packed as the B operands of O^T
-        v4i ph[2], pl[2], pm[2];
+        // ---- p = 2^(t - m_ref); the digits of p * w, per scale group, are the B operands of O^T += V^T . P^T,
+        // run over the group's four 16-dim blocks. V^T rows come from two transposing reads per block.
+        float p[4][4];
 #pragma unroll
-        for (int b = 0; b < 4; b++) {
-            const int cl0 = 16 * G4 + 4 * b;
-            const float4 vsa = *reinterpret_cast<const float4 *>(&T.vs[2 * cl0]);
-            const float4 vsb = *reinterpret_cast<const float4 *>(&T.vs[2 * cl0 + 4]);
-            const float w0[4] = {vsa.x, vsa.z, vsb.x, vsb.z}, w1[4] = {vsa.y, vsa.w, vsb.y, vsb.w};
-            uint32_t u0[4], u1[4];
+        for (int b = 0; b < 4; b++)
 #pragma unroll
             for (int v = 0; v < 4; v++) {
-                const float p = __builtin_amdgcn_exp2f(t2[b][v] - mexp);
-                lsum += p;
-                u0[v] = __float_as_uint(fmaf(p, w0[v], MAGIC)) - MAGIC_BIAS;
-                u1[v] = __float_as_uint(fmaf(p, w1[v], MAGIC)) - MAGIC_BIAS;
+                p[b][v] = __builtin_amdgcn_exp2f(fmaf(t2[b][v], crow, -mexp));
+                lsum += p[b][v];
+            }
+        const int i = n16 >> 1, hh = n16 & 1;
+        const int c0 = 16 * G4 + i, c1 = c0 + 8;   // (c & 7) == i for both
+#pragma unroll
+        for (int grp = 0; grp < 2; grp++) {
+            v4i pd[4];   // digit planes d3, d2, d1, d0 of the lane's 16 cells
+#pragma unroll
+            for (int b = 0; b < 4; b++) {
+                const int cl0 = 16 * G4 + 4 * b;
+                const float4 wa = *reinterpret_cast<const float4 *>(&T.vs[2 * cl0]);
+                const float4 wb = *reinterpret_cast<const float4 *>(&T.vs[2 * cl0 + 4]);
+                const float wv[4] = {grp ? wa.y : wa.x, grp ? wa.w : wa.z, grp ? wb.y : wb.x, grp ? wb.w : wb.z};
+                uint32_t u[4];
+#pragma unroll
+                for (int v = 0; v < 4; v++) u[v] = (uint32_t)fmaf(p[b][v], wv[v], PBIAS);
+                const uint32_t A01 = bperm(u[1], u[0], 0x05010400u), B01 = bperm(u[1], u[0], 0x07030602u);
+                const uint32_t A23 = bperm(u[3], u[2], 0x05010400u), B23 = bperm(u[3], u[2], 0x07030602u);
+                pd[3][b] = (int32_t)(bperm(A23, A01, 0x05040100u) ^ 0x80808080u);
+                pd[2][b] = (int32_t)(bperm(A23, A01, 0x07060302u) ^ 0x80808080u);
+                pd[1][b] = (int32_t)(bperm(B23, B01, 0x05040100u) ^ 0x80808080u);
+                pd[0][b] = (int32_t)bperm(B23, B01, 0x07060302u);
             }
 #pragma unroll
-            for (int grp = 0; grp < 2; grp++) {
-                const uint32_t *u = grp ? u1 : u0;
-                const uint32_t A01 = bperm(u[1], u[0], 0x05010400u), B01 = bperm(u[1], u[0], 0x0c0c0602u);
-                const uint32_t A23 = bperm(u[3], u[2], 0x05010400u), B23 = bperm(u[3], u[2], 0x0c0c0602u);
-                pm[grp][b] = (int32_t)(bperm(A23, A01, 0x05040100u) ^ 0x80808080u);
-                pl[grp][b] = (int32_t)(bperm(A23, A01, 0x07060302u) ^ 0x80808080u);
-                ph[grp][b] = (int32_t)(bperm(B23, B01, 0x05040100u) ^ 0x80808080u);
+            for (int dq = 0; dq < 4; dq++) {
+                const int db = 4 * grp + dq, ch = 2 * db + hh;   // 8-byte chunk of the cell's 128-byte row
+                const v2i lo = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                    (QSA_LDS v2i *)(T.v + c0 * PD + 8 * (ch ^ (2 * i))));
+                const v2i hi = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                    (QSA_LDS v2i *)(T.v + c1 * PD + 8 * (ch ^ (2 * i))));
+                const v4i va = v4i{lo[0], lo[1], hi[0], hi[1]};
+#pragma unroll
+                for (int pl = 0; pl < 4; pl++)
+                    acc[pl][db] = __builtin_amdgcn_mfma_i32_16x16x64_i8(va, pd[pl], acc[pl][db], 0, 0, 0);
             }
         }
 
-        // ---- O^T += V^T . P^T over 8 blocks of 16 dims
-#pragma unroll
-        for (int db = 0; db < 8; db++) {
-            const int grp = db >> 2, dim = 16 * db + n16;
-            const v4i va = *reinterpret_cast<const v4i *>(T.vt + dim * PT + 16 * (G4 ^ swz_v(dim)));
-            accH[db] = __builtin_amdgcn_mfma_i32_16x16x64_i8(va, ph[grp], accH[db], 0, 0, 0);
-            accL[db] = __builtin_amdgcn_mfma_i32_16x16x64_i8(va, pl[grp], accL[db], 0, 0, 0);
-            accM[db] = __builtin_amdgcn_mfma_i32_16x16x64_i8(va, pm[grp], accM[db], 0, 0, 0);
-        }
-
-        if (t + 1 < t1) commit(buf ^ 1);
+        __builtin_amdgcn_s_waitcnt(0);   // this wave's loads of the next tile have landed in LDS
         __syncthreads();
-    }
+    };
+    int32_t t = t0;
+    for (; t < min(t_mask, t1); t++) step(t, std::false_type{});
+    for (; t < t1; t++) step(t, std::true_type{});
 
     // ---- final fold and output
-#pragma unroll
-    for (int db = 0; db < 8; db++) {
-        const float sw = db < 4 ? sw0 : sw1;
-#pragma unroll
-        for (int v = 0; v < 4; v++) {
-            const float part = fmaf((float)accH[db][v], 65536.f, fmaf((float)accL[db][v], 256.f, (float)accM[db][v]));
-            O[db][v] = fmaf(part, sw, O[db][v]);
-        }
-    }
     lsum = sum16(lsum);
     lsum = sum32(lsum);
     if (!row_ok) return;
-    const int32_t h = g * a.G + (r % a.G);
     const bool empty = mref == -INFINITY;
+    float4 o[8];
+    fold(1.f, o);
     if (a.S == 1) {
         const float inv = empty ? 0.f : 1.f / lsum;
-        float *dst = a.out + ((int64_t)qi * a.n_qh + h) * PD;
 #pragma unroll
         for (int db = 0; db < 8; db++)
-            *reinterpret_cast<float4 *>(dst + 16 * db + 4 * G4) =
-                make_float4(O[db][0] * inv, O[db][1] * inv, O[db][2] * inv, O[db][3] * inv);
+            *reinterpret_cast<float4 *>(orow + 16 * db) =
+                make_float4(o[db].x * inv, o[db].y * inv, o[db].z * inv, o[db].w * inv);
     } else {
-        const int64_t idx = ((int64_t)qi * a.n_qh + h) * a.S + j;
-        float *dst = a.o_out + idx * PD;
 #pragma unroll
         for (int db = 0; db < 8; db++)
-            *reinterpret_cast<float4 *>(dst + 16 * db + 4 * G4) =
-                empty ? make_float4(0.f, 0.f, 0.f, 0.f) : make_float4(O[db][0], O[db][1], O[db][2], O[db][3]);
+            *reinterpret_cast<float4 *>(orow + 16 * db) = empty ? make_float4(0.f, 0.f, 0.f, 0.f) : o[db];
         if (G4 == 0) {
-            a.m_out[idx] = empty ? -INFINITY : mref * PLN2;
-            a.l_out[idx] = empty ? 0.f : lsum;
-            a.e_out[idx] = empty ? 1 : 0;
+            a.m_out[orow_idx] = empty ? -INFINITY : mref * PLN2;
+            a.l_out[orow_idx] = empty ? 0.f : lsum;
+            a.e_out[orow_idx] = empty ? 1 : 0;
         }
     }
 }
@@ -414,10 +434,11 @@ int prompt_chunks(int32_t n_q, const qsa_dims &d)
 }
 
 struct PromptScratch {
-    size_t qd, qs, vs, m, l, o, e, total;
+    size_t qd, qs, vs, w, m, l, o, e, total;
 };
 
-PromptScratch prompt_layout(int32_t n_q, const qsa_dims &d)
+// n_cells: pool cells the call sees (scaled v_scale is kept for each of them).
+PromptScratch prompt_layout(int32_t n_q, int64_t n_cells, const qsa_dims &d)
 {
     auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
     const size_t rows = (size_t)n_q * d.n_q_heads;
@@ -426,7 +447,8 @@ PromptScratch prompt_layout(int32_t n_q, const qsa_dims &d)
     size_t off = 0;
     s.qd = off; off += al(rows * 3 * PD);
     s.qs = off; off += al(rows * sizeof(float));
-    s.vs = off; off += al((size_t)d.n_kv_heads * 2 * sizeof(float));
+    s.vs = off; off += al((size_t)d.n_kv_heads * VS_SLICES * sizeof(float));
+    s.w = off; off += al((size_t)d.n_kv_heads * (size_t)n_cells * 2 * sizeof(float));
     if (S > 1) {
         s.m = off; off += al(rows * S * sizeof(float));
         s.l = off; off += al(rows * S * sizeof(float));
@@ -441,10 +463,10 @@ PromptScratch prompt_layout(int32_t n_q, const qsa_dims &d)
 
 using namespace qsa;
 
-extern "C" size_t qsa_prompt_scratch_bytes(int32_t n_q, qsa_dims dims)
+extern "C" size_t qsa_prompt_scratch_bytes(int32_t n_q, int32_t pos0, qsa_dims dims)
 {
-    if (n_q <= 0 || check_dims(dims) != QSA_OK || dims.head_dim != PD) return 0;
-    return prompt_layout(n_q, dims).total;
+    if (n_q <= 0 || pos0 < 0 || check_dims(dims) != QSA_OK || dims.head_dim != PD) return 0;
+    return prompt_layout(n_q, (int64_t)pos0 + n_q, dims).total;
 }
 
 extern "C" qsa_status qsa_prompt_attn(const float *q, int32_t n_q, int32_t pos0, const qsa_pool *pool, qsa_dims dims,
@@ -458,7 +480,9 @@ extern "C" qsa_status qsa_prompt_attn(const float *q, int32_t n_q, int32_t pos0,
     if (n_q < 0 || pos0 < 0) return QSA_ERR_RANGE;
     if (dims.head_dim != PD) return QSA_ERR_UNSUPPORTED;
     if (n_q == 0) return QSA_OK;
-    const PromptScratch lay = prompt_layout(n_q, dims);
+    const int64_t last = (int64_t)pos0 + n_q;
+    const int32_t n_cells = (int32_t)(last < pool->n_valid ? last : pool->n_valid);
+    const PromptScratch lay = prompt_layout(n_q, n_cells, dims);
     if (!scratch) return QSA_ERR_NULL;
     if (scratch_bytes < lay.total) return QSA_ERR_SCRATCH;
     const int32_t G = dims.n_q_heads / dims.n_kv_heads;
@@ -470,15 +494,17 @@ extern "C" qsa_status qsa_prompt_attn(const float *q, int32_t n_q, int32_t pos0,
 
     int8_t *qd = reinterpret_cast<int8_t *>(base + lay.qd);
     float *qs = reinterpret_cast<float *>(base + lay.qs);
-    float *VS = reinterpret_cast<float *>(base + lay.vs);
+    float *VSp = reinterpret_cast<float *>(base + lay.vs);
     prompt_qsplit_kernel<<<dim3((uint32_t)n_q * dims.n_q_heads), 64, 0, s>>>(q, dims.n_q_heads, G, (int32_t)R,
                                                                              sm_scale * PLOG2E, qd, qs);
-    const int64_t last = (int64_t)pos0 + n_q;
-    const int32_t n_cells = (int32_t)(last < pool->n_valid ? last : pool->n_valid);
-    prompt_vsmax_kernel<<<dim3(dims.n_kv_heads * 2), 256, 0, s>>>(pool->v_scale, pool->capacity, n_cells, VS);
+    float *w = reinterpret_cast<float *>(base + lay.w);
+    prompt_vsmax_kernel<<<dim3(dims.n_kv_heads, VS_SLICES), 256, 0, s>>>(pool->v_scale, pool->capacity, n_cells, VSp);
+    if (n_cells > 0)
+        prompt_vscale_kernel<<<dim3((uint32_t)((2 * (int64_t)n_cells + 255) / 256), dims.n_kv_heads), 256, 0, s>>>(
+            pool->v_scale, pool->capacity, n_cells, VSp, w);
 
     PromptArgs a{};
-    a.qd = qd; a.qs = qs; a.VS = VS;
+    a.qd = qd; a.qs = qs; a.VSp = VSp; a.w = w; a.w_cells = n_cells;
     a.pool = PoolArg{pool->k, pool->k_scale, pool->v, pool->v_scale, pool->capacity, pool->n_valid};
     a.out = out;
     a.n_q = n_q; a.pos0 = pos0; a.n_qh = dims.n_q_heads; a.G = G; a.R = (int32_t)R; a.S = S;

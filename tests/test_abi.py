@@ -157,13 +157,15 @@ def test_prompt_validation():
 
 def test_prompt_scratch_sizing_and_checks():
     L = qsa.lib_handle()
-    n = L.qsa_prompt_scratch_bytes(2048, GOOD)
+    n = L.qsa_prompt_scratch_bytes(2048, 30720, GOOD)
     assert n >= 2048 * 24 * (3 * 128 + 4)          # q digits and row scales at least
-    assert L.qsa_prompt_scratch_bytes(0, GOOD) == 0
-    assert L.qsa_prompt_scratch_bytes(16, D(24, 4, 64, 64)) == 0   # head_dim 64 has no prompt kernel
+    assert n >= L.qsa_prompt_scratch_bytes(2048, 0, GOOD) + 4 * 30720 * 2 * 4   # scaled v_scale per seen cell
+    assert L.qsa_prompt_scratch_bytes(0, 0, GOOD) == 0
+    assert L.qsa_prompt_scratch_bytes(16, -1, GOOD) == 0
+    assert L.qsa_prompt_scratch_bytes(16, 0, D(24, 4, 64, 64)) == 0   # head_dim 64 has no prompt kernel
     p = _pool()
     assert L.qsa_prompt_attn(1, 16, 0, ctypes.byref(p), GOOD, 1.0, 1, None, 0, None) == -1       # no scratch
-    need = L.qsa_prompt_scratch_bytes(16, GOOD)
+    need = L.qsa_prompt_scratch_bytes(16, 0, GOOD)
     assert L.qsa_prompt_attn(1, 16, 0, ctypes.byref(p), GOOD, 1.0, 1, 1, need - 1, None) == -4
     assert L.qsa_prompt_attn(1, 16, 0, ctypes.byref(p), D(24, 4, 64, 64), 1.0, 1, 1, need, None) == -3
     assert L.qsa_prompt_attn(1, 0, 0, ctypes.byref(p), GOOD, 1.0, 1, None, 0, None) == 0

@@ -15,7 +15,7 @@ TOL = 1e-5
 
 def run_prompt(q, pos0, p_dev, dims, sm_scale=1.0):
     n_q = q.shape[0]
-    nbytes = qsa.qsa_prompt_scratch_bytes(n_q, dims)
+    nbytes = qsa.qsa_prompt_scratch_bytes(n_q, pos0, dims)
     scratch = torch.empty(max(nbytes, 1), dtype=torch.uint8, device="cuda")
     out = torch.full((n_q, dims.n_q_heads, dims.head_dim), float("nan"), dtype=torch.float32, device="cuda")
     qsa.qsa_prompt_attn(dev(q), pos0, p_dev, dims, out, sm_scale=sm_scale, scratch=scratch)
@@ -78,10 +78,13 @@ def test_prompt_chunk_full_size_sampled():
     assert np.all(np.isfinite(got))
     rng = np.random.default_rng(7)
     picks = [(0, 0), (1, 23), (63, 5), (64, 6), (1023, 11), (2047, 17), (2047, 0)]
-    picks += [(int(i), int(h)) for i, h in zip(rng.integers(0, 2048, 8), rng.integers(0, 24, 8))]
+    picks += [(int(i), int(h)) for i, h in zip(rng.integers(0, 2048, 33), rng.integers(0, 24, 33))]
+    errs = []
     for i, h in picks:
         ref, _ = oracle.attn_one(w.q, w.pos, i, h, pool, w.n_kv_heads)
-        assert rel_err_rows(got[i, h][None], ref[None]).max() <= TOL, (i, h)
+        errs.append(rel_err_rows(got[i, h][None], ref[None]).max())
+        assert errs[-1] <= TOL, (i, h)
+    print(f"prompt_chunk sampled rows: max rel err {max(errs):.3e} over {len(picks)} rows")
 
 
 def test_prompt_last_row_equals_dense_decode():
@@ -105,7 +108,7 @@ def test_prompt_last_row_equals_dense_decode():
 def test_prompt_scratch_too_small_is_rejected():
     pool = synth.random_pool(331, 2, 300, 260, 128)
     dims = qsa.Dims(12, 2, 128)
-    n = qsa.qsa_prompt_scratch_bytes(20, dims)
+    n = qsa.qsa_prompt_scratch_bytes(20, 230, dims)
     scratch = torch.empty(n - 1, dtype=torch.uint8, device="cuda")
     out = torch.empty(20, 12, 128, dtype=torch.float32, device="cuda")
     with pytest.raises(qsa.QSAError) as e:
