@@ -38,6 +38,7 @@ constexpr int PD = 128;          // head dim of the prompt kernel
 constexpr int PT = 64;           // cells per tile
 constexpr int PW = 4;            // waves per workgroup
 constexpr int PROWS = 16 * PW;   // rows (query, head) per workgroup
+constexpr int NBUF = 3;          // K/V tile buffers
 constexpr float PLOG2E = 1.4426950408889634f;
 constexpr float PLN2 = 0.6931471805599453f;
 constexpr float PDELTA = 4.0f;   // headroom (log2 units) added to the reference max at a fold
@@ -61,14 +62,24 @@ __device__ __forceinline__ uint32_t bperm(uint32_t s0, uint32_t s1, uint32_t sel
     return __builtin_amdgcn_perm(s0, s1, sel);
 }
 
-__device__ __forceinline__ void load_lds16(const void *src, QSA_LDS void *dst)
+// Global -> LDS copies (global_load_lds): lane l's bytes land at lds + size * l; lds must be wave-uniform. Written
+// as inline assembly so that the compiler does not track them: it would otherwise wait for every such load before
+// the next LDS read, which serialises the prefetch of the next tiles. The kernel waits for them itself (vmcnt).
+__device__ __forceinline__ void load_lds16(const void *src, uint32_t lds)
 {
-    __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
+    asm volatile("global_load_lds_dwordx4 %0, off" : : "v"(src), "{m0}"(lds) : "memory");
 }
-__device__ __forceinline__ void load_lds4(const void *src, QSA_LDS void *dst)
+__device__ __forceinline__ void load_lds4(const void *src, uint32_t lds)
 {
-    __builtin_amdgcn_global_load_lds(src, dst, 4, 0, 0);
+    asm volatile("global_load_lds_dword %0, off" : : "v"(src), "{m0}"(lds) : "memory");
 }
+__device__ __forceinline__ uint32_t lds_addr(const void *p)
+{
+    return (uint32_t)(uintptr_t)(const QSA_LDS void *)p;
+}
+// s_waitcnt immediates (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
+constexpr int WAIT_VM0_LGKM0 = 0x0070;   // all vector memory and LDS operations done
+constexpr int WAIT_VM5_LGKM0 = 0x0075;   // all but the 5 newest vector memory operations done, LDS done
 
 // ---------------------------------------------------------------------------------------------- q digits
 // One wave per (query, q head): qd[g][r][plane][d] int8 with r = query * G + head-in-group, plane 0/1/2 = h/l/m,
@@ -172,9 +183,10 @@ struct __align__(16) PromptTile {
 
 __global__ __launch_bounds__(256, 2) void prompt_attn_kernel(const PromptArgs a)
 {
-    __shared__ PromptTile tile[2];
+    __shared__ PromptTile tile[NBUF];
     __shared__ __align__(16) int8_t sq[PROWS * QROW];  // q digits of the workgroup's rows: [row][plane][128]
-    const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
+    const int tid = threadIdx.x, lane = tid % 64;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / 64);   // scalar: LDS destinations of the tile copies
     const int n16 = lane & 15, G4 = lane >> 4;
     const int32_t g = blockIdx.z, j = blockIdx.y;
     const int32_t row0 = blockIdx.x * PROWS;
@@ -244,6 +256,7 @@ __global__ __launch_bounds__(256, 2) void prompt_attn_kernel(const PromptArgs a)
     const int8_t *vg = P.v + (int64_t)g * P.capacity * PD;
     const float *ksg = P.ks + (int64_t)g * P.capacity * 2;
     const float *vsg = a.w + (int64_t)g * a.w_cells * 2;
+    // (each wave issues 5 copies per tile)
     auto stage = [&](int32_t t, int buf) {
         const int32_t cb = t * PT;
         PromptTile &T = tile[buf];
@@ -252,19 +265,21 @@ __global__ __launch_bounds__(256, 2) void prompt_attn_kernel(const PromptArgs a)
             const int slot = 128 * wave + 64 * h + lane;
             const int cell = slot >> 3, pos = slot & 7;
             const int32_t c = min(cb + cell, c_last);
-            load_lds16(kg + (int64_t)c * PD + 16 * (pos ^ swz_k(cell)),
-                       (QSA_LDS void *)(T.k + 1024 * (2 * wave + h)));
-            load_lds16(vg + (int64_t)c * PD + 16 * (pos ^ swz_v(cell)),
-                       (QSA_LDS void *)(T.v + 1024 * (2 * wave + h)));
+            load_lds16(kg + (int64_t)c * PD + 16 * (pos ^ swz_k(cell)), lds_addr(T.k + 1024 * (2 * wave + h)));
+            load_lds16(vg + (int64_t)c * PD + 16 * (pos ^ swz_v(cell)), lds_addr(T.v + 1024 * (2 * wave + h)));
         }
         const int e = 64 * (wave & 1) + lane;  // float e of the tile's [cell][grp] scales
         const int32_t c = min(cb + (e >> 1), c_last);
-        if (wave < 2) load_lds4(ksg + (int64_t)c * 2 + (e & 1), (QSA_LDS void *)(T.ks + 64 * (wave & 1)));
-        else load_lds4(vsg + (int64_t)c * 2 + (e & 1), (QSA_LDS void *)(T.vs + 64 * (wave & 1)));
+        if (wave < 2) load_lds4(ksg + (int64_t)c * 2 + (e & 1), lds_addr(T.ks + 64 * (wave & 1)));
+        else load_lds4(vsg + (int64_t)c * 2 + (e & 1), lds_addr(T.vs + 64 * (wave & 1)));
     };
 
+    // Tiles are triple-buffered and prefetched two ahead: tile t lives in buffer (t - t0) % 3, and its copies are
+    // issued at the start of step t - 2, so they have two steps to land.
     if (t0 < t1) stage(t0, 0);
-    __builtin_amdgcn_s_waitcnt(0);
+    if (t0 + 1 < t1) stage(t0 + 1, 1);
+    if (t0 + 1 < t1) __builtin_amdgcn_s_waitcnt(WAIT_VM5_LGKM0);   // tile t0 has landed
+    else __builtin_amdgcn_s_waitcnt(WAIT_VM0_LGKM0);
     __syncthreads();
 
     // Tiles before t_mask end at or before the wave's smallest limit and need no causal mask; the loop is split so
@@ -272,13 +287,14 @@ __global__ __launch_bounds__(256, 2) void prompt_attn_kernel(const PromptArgs a)
     const int32_t t_mask = wave_lim < PT - 1 ? 0 : (wave_lim - (PT - 1)) / PT + 1;
     auto step = [&](int32_t t, auto masked_tag) {
         constexpr bool masked = decltype(masked_tag)::value;
-        const int buf = (t - t0) & 1;
-        if (t + 1 < t1) stage(t + 1, buf ^ 1);
+        const int buf = (t - t0) % NBUF;
+        if (t + 2 < t1) stage(t + 2, (t + 2 - t0) % NBUF);   // the buffer tile t - 1 used
         const PromptTile &T = tile[buf];
         const int32_t cb = t * PT;
 
         // ---- S^T = K . Q^T, four 16-cell blocks; lane l ends with cells 16*G4 + 4b + v of row n16
         float t2[4][4];
+        __builtin_amdgcn_s_setprio(1);   // MFMA sections get issue priority over the other waves' VALU work
 #pragma unroll
         for (int b = 0; b < 4; b++) {
             const int cellA = 16 * (n16 >> 2) + 4 * b + (n16 & 3);
@@ -311,6 +327,7 @@ __global__ __launch_bounds__(256, 2) void prompt_attn_kernel(const PromptArgs a)
             }
         }
 
+        __builtin_amdgcn_s_setprio(0);
         // ---- row max over the tile; fold the int32 PV sums when it passes the reference
         float rm = t2[0][0];
 #pragma unroll
@@ -333,6 +350,7 @@ __global__ __launch_bounds__(256, 2) void prompt_attn_kernel(const PromptArgs a)
                 lsum *= alpha;
                 mref = mnew;
             }
+            __builtin_amdgcn_s_waitcnt(WAIT_VM0_LGKM0);   // the fold's stores are not left behind the tile copies
         }
         const float mexp = mref == -INFINITY ? 0.f : mref;
 
@@ -348,6 +366,7 @@ __global__ __launch_bounds__(256, 2) void prompt_attn_kernel(const PromptArgs a)
             }
         const int i = n16 >> 1, hh = n16 & 1;
         const int c0 = 16 * G4 + i, c1 = c0 + 8;   // (c & 7) == i for both
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int grp = 0; grp < 2; grp++) {
             v4i pd[4];   // digit planes d3, d2, d1, d0 of the lane's 16 cells
@@ -381,7 +400,10 @@ __global__ __launch_bounds__(256, 2) void prompt_attn_kernel(const PromptArgs a)
             }
         }
 
-        __builtin_amdgcn_s_waitcnt(0);   // this wave's loads of the next tile have landed in LDS
+        __builtin_amdgcn_s_setprio(0);
+        // this wave's copies of tile t + 1 have landed (those of tile t + 2 may still be in flight)
+        if (t + 2 < t1) __builtin_amdgcn_s_waitcnt(WAIT_VM5_LGKM0);
+        else __builtin_amdgcn_s_waitcnt(WAIT_VM0_LGKM0);
         __syncthreads();
     };
     int32_t t = t0;
