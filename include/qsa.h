@@ -3,7 +3,8 @@
  *
  * The decode path for one layer is four calls on one stream:
  *   qsa_block_scores -> qsa_topk -> qsa_attn_chunk -> qsa_attn_merge
- * (plus qsa_block_index when cells are appended), and the prompt path is one call, qsa_prompt_attn.
+ * or the same work as one call in three launches, qsa_decode_layer (plus qsa_block_index when cells are
+ * appended); the prompt path is one call, qsa_prompt_attn.
  *
  * Sources for what each call computes (pull requests against one inference engine):
  *   [1888] "#1888 QSA decode attention: split each query's cells across blocks on the int8 mma path"
@@ -152,6 +153,34 @@ size_t qsa_prompt_scratch_bytes(int32_t n_q, int32_t pos0, qsa_dims dims);
  * (QSA_ERR_UNSUPPORTED otherwise) and scratch_bytes >= qsa_prompt_scratch_bytes (QSA_ERR_SCRATCH). */
 qsa_status qsa_prompt_attn(const float *q, int32_t n_q, int32_t pos0, const qsa_pool *pool, qsa_dims dims,
                            float sm_scale, float *out, void *scratch, size_t scratch_bytes, qsa_stream_t stream);
+
+/* Block scores and radix top-k in one launch ([2806] Summary), one workgroup per (row, KV head) holding its score
+ * row in LDS: the same scores as qsa_block_scores (same fp32 arithmetic in the same order) over n_blocks columns
+ * of each row's pool (pools[row_pool[i]], row_pool NULL = pool 0), and the same ids and counts as qsa_topk with k.
+ * ids [n_rows][n_kv][k] and counts [n_rows][n_kv] are required; scores [n_rows][n_kv][n_blocks] may be NULL. A row
+ * whose device-side row_pool value is out of range has no eligible block. Requires every pool to carry K, V, both
+ * scales and an index, 1 <= k <= n_blocks <= 16,384 and n_blocks <= ceil(capacity / 64) for every pool. */
+qsa_status qsa_decode_select(const float *q, const int32_t *pos, int32_t n_rows, const qsa_pool *pools,
+                             int32_t n_pools, const int32_t *row_pool, qsa_dims dims, int32_t n_blocks, int32_t k,
+                             float *scores, int32_t *ids, int32_t *counts, qsa_stream_t stream);
+
+/* Scratch bytes qsa_decode_layer needs (0 if the arguments are invalid). */
+size_t qsa_decode_layer_scratch_bytes(int32_t n_rows, qsa_dims dims, int32_t k, int32_t n_chunks);
+
+/* One decode layer in three launches: qsa_decode_select, then qsa_attn_chunk in sparse mode with n_chunks, then
+ * qsa_attn_merge over all n_chunks ([2806] Summary: fewer, shorter launches per layer). For every row i (pool
+ * pools[row_pool[i]], row_pool NULL = pool 0) and KV head g it computes the same scores, ids and counts as
+ * qsa_block_scores + qsa_topk, and the same output as qsa_attn_chunk + qsa_attn_merge on them:
+ *   out [n_rows][n_q_heads][head_dim]; lse [n_rows][n_q_heads] (may be NULL).
+ * scores [n_rows][n_kv][n_blocks], ids [n_rows][n_kv][k] and counts [n_rows][n_kv] are optional outputs (NULL:
+ * kept in scratch). Requires every pool to carry K, V, both scales and an index, 1 <= k <= n_blocks <= 16,384,
+ * n_blocks <= ceil(capacity / 64) for every pool, n_chunks >= 1, and scratch_bytes >=
+ * qsa_decode_layer_scratch_bytes (QSA_ERR_SCRATCH); scratch holds the chunk partials (and ids and counts when they
+ * are not asked for). Calls sharing one scratch buffer must be ordered on one stream. */
+qsa_status qsa_decode_layer(const float *q, const int32_t *pos, int32_t n_rows, const qsa_pool *pools, int32_t n_pools,
+                            const int32_t *row_pool, qsa_dims dims, int32_t n_blocks, int32_t k, int32_t n_chunks,
+                            float sm_scale, float *out, float *lse, float *scores, int32_t *ids, int32_t *counts,
+                            void *scratch, size_t scratch_bytes, qsa_stream_t stream);
 
 /* Static, human-readable name of a status code. */
 const char *qsa_status_str(qsa_status status);

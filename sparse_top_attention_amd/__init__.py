@@ -69,10 +69,15 @@ def _lib():
         L.qsa_prompt_scratch_bytes.argtypes = [I32, I32, PD]
         L.qsa_prompt_scratch_bytes.restype = SZ
         L.qsa_prompt_attn.argtypes = [P, I32, I32, PP, PD, ctypes.c_float, P, P, SZ, P]
+        L.qsa_decode_select.argtypes = [P, P, I32, PP, I32, P, PD, I32, I32, P, P, P, P]
+        L.qsa_decode_layer_scratch_bytes.argtypes = [I32, PD, I32, I32]
+        L.qsa_decode_layer_scratch_bytes.restype = SZ
+        L.qsa_decode_layer.argtypes = [P, P, I32, PP, I32, P, PD, I32, I32, I32, ctypes.c_float, P, P, P, P, P, P,
+                                       SZ, P]
         L.qsa_status_str.argtypes = [I32]
         L.qsa_status_str.restype = ctypes.c_char_p
         for fn in ("qsa_block_index", "qsa_block_scores", "qsa_topk", "qsa_attn_chunk", "qsa_attn_merge",
-                   "qsa_prompt_attn"):
+                   "qsa_prompt_attn", "qsa_decode_layer", "qsa_decode_select"):
             getattr(L, fn).restype = I32
         _L = L
     return _L
@@ -217,6 +222,36 @@ def qsa_attn_merge(part: Partials, dims: Dims, n_chunks: int, out, lse=None, n_a
     return out
 
 
+def qsa_decode_select(q, pos, pools: Sequence[Pool], dims: Dims, n_blocks: int, k: int, ids, counts, scores=None,
+                      row_pool=None, stream=None):
+    arr = (_Pool * len(pools))(*[p.c() for p in pools])
+    _check("qsa_decode_select", _lib().qsa_decode_select(
+        _ptr(q, torch.float32, "q"), _ptr(pos, torch.int32, "pos"), q.shape[0], arr, len(pools),
+        _ptr(row_pool, torch.int32, "row_pool", allow_none=True), dims.c(), n_blocks, k,
+        _ptr(scores, torch.float32, "scores", allow_none=True), _ptr(ids, torch.int32, "ids"),
+        _ptr(counts, torch.int32, "counts"), _stream(stream)))
+    return ids, counts
+
+
+def qsa_decode_layer_scratch_bytes(n_rows, dims: Dims, k, n_chunks):
+    return _lib().qsa_decode_layer_scratch_bytes(n_rows, dims.c(), k, n_chunks)
+
+
+def qsa_decode_layer(q, pos, pools: Sequence[Pool], dims: Dims, n_blocks: int, k: int, n_chunks: int, out, lse=None,
+                     sm_scale: float = 1.0, row_pool=None, scores=None, ids=None, counts=None, scratch=None,
+                     stream=None):
+    arr = (_Pool * len(pools))(*[p.c() for p in pools])
+    sp = None if scratch is None else _ptr(scratch, torch.uint8, "scratch")
+    nbytes = 0 if scratch is None else scratch.numel()
+    _check("qsa_decode_layer", _lib().qsa_decode_layer(
+        _ptr(q, torch.float32, "q"), _ptr(pos, torch.int32, "pos"), q.shape[0], arr, len(pools),
+        _ptr(row_pool, torch.int32, "row_pool", allow_none=True), dims.c(), n_blocks, k, n_chunks, sm_scale,
+        _ptr(out, torch.float32, "out"), _ptr(lse, torch.float32, "lse", allow_none=True),
+        _ptr(scores, torch.float32, "scores", allow_none=True), _ptr(ids, torch.int32, "ids", allow_none=True),
+        _ptr(counts, torch.int32, "counts", allow_none=True), sp, nbytes, _stream(stream)))
+    return out
+
+
 def qsa_prompt_scratch_bytes(n_q, pos0, dims: Dims):
     return _lib().qsa_prompt_scratch_bytes(n_q, pos0, dims.c())
 
@@ -237,4 +272,5 @@ def qsa_status_str(status: int) -> str:
 
 __all__ = ["Dims", "Pool", "Partials", "QSAError", "qsa_block_index", "qsa_block_scores", "qsa_topk_scratch_bytes",
            "qsa_topk", "qsa_attn_chunk", "qsa_attn_merge", "qsa_prompt_scratch_bytes", "qsa_prompt_attn",
+           "qsa_decode_select", "qsa_decode_layer_scratch_bytes", "qsa_decode_layer",
            "qsa_status_str", "lib_handle"]

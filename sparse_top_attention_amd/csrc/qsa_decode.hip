@@ -14,6 +14,7 @@
 namespace qsa {
 
 constexpr float LOG2E = 1.4426950408889634f;
+
 constexpr float LN2 = 0.6931471805599453f;
 
 __device__ __forceinline__ void unpack16(const int4 w, float (&x)[16])
@@ -84,19 +85,20 @@ __global__ __launch_bounds__(64) void block_scores_kernel(const float *__restric
     const int32_t bw = blockIdx.x * (BPS * NSTEP);
     float rv[NSTEP][8];
     int32_t bidx[NSTEP];
+    // unconditional loads (a dead block reads block 0, then counts as zeros), so all are issued before any wait
+    const int32_t n_live = min(n_blocks, (int32_t)(((int64_t)n_valid + QSA_BLOCK - 1) / QSA_BLOCK));
 #pragma unroll
     for (int st = 0; st < NSTEP; st++) {
         const int32_t b = bw + st * BPS + rb;
         bidx[st] = b;
-        if (b < n_blocks && (int64_t)b * QSA_BLOCK < n_valid) {
-            const float4 *src = reinterpret_cast<const float4 *>(index + ((int64_t)g * blk_stride + b) * D + 8 * s);
-            const float4 u = src[0], w = src[1];
-            rv[st][0] = u.x; rv[st][1] = u.y; rv[st][2] = u.z; rv[st][3] = u.w;
-            rv[st][4] = w.x; rv[st][5] = w.y; rv[st][6] = w.z; rv[st][7] = w.w;
-        } else {
+        const bool live = b < n_live;
+        const float4 *src =
+            reinterpret_cast<const float4 *>(index + ((int64_t)g * blk_stride + (live ? b : 0)) * D + 8 * s);
+        const float4 u = src[0], w = src[1];
+        rv[st][0] = u.x; rv[st][1] = u.y; rv[st][2] = u.z; rv[st][3] = u.w;
+        rv[st][4] = w.x; rv[st][5] = w.y; rv[st][6] = w.z; rv[st][7] = w.w;
 #pragma unroll
-            for (int e = 0; e < 8; e++) rv[st][e] = 0.f;
-        }
+        for (int e = 0; e < 8; e++) rv[st][e] = live ? rv[st][e] : 0.f;
     }
     for (int32_t i0 = 0; i0 < n_rows; i0 += 8) {
         const int nr = min(8, n_rows - i0);
@@ -151,7 +153,6 @@ struct ChunkArgs {
     int32_t n_qh;
     int32_t n_kv;
     int32_t G;
-    int32_t n_hsub;
     int32_t topk;
     int32_t bpc;
     int32_t n_chunks;
@@ -159,24 +160,40 @@ struct ChunkArgs {
     float qscale;  // sm_scale * log2(e): logits are kept in base-2 units inside the kernel
 };
 
-// One workgroup of CW waves per (chunk j, KV head g x head subset, row i); wave w takes blocks w, w + CW, ... of
-// the chunk's run. In a wave each lane owns one cell slot r (cells r, r + CPS, ... of a block) and one 16-dim
-// slice s. Per block: all K/V loads are issued first (addresses clamped to a visible cell, invisible cells masked
-// afterwards), then q.k for HPW heads, a wave-wide block max per head, then p.v. The running max is shared by
-// the whole wave, so the cell slots are folded with plain sums at the end; the CW waves are combined through LDS
-// with a log-sum-exp rescale.
+// One workgroup of CW waves per (chunk j, KV head g, row i); every wave handles all G q heads of the KV head, so
+// each K/V byte is converted once for all of them. The chunk's blocks are cut into pieces of PC cells; wave w takes
+// pieces w, w + CW, ... and keeps a running (max, sum, output) per head over them.
+//
+// q . k runs in the "cell x slice" layout (LPC lanes per cell, 16 dims each; a 3-4 step DPP sum finishes each
+// logit, after which all lanes of the cell hold it). p . v runs in a "lane owns dims" layout: the piece's V codes go
+// from HBM straight into the wave's LDS (global_load_lds, 16-byte chunks swizzled by cell), and ds_read_b64_tr_b8
+// hands each lane 8 cells of one dim per read; p * v_scale per (cell, scale group, head) is written to LDS by the
+// q . k lanes and read back as a broadcast. Each lane then owns D/64 output dims of every head, so nothing is summed
+// across lanes at the end; the CW waves are combined through LDS with a log-sum-exp rescale.
 constexpr int CW = 4;
 
-template <int D, int HPW>
+template <int D, int G>
 __global__ __launch_bounds__(64 * CW) void attn_chunk_kernel(const ChunkArgs a)
 {
-    constexpr int LPC = D / 16, CPS = 64 / LPC, STEPS = QSA_BLOCK / CPS, NG = D / QSA_GROUP;
-    __shared__ float sm[CW][HPW], sl[CW][HPW];
-    __shared__ float so[CW][HPW][D];
-    const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
-    const int r = lane / LPC, s = lane % LPC, grp = (16 * s) / QSA_GROUP;
-    const int32_t j = blockIdx.x, i = blockIdx.z;
-    const int32_t g = blockIdx.y / a.n_hsub, h0 = g * a.G + (blockIdx.y % a.n_hsub) * HPW;
+    constexpr int PC = D <= 128 ? 32 : 16;           // cells per piece
+    constexpr int LPC = D / 16, CPS = 64 / LPC, STEPS = PC / CPS, NG = D / QSA_GROUP;
+    constexpr int DPL = D / 64;                      // output dims per lane
+    constexpr int SUBS = 4 / NG;                     // 16-lane subgroups per scale group in the p . v layout
+    constexpr int CHUNKS = D / 16;                   // 16-byte chunks per cell row
+    constexpr int SWZ = (CHUNKS < 8 ? CHUNKS : 8) - 1;
+    constexpr int VCH = PC * D / 1024;               // 1 KB global -> LDS copies per piece
+    constexpr int GP = (G + 3) & ~3;                 // p * v_scale row padded to float4s
+    __shared__ __align__(16) int8_t sv[CW][PC * D];  // the wave's V piece: [cell][D], chunk c of row r at c ^ (r & SWZ)
+    __shared__ __align__(16) float sp[CW][PC][NG][GP];
+    __shared__ float sm[CW][G], sl[CW][G];
+    __shared__ float so[CW][G][D];
+    const int tid = threadIdx.x, lane = tid % 64;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
+    const int r = lane / LPC, s = lane % LPC, grp_s = s / (LPC / NG);
+    const int G4 = lane >> 4, jl = lane & 15;
+    const int grp_v = G4 / SUBS, sub_v = G4 % SUBS;  // the p . v lane's scale group and subgroup
+    const int32_t j = blockIdx.x, g = blockIdx.y, i = blockIdx.z;
+    const int32_t h0 = g * G;
 
     const int32_t pidx = a.row_pool ? a.row_pool[i] : 0;
     const bool pool_ok = pidx >= 0 && pidx < a.n_pools;
@@ -185,73 +202,83 @@ __global__ __launch_bounds__(64 * CW) void attn_chunk_kernel(const ChunkArgs a)
 
     int32_t n_blk, first;
     const int32_t *blist = nullptr;
+    int32_t idv = 0;   // with k <= 64: the row's whole id list, one id per lane, loaded alongside its count
     if (a.ids) {
+        blist = a.ids + ((int64_t)i * a.n_kv + g) * a.topk;
+        if (a.topk <= 64) idv = blist[lane < a.topk ? lane : 0];   // unconditional load: no wait at a branch end
         int32_t cnt = a.counts[(int64_t)i * a.n_kv + g];
         cnt = cnt < 0 ? 0 : (cnt > a.topk ? a.topk : cnt);
         const int32_t base = cnt / a.n_chunks, rem = cnt % a.n_chunks;
         n_blk = base + (j < rem ? 1 : 0);
         first = j * base + (j < rem ? j : rem);
-        blist = a.ids + ((int64_t)i * a.n_kv + g) * a.topk;
     } else {
         n_blk = a.bpc;
         first = j * a.bpc;
     }
 
-    float qv[HPW][16];
+    float qv[G][16];
 #pragma unroll
-    for (int h = 0; h < HPW; h++) {
+    for (int h = 0; h < G; h++) {
         const float4 *src = reinterpret_cast<const float4 *>(a.q + ((int64_t)i * a.n_qh + h0 + h) * D + 16 * s);
 #pragma unroll
         for (int jj = 0; jj < 4; jj++) {
             const float4 u = src[jj];
-            qv[h][4 * jj + 0] = u.x * a.qscale;
-            qv[h][4 * jj + 1] = u.y * a.qscale;
-            qv[h][4 * jj + 2] = u.z * a.qscale;
-            qv[h][4 * jj + 3] = u.w * a.qscale;
+            qv[h][4 * jj + 0] = u.x;
+            qv[h][4 * jj + 1] = u.y;
+            qv[h][4 * jj + 2] = u.z;
+            qv[h][4 * jj + 3] = u.w;
         }
     }
-    float mrun[HPW], lrun[HPW], o[HPW][16];
+    float mrun[G], lpart[G], o[G][DPL];
 #pragma unroll
-    for (int h = 0; h < HPW; h++) {
+    for (int h = 0; h < G; h++) {
         mrun[h] = -INFINITY;
-        lrun[h] = 0.f;
+        lpart[h] = 0.f;
 #pragma unroll
-        for (int e = 0; e < 16; e++) o[h][e] = 0.f;
+        for (int t = 0; t < DPL; t++) o[h][t] = 0.f;
     }
 
     const int8_t *kbase = P.k + (int64_t)g * P.capacity * D + 16 * s;
-    const int8_t *vbase = P.v + (int64_t)g * P.capacity * D + 16 * s;
-    const float *ksbase = P.ks + (int64_t)g * P.capacity * NG + grp;
-    const float *vsbase = P.vs + (int64_t)g * P.capacity * NG + grp;
+    const int8_t *vbase = P.v + (int64_t)g * P.capacity * D;
+    const float *ksbase = P.ks + (int64_t)g * P.capacity * NG + grp_s;
+    const float *vsbase = P.vs + (int64_t)g * P.capacity * NG + (s < NG ? s : 0);
+    int8_t *svw = sv[wave];
+    constexpr int PPB = QSA_BLOCK / PC;              // pieces per block
 
-    for (int32_t t = wave; t < n_blk; t += CW) {
-        const int32_t b = blist ? blist[first + t] : first + t;
-        if (b < 0 || (int64_t)b * QSA_BLOCK > limit) continue;  // negative id, or no visible valid cell
-        const int32_t cb = b * QSA_BLOCK;
+    for (int32_t pc = wave; pc < n_blk * PPB; pc += CW) {
+        const int32_t t_blk = first + pc / PPB;
+        const int32_t b = !blist ? t_blk : (a.topk <= 64 ? __builtin_amdgcn_readlane(idv, t_blk) : blist[t_blk]);
+        // negative id, or no visible valid cell in the piece (64-bit: ids past the pool may be huge)
+        if (b < 0 || (int64_t)b * QSA_BLOCK + (pc % PPB) * PC > limit) continue;
+        const int32_t cb = b * QSA_BLOCK + (pc % PPB) * PC;
 
-        int4 kw[STEPS], vw[STEPS];
+        // ---- loads: K slices and scales into registers, the V piece into LDS
+        int4 kw[STEPS];
         float ksc[STEPS], vsc[STEPS];
 #pragma unroll
         for (int st = 0; st < STEPS; st++) {
             const int32_t c = min(cb + st * CPS + r, limit);
             kw[st] = *reinterpret_cast<const int4 *>(kbase + (int64_t)c * D);
-            ksc[st] = ksbase[(int64_t)c * NG];
-        }
-#pragma unroll
-        for (int st = 0; st < STEPS; st++) {
-            const int32_t c = min(cb + st * CPS + r, limit);
-            vw[st] = *reinterpret_cast<const int4 *>(vbase + (int64_t)c * D);
+            ksc[st] = ksbase[(int64_t)c * NG] * a.qscale;   // sm_scale * log2(e) rides on the key scale
             vsc[st] = vsbase[(int64_t)c * NG];
         }
+#pragma unroll
+        for (int q = 0; q < VCH; q++) {
+            const int slot = 64 * q + lane, cell = slot / CHUNKS, pch = slot % CHUNKS;
+            const int32_t c = min(cb + cell, limit);
+            __builtin_amdgcn_global_load_lds(vbase + (int64_t)c * D + 16 * (pch ^ (cell & SWZ)),
+                                             (QSA_LDS void *)(svw + 1024 * q), 16, 0, 0);
+        }
 
-        float lg[STEPS][HPW];
+        // ---- logits (base-2 units), masked past the limit
+        float lg[STEPS][G];
 #pragma unroll
         for (int st = 0; st < STEPS; st++) {
             const bool vis = cb + st * CPS + r <= limit;
             float x[16];
             unpack16(kw[st], x);
 #pragma unroll
-            for (int h = 0; h < HPW; h++) {
+            for (int h = 0; h < G; h++) {
                 float dot = 0.f;
 #pragma unroll
                 for (int e = 0; e < 16; e++) dot = fmaf(qv[h][e], x[e], dot);
@@ -259,58 +286,98 @@ __global__ __launch_bounds__(64 * CW) void attn_chunk_kernel(const ChunkArgs a)
                 lg[st][h] = vis ? dot : -INFINITY;
             }
         }
+
+        // ---- running max per head; p = 2^(logit - max); p * v_scale to LDS by the first NG lanes of each cell
 #pragma unroll
-        for (int h = 0; h < HPW; h++) {
+        for (int h = 0; h < G; h++) {
             float mb = lg[0][h];
 #pragma unroll
             for (int st = 1; st < STEPS; st++) mb = fmaxf(mb, lg[st][h]);
-            mb = strided_max<LPC>(mb);            // the block holds a visible cell, so mb is finite
+            mb = strided_max<LPC>(mb);            // the piece holds a visible cell, so mb is finite
             const float mnew = fmaxf(mrun[h], mb);
-            const float alpha = __builtin_amdgcn_exp2f(mrun[h] - mnew);  // 0 on the first block
+            const float alpha = __builtin_amdgcn_exp2f(mrun[h] - mnew);  // 0 on the first piece
             mrun[h] = mnew;
-            lrun[h] *= alpha;
+            lpart[h] *= alpha;
 #pragma unroll
-            for (int e = 0; e < 16; e++) o[h][e] *= alpha;
+            for (int t = 0; t < DPL; t++) o[h][t] *= alpha;
+#pragma unroll
+            for (int st = 0; st < STEPS; st++) {
+                const float p = __builtin_amdgcn_exp2f(lg[st][h] - mnew);   // masked cells: 2^-inf = 0
+                lpart[h] += p;
+                lg[st][h] = p;
+            }
         }
+        if (s < NG) {
 #pragma unroll
-        for (int st = 0; st < STEPS; st++) {
-            float x[16];
-            unpack16(vw[st], x);
+            for (int st = 0; st < STEPS; st++) {
+                float *dst = &sp[wave][st * CPS + r][s][0];
+                // masked cells have p = 0 but their v_scale may be anything (even NaN): their rows are zeroed
+                const float w = cb + st * CPS + r <= limit ? vsc[st] : 0.f;
 #pragma unroll
-            for (int h = 0; h < HPW; h++) {
-                const float p = __builtin_amdgcn_exp2f(lg[st][h] - mrun[h]);   // masked cells: 2^-inf = 0
-                lrun[h] += p;
-                const float wgt = p * vsc[st];
+                for (int h4 = 0; h4 < GP; h4 += 4) {
+                    float4 v4;
+                    v4.x = h4 + 0 < G ? lg[st][h4 + 0 < G ? h4 + 0 : 0] * w : 0.f;
+                    v4.y = h4 + 1 < G ? lg[st][h4 + 1 < G ? h4 + 1 : 0] * w : 0.f;
+                    v4.z = h4 + 2 < G ? lg[st][h4 + 2 < G ? h4 + 2 : 0] * w : 0.f;
+                    v4.w = h4 + 3 < G ? lg[st][h4 + 3 < G ? h4 + 3 : 0] * w : 0.f;
+                    *reinterpret_cast<float4 *>(dst + h4) = v4;
+                }
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(0);   // the V piece has landed and the p rows are written (this wave only)
+
+        // ---- o[h][dim] += sum over cells of (p * v_scale)[cell][h] * v[cell][dim]
+        const int i8 = jl >> 1, hh = jl & 1;
 #pragma unroll
-                for (int e = 0; e < 16; e++) o[h][e] = fmaf(wgt, x[e], o[h][e]);
+        for (int co = 0; co < PC / 8; co++) {
+            v2i vb[DPL];
+#pragma unroll
+            for (int t = 0; t < DPL; t++) {
+                const int lc = 4 * grp_v + sub_v + SUBS * t;   // logical 16-byte chunk of the lane's dim block
+                const int cell = 8 * co + i8;
+                vb[t] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                    (QSA_LDS v2i *)(svw + cell * D + 16 * (lc ^ (cell & SWZ)) + 8 * hh));
+            }
+#pragma unroll
+            for (int ci = 0; ci < 8; ci++) {
+                const float *prow = &sp[wave][8 * co + ci][grp_v][0];
+                float pw[GP];
+#pragma unroll
+                for (int h4 = 0; h4 < GP; h4 += 4) {
+                    const float4 v4 = *reinterpret_cast<const float4 *>(prow + h4);
+                    pw[h4] = v4.x; pw[h4 + 1] = v4.y; pw[h4 + 2] = v4.z; pw[h4 + 3] = v4.w;
+                }
+#pragma unroll
+                for (int t = 0; t < DPL; t++) {
+                    const int32_t word = ci < 4 ? vb[t][0] : vb[t][1];
+                    const float x = (float)((word << (24 - 8 * (ci & 3))) >> 24);
+#pragma unroll
+                    for (int h = 0; h < G; h++) o[h][t] = fmaf(pw[h], x, o[h][t]);
+                }
             }
         }
     }
 
-    // fold the cell slots (lanes LPC apart share a slice) and hand the wave's partial to LDS
+    // ---- hand the wave's partial to LDS: lane 0 the maxima and sums, every lane its own dims of o
 #pragma unroll
-    for (int h = 0; h < HPW; h++) {
-        lrun[h] = strided_sum<LPC>(lrun[h]);
-#pragma unroll
-        for (int e = 0; e < 16; e++) o[h][e] = strided_sum<LPC>(o[h][e]);
-    }
+    for (int h = 0; h < G; h++) lpart[h] = strided_sum<LPC>(lpart[h]);
     if (lane == 0) {
 #pragma unroll
-        for (int h = 0; h < HPW; h++) {
+        for (int h = 0; h < G; h++) {
             sm[wave][h] = mrun[h];
-            sl[wave][h] = lrun[h];
+            sl[wave][h] = lpart[h];
         }
     }
 #pragma unroll
-    for (int h = 0; h < HPW; h++)
-        if (r == h % CPS) {
+    for (int t = 0; t < DPL; t++) {
+        const int d = 64 * grp_v + 16 * sub_v + 16 * SUBS * t + jl;
 #pragma unroll
-            for (int e = 0; e < 16; e++) so[wave][h][16 * s + e] = o[h][e];
-        }
+        for (int h = 0; h < G; h++) so[wave][h][d] = o[h][t];
+    }
     __syncthreads();
 
     // combine the CW waves: M = max m_w, out = sum e^(m_w - M) o_w (waves without a cell have m_w = -inf)
-    for (int idx = tid; idx < HPW * D; idx += 64 * CW) {
+    for (int idx = tid; idx < G * D; idx += 64 * CW) {
         const int h = idx / D, d = idx % D;
         float M = sm[0][h];
 #pragma unroll
@@ -323,7 +390,7 @@ __global__ __launch_bounds__(64 * CW) void attn_chunk_kernel(const ChunkArgs a)
         }
         a.o_out[(((int64_t)i * a.n_qh + h0 + h) * a.max_chunks + j) * D + d] = num;
     }
-    if (tid < HPW) {
+    if (tid < G) {
         const int h = tid;
         float M = sm[0][h];
 #pragma unroll
@@ -455,30 +522,27 @@ extern "C" qsa_status qsa_block_scores(const float *q, const int32_t *pos, int32
 
 namespace {
 template <int D>
-void launch_chunk(int hpw, dim3 grid, hipStream_t s, const ChunkArgs &a)
+void launch_chunk(int G, dim3 grid, hipStream_t s, const ChunkArgs &a)
 {
-    // only the head counts heads_per_wave can pick for this head dim are instantiated
-    if constexpr (D == 256) {
-        attn_chunk_kernel<D, 1><<<grid, 64 * CW, 0, s>>>(a);
-    } else {
-        switch (hpw) {
-        case 1: attn_chunk_kernel<D, 1><<<grid, 64 * CW, 0, s>>>(a); break;
-        case 2: attn_chunk_kernel<D, 2><<<grid, 64 * CW, 0, s>>>(a); break;
-        case 3: attn_chunk_kernel<D, 3><<<grid, 64 * CW, 0, s>>>(a); break;
-        default:
-            if constexpr (D == 64) attn_chunk_kernel<D, 4><<<grid, 64 * CW, 0, s>>>(a);
-            break;
-        }
+    switch (G) {
+    case 1: attn_chunk_kernel<D, 1><<<grid, 64 * CW, 0, s>>>(a); break;
+    case 2: attn_chunk_kernel<D, 2><<<grid, 64 * CW, 0, s>>>(a); break;
+    case 3: attn_chunk_kernel<D, 3><<<grid, 64 * CW, 0, s>>>(a); break;
+    case 4: attn_chunk_kernel<D, 4><<<grid, 64 * CW, 0, s>>>(a); break;
+    case 5: attn_chunk_kernel<D, 5><<<grid, 64 * CW, 0, s>>>(a); break;
+    case 6: attn_chunk_kernel<D, 6><<<grid, 64 * CW, 0, s>>>(a); break;
+    case 7: attn_chunk_kernel<D, 7><<<grid, 64 * CW, 0, s>>>(a); break;
+    default: attn_chunk_kernel<D, 8><<<grid, 64 * CW, 0, s>>>(a); break;
     }
 }
 
-// q heads handled by one wave: the largest divisor of G within the register budget of the head dim.
-int heads_per_wave(int G, int D)
+void launch_chunk_d(int D, int G, dim3 grid, hipStream_t s, const ChunkArgs &a)
 {
-    const int cap = D == 64 ? 4 : (D == 128 ? 3 : 1);
-    for (int h = cap; h >= 1; h--)
-        if (G % h == 0) return h;
-    return 1;
+    switch (D) {
+    case 64: launch_chunk<64>(G, grid, s, a); break;
+    case 128: launch_chunk<128>(G, grid, s, a); break;
+    default: launch_chunk<256>(G, grid, s, a); break;
+    }
 }
 }  // namespace
 
@@ -514,17 +578,11 @@ extern "C" qsa_status qsa_attn_chunk(const float *q, const int32_t *pos, int32_t
                              pools[p].n_valid};
     a.n_pools = row_pool ? n_pools : 1;
     a.n_qh = dims.n_q_heads; a.n_kv = dims.n_kv_heads; a.G = dims.n_q_heads / dims.n_kv_heads;
-    const int hpw = heads_per_wave(a.G, dims.head_dim);
-    a.n_hsub = a.G / hpw;
     a.topk = k; a.bpc = blocks_per_chunk; a.n_chunks = n_chunks; a.max_chunks = out->max_chunks;
     a.qscale = sm_scale * LOG2E;
-    dim3 grid(n_chunks, dims.n_kv_heads * a.n_hsub, n_rows);
+    dim3 grid(n_chunks, dims.n_kv_heads, n_rows);
     hipStream_t s = (hipStream_t)stream;
-    switch (dims.head_dim) {
-    case 64: launch_chunk<64>(hpw, grid, s, a); break;
-    case 128: launch_chunk<128>(hpw, grid, s, a); break;
-    default: launch_chunk<256>(hpw, grid, s, a); break;
-    }
+    launch_chunk_d(dims.head_dim, a.G, grid, s, a);
     return launch_status();
 }
 
@@ -555,6 +613,119 @@ extern "C" qsa_status qsa_attn_merge(const qsa_partials *in, int32_t n_rows, qsa
     if (n_rows == 0) return QSA_OK;
     return merge_launch(in->m, in->l, in->o, in->empty, in->max_chunks, n_chunks, n_active, n_rows, dims.n_q_heads,
                         dims.head_dim, out, lse, (hipStream_t)stream);
+}
+
+// ======================================================================================= fused decode layer
+namespace {
+struct LayerScratch {
+    size_t m, l, e, o, ids, counts, total;
+};
+
+LayerScratch layer_layout(int32_t n_rows, const qsa_dims &d, int32_t k, int32_t n_chunks)
+{
+    auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    const size_t rh = (size_t)n_rows * d.n_q_heads * n_chunks;
+    const size_t rk = (size_t)n_rows * d.n_kv_heads;
+    LayerScratch s{};
+    size_t off = 0;
+    s.m = off; off += al(rh * sizeof(float));
+    s.l = off; off += al(rh * sizeof(float));
+    s.e = off; off += al(rh);
+    s.o = off; off += al(rh * d.head_dim * sizeof(float));
+    s.ids = off; off += al(rk * k * sizeof(int32_t));
+    s.counts = off; off += al(rk * sizeof(int32_t));
+    s.total = off;
+    return s;
+}
+}  // namespace
+
+namespace {
+// Shared argument checks and pool marshalling of the fused selection.
+qsa_status select_setup(const float *q, const int32_t *pos, int32_t n_rows, const qsa_pool *pools, int32_t n_pools,
+                        const int32_t *row_pool, const qsa_dims &dims, int32_t n_blocks, int32_t k, SelectArgs &sa)
+{
+    qsa_status st = check_dims(dims);
+    if (st != QSA_OK) return st;
+    if (!q || !pos || !pools) return QSA_ERR_NULL;
+    if (n_rows < 0 || n_pools <= 0 || n_blocks < 0) return QSA_ERR_SHAPE;
+    if (n_pools > QSA_MAX_POOLS) return QSA_ERR_UNSUPPORTED;
+    for (int32_t p = 0; p < n_pools; p++) {
+        if ((st = check_pool(&pools[p], true)) != QSA_OK) return st;
+        if (!pools[p].index) return QSA_ERR_NULL;
+        if (n_blocks > ceil_div(pools[p].capacity, QSA_BLOCK)) return QSA_ERR_RANGE;
+    }
+    if (k < 1 || k > n_blocks) return QSA_ERR_RANGE;
+    if (n_blocks > 256 * 64) return QSA_ERR_UNSUPPORTED;
+    if (n_rows > 65535) return QSA_ERR_UNSUPPORTED;
+    sa = SelectArgs{};
+    sa.q = q; sa.pos = pos; sa.row_pool = row_pool;
+    for (int32_t p = 0; p < n_pools; p++)
+        sa.pools[p] = PoolArg{pools[p].k, pools[p].k_scale, pools[p].v, pools[p].v_scale, pools[p].capacity,
+                              pools[p].n_valid, pools[p].index};
+    sa.n_pools = row_pool ? n_pools : 1;
+    sa.n_qh = dims.n_q_heads; sa.n_kv = dims.n_kv_heads; sa.G = dims.n_q_heads / dims.n_kv_heads;
+    sa.width = n_blocks; sa.k = k;
+    return QSA_OK;
+}
+}  // namespace
+
+extern "C" qsa_status qsa_decode_select(const float *q, const int32_t *pos, int32_t n_rows, const qsa_pool *pools,
+                                        int32_t n_pools, const int32_t *row_pool, qsa_dims dims, int32_t n_blocks,
+                                        int32_t k, float *scores, int32_t *ids, int32_t *counts, qsa_stream_t stream)
+{
+    SelectArgs sa;
+    qsa_status st = select_setup(q, pos, n_rows, pools, n_pools, row_pool, dims, n_blocks, k, sa);
+    if (st != QSA_OK) return st;
+    if (!ids || !counts) return QSA_ERR_NULL;
+    if (n_rows == 0) return QSA_OK;
+    sa.ids = ids; sa.counts = counts; sa.scores = scores;
+    return select_launch(sa, n_rows, dims.n_kv_heads, dims.head_dim, (hipStream_t)stream);
+}
+
+extern "C" size_t qsa_decode_layer_scratch_bytes(int32_t n_rows, qsa_dims dims, int32_t k, int32_t n_chunks)
+{
+    if (n_rows <= 0 || k <= 0 || n_chunks <= 0 || check_dims(dims) != QSA_OK) return 0;
+    return layer_layout(n_rows, dims, k, n_chunks).total;
+}
+
+extern "C" qsa_status qsa_decode_layer(const float *q, const int32_t *pos, int32_t n_rows, const qsa_pool *pools,
+                                       int32_t n_pools, const int32_t *row_pool, qsa_dims dims, int32_t n_blocks,
+                                       int32_t k, int32_t n_chunks, float sm_scale, float *out, float *lse,
+                                       float *scores, int32_t *ids, int32_t *counts, void *scratch,
+                                       size_t scratch_bytes, qsa_stream_t stream)
+{
+    SelectArgs sa;
+    qsa_status st = select_setup(q, pos, n_rows, pools, n_pools, row_pool, dims, n_blocks, k, sa);
+    if (st != QSA_OK) return st;
+    if (!out) return QSA_ERR_NULL;
+    if (n_chunks < 1) return QSA_ERR_RANGE;
+    if (n_rows == 0) return QSA_OK;
+    const LayerScratch lay = layer_layout(n_rows, dims, k, n_chunks);
+    if (!scratch) return QSA_ERR_NULL;
+    if (scratch_bytes < lay.total) return QSA_ERR_SCRATCH;
+    char *base = static_cast<char *>(scratch);
+    hipStream_t s = (hipStream_t)stream;
+
+    sa.ids = ids ? ids : reinterpret_cast<int32_t *>(base + lay.ids);
+    sa.counts = counts ? counts : reinterpret_cast<int32_t *>(base + lay.counts);
+    sa.scores = scores;
+    if ((st = select_launch(sa, n_rows, dims.n_kv_heads, dims.head_dim, s)) != QSA_OK) return st;
+
+    ChunkArgs a{};
+    a.q = q; a.pos = pos; a.row_pool = row_pool; a.ids = sa.ids; a.counts = sa.counts;
+    a.m_out = reinterpret_cast<float *>(base + lay.m);
+    a.l_out = reinterpret_cast<float *>(base + lay.l);
+    a.o_out = reinterpret_cast<float *>(base + lay.o);
+    a.empty_out = reinterpret_cast<uint8_t *>(base + lay.e);
+    for (int32_t p = 0; p < n_pools; p++) a.pools[p] = sa.pools[p];
+    a.n_pools = sa.n_pools;
+    a.n_qh = dims.n_q_heads; a.n_kv = dims.n_kv_heads; a.G = sa.G;
+    a.topk = k; a.bpc = 0; a.n_chunks = n_chunks; a.max_chunks = n_chunks;
+    a.qscale = sm_scale * LOG2E;
+    launch_chunk_d(dims.head_dim, a.G, dim3(n_chunks, dims.n_kv_heads, n_rows), s, a);
+    if ((st = launch_status()) != QSA_OK) return st;
+    return merge_launch(a.m_out, a.l_out, a.o_out, a.empty_out, n_chunks, n_chunks, nullptr, n_rows, dims.n_q_heads,
+                        dims.head_dim, out, lse, s);
 }
 
 extern "C" const char *qsa_status_str(qsa_status status)

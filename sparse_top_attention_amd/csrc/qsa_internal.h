@@ -55,7 +55,26 @@ struct PoolArg {
     const float *vs;
     int32_t capacity;
     int32_t n_valid;
+    const float *index;   // block index (selection only; may be null elsewhere)
 };
+
+// Fused block scores + top-k of a decode layer: one workgroup per (KV head, row).
+struct SelectArgs {
+    const float *q;
+    const int32_t *pos;
+    const int32_t *row_pool;
+    PoolArg pools[QSA_MAX_POOLS];
+    int32_t n_pools;
+    int32_t n_qh;
+    int32_t n_kv;
+    int32_t G;
+    int32_t width;       // score columns (blocks) per row
+    int32_t k;
+    int32_t *ids;        // [n_rows][n_kv][k]
+    int32_t *counts;     // [n_rows][n_kv]
+    float *scores;       // optional [n_rows][n_kv][width]
+};
+qsa_status select_launch(const SelectArgs &a, int32_t n_rows, int32_t n_kv, int32_t head_dim, hipStream_t s);
 
 // Launches the log-sum-exp merge of chunk partials laid out [n_rows][n_qh][max_chunks] (+[head_dim] for o).
 qsa_status merge_launch(const float *m, const float *l, const float *o, const uint8_t *empty, int32_t max_chunks,
@@ -63,6 +82,10 @@ qsa_status merge_launch(const float *m, const float *l, const float *o, const ui
                         float *out, float *lse, hipStream_t stream);
 
 // ---------------------------------------------------------------------------------------------- device side
+typedef int32_t v4i __attribute__((ext_vector_type(4)));
+typedef int32_t v2i __attribute__((ext_vector_type(2)));
+#define QSA_LDS __attribute__((address_space(3)))
+
 // DPP controls (gfx9 encoding).
 constexpr int DPP_QUAD_XOR1 = 0xB1;     // quad_perm [1,0,3,2]
 constexpr int DPP_QUAD_XOR2 = 0x4E;     // quad_perm [2,3,0,1]

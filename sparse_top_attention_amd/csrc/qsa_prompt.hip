@@ -30,9 +30,6 @@
 
 namespace qsa {
 
-typedef int32_t v4i __attribute__((ext_vector_type(4)));
-typedef int32_t v2i __attribute__((ext_vector_type(2)));
-#define QSA_LDS __attribute__((address_space(3)))
 
 constexpr int PD = 128;          // head dim of the prompt kernel
 constexpr int PT = 64;           // cells per tile

@@ -17,16 +17,25 @@ __device__ __forceinline__ uint32_t score_key(float f)
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave with DPP moves (a few cycles each, no LDS round trips): shifts
+// by 1, 2, 4, 8 within each row of 16 lanes, then the last lane of row 0 / rows 0-1 is broadcast into the later rows.
+__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t x)
+{
+    int v = (int)x;
+    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true);   // row_shr:1
+    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true);   // row_shr:2
+    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true);   // row_shr:4
+    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true);   // row_shr:8
+    v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);  // row_bcast:15 into rows 1 and 3
+    v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);  // row_bcast:31 into rows 2 and 3
+    return (uint32_t)v;
+}
+
 // Exclusive prefix sum over the 256 threads of the workgroup; `total` receives the sum over all threads.
 __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t *sh_wave, uint32_t &total)
 {
     const int lane = threadIdx.x % 64, wave = threadIdx.x / 64;
-    uint32_t x = v;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t y = __shfl_up(x, off);
-        if (lane >= off) x += y;
-    }
+    const uint32_t x = wave_inclusive_scan(v);
     if (lane == 63) sh_wave[wave] = x;
     __syncthreads();
     uint32_t before = 0, all = 0;
@@ -41,27 +50,22 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t *s
     return before + x - v;
 }
 
+// Top-k over one row of keys held KPT per thread (thread t owns entries [t KPT, t KPT + KPT)); writes the k ids
+// (index order, -1 padded) and the count. Every thread of the 256-thread workgroup must call it.
 template <int KPT>
-__global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ scores, int32_t width, int32_t k,
-                                                   int32_t *__restrict__ ids, int32_t *__restrict__ counts)
+__device__ __forceinline__ void radix_topk(const uint32_t (&key)[KPT], int32_t k, int32_t *__restrict__ dst,
+                                           int32_t *__restrict__ count)
 {
-    __shared__ uint32_t hist[256];
+    __shared__ uint32_t hist[2][256];
     __shared__ uint32_t sh_wave[4];
     __shared__ uint32_t sh_digit, sh_remaining;
     __shared__ bool sh_whole;
     const int tid = threadIdx.x;
-    const int64_t row = blockIdx.x;
-    const float *src = scores + row * width;
     const int32_t i0 = tid * KPT;
 
-    uint32_t key[KPT];
     uint32_t mine = 0;
 #pragma unroll
-    for (int e = 0; e < KPT; e++) {
-        const int32_t idx = i0 + e;
-        key[e] = idx < width ? score_key(src[idx]) : 0u;
-        mine += key[e] != 0u;
-    }
+    for (int e = 0; e < KPT; e++) mine += key[e] != 0u;
     uint32_t n_elig;
     block_exclusive_scan(mine, sh_wave, n_elig);
     const uint32_t kk = n_elig < (uint32_t)k ? n_elig : (uint32_t)k;
@@ -74,31 +78,44 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ sco
     } else {
         uint32_t prefix = 0, mask = 0, remaining = kk;
         bool done_early = false;
+        hist[0][tid] = 0;
+        __syncthreads();
+        // Two histograms alternate (the next one is cleared while the current one fills), and one wave scans the 256
+        // bins, so a pass costs two barriers.
 #pragma unroll 1
         for (int pass = 0; pass < 4; pass++) {
             const int shift = 24 - 8 * pass;
-            hist[tid] = 0;
-            __syncthreads();
+            uint32_t *hc = hist[pass & 1];
 #pragma unroll
             for (int e = 0; e < KPT; e++)
-                if (key[e] != 0u && (key[e] & mask) == prefix) atomicAdd(&hist[(key[e] >> shift) & 255u], 1u);
+                if (key[e] != 0u && (key[e] & mask) == prefix) atomicAdd(&hc[(key[e] >> shift) & 255u], 1u);
+            hist[(pass + 1) & 1][tid] = 0;
             __syncthreads();
-            // thread t looks at digit 255 - t: cum = number of matching keys whose digit is >= 255 - t
-            const uint32_t v = hist[255 - tid];
-            uint32_t tot;
-            const uint32_t cum = block_exclusive_scan(v, sh_wave, tot) + v;
-            if (cum >= remaining && cum - v < remaining) {
-                sh_digit = 255u - (uint32_t)tid;
-                sh_remaining = remaining - (cum - v);
-                sh_whole = (remaining - (cum - v)) == v;   // the whole bin is taken
+            if (tid < 64) {
+                // lane l holds digits 255 - 4l - e (e = 0..3), highest first; cum counts the matching keys whose digit
+                // is at least the current one
+                uint32_t c[4];
+#pragma unroll
+                for (int e = 0; e < 4; e++) c[e] = hc[255 - 4 * tid - e];
+                const uint32_t lsum = (c[0] + c[1]) + (c[2] + c[3]);
+                const uint32_t incl = wave_inclusive_scan(lsum);
+                uint32_t cum = incl - lsum;
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    const uint32_t before = cum;
+                    cum += c[e];
+                    if (cum >= remaining && before < remaining) {
+                        sh_digit = 255u - 4u * (uint32_t)tid - (uint32_t)e;
+                        sh_remaining = remaining - before;
+                        sh_whole = (remaining - before) == c[e];   // the whole bin is taken
+                    }
+                }
             }
             __syncthreads();
             prefix |= sh_digit << shift;
             mask |= 255u << shift;
             remaining = sh_remaining;
-            const bool whole = sh_whole;
-            __syncthreads();
-            if (whole) {  // every key with this prefix is kept: keep all keys >= prefix, no tie to break
+            if (sh_whole) {  // every key with this prefix is kept: keep all keys >= prefix, no tie to break
                 done_early = true;
                 break;
             }
@@ -129,17 +146,132 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ sco
     }
     uint32_t tot_sel;
     uint32_t at = block_exclusive_scan(n_sel, sh_wave, tot_sel);
-    int32_t *dst = ids + row * k;
 #pragma unroll
     for (int e = 0; e < KPT; e++)
         if (sel[e]) dst[at++] = i0 + e;
     for (int32_t jj = (int32_t)kk + tid; jj < k; jj += 256) dst[jj] = -1;
-    if (tid == 0) counts[row] = (int32_t)kk;
+    if (tid == 0) *count = (int32_t)kk;
+}
+
+template <int KPT>
+__global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ scores, int32_t width, int32_t k,
+                                                   int32_t *__restrict__ ids, int32_t *__restrict__ counts)
+{
+    const int64_t row = blockIdx.x;
+    const float *src = scores + row * width;
+    const int32_t i0 = threadIdx.x * KPT;
+    uint32_t key[KPT];
+#pragma unroll
+    for (int e = 0; e < KPT; e++) {
+        const int32_t idx = i0 + e;
+        key[e] = idx < width ? score_key(src[idx]) : 0u;
+    }
+    radix_topk<KPT>(key, k, ids + row * k, counts + row);
+}
+
+// ------------------------------------------------------------------------------- fused block scores + top-k
+// One 256-thread workgroup per (KV head g, row i) of a decode layer: the row's q heads of g are summed, every
+// block's score qsum . index[g][b] is computed (the same arithmetic, in the same order, as the block-score kernel:
+// 8-dim fmaf chains per lane, then a DPP sum over the D/8 lanes of a block) into LDS, and the radix top-k selects
+// from them.
+template <int D, int KPT>
+__global__ __launch_bounds__(256) void select_kernel(const SelectArgs a)
+{
+    constexpr int LPB = D / 8, BPS = 64 / LPB;       // lanes per block, blocks per wave step
+    __shared__ float sqs[D];
+    __shared__ float ssc[256 * KPT];
+    const int tid = threadIdx.x, lane = tid % 64, wave = tid / 64;
+    const int32_t g = blockIdx.x, i = blockIdx.y;
+    const int32_t pidx = a.row_pool ? a.row_pool[i] : 0;
+    const bool pool_ok = pidx >= 0 && pidx < a.n_pools;
+    const PoolArg P = a.pools[pool_ok ? pidx : 0];
+    const int32_t p = a.pos[i];
+    const int32_t n_valid = pool_ok ? P.n_valid : 0;
+    const int32_t stride = (P.capacity + QSA_BLOCK - 1) / QSA_BLOCK;
+
+    const int rb = lane / LPB, s = lane % LPB;
+    const float *idx_g = P.index + (int64_t)g * stride * D + 8 * s;
+    const int32_t n_live = min(a.width, (int32_t)((n_valid + QSA_BLOCK - 1) / QSA_BLOCK));
+    // batches of NST steps of 4 * BPS blocks each. Loads are unconditional (a dead block reads block 0 and is zeroed
+    // afterwards) so a whole batch is in flight before the first wait; the first batch is issued before the q sums.
+    constexpr int NST = 16;
+    float rv[NST][8];
+    auto load_batch = [&](int32_t base) {
+#pragma unroll
+        for (int st = 0; st < NST; st++) {
+            const int32_t b = base + st * 4 * BPS + wave * BPS + rb;
+            const float4 *src = reinterpret_cast<const float4 *>(idx_g + (int64_t)(b < n_live ? b : 0) * D);
+            const float4 u = src[0], w = src[1];
+            rv[st][0] = u.x; rv[st][1] = u.y; rv[st][2] = u.z; rv[st][3] = u.w;
+            rv[st][4] = w.x; rv[st][5] = w.y; rv[st][6] = w.z; rv[st][7] = w.w;
+        }
+    };
+    load_batch(0);
+
+    // qsum over the row's q heads of g, summed in head order
+    for (int d = tid; d < D; d += 256) {
+        float acc = 0.f;
+        for (int32_t h = g * a.G; h < (g + 1) * a.G; h++) acc += a.q[((int64_t)i * a.n_qh + h) * D + d];
+        sqs[d] = acc;
+    }
+    __syncthreads();
+    float qt[8];
+#pragma unroll
+    for (int e = 0; e < 8; e++) qt[e] = sqs[8 * s + e];
+    for (int32_t base = 0; base < 256 * KPT; base += NST * 4 * BPS) {
+        if (base > 0) load_batch(base);
+#pragma unroll
+        for (int st = 0; st < NST; st++) {
+            const int32_t b = base + st * 4 * BPS + wave * BPS + rb;
+            const bool live = b < n_live;
+            float dot = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; e++) dot = fmaf(qt[e], live ? rv[st][e] : 0.f, dot);
+            dot = group_sum<LPB>(dot);
+            if (s == 0 && b < 256 * KPT) {
+                const int64_t first = (int64_t)b * QSA_BLOCK;
+                const float sc = (b < a.width && first <= p && first < n_valid) ? dot : -INFINITY;
+                ssc[b] = sc;
+                if (a.scores && b < a.width) a.scores[((int64_t)i * a.n_kv + g) * a.width + b] = sc;
+            }
+        }
+    }
+    __syncthreads();
+    uint32_t key[KPT];
+#pragma unroll
+    for (int e = 0; e < KPT; e++) key[e] = score_key(ssc[tid * KPT + e]);   // past the width: -inf, key 0
+    const int64_t row = (int64_t)i * a.n_kv + g;
+    radix_topk<KPT>(key, a.k, a.ids + row * a.k, a.counts + row);
 }
 
 }  // namespace qsa
 
 using namespace qsa;
+
+qsa_status qsa::select_launch(const SelectArgs &a, int32_t n_rows, int32_t n_kv, int32_t head_dim, hipStream_t s)
+{
+    dim3 grid(n_kv, n_rows);
+    const int kpt = (a.width + 255) / 256;
+#define QSA_SEL(DD, K) select_kernel<DD, K><<<grid, 256, 0, s>>>(a)
+#define QSA_SEL_D(DD)                                                                                               \
+    do {                                                                                                          \
+        if (kpt <= 1) QSA_SEL(DD, 1);                                                                             \
+        else if (kpt <= 2) QSA_SEL(DD, 2);                                                                        \
+        else if (kpt <= 4) QSA_SEL(DD, 4);                                                                        \
+        else if (kpt <= 8) QSA_SEL(DD, 8);                                                                        \
+        else if (kpt <= 16) QSA_SEL(DD, 16);                                                                      \
+        else if (kpt <= 32) QSA_SEL(DD, 32);                                                                      \
+        else QSA_SEL(DD, 64);                                                                                     \
+    } while (0)
+    switch (head_dim) {
+    case 64: QSA_SEL_D(64); break;
+    case 128: QSA_SEL_D(128); break;
+    default: QSA_SEL_D(256); break;
+    }
+#undef QSA_SEL_D
+#undef QSA_SEL
+    return launch_status();
+}
 
 extern "C" size_t qsa_topk_scratch_bytes(int32_t n_rows, int32_t width, int32_t k)
 {

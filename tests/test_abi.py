@@ -23,7 +23,8 @@ def declared_functions():
 def test_header_declares_the_calls():
     names = declared_functions()
     for fn in ["qsa_block_index", "qsa_block_scores", "qsa_topk", "qsa_topk_scratch_bytes", "qsa_attn_chunk",
-               "qsa_attn_merge", "qsa_prompt_attn", "qsa_prompt_scratch_bytes", "qsa_status_str"]:
+               "qsa_attn_merge", "qsa_prompt_attn", "qsa_prompt_scratch_bytes", "qsa_decode_layer",
+               "qsa_decode_layer_scratch_bytes", "qsa_decode_select", "qsa_status_str"]:
         assert fn in names
 
 
@@ -169,3 +170,44 @@ def test_prompt_scratch_sizing_and_checks():
     assert L.qsa_prompt_attn(1, 16, 0, ctypes.byref(p), GOOD, 1.0, 1, 1, need - 1, None) == -4
     assert L.qsa_prompt_attn(1, 16, 0, ctypes.byref(p), D(24, 4, 64, 64), 1.0, 1, 1, need, None) == -3
     assert L.qsa_prompt_attn(1, 0, 0, ctypes.byref(p), GOOD, 1.0, 1, None, 0, None) == 0
+
+
+def test_decode_layer_validation():
+    L = qsa.lib_handle()
+    pools = (qsa._Pool * 2)(_pool(), _pool())
+    need = L.qsa_decode_layer_scratch_bytes(4, GOOD, 8, 4)
+    assert need >= 4 * 24 * 4 * (128 * 4 + 9)             # the partials at least
+    assert L.qsa_decode_layer_scratch_bytes(0, GOOD, 8, 4) == 0
+    assert L.qsa_decode_layer_scratch_bytes(4, GOOD, 0, 4) == 0
+    args = dict(q=1, pos=1, n_rows=4, pools=pools, n_pools=2, row_pool=1, dims=GOOD, nb=16, k=8, S=4, sm=1.0,
+                out=1, lse=None, scores=None, ids=None, counts=None, scratch=1, nbytes=need, stream=None)
+
+    def call(**kw):
+        a = dict(args)
+        a.update(kw)
+        return L.qsa_decode_layer(a["q"], a["pos"], a["n_rows"], a["pools"], a["n_pools"], a["row_pool"],
+                                  a["dims"], a["nb"], a["k"], a["S"], a["sm"], a["out"], a["lse"], a["scores"],
+                                  a["ids"], a["counts"], a["scratch"], a["nbytes"], a["stream"])
+    assert call(q=None) == -1
+    assert call(out=None) == -1
+    assert call(scratch=None) == -1
+    assert call(nbytes=need - 1) == -4
+    assert call(k=0) == -5
+    assert call(k=17) == -5                                # k > n_blocks
+    assert call(nb=17) == -5                               # wider than ceil(cap / 64)
+    assert call(S=0) == -5
+    assert call(n_pools=9) == -3
+    assert call(dims=D(24, 4, 96, 64)) == -3
+    noidx = (qsa._Pool * 2)(_pool(), _pool(index=None))
+    assert call(pools=noidx) == -1
+    assert call(n_rows=0) == 0
+
+
+def test_decode_select_validation():
+    L = qsa.lib_handle()
+    pools = (qsa._Pool * 1)(_pool())
+    assert L.qsa_decode_select(1, 1, 4, pools, 1, None, GOOD, 16, 8, None, None, 1, None) == -1   # ids required
+    assert L.qsa_decode_select(1, 1, 4, pools, 1, None, GOOD, 16, 8, None, 1, None, None) == -1   # counts required
+    assert L.qsa_decode_select(1, 1, 4, pools, 1, None, GOOD, 16, 0, None, 1, 1, None) == -5
+    assert L.qsa_decode_select(1, 1, 4, pools, 1, None, GOOD, 17, 8, None, 1, 1, None) == -5
+    assert L.qsa_decode_select(1, 1, 0, pools, 1, None, GOOD, 16, 8, None, 1, 1, None) == 0
