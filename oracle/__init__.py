@@ -55,6 +55,8 @@ def _declare(L):
     L.orc_split24.argtypes = [P, I64, P, P, P]
     L.orc_split24.restype = ctypes.c_int
     L.orc_quant24.argtypes = [P, I64, F64, P]
+    L.orc_encode_group.argtypes = [P, I32, P, P]
+    L.orc_kv_append.argtypes = [P, P, P, P, I32, I32, I32, I32, P, P, P, I32]
 
 
 def _c(a, dtype):
@@ -210,3 +212,27 @@ def full_selection(pos, n_kv, n_valid, n_blocks_k):
             ids[i, g, :len(elig)] = elig
             counts[i, g] = len(elig)
     return ids, counts
+
+
+def encode_group(x):
+    """int8 codes and the fp32 scale of one group of values (fp32 decisions, see orc_encode_group)."""
+    x = _c(x, np.float32)
+    codes = np.zeros(x.shape[0], np.int8)
+    scale = np.zeros(1, np.float32)
+    lib().orc_encode_group(_p(x), x.shape[0], _p(codes), _p(scale))
+    return codes, float(scale[0])
+
+
+def kv_append(pool, k_new, v_new, cells, n_valid=None):
+    """A copy of ``pool`` (a synth.Pool) with rows k_new, v_new [n_rows][n_kv][d] appended at cells [n_rows];
+    n_valid is the count after the append (default: the pool's)."""
+    import copy
+    out = copy.copy(pool)
+    out.k, out.ks, out.v, out.vs = (np.array(a, copy=True, order="C") for a in (pool.k, pool.ks, pool.v, pool.vs))
+    out.n_valid = pool.n_valid if n_valid is None else n_valid
+    n_kv, cap, d = out.k.shape
+    kn, vn = _c(k_new, np.float32), _c(v_new, np.float32)
+    cl = _c(cells, np.int32)
+    lib().orc_kv_append(_p(out.k), _p(out.ks), _p(out.v), _p(out.vs), n_kv, cap, out.n_valid, d, _p(kn), _p(vn),
+                        _p(cl), cl.shape[0])
+    return out

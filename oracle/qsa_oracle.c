@@ -338,3 +338,52 @@ void orc_quant24(const double *x, int64_t n, double amax, int32_t *X)
         X[j] = (int32_t)nearbyint(xs * 65536.0);
     }
 }
+
+/* int8 encode of one 64-dim scale group, the write side of the int8 KV pool ([2806] "Extra Notes": K/V appended
+ * per row, with per-64-dim scales, [1888] Summary). The pages name the format but not its encoder; reading:
+ * symmetric absmax per (cell, KV head, group) -- amax = max |x|, scale = amax / 127, code = rint(x * (127 / amax))
+ * clamped to [-127, 127], and amax = 0 gives scale 0 and all-zero codes. The quantised code is an integer decided by
+ * floating point, so it is decided here in fp32 with the same three roundings the GPU makes (127 / amax, the
+ * product, rint half-to-even); nothing else in this file is fp32. Pinned by brute force (nearest code over all 255),
+ * exact recovery of power-of-two grids, and the reconstruction bound. */
+void orc_encode_group(const float *x, int32_t n, int8_t *codes, float *scale)
+{
+    float amax = 0.0f;
+    for (int32_t e = 0; e < n; e++) {
+        const float a = fabsf(x[e]);
+        if (a > amax) amax = a;
+    }
+    if (amax == 0.0f) {
+        for (int32_t e = 0; e < n; e++) codes[e] = 0;
+        *scale = 0.0f;
+        return;
+    }
+    const float inv = 127.0f / amax;
+    for (int32_t e = 0; e < n; e++) {
+        float c = rintf(x[e] * inv);
+        if (c > 127.0f) c = 127.0f;
+        if (c < -127.0f) c = -127.0f;
+        codes[e] = (int8_t)c;
+    }
+    *scale = amax / 127.0f;
+}
+
+/* Append of n_rows new cells to one pool: row i writes cell cells[i] of every KV head, K from k_new and V from v_new
+ * ([n_rows][n_kv][d] f32), one orc_encode_group per 64-dim group. Rows whose cell is outside [0, n_valid) are
+ * skipped (n_valid is the pool's count after the append). Index rows are recomputed by orc_block_index. */
+void orc_kv_append(int8_t *k, float *ks, int8_t *v, float *vs, int32_t n_kv, int32_t cap, int32_t n_valid, int32_t d,
+                   const float *k_new, const float *v_new, const int32_t *cells, int32_t n_rows)
+{
+    const int32_t ng = d / ORC_GROUP;
+    for (int32_t i = 0; i < n_rows; i++) {
+        const int32_t c = cells[i];
+        if (c < 0 || c >= n_valid || c >= cap) continue;
+        for (int32_t g = 0; g < n_kv; g++) {
+            const int64_t src = ((int64_t)i * n_kv + g) * d, dst = ((int64_t)g * cap + c);
+            for (int32_t t = 0; t < ng; t++) {
+                orc_encode_group(k_new + src + t * ORC_GROUP, ORC_GROUP, k + dst * d + t * ORC_GROUP, ks + dst * ng + t);
+                orc_encode_group(v_new + src + t * ORC_GROUP, ORC_GROUP, v + dst * d + t * ORC_GROUP, vs + dst * ng + t);
+            }
+        }
+    }
+}

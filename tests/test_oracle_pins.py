@@ -6,7 +6,9 @@
 * closed forms: constant V, all-zero K, one dominant cell, q = 0;
 * score identity: (sum of a group's q heads) . (block mean key) = the mean of the per-cell, per-head logits;
 * merge algebra: empty or out-of-range chunks change nothing, bit for bit;
-* the 24-bit split: exact for every integer in range, error of the scaling step within 2^-17.
+* the 24-bit split: exact for every integer in range, error of the scaling step within 2^-17;
+* the int8 encoder (append path): nearest code by brute force over all 255 codes, exact recovery of power-of-two
+  grids, the reconstruction bound, and appends that touch only their cells.
 """
 import math
 
@@ -332,3 +334,68 @@ def test_quant24_error_bound():
     halves = np.array([0.5, 1.5, 2.5, -0.5, -1.5]) / 65536.0 * 1.0
     Xh = oracle.quant24(halves, 127.0)
     assert list(Xh) == [0, 2, 2, 0, -2]
+
+
+# ------------------------------------------------------------------------------------------------ int8 encoder
+def _f32(x):
+    return np.float32(x)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_encode_is_nearest_code_by_brute_force(seed):
+    rng = np.random.default_rng(900 + seed)
+    x = (rng.standard_normal(64) * rng.choice([1e-3, 1.0, 37.0])).astype(np.float32)
+    codes, scale = oracle.encode_group(x)
+    amax = np.float32(np.abs(x).max())
+    inv = _f32(np.float32(127.0) / amax)
+    y = (x * inv).astype(np.float32)                         # the fp32 product the code is taken from
+    cand = np.arange(-127, 128, dtype=np.float64)
+    dist = np.abs(y.astype(np.float64)[:, None] - cand[None, :])
+    best = cand[np.argmin(dist, axis=1)]                      # nearest of the 255 codes (lower on a tie...)
+    ties = np.abs(np.abs(y - np.trunc(y)) - 0.5) == 0         # ...so exact halves are checked separately: even code
+    assert np.all(codes[~ties] == best[~ties])
+    assert np.all(codes[ties] % 2 == 0)
+    assert scale == np.float32(amax / np.float32(127.0))
+    assert np.abs(codes[np.argmax(np.abs(x))]) == 127          # the largest magnitude maps to +-127
+    assert np.all(np.sign(codes[codes != 0]) == np.sign(x[codes != 0]))
+
+
+def test_encode_recovers_power_of_two_grids_exactly():
+    rng = np.random.default_rng(910)
+    for e in (-12, -3, 0, 5):
+        k = rng.integers(-127, 128, 64)
+        k[7] = 127 if rng.random() < 0.5 else -127               # amax = 127 * 2^e: 127 / amax = 2^-e exactly
+        x = (k * 2.0 ** e).astype(np.float32)
+        codes, scale = oracle.encode_group(x)
+        assert np.array_equal(codes.astype(np.int64), k)
+        assert scale == np.float32(2.0 ** e)
+
+
+def test_encode_zero_group_and_reconstruction_bound():
+    codes, scale = oracle.encode_group(np.zeros(64, np.float32))
+    assert scale == 0.0 and np.all(codes == 0)
+    rng = np.random.default_rng(920)
+    for _ in range(20):
+        x = (rng.standard_normal(64) * 3.0).astype(np.float32)
+        codes, scale = oracle.encode_group(x)
+        err = np.abs(x.astype(np.float64) - scale * codes.astype(np.float64))
+        assert err.max() <= 0.5 * scale * (1 + 2.0 ** -20) + 1e-12 * np.abs(x).max()
+
+
+def test_kv_append_touches_only_its_cells():
+    pool = synth.random_pool(930, 2, 300, 290, 128, poison=False)
+    rng = np.random.default_rng(931)
+    kn = rng.standard_normal((3, 2, 128)).astype(np.float32)
+    vn = rng.standard_normal((3, 2, 128)).astype(np.float32)
+    cells = np.array([5, 289, 295], np.int32)                 # 295 >= n_valid: skipped
+    out = oracle.kv_append(pool, kn, vn, cells)
+    changed = np.any(out.k != pool.k, axis=-1) | np.any(out.v != pool.v, axis=-1)
+    assert set(np.nonzero(changed.any(axis=0))[0]) <= {5, 289}
+    assert np.array_equal(out.k[:, 295], pool.k[:, 295]) and np.array_equal(out.ks[:, 295], pool.ks[:, 295])
+    for r, c in enumerate(cells[:2]):
+        for g in range(2):
+            for t in range(2):
+                codes, scale = oracle.encode_group(kn[r, g, 64 * t:64 * t + 64])
+                assert np.array_equal(out.k[g, c, 64 * t:64 * t + 64], codes) and out.ks[g, c, t] == np.float32(scale)
+                codes, scale = oracle.encode_group(vn[r, g, 64 * t:64 * t + 64])
+                assert np.array_equal(out.v[g, c, 64 * t:64 * t + 64], codes) and out.vs[g, c, t] == np.float32(scale)
