@@ -233,9 +233,26 @@ def bench_decode(args):
         breakdown["select"] = kernel_avg_us(fused_select)
     breakdown["attn_chunk"] = kernel_avg_us(attend)
     breakdown["attn_merge"] = kernel_avg_us(lambda p: merge())
+    capacity_wide = None
     if not dense:
         t_sep = kernel_avg_us(layer_separate)
         separate = {"us_per_layer": round(t_sep, 3), "block_scores+topk_us": round(kernel_avg_us(select), 3)}
+        # capacity-wide selection: score rows over every block of the capacity (-inf past n_valid)
+        nb_cap = -(-pool_np.capacity // BLOCK)
+
+        def wide_select(p):
+            qsa.qsa_decode_select(q, pos, [p], dims, nb_cap, w.topk, ids, counts)
+
+        def wide_layer(p):
+            qsa.qsa_decode_layer(q, pos, [p], dims, nb_cap, w.topk, S, out, lse, sm_scale=w.sm_scale, ids=ids,
+                                 counts=counts, scratch=layer_scratch)
+        capacity_wide = {"score_columns": nb_cap, "us_per_layer": round(kernel_avg_us(wide_layer), 3),
+                         "select_us": round(kernel_avg_us(wide_select), 3)}
+        # append path: the window's rows encode their new K/V cells (at their own positions) and refresh the index
+        rng = np.random.default_rng(77)
+        k_new = t(rng.standard_normal((n_rows, n_kv, D)).astype(np.float32))
+        v_new = t(rng.standard_normal((n_rows, n_kv, D)).astype(np.float32))
+        breakdown["kv_append"] = kernel_avg_us(lambda p: qsa.qsa_kv_append([p], dims, k_new, v_new, pos))
     chunk_key = "attn_chunk"
 
     # ---- algorithmic bytes
@@ -274,6 +291,7 @@ def bench_decode(args):
                    "layer_bytes": int(layer_bytes), "kv_union_cells": int(kv_cells)},
         "kernels_us": {k2: round(v2, 3) for k2, v2 in breakdown.items()},
         "four_call_layer": separate,
+        "capacity_wide": capacity_wide,
         "roofline": {"bound": "hbm", "kernel": chunk_key, "achieved": round(chunk_gbs, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(chunk_gbs / HBM_PEAK_GBS, 4),
                      "bytes_per_launch": int(chunk_bytes),

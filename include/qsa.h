@@ -94,6 +94,21 @@ typedef struct {
 qsa_status qsa_block_index(const qsa_pool *pool, qsa_dims dims, int32_t cell_begin, int32_t cell_end, float *index,
                            qsa_stream_t stream);
 
+/* Append path: K/V and indexer appends per row ([2806] "What it leaves alone" and "What changed": a window's K/V and
+ * indexer appends; per-slot appends as a follow-up). Row i encodes k_new[i] and v_new[i] ([n_rows][n_kv_heads]
+ * [head_dim] f32) into cell cells[i] (device memory) of every KV head of pool pools[row_pool[i]] (row_pool NULL =
+ * pool 0), writing codes and scales through the pool's pointers, which must therefore be writable. The pages give
+ * the int8 format with per-64-dim scales but not its encoder; the encoding is symmetric absmax per (cell, KV head,
+ * 64-dim group): amax = max |x|, scale = amax / 127, code = rint(x * (127 / amax)) clamped to [-127, 127], all in
+ * fp32 with correctly rounded division and round-half-to-even; amax = 0 gives scale 0 and zero codes. Then, for
+ * every pool with a non-NULL index, the index row of each block that received a cell is recomputed as
+ * qsa_block_index does (after all rows are written, so rows may share a block). The pools' n_valid must already
+ * count the new cells: a row whose cell is outside [0, n_valid) or whose device-side row_pool value is out of
+ * range writes nothing. Two launches. */
+qsa_status qsa_kv_append(const qsa_pool *pools, int32_t n_pools, const int32_t *row_pool, qsa_dims dims,
+                         const float *k_new, const float *v_new, const int32_t *cells, int32_t n_rows,
+                         qsa_stream_t stream);
+
 /* Block scores ([2806] Summary table, block-score row: one sum per (query, KV head) per block):
  * scores[i][g][b] = (sum over the q heads h of KV head g of q[i][h]) . pool->index[g][b], for every block whose
  * first cell is visible (64b <= pos[i]) and valid (64b < n_valid); -inf for every other b < n_blocks.

@@ -69,6 +69,7 @@ def _lib():
         L.qsa_prompt_scratch_bytes.argtypes = [I32, I32, PD]
         L.qsa_prompt_scratch_bytes.restype = SZ
         L.qsa_prompt_attn.argtypes = [P, I32, I32, PP, PD, ctypes.c_float, P, P, SZ, P]
+        L.qsa_kv_append.argtypes = [PP, I32, P, PD, P, P, P, I32, P]
         L.qsa_decode_select.argtypes = [P, P, I32, PP, I32, P, PD, I32, I32, P, P, P, P]
         L.qsa_decode_layer_scratch_bytes.argtypes = [I32, PD, I32, I32]
         L.qsa_decode_layer_scratch_bytes.restype = SZ
@@ -77,7 +78,7 @@ def _lib():
         L.qsa_status_str.argtypes = [I32]
         L.qsa_status_str.restype = ctypes.c_char_p
         for fn in ("qsa_block_index", "qsa_block_scores", "qsa_topk", "qsa_attn_chunk", "qsa_attn_merge",
-                   "qsa_prompt_attn", "qsa_decode_layer", "qsa_decode_select"):
+                   "qsa_prompt_attn", "qsa_decode_layer", "qsa_decode_select", "qsa_kv_append"):
             getattr(L, fn).restype = I32
         _L = L
     return _L
@@ -222,6 +223,14 @@ def qsa_attn_merge(part: Partials, dims: Dims, n_chunks: int, out, lse=None, n_a
     return out
 
 
+def qsa_kv_append(pools: Sequence[Pool], dims: Dims, k_new, v_new, cells, row_pool=None, stream=None):
+    arr = (_Pool * len(pools))(*[p.c() for p in pools])
+    _check("qsa_kv_append", _lib().qsa_kv_append(
+        arr, len(pools), _ptr(row_pool, torch.int32, "row_pool", allow_none=True), dims.c(),
+        _ptr(k_new, torch.float32, "k_new"), _ptr(v_new, torch.float32, "v_new"), _ptr(cells, torch.int32, "cells"),
+        k_new.shape[0], _stream(stream)))
+
+
 def qsa_decode_select(q, pos, pools: Sequence[Pool], dims: Dims, n_blocks: int, k: int, ids, counts, scores=None,
                       row_pool=None, stream=None):
     arr = (_Pool * len(pools))(*[p.c() for p in pools])
@@ -272,5 +281,5 @@ def qsa_status_str(status: int) -> str:
 
 __all__ = ["Dims", "Pool", "Partials", "QSAError", "qsa_block_index", "qsa_block_scores", "qsa_topk_scratch_bytes",
            "qsa_topk", "qsa_attn_chunk", "qsa_attn_merge", "qsa_prompt_scratch_bytes", "qsa_prompt_attn",
-           "qsa_decode_select", "qsa_decode_layer_scratch_bytes", "qsa_decode_layer",
+           "qsa_decode_select", "qsa_decode_layer_scratch_bytes", "qsa_decode_layer", "qsa_kv_append",
            "qsa_status_str", "lib_handle"]

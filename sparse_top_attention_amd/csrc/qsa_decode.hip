@@ -30,15 +30,14 @@ __device__ __forceinline__ void unpack16(const int4 w, float (&x)[16])
 }
 
 // --------------------------------------------------------------------------------------------- block index
-// index[g][b][:] = mean of the dequantised keys of block b's valid cells. One wave per (block, KV head).
+// index[g][b][:] = mean of the dequantised keys of block b's valid cells, computed by one wave.
 template <int D>
-__global__ __launch_bounds__(64) void block_index_kernel(const int8_t *__restrict__ k, const float *__restrict__ ks,
-                                                         int32_t cap, int32_t n_valid, int32_t b_first,
-                                                         int32_t blk_stride, float *__restrict__ index)
+__device__ __forceinline__ void block_mean(const int8_t *__restrict__ k, const float *__restrict__ ks, int32_t cap,
+                                           int32_t n_valid, int32_t g, int32_t b, int32_t blk_stride,
+                                           float *__restrict__ index)
 {
     constexpr int LPC = D / 16, CPS = 64 / LPC, STEPS = QSA_BLOCK / CPS, NG = D / QSA_GROUP;
-    const int lane = threadIdx.x, r = lane / LPC, s = lane % LPC, grp = (16 * s) / QSA_GROUP;
-    const int32_t b = b_first + blockIdx.x, g = blockIdx.y;
+    const int lane = threadIdx.x % 64, r = lane / LPC, s = lane % LPC, grp = (16 * s) / QSA_GROUP;
     const int32_t c0 = b * QSA_BLOCK;
     float acc[16];
 #pragma unroll
@@ -67,6 +66,80 @@ __global__ __launch_bounds__(64) void block_index_kernel(const int8_t *__restric
         for (int j = 0; j < 4; j++)
             dst[j] = make_float4(acc[4 * j] * inv, acc[4 * j + 1] * inv, acc[4 * j + 2] * inv, acc[4 * j + 3] * inv);
     }
+}
+
+// One wave per (block, KV head).
+template <int D>
+__global__ __launch_bounds__(64) void block_index_kernel(const int8_t *__restrict__ k, const float *__restrict__ ks,
+                                                         int32_t cap, int32_t n_valid, int32_t b_first,
+                                                         int32_t blk_stride, float *__restrict__ index)
+{
+    block_mean<D>(k, ks, cap, n_valid, blockIdx.y, b_first + blockIdx.x, blk_stride, index);
+}
+
+// ----------------------------------------------------------------------------------------------------- append
+// Write side of the int8 pool: row i encodes its new K and V rows into cell cells[i] of pool pools[row_pool[i]]
+// (every KV head), then the index rows of the blocks holding new cells are recomputed. One wave per (row, KV head);
+// in the encoder lane l holds dim l + 64 t of scale group t, so a group's absmax is one wave-wide max.
+struct AppendArgs {
+    PoolArg pools[QSA_MAX_POOLS];
+    int32_t n_pools;
+    const int32_t *row_pool;
+    const float *k_new;
+    const float *v_new;
+    const int32_t *cells;
+    int32_t n_kv;
+};
+
+__device__ __forceinline__ bool append_row(const AppendArgs &a, int32_t i, PoolArg &P, int32_t &c)
+{
+    const int32_t pidx = a.row_pool ? a.row_pool[i] : 0;
+    if (pidx < 0 || pidx >= a.n_pools) return false;
+    P = a.pools[pidx];
+    c = a.cells[i];
+    return c >= 0 && c < P.n_valid;
+}
+
+// int8 encode of one 64-dim group held one value per lane: amax = max |x|, scale = amax / 127,
+// code = rint(x * (127 / amax)) clamped to [-127, 127] (all fp32, correctly rounded); amax = 0 gives zeros.
+template <int D>
+__global__ __launch_bounds__(64) void append_encode_kernel(const AppendArgs a)
+{
+    constexpr int NG = D / QSA_GROUP;
+    const int lane = threadIdx.x;
+    const int32_t i = blockIdx.x, g = blockIdx.y;
+    PoolArg P;
+    int32_t c;
+    if (!append_row(a, i, P, c)) return;
+    const int64_t src = ((int64_t)i * a.n_kv + g) * D, dst = (int64_t)g * P.capacity + c;
+#pragma unroll
+    for (int which = 0; which < 2; which++) {
+        const float *x = (which ? a.v_new : a.k_new) + src;
+        int8_t *codes = const_cast<int8_t *>(which ? P.v : P.k) + dst * D;
+        float *scales = const_cast<float *>(which ? P.vs : P.ks) + dst * NG;
+        float xv[NG];
+#pragma unroll
+        for (int t = 0; t < NG; t++) xv[t] = x[QSA_GROUP * t + lane];
+#pragma unroll
+        for (int t = 0; t < NG; t++) {
+            const float amax = group_max<64>(fabsf(xv[t]));
+            float code = 0.f;
+            if (amax > 0.f) code = fminf(fmaxf(rintf(xv[t] * (127.0f / amax)), -127.f), 127.f);
+            codes[QSA_GROUP * t + lane] = (int8_t)(int32_t)code;
+            if (lane == 0) scales[t] = amax / 127.0f;
+        }
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(64) void append_index_kernel(const AppendArgs a)
+{
+    const int32_t i = blockIdx.x, g = blockIdx.y;
+    PoolArg P;
+    int32_t c;
+    if (!append_row(a, i, P, c) || !P.index) return;
+    block_mean<D>(P.k, P.ks, P.capacity, P.n_valid, g, c / QSA_BLOCK, (P.capacity + QSA_BLOCK - 1) / QSA_BLOCK,
+                  const_cast<float *>(P.index));
 }
 
 // -------------------------------------------------------------------------------------------- block scores
@@ -491,6 +564,35 @@ extern "C" qsa_status qsa_block_index(const qsa_pool *pool, qsa_dims dims, int32
     case 64: block_index_kernel<64><<<grid, 64, 0, s>>>(pool->k, pool->k_scale, pool->capacity, pool->n_valid, b0, stride, index); break;
     case 128: block_index_kernel<128><<<grid, 64, 0, s>>>(pool->k, pool->k_scale, pool->capacity, pool->n_valid, b0, stride, index); break;
     default: block_index_kernel<256><<<grid, 64, 0, s>>>(pool->k, pool->k_scale, pool->capacity, pool->n_valid, b0, stride, index); break;
+    }
+    return launch_status();
+}
+
+extern "C" qsa_status qsa_kv_append(const qsa_pool *pools, int32_t n_pools, const int32_t *row_pool, qsa_dims dims,
+                                    const float *k_new, const float *v_new, const int32_t *cells, int32_t n_rows,
+                                    qsa_stream_t stream)
+{
+    qsa_status st = check_dims(dims);
+    if (st != QSA_OK) return st;
+    if (!pools || !k_new || !v_new || !cells) return QSA_ERR_NULL;
+    if (n_rows < 0 || n_pools <= 0) return QSA_ERR_SHAPE;
+    if (n_pools > QSA_MAX_POOLS) return QSA_ERR_UNSUPPORTED;
+    for (int32_t p = 0; p < n_pools; p++)
+        if ((st = check_pool(&pools[p], true)) != QSA_OK) return st;
+    if (n_rows == 0) return QSA_OK;
+    if (n_rows > 65535) return QSA_ERR_UNSUPPORTED;
+    AppendArgs a{};
+    for (int32_t p = 0; p < n_pools; p++)
+        a.pools[p] = PoolArg{pools[p].k, pools[p].k_scale, pools[p].v, pools[p].v_scale, pools[p].capacity,
+                             pools[p].n_valid, pools[p].index};
+    a.n_pools = row_pool ? n_pools : 1;
+    a.row_pool = row_pool; a.k_new = k_new; a.v_new = v_new; a.cells = cells; a.n_kv = dims.n_kv_heads;
+    dim3 grid(n_rows, dims.n_kv_heads);
+    hipStream_t s = (hipStream_t)stream;
+    switch (dims.head_dim) {
+    case 64: append_encode_kernel<64><<<grid, 64, 0, s>>>(a); append_index_kernel<64><<<grid, 64, 0, s>>>(a); break;
+    case 128: append_encode_kernel<128><<<grid, 64, 0, s>>>(a); append_index_kernel<128><<<grid, 64, 0, s>>>(a); break;
+    default: append_encode_kernel<256><<<grid, 64, 0, s>>>(a); append_index_kernel<256><<<grid, 64, 0, s>>>(a); break;
     }
     return launch_status();
 }

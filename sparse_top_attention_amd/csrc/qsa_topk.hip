@@ -206,7 +206,14 @@ __global__ __launch_bounds__(256) void select_kernel(const SelectArgs a)
             rv[st][4] = w.x; rv[st][5] = w.y; rv[st][6] = w.z; rv[st][7] = w.w;
         }
     };
-    load_batch(0);
+    // only blocks below n_live hold a score; the rest of the row is -inf without a load
+    const int32_t b_end = min(256 * KPT, (n_live + NST * 4 * BPS - 1) / (NST * 4 * BPS) * (NST * 4 * BPS));
+    for (int e = tid; e < 256 * KPT; e += 256)
+        if (e >= b_end) {
+            ssc[e] = -INFINITY;
+            if (a.scores && e < a.width) a.scores[((int64_t)i * a.n_kv + g) * a.width + e] = -INFINITY;
+        }
+    if (b_end > 0) load_batch(0);
 
     // qsum over the row's q heads of g, summed in head order
     for (int d = tid; d < D; d += 256) {
@@ -218,7 +225,7 @@ __global__ __launch_bounds__(256) void select_kernel(const SelectArgs a)
     float qt[8];
 #pragma unroll
     for (int e = 0; e < 8; e++) qt[e] = sqs[8 * s + e];
-    for (int32_t base = 0; base < 256 * KPT; base += NST * 4 * BPS) {
+    for (int32_t base = 0; base < b_end; base += NST * 4 * BPS) {
         if (base > 0) load_batch(base);
 #pragma unroll
         for (int st = 0; st < NST; st++) {

@@ -24,7 +24,7 @@ def test_header_declares_the_calls():
     names = declared_functions()
     for fn in ["qsa_block_index", "qsa_block_scores", "qsa_topk", "qsa_topk_scratch_bytes", "qsa_attn_chunk",
                "qsa_attn_merge", "qsa_prompt_attn", "qsa_prompt_scratch_bytes", "qsa_decode_layer",
-               "qsa_decode_layer_scratch_bytes", "qsa_decode_select", "qsa_status_str"]:
+               "qsa_decode_layer_scratch_bytes", "qsa_decode_select", "qsa_kv_append", "qsa_status_str"]:
         assert fn in names
 
 
@@ -211,3 +211,16 @@ def test_decode_select_validation():
     assert L.qsa_decode_select(1, 1, 4, pools, 1, None, GOOD, 16, 0, None, 1, 1, None) == -5
     assert L.qsa_decode_select(1, 1, 4, pools, 1, None, GOOD, 17, 8, None, 1, 1, None) == -5
     assert L.qsa_decode_select(1, 1, 0, pools, 1, None, GOOD, 16, 8, None, 1, 1, None) == 0
+
+
+def test_kv_append_validation():
+    L = qsa.lib_handle()
+    pools = (qsa._Pool * 2)(_pool(), _pool())
+    assert L.qsa_kv_append(pools, 2, 1, GOOD, None, 1, 1, 4, None) == -1
+    assert L.qsa_kv_append(pools, 2, 1, GOOD, 1, 1, None, 4, None) == -1
+    assert L.qsa_kv_append(pools, 9, 1, GOOD, 1, 1, 1, 4, None) == -3
+    assert L.qsa_kv_append(pools, 2, 1, D(24, 4, 96, 64), 1, 1, 1, 4, None) == -3
+    assert L.qsa_kv_append(pools, 2, 1, GOOD, 1, 1, 1, -1, None) == -2
+    bad = (qsa._Pool * 1)(_pool(n_valid=2000))
+    assert L.qsa_kv_append(bad, 1, None, GOOD, 1, 1, 1, 4, None) == -5
+    assert L.qsa_kv_append(pools, 2, 1, GOOD, 1, 1, 1, 0, None) == 0

@@ -152,3 +152,21 @@ def test_select_wide_rows():
     qsa.qsa_decode_select(q, pos, [p], dims, nb, 40, i, c)
     torch.cuda.synchronize()
     assert np.array_equal(i.cpu().numpy(), i_sep.cpu().numpy()) and np.array_equal(c.cpu().numpy(), c_sep.cpu().numpy())
+
+
+def test_capacity_wide_selection():
+    """Score rows over the whole 200,000-cell capacity (3,125 blocks, -inf past n_valid) select what rows over the
+    valid blocks select, and the layer output is the same."""
+    w = synth.workload("verify_window")
+    dims = dims_of(w)
+    p = build_index(to_device(w.pools[0]), dims)
+    nb_valid = -(-w.pools[0].n_valid // BLOCK)
+    nb_cap = -(-w.pools[0].capacity // BLOCK)
+    narrow = run_layer(w, [p], dims, 16, nb=nb_valid)
+    wide = run_layer(w, [p], dims, 16, nb=nb_cap)
+    assert wide["scores"].shape[-1] == 3125
+    assert np.array_equal(wide["scores"][..., :nb_valid], narrow["scores"])
+    assert np.all(np.isneginf(wide["scores"][..., nb_valid:]))
+    assert np.array_equal(wide["ids"], narrow["ids"]) and np.array_equal(wide["counts"], narrow["counts"])
+    assert np.array_equal(wide["out"], narrow["out"])
+    _check_end_to_end(w, narrow)
