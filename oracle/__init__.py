@@ -47,16 +47,17 @@ def _declare(L):
     L.orc_block_index.argtypes = [P, P, I32, I32, I32, I32, I32, I32, P]
     L.orc_block_scores.argtypes = [P, P, I32, I32, I32, I32, P, I32, I32, I32, I32, P]
     L.orc_topk.argtypes = [P, I32, I32, I32, P, P]
-    L.orc_attn_one.argtypes = [P, P, I32, I32, P, P, P, P, I32, I32, I32, I32, I32, I32, P, P, I32, F64, P, P]
-    L.orc_attn.argtypes = [P, P, I32, P, P, P, P, I32, I32, I32, I32, I32, I32, P, P, I32, F64, P, P]
+    L.orc_attn_one.argtypes = [P, P, I32, I32, P, P, P, P, I32, I32, I32, I32, I32, I32, P, P, I32, F64, P, P, I32]
+    L.orc_attn.argtypes = [P, P, I32, P, P, P, P, I32, I32, I32, I32, I32, I32, P, P, I32, F64, P, P, I32]
     L.orc_chunk_partials.argtypes = [P, P, I32, P, P, P, P, I32, I32, I32, I32, I32, I32, P, P, I32, I32, I32, F64,
-                                     P, P, P, P]
+                                     P, P, P, P, I32]
     L.orc_merge.argtypes = [P, P, P, P, I32, I32, I32, I32, P, P, P]
     L.orc_split24.argtypes = [P, I64, P, P, P]
     L.orc_split24.restype = ctypes.c_int
     L.orc_quant24.argtypes = [P, I64, F64, P]
     L.orc_encode_group.argtypes = [P, I32, P, P]
-    L.orc_kv_append.argtypes = [P, P, P, P, I32, I32, I32, I32, P, P, P, I32]
+    L.orc_kv_append.argtypes = [P, P, P, P, I32, I32, I32, I32, P, P, P, I32, I32]
+    L.orc_encode_group4.argtypes = [P, I32, P, P]
 
 
 def _c(a, dtype):
@@ -66,6 +67,10 @@ def _c(a, dtype):
 
 def _p(a):
     return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _v_bits(pool):
+    return int(getattr(pool, "v_bits", 8))
 
 
 def _pool_args(pool):
@@ -122,7 +127,7 @@ def attn(q, pos, pool, n_kv, ids=None, counts=None, topk_=0, sm_scale=1.0):
     out = np.zeros((n_rows, n_qh, d), np.float64)
     lse = np.zeros((n_rows, n_qh), np.float64)
     lib().orc_attn(_p(q), _p(pos), n_rows, _p(k), _p(ks), _p(v), _p(vs), pool.capacity, pool.n_valid, n_qh, n_kv,
-                   d, BLOCK, _p(ids), _p(counts), topk_, sm_scale, _p(out), _p(lse))
+                   d, BLOCK, _p(ids), _p(counts), topk_, sm_scale, _p(out), _p(lse), _v_bits(pool))
     return out, lse
 
 
@@ -140,7 +145,7 @@ def attn_one(q, pos, i, h, pool, n_kv, ids=None, counts=None, sm_scale=1.0):
     out = np.zeros(d, np.float64)
     lse = np.zeros(1, np.float64)
     lib().orc_attn_one(_p(q), _p(pos), i, h, _p(k), _p(ks), _p(v), _p(vs), pool.capacity, pool.n_valid, n_qh,
-                       n_kv, d, BLOCK, _p(ids), _p(counts), topk_, sm_scale, _p(out), _p(lse))
+                       n_kv, d, BLOCK, _p(ids), _p(counts), topk_, sm_scale, _p(out), _p(lse), _v_bits(pool))
     return out, float(lse[0])
 
 
@@ -161,7 +166,7 @@ def chunk_partials(q, pos, pool, n_kv, n_chunks, ids=None, counts=None, bpc=1, s
     e = np.zeros((n_rows, n_qh, n_chunks), np.uint8)
     lib().orc_chunk_partials(_p(q), _p(pos), n_rows, _p(k), _p(ks), _p(v), _p(vs), pool.capacity, pool.n_valid,
                              n_qh, n_kv, d, BLOCK, _p(ids), _p(counts), topk_, bpc, n_chunks, sm_scale, _p(m), _p(l),
-                             _p(o), _p(e))
+                             _p(o), _p(e), _v_bits(pool))
     return m, l, o, e
 
 
@@ -223,6 +228,15 @@ def encode_group(x):
     return codes, float(scale[0])
 
 
+def encode_group4(x):
+    """4-bit codes (as int8 in [-7, 7]) and the fp32 scale of one group (see orc_encode_group4)."""
+    x = _c(x, np.float32)
+    codes = np.zeros(x.shape[0], np.int8)
+    scale = np.zeros(1, np.float32)
+    lib().orc_encode_group4(_p(x), x.shape[0], _p(codes), _p(scale))
+    return codes, float(scale[0])
+
+
 def kv_append(pool, k_new, v_new, cells, n_valid=None):
     """A copy of ``pool`` (a synth.Pool) with rows k_new, v_new [n_rows][n_kv][d] appended at cells [n_rows];
     n_valid is the count after the append (default: the pool's)."""
@@ -231,8 +245,8 @@ def kv_append(pool, k_new, v_new, cells, n_valid=None):
     out.k, out.ks, out.v, out.vs = (np.array(a, copy=True, order="C") for a in (pool.k, pool.ks, pool.v, pool.vs))
     out.n_valid = pool.n_valid if n_valid is None else n_valid
     n_kv, cap, d = out.k.shape
-    kn, vn = _c(k_new, np.float32), _c(v_new, np.float32)
+    kn, vn = _c(k_new, np.float32), _c(v_new, np.float32)   # d from K: a K8V4 pool's V rows are d/2 bytes
     cl = _c(cells, np.int32)
     lib().orc_kv_append(_p(out.k), _p(out.ks), _p(out.v), _p(out.vs), n_kv, cap, out.n_valid, d, _p(kn), _p(vn),
-                        _p(cl), cl.shape[0])
+                        _p(cl), cl.shape[0], _v_bits(pool))
     return out

@@ -44,12 +44,27 @@ typedef struct {
     const int8_t *k, *v;
     const float *ks, *vs;
     int32_t capacity, n_valid;
+    int32_t v_bits;   /* 8: int8 V codes [n_kv][cap][d]; 4: bytes [n_kv][cap][d/2], two signed 4-bit codes each */
 } orc_pool;
 
 static double deq(const int8_t *codes, const float *scales, int32_t cap, int32_t d, int32_t g, int32_t c, int32_t e)
 {
     const int32_t ng = d / ORC_GROUP;
     return (double)scales[((int64_t)g * cap + c) * ng + e / ORC_GROUP] * (double)codes[((int64_t)g * cap + c) * d + e];
+}
+
+/* Dequantised value of V. v_bits = 4 is the K8V4 cache the pages list beside int8 ([1888] "What changed", formats
+ * left alone; [2075] "Bit for bit", parity cases by KV format) without giving its layout. Reading: V codes are signed
+ * 4-bit integers (two's complement nibbles, -7..7 written), two per byte -- dim 2j in the low nibble, 2j + 1 in the
+ * high one -- with the same per-64-dim fp32 scales as int8 V. Pinned against an independent numpy unpacking. */
+static double deq_v(const orc_pool *p, int32_t d, int32_t g, int32_t c, int32_t e)
+{
+    if (p->v_bits != 4) return deq(p->v, p->vs, p->capacity, d, g, c, e);
+    const int32_t ng = d / ORC_GROUP;
+    const uint8_t byte = (uint8_t)p->v[((int64_t)g * p->capacity + c) * (d / 2) + e / 2];
+    int32_t nib = (e & 1) ? (byte >> 4) : (byte & 15);
+    if (nib >= 8) nib -= 16;
+    return (double)p->vs[((int64_t)g * p->capacity + c) * ng + e / ORC_GROUP] * (double)nib;
 }
 
 /* Per-block key summary ("indexer"): [2806] names an indexer that is appended per row next to K/V, without its
@@ -176,7 +191,7 @@ static void attend(const float *qrow, const orc_pool *p, int32_t g, int32_t d, c
     for (int32_t j = 0; j < n; j++) {
         double w = exp(t[j] - M);
         L += w;
-        for (int32_t e = 0; e < d; e++) out[e] += w * deq(p->v, p->vs, p->capacity, d, g, cells[j], e);
+        for (int32_t e = 0; e < d; e++) out[e] += w * deq_v(p, d, g, cells[j], e);
     }
     for (int32_t e = 0; e < d; e++) out[e] /= L;
     *lse = M + log(L);
@@ -187,9 +202,9 @@ static void attend(const float *qrow, const orc_pool *p, int32_t g, int32_t d, c
 void orc_attn_one(const float *q, const int32_t *pos, int32_t i, int32_t h, const int8_t *k, const float *ks,
                   const int8_t *v, const float *vs, int32_t cap, int32_t n_valid, int32_t n_qh, int32_t n_kv,
                   int32_t d, int32_t block, const int32_t *ids, const int32_t *counts, int32_t topk, double sm_scale,
-                  double *out, double *lse)
+                  double *out, double *lse, int32_t v_bits)
 {
-    orc_pool p = {k, v, ks, vs, cap, n_valid};
+    orc_pool p = {k, v, ks, vs, cap, n_valid, v_bits};
     const int32_t G = n_qh / n_kv, g = h / G;
     int32_t max_cells = ids ? topk * block : ((n_valid + block - 1) / block) * block;
     int32_t *cells = (int32_t *)malloc(sizeof(int32_t) * (size_t)(max_cells > 0 ? max_cells : 1));
@@ -210,12 +225,13 @@ void orc_attn_one(const float *q, const int32_t *pos, int32_t i, int32_t h, cons
 /* All rows and heads: out [n_rows][n_qh][d], lse [n_rows][n_qh]. */
 void orc_attn(const float *q, const int32_t *pos, int32_t n_rows, const int8_t *k, const float *ks, const int8_t *v,
               const float *vs, int32_t cap, int32_t n_valid, int32_t n_qh, int32_t n_kv, int32_t d, int32_t block,
-              const int32_t *ids, const int32_t *counts, int32_t topk, double sm_scale, double *out, double *lse)
+              const int32_t *ids, const int32_t *counts, int32_t topk, double sm_scale, double *out, double *lse,
+              int32_t v_bits)
 {
     for (int32_t i = 0; i < n_rows; i++)
         for (int32_t h = 0; h < n_qh; h++)
             orc_attn_one(q, pos, i, h, k, ks, v, vs, cap, n_valid, n_qh, n_kv, d, block, ids, counts, topk,
-                         sm_scale, out + ((int64_t)i * n_qh + h) * d, lse + (int64_t)i * n_qh + h);
+                         sm_scale, out + ((int64_t)i * n_qh + h) * d, lse + (int64_t)i * n_qh + h, v_bits);
 }
 
 /* Chunk partials, for checking a split-K chunk kernel's scratch: [1888] "What changed" (one split of one query's
@@ -228,9 +244,9 @@ void orc_chunk_partials(const float *q, const int32_t *pos, int32_t n_rows, cons
                         const int8_t *v, const float *vs, int32_t cap, int32_t n_valid, int32_t n_qh, int32_t n_kv,
                         int32_t d, int32_t block, const int32_t *ids, const int32_t *counts, int32_t topk,
                         int32_t bpc, int32_t n_chunks, double sm_scale, double *m, double *l, double *o,
-                        uint8_t *empty)
+                        uint8_t *empty, int32_t v_bits)
 {
-    orc_pool p = {k, v, ks, vs, cap, n_valid};
+    orc_pool p = {k, v, ks, vs, cap, n_valid, v_bits};
     const int32_t G = n_qh / n_kv;
     int32_t max_blocks = ids ? topk : bpc;
     int32_t *cells = (int32_t *)malloc(sizeof(int32_t) * (size_t)(max_blocks * block + 1));
@@ -269,7 +285,7 @@ void orc_chunk_partials(const float *q, const int32_t *pos, int32_t n_rows, cons
                 for (int32_t c = 0; c < n; c++) {
                     double w = exp(t[c] - mj);
                     lj += w;
-                    for (int32_t e = 0; e < d; e++) oj[e] += w * deq(p.v, p.vs, cap, d, g, cells[c], e);
+                    for (int32_t e = 0; e < d; e++) oj[e] += w * deq_v(&p, d, g, cells[c], e);
                 }
                 m[idx] = mj; l[idx] = lj; empty[idx] = 0;
             }
@@ -368,12 +384,37 @@ void orc_encode_group(const float *x, int32_t n, int8_t *codes, float *scale)
     *scale = amax / 127.0f;
 }
 
+/* The same encoder for the 4-bit V codes of a K8V4 pool (reading, as above): scale = amax / 7,
+ * code = rint(x * (7 / amax)) clamped to [-7, 7], in fp32. */
+void orc_encode_group4(const float *x, int32_t n, int8_t *codes, float *scale)
+{
+    float amax = 0.0f;
+    for (int32_t e = 0; e < n; e++) {
+        const float a = fabsf(x[e]);
+        if (a > amax) amax = a;
+    }
+    if (amax == 0.0f) {
+        for (int32_t e = 0; e < n; e++) codes[e] = 0;
+        *scale = 0.0f;
+        return;
+    }
+    const float inv = 7.0f / amax;
+    for (int32_t e = 0; e < n; e++) {
+        float c = rintf(x[e] * inv);
+        if (c > 7.0f) c = 7.0f;
+        if (c < -7.0f) c = -7.0f;
+        codes[e] = (int8_t)c;
+    }
+    *scale = amax / 7.0f;
+}
+
 /* Append of n_rows new cells to one pool: row i writes cell cells[i] of every KV head, K from k_new and V from v_new
- * ([n_rows][n_kv][d] f32), one orc_encode_group per 64-dim group. Rows whose cell is outside [0, n_valid) are
+ * ([n_rows][n_kv][d] f32), one orc_encode_group per 64-dim group (orc_encode_group4 for a K8V4 pool's V). Rows whose cell is outside [0, n_valid) are
  * skipped (n_valid is the pool's count after the append). Index rows are recomputed by orc_block_index. */
 void orc_kv_append(int8_t *k, float *ks, int8_t *v, float *vs, int32_t n_kv, int32_t cap, int32_t n_valid, int32_t d,
-                   const float *k_new, const float *v_new, const int32_t *cells, int32_t n_rows)
+                   const float *k_new, const float *v_new, const int32_t *cells, int32_t n_rows, int32_t v_bits)
 {
+    int8_t c4[ORC_GROUP];
     const int32_t ng = d / ORC_GROUP;
     for (int32_t i = 0; i < n_rows; i++) {
         const int32_t c = cells[i];
@@ -382,7 +423,13 @@ void orc_kv_append(int8_t *k, float *ks, int8_t *v, float *vs, int32_t n_kv, int
             const int64_t src = ((int64_t)i * n_kv + g) * d, dst = ((int64_t)g * cap + c);
             for (int32_t t = 0; t < ng; t++) {
                 orc_encode_group(k_new + src + t * ORC_GROUP, ORC_GROUP, k + dst * d + t * ORC_GROUP, ks + dst * ng + t);
-                orc_encode_group(v_new + src + t * ORC_GROUP, ORC_GROUP, v + dst * d + t * ORC_GROUP, vs + dst * ng + t);
+                if (v_bits != 4) {
+                    orc_encode_group(v_new + src + t * ORC_GROUP, ORC_GROUP, v + dst * d + t * ORC_GROUP, vs + dst * ng + t);
+                } else {   /* pack two 4-bit codes per byte, dim 2j low */
+                    orc_encode_group4(v_new + src + t * ORC_GROUP, ORC_GROUP, c4, vs + dst * ng + t);
+                    for (int32_t e = 0; e < ORC_GROUP; e += 2)
+                        v[dst * (d / 2) + (t * ORC_GROUP + e) / 2] = (int8_t)(uint8_t)((c4[e] & 15) | ((c4[e + 1] & 15) << 4));
+                }
             }
         }
     }

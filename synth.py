@@ -15,7 +15,9 @@ Value distributions (the pages give none): codes uniform on [-127, 127], scales 
 q ~ N(0, 1)/sqrt(head_dim) drawn in float64 and rounded to float32. Cells past ``n_valid`` hold poison (codes
 -128, NaN scales) for parity runs, so any read outside the valid range shows up, or zeros for timing runs.
 
-Pool layout: codes ``[n_kv][capacity][d]`` int8, scales ``[n_kv][capacity][d // 64]`` float32.
+Pool layout: codes ``[n_kv][capacity][d]`` int8, scales ``[n_kv][capacity][d // 64]`` float32. A K8V4 pool
+(``v_bits=4``, a cache format the pages list beside int8 without its layout) keeps int8 K and stores V as signed
+4-bit codes (uniform on [-7, 7]) packed two per byte, ``[n_kv][capacity][d // 2]``, dim 2j in the low nibble.
 """
 from __future__ import annotations
 
@@ -33,10 +35,11 @@ POISON_CODE = -128
 class Pool:
     k: np.ndarray        # int8  [n_kv][cap][d]
     ks: np.ndarray       # f32   [n_kv][cap][d/64]
-    v: np.ndarray        # int8  [n_kv][cap][d]
+    v: np.ndarray        # int8  [n_kv][cap][d] (v_bits 8) or bytes [n_kv][cap][d/2] of two 4-bit codes (v_bits 4)
     vs: np.ndarray       # f32   [n_kv][cap][d/64]
     capacity: int
     n_valid: int
+    v_bits: int = 8
 
 
 @dataclasses.dataclass
@@ -66,25 +69,37 @@ def _scales(rng, shape):
     return rng.uniform(0.005, 0.02, size=shape).astype(np.float32)
 
 
-def make_pool(rng, n_kv, capacity, n_valid, d, poison=True):
-    """Draw one pool's valid cells in the fixed order K codes, K scales, V codes, V scales."""
-    assert d % GROUP == 0 and 0 <= n_valid <= capacity
+def pack_v4(codes):
+    """Signed 4-bit codes [..., d] (in [-8, 7]) -> bytes [..., d/2] as int8: dim 2j in the low nibble, 2j + 1 in the
+    high nibble (the K8V4 layout of the pool's V)."""
+    c = codes.astype(np.int16) & 15
+    return (c[..., 0::2] | (c[..., 1::2] << 4)).astype(np.uint8).view(np.int8)
+
+
+def make_pool(rng, n_kv, capacity, n_valid, d, poison=True, v_bits=8):
+    """Draw one pool's valid cells in the fixed order K codes, K scales, V codes, V scales. v_bits = 4 (K8V4) draws
+    V codes uniform on [-7, 7] and packs two per byte; the K side is the same as for v_bits = 8."""
+    assert d % GROUP == 0 and 0 <= n_valid <= capacity and v_bits in (4, 8)
     ng = d // GROUP
     kc = _codes(rng, (n_kv, n_valid, d))
     ksc = _scales(rng, (n_kv, n_valid, ng))
-    vc = _codes(rng, (n_kv, n_valid, d))
+    vc = _codes(rng, (n_kv, n_valid, d)) if v_bits == 8 else rng.integers(-7, 8, (n_kv, n_valid, d)).astype(np.int8)
     vsc = _scales(rng, (n_kv, n_valid, ng))
     fill_code = POISON_CODE if poison else 0
     fill_scale = np.float32(np.nan) if poison else np.float32(0)
     k = np.full((n_kv, capacity, d), fill_code, dtype=np.int8)
-    v = np.full((n_kv, capacity, d), fill_code, dtype=np.int8)
     ks = np.full((n_kv, capacity, ng), fill_scale, dtype=np.float32)
     vs = np.full((n_kv, capacity, ng), fill_scale, dtype=np.float32)
     k[:, :n_valid] = kc
-    v[:, :n_valid] = vc
     ks[:, :n_valid] = ksc
     vs[:, :n_valid] = vsc
-    return Pool(k, ks, v, vs, capacity, n_valid)
+    if v_bits == 8:
+        v = np.full((n_kv, capacity, d), fill_code, dtype=np.int8)
+        v[:, :n_valid] = vc
+    else:   # poison: code -8 in both nibbles
+        v = pack_v4(np.full((n_kv, capacity, d), -8 if poison else 0, dtype=np.int8))
+        v[:, :n_valid] = pack_v4(vc)
+    return Pool(k, ks, v, vs, capacity, n_valid, v_bits)
 
 
 def make_q(rng, n_rows, n_q_heads, d):
@@ -123,7 +138,7 @@ def workload(name, poison=True, seed=None, **override):
     if seed is None:
         seed = 1000 + WORKLOAD_ORDER.index(name)
     rng = np.random.Generator(np.random.PCG64(seed))
-    pools = [make_pool(rng, spec["hkv"], spec["cap"], spec["n_valid"], spec["d"], poison)
+    pools = [make_pool(rng, spec["hkv"], spec["cap"], spec["n_valid"], spec["d"], poison, spec.get("v_bits", 8))
              for _ in range(spec["slots"])]
     n_rows = spec["slots"] * spec["rows"]
     q = make_q(rng, n_rows, spec["hq"], spec["d"])
@@ -140,9 +155,9 @@ def workload(name, poison=True, seed=None, **override):
                     prompt=prompt, pos0=int(pos[0]) if prompt else 0)
 
 
-def random_pool(seed, n_kv, capacity, n_valid, d, poison=True):
+def random_pool(seed, n_kv, capacity, n_valid, d, poison=True, v_bits=8):
     rng = np.random.Generator(np.random.PCG64(seed))
-    return make_pool(rng, n_kv, capacity, n_valid, d, poison)
+    return make_pool(rng, n_kv, capacity, n_valid, d, poison, v_bits)
 
 
 def random_q(seed, n_rows, n_q_heads, d):

@@ -17,6 +17,22 @@ def dequant(codes, scales):
     return codes.astype(np.float64) * np.repeat(scales.astype(np.float64), GROUP, axis=-1)
 
 
+def v_codes(pool):
+    """V codes [n_kv][cap][d] as int8: the stored array, or the two signed nibbles of each byte of a K8V4 pool
+    (low nibble = even dim), unpacked here with numpy bit operations."""
+    if getattr(pool, "v_bits", 8) != 4:
+        return pool.v
+    b = pool.v.view(np.uint8)
+    lo = (b & 0x0F).astype(np.int16)
+    hi = (b >> 4).astype(np.int16)
+    lo = np.where(lo >= 8, lo - 16, lo)
+    hi = np.where(hi >= 8, hi - 16, hi)
+    out = np.empty(b.shape[:-1] + (2 * b.shape[-1],), np.int8)
+    out[..., 0::2] = lo
+    out[..., 1::2] = hi
+    return out
+
+
 def repeat_kv(x, n_q_heads):
     """[n_kv][...] -> [n_q_heads][...]: q head h reads KV head h // (n_q_heads // n_kv)."""
     return np.repeat(x, n_q_heads // x.shape[0], axis=0)
@@ -29,7 +45,7 @@ def textbook_attention(q, pos, pool, selected_blocks=None, sm_scale=1.0):
     n_rows, n_qh, d = q.shape
     n_kv = pool.k.shape[0]
     K = repeat_kv(dequant(pool.k[:, :pool.n_valid], pool.ks[:, :pool.n_valid]), n_qh)
-    V = repeat_kv(dequant(pool.v[:, :pool.n_valid], pool.vs[:, :pool.n_valid]), n_qh)
+    V = repeat_kv(dequant(v_codes(pool)[:, :pool.n_valid], pool.vs[:, :pool.n_valid]), n_qh)
     G = n_qh // n_kv
     out = np.zeros((n_rows, n_qh, d))
     for i in range(n_rows):
@@ -56,7 +72,7 @@ def matrix_attention(q, pos, pool, sm_scale=1.0):
     """Dense causal attention as masked matrix products (numpy float64), for medium sizes."""
     n_rows, n_qh, d = q.shape
     K = repeat_kv(dequant(pool.k[:, :pool.n_valid], pool.ks[:, :pool.n_valid]), n_qh)   # [Hq][n][d]
-    V = repeat_kv(dequant(pool.v[:, :pool.n_valid], pool.vs[:, :pool.n_valid]), n_qh)
+    V = repeat_kv(dequant(v_codes(pool)[:, :pool.n_valid], pool.vs[:, :pool.n_valid]), n_qh)
     Q = q.astype(np.float64).transpose(1, 0, 2)                                           # [Hq][rows][d]
     S = sm_scale * np.matmul(Q, K.transpose(0, 2, 1))                                     # [Hq][rows][n]
     mask = np.arange(pool.n_valid)[None, :] <= np.asarray(pos)[:, None]                   # [rows][n]

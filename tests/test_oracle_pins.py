@@ -399,3 +399,74 @@ def test_kv_append_touches_only_its_cells():
                 assert np.array_equal(out.k[g, c, 64 * t:64 * t + 64], codes) and out.ks[g, c, t] == np.float32(scale)
                 codes, scale = oracle.encode_group(vn[r, g, 64 * t:64 * t + 64])
                 assert np.array_equal(out.v[g, c, 64 * t:64 * t + 64], codes) and out.vs[g, c, t] == np.float32(scale)
+
+
+# ------------------------------------------------------------------------------------------------------ K8V4
+def k8v4_case(seed, d=128, cap=400, n_valid=330, rows=3):
+    pool = synth.random_pool(seed, 2, cap, n_valid, d, poison=True, v_bits=4)
+    q = synth.random_q(seed + 1, rows, 6, d)
+    pos = np.array([n_valid - rows + r for r in range(rows)], np.int32)
+    return pool, q, pos
+
+
+@pytest.mark.parametrize("d", [128, 256])
+def test_k8v4_dense_and_selected_equal_textbook(d):
+    """4-bit V unpacked by numpy in the brute-force path; poison (code -8, NaN scales) past n_valid stays unread."""
+    pool, q, pos = k8v4_case(950 + d, d=d)
+    assert pool.v.shape[-1] == d // 2
+    out, _ = oracle.attn(q, pos, pool, n_kv=2)
+    np.testing.assert_allclose(out, brute.textbook_attention(q, pos, pool), rtol=0, atol=1e-12)
+    sel = [[{0, 3, 5}, {1, 2}], [{4}, {0, 5}], [{5, 2, 1}, {3}]]
+    ids = np.full((3, 2, 3), -1, np.int32)
+    counts = np.zeros((3, 2), np.int32)
+    for i in range(3):
+        for g in range(2):
+            b = sorted(sel[i][g])
+            ids[i, g, :len(b)] = b
+            counts[i, g] = len(b)
+    out, _ = oracle.attn(q, pos, pool, 2, ids=ids, counts=counts)
+    np.testing.assert_allclose(out, brute.textbook_attention(q, pos, pool, selected_blocks=sel), rtol=0, atol=1e-12)
+
+
+def test_k8v4_v_differs_from_int8_reading():
+    """A plausible slip -- reading the packed bytes as int8 V -- changes the result (the pin above would see it)."""
+    pool, q, pos = k8v4_case(970)
+    wrong = synth.Pool(pool.k, pool.ks, np.repeat(pool.v, 2, axis=-1), pool.vs, pool.capacity, pool.n_valid, 8)
+    a, _ = oracle.attn(q, pos, pool, 2)
+    b, _ = oracle.attn(q, pos, wrong, 2)
+    assert np.abs(a - b).max() > 1e-3
+
+
+def test_encode4_is_nearest_code_and_recovers_grids():
+    rng = np.random.default_rng(980)
+    for _ in range(6):
+        x = (rng.standard_normal(64) * rng.choice([1e-2, 1.0, 9.0])).astype(np.float32)
+        codes, scale = oracle.encode_group4(x)
+        amax = np.float32(np.abs(x).max())
+        y = (x * np.float32(np.float32(7.0) / amax)).astype(np.float32)
+        cand = np.arange(-7, 8, dtype=np.float64)
+        best = cand[np.argmin(np.abs(y.astype(np.float64)[:, None] - cand[None, :]), axis=1)]
+        ties = np.abs(np.abs(y - np.trunc(y)) - 0.5) == 0
+        assert np.all(codes[~ties] == best[~ties]) and np.all(codes[ties] % 2 == 0)
+        assert scale == np.float32(amax / np.float32(7.0))
+    for e in (-5, 0, 3):
+        k = rng.integers(-7, 8, 64)
+        k[3] = 7
+        codes, scale = oracle.encode_group4((k * 2.0 ** e).astype(np.float32))
+        assert np.array_equal(codes.astype(np.int64), k) and scale == np.float32(2.0 ** e)
+
+
+def test_kv_append_k8v4_packs_nibbles():
+    pool = synth.random_pool(990, 2, 200, 150, 128, poison=False, v_bits=4)
+    rng = np.random.default_rng(991)
+    kn = rng.standard_normal((2, 2, 128)).astype(np.float32)
+    vn = rng.standard_normal((2, 2, 128)).astype(np.float32)
+    cells = np.array([10, 149], np.int32)
+    out = oracle.kv_append(pool, kn, vn, cells)
+    unpacked = brute.v_codes(out)
+    for r, c in enumerate(cells):
+        for g in range(2):
+            for t in range(2):
+                codes, scale = oracle.encode_group4(vn[r, g, 64 * t:64 * t + 64])
+                assert np.array_equal(unpacked[g, c, 64 * t:64 * t + 64], codes) and out.vs[g, c, t] == np.float32(scale)
+    assert np.array_equal(brute.v_codes(out)[:, 11:149], brute.v_codes(pool)[:, 11:149])
