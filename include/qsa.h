@@ -62,15 +62,22 @@ typedef struct {
     int32_t block_cells; /* must be 64 */
 } qsa_dims;
 
-/* One int8 KV pool (one slot's cache). Cells c < n_valid are valid; c in [n_valid, capacity) are never read. */
+/* One int8 KV pool (one slot's cache). Cells c < n_valid are valid; c in [n_valid, capacity) are never read.
+ * v_bits selects the V format: 8 (or 0) = int8 V codes like K; 4 = K8V4, the cache format the pages list beside
+ * int8 (#1888, "What changed": formats left alone; #2075, "Bit for bit": parity cases per KV format) without its
+ * layout -- V codes are signed 4-bit integers (-7..7), two per byte (dim 2j in the low nibble, 2j + 1 in the high
+ * one), v is [n_kv_heads][capacity][head_dim / 2] bytes, and v_scale is as for int8. K8V4 is supported by the decode
+ * calls at head_dim 128 and 256 (QSA_ERR_UNSUPPORTED otherwise and in qsa_prompt_attn); the pools of one call must
+ * share a format. */
 typedef struct {
     const int8_t *k;
     const float *k_scale;
     const int8_t *v;
     const float *v_scale;
-    const float *index; /* block index from qsa_block_index; read only by qsa_block_scores */
+    const float *index; /* block index from qsa_block_index; read only by the selection calls */
     int32_t capacity;
     int32_t n_valid;
+    int32_t v_bits;     /* 8 (or 0): int8 V; 4: K8V4 */
 } qsa_pool;
 
 /* Split-K chunk partials ("partials in the decode scratch", [1888] "What changed"), owned by the caller.

@@ -39,7 +39,7 @@ class _Dims(ctypes.Structure):
 class _Pool(ctypes.Structure):
     _fields_ = [("k", ctypes.c_void_p), ("k_scale", ctypes.c_void_p), ("v", ctypes.c_void_p),
                 ("v_scale", ctypes.c_void_p), ("index", ctypes.c_void_p), ("capacity", ctypes.c_int32),
-                ("n_valid", ctypes.c_int32)]
+                ("n_valid", ctypes.c_int32), ("v_bits", ctypes.c_int32)]
 
 
 class _Partials(ctypes.Structure):
@@ -128,14 +128,16 @@ class Dims:
 
 @dataclasses.dataclass
 class Pool:
-    """Device tensors of one int8 KV pool: k, v int8 [n_kv][cap][d]; k_scale, v_scale f32 [n_kv][cap][d/64];
-    index f32 [n_kv][ceil(cap/64)][d] (optional, needed by qsa_block_scores)."""
+    """Device tensors of one int8 KV pool: k int8 [n_kv][cap][d]; v int8 [n_kv][cap][d] (v_bits 8) or
+    [n_kv][cap][d/2] bytes of two 4-bit codes (v_bits 4, K8V4); k_scale, v_scale f32 [n_kv][cap][d/64];
+    index f32 [n_kv][ceil(cap/64)][d] (optional, needed by the selection calls)."""
     k: torch.Tensor
     k_scale: torch.Tensor
     v: torch.Tensor
     v_scale: torch.Tensor
     n_valid: int
     index: Optional[torch.Tensor] = None
+    v_bits: int = 8
 
     @property
     def capacity(self):
@@ -144,7 +146,8 @@ class Pool:
     def c(self):
         return _Pool(_ptr(self.k, torch.int8, "k"), _ptr(self.k_scale, torch.float32, "k_scale"),
                      _ptr(self.v, torch.int8, "v"), _ptr(self.v_scale, torch.float32, "v_scale"),
-                     _ptr(self.index, torch.float32, "index", allow_none=True), self.capacity, self.n_valid)
+                     _ptr(self.index, torch.float32, "index", allow_none=True), self.capacity, self.n_valid,
+                     self.v_bits)
 
 
 @dataclasses.dataclass

@@ -100,9 +100,11 @@ __device__ __forceinline__ bool append_row(const AppendArgs &a, int32_t i, PoolA
     return c >= 0 && c < P.n_valid;
 }
 
-// int8 encode of one 64-dim group held one value per lane: amax = max |x|, scale = amax / 127,
-// code = rint(x * (127 / amax)) clamped to [-127, 127] (all fp32, correctly rounded); amax = 0 gives zeros.
-template <int D>
+// Encode of one 64-dim group held one value per lane, with QMAX = 2^(bits-1) - 1 (127 for int8, 7 for the 4-bit V
+// of a K8V4 pool): amax = max |x|, scale = amax / QMAX, code = rint(x * (QMAX / amax)) clamped to [-QMAX, QMAX]
+// (all fp32, correctly rounded); amax = 0 gives zeros. 4-bit codes are packed two per byte, dim 2j in the low
+// nibble: the even lane of each pair takes its odd partner's code and writes the byte.
+template <int D, int VB>
 __global__ __launch_bounds__(64) void append_encode_kernel(const AppendArgs a)
 {
     constexpr int NG = D / QSA_GROUP;
@@ -114,8 +116,10 @@ __global__ __launch_bounds__(64) void append_encode_kernel(const AppendArgs a)
     const int64_t src = ((int64_t)i * a.n_kv + g) * D, dst = (int64_t)g * P.capacity + c;
 #pragma unroll
     for (int which = 0; which < 2; which++) {
+        const bool v4 = which == 1 && VB == 4;
+        const float qmax = v4 ? 7.0f : 127.0f;
         const float *x = (which ? a.v_new : a.k_new) + src;
-        int8_t *codes = const_cast<int8_t *>(which ? P.v : P.k) + dst * D;
+        int8_t *codes = const_cast<int8_t *>(which ? P.v : P.k) + dst * (v4 ? D / 2 : D);
         float *scales = const_cast<float *>(which ? P.vs : P.ks) + dst * NG;
         float xv[NG];
 #pragma unroll
@@ -124,9 +128,15 @@ __global__ __launch_bounds__(64) void append_encode_kernel(const AppendArgs a)
         for (int t = 0; t < NG; t++) {
             const float amax = group_max<64>(fabsf(xv[t]));
             float code = 0.f;
-            if (amax > 0.f) code = fminf(fmaxf(rintf(xv[t] * (127.0f / amax)), -127.f), 127.f);
-            codes[QSA_GROUP * t + lane] = (int8_t)(int32_t)code;
-            if (lane == 0) scales[t] = amax / 127.0f;
+            if (amax > 0.f) code = fminf(fmaxf(rintf(xv[t] * (qmax / amax)), -qmax), qmax);
+            const int32_t ci = (int32_t)code;
+            if (v4) {
+                const int32_t hi = __shfl_xor(ci, 1);
+                if (!(lane & 1)) codes[(QSA_GROUP * t + lane) / 2] = (int8_t)((ci & 15) | ((hi & 15) << 4));
+            } else {
+                codes[QSA_GROUP * t + lane] = (int8_t)ci;
+            }
+            if (lane == 0) scales[t] = amax / qmax;
         }
     }
 }
@@ -245,18 +255,29 @@ struct ChunkArgs {
 // across lanes at the end; the CW waves are combined through LDS with a log-sum-exp rescale.
 constexpr int CW = 4;
 
-template <int D, int G>
+//
+// VB is the V code width: 8 (int8) or 4 (K8V4: two signed 4-bit codes per byte, dim 2j in the low nibble). A V row
+// is RB = D * VB / 8 bytes; a 16-byte chunk of it holds DPC = 128 / VB dims, so a transposing read gives each lane
+// 8 / VB dims of 8 cells and a lane makes NT = DPL * VB / 8 reads per 8 cells. The K side is the same for both.
+template <int D, int G, int VB>
 __global__ __launch_bounds__(64 * CW) void attn_chunk_kernel(const ChunkArgs a)
 {
+    static_assert(VB == 8 || (VB == 4 && D >= 128), "K8V4 needs head_dim >= 128");
     constexpr int PC = D <= 128 ? 32 : 16;           // cells per piece
     constexpr int LPC = D / 16, CPS = 64 / LPC, STEPS = PC / CPS, NG = D / QSA_GROUP;
     constexpr int DPL = D / 64;                      // output dims per lane
+    constexpr int RB = D * VB / 8;                   // V bytes per cell row
+    constexpr int NPB = 8 / VB;                      // V codes per byte
+    constexpr int NT = DPL / NPB;                    // transposing reads per lane per 8 cells
+    constexpr int DPC = 16 * NPB;                    // dims per 16-byte chunk
+    constexpr int CPG = QSA_GROUP / DPC;             // 16-byte chunks per scale group
     constexpr int SUBS = 4 / NG;                     // 16-lane subgroups per scale group in the p . v layout
-    constexpr int CHUNKS = D / 16;                   // 16-byte chunks per cell row
+    constexpr int CHUNKS = RB / 16;                  // 16-byte chunks per V row
     constexpr int SWZ = (CHUNKS < 8 ? CHUNKS : 8) - 1;
-    constexpr int VCH = PC * D / 1024;               // 1 KB global -> LDS copies per piece
+    constexpr int VCH = PC * RB / 1024;              // 1 KB global -> LDS copies per piece
     constexpr int GP = (G + 3) & ~3;                 // p * v_scale row padded to float4s
-    __shared__ __align__(16) int8_t sv[CW][PC * D];  // the wave's V piece: [cell][D], chunk c of row r at c ^ (r & SWZ)
+    static_assert(CPG == SUBS * NT && VCH * 1024 == PC * RB, "p . v lane layout");
+    __shared__ __align__(16) int8_t sv[CW][PC * RB]; // the wave's V piece: [cell][RB], chunk c of row r at c ^ (r & SWZ)
     __shared__ __align__(16) float sp[CW][PC][NG][GP];
     __shared__ float sm[CW][G], sl[CW][G];
     __shared__ float so[CW][G][D];
@@ -312,7 +333,7 @@ __global__ __launch_bounds__(64 * CW) void attn_chunk_kernel(const ChunkArgs a)
     }
 
     const int8_t *kbase = P.k + (int64_t)g * P.capacity * D + 16 * s;
-    const int8_t *vbase = P.v + (int64_t)g * P.capacity * D;
+    const int8_t *vbase = P.v + (int64_t)g * P.capacity * RB;
     const float *ksbase = P.ks + (int64_t)g * P.capacity * NG + grp_s;
     const float *vsbase = P.vs + (int64_t)g * P.capacity * NG + (s < NG ? s : 0);
     int8_t *svw = sv[wave];
@@ -339,7 +360,7 @@ __global__ __launch_bounds__(64 * CW) void attn_chunk_kernel(const ChunkArgs a)
         for (int q = 0; q < VCH; q++) {
             const int slot = 64 * q + lane, cell = slot / CHUNKS, pch = slot % CHUNKS;
             const int32_t c = min(cb + cell, limit);
-            __builtin_amdgcn_global_load_lds(vbase + (int64_t)c * D + 16 * (pch ^ (cell & SWZ)),
+            __builtin_amdgcn_global_load_lds(vbase + (int64_t)c * RB + 16 * (pch ^ (cell & SWZ)),
                                              (QSA_LDS void *)(svw + 1024 * q), 16, 0, 0);
         }
 
@@ -403,13 +424,13 @@ __global__ __launch_bounds__(64 * CW) void attn_chunk_kernel(const ChunkArgs a)
         const int i8 = jl >> 1, hh = jl & 1;
 #pragma unroll
         for (int co = 0; co < PC / 8; co++) {
-            v2i vb[DPL];
+            v2i vb[NT];
 #pragma unroll
-            for (int t = 0; t < DPL; t++) {
-                const int lc = 4 * grp_v + sub_v + SUBS * t;   // logical 16-byte chunk of the lane's dim block
+            for (int t = 0; t < NT; t++) {
+                const int lc = CPG * grp_v + sub_v + SUBS * t;   // logical 16-byte chunk of the lane's dims
                 const int cell = 8 * co + i8;
                 vb[t] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-                    (QSA_LDS v2i *)(svw + cell * D + 16 * (lc ^ (cell & SWZ)) + 8 * hh));
+                    (QSA_LDS v2i *)(svw + cell * RB + 16 * (lc ^ (cell & SWZ)) + 8 * hh));
             }
 #pragma unroll
             for (int ci = 0; ci < 8; ci++) {
@@ -421,11 +442,15 @@ __global__ __launch_bounds__(64 * CW) void attn_chunk_kernel(const ChunkArgs a)
                     pw[h4] = v4.x; pw[h4 + 1] = v4.y; pw[h4 + 2] = v4.z; pw[h4 + 3] = v4.w;
                 }
 #pragma unroll
-                for (int t = 0; t < DPL; t++) {
+                for (int t = 0; t < NT; t++) {
                     const int32_t word = ci < 4 ? vb[t][0] : vb[t][1];
-                    const float x = (float)((word << (24 - 8 * (ci & 3))) >> 24);
 #pragma unroll
-                    for (int h = 0; h < G; h++) o[h][t] = fmaf(pw[h], x, o[h][t]);
+                    for (int n = 0; n < NPB; n++) {
+                        // signed field of VB bits at bit 8 * (ci & 3) + VB * n
+                        const float x = (float)((word << (32 - VB - 8 * (ci & 3) - VB * n)) >> (32 - VB));
+#pragma unroll
+                        for (int h = 0; h < G; h++) o[h][NPB * t + n] = fmaf(pw[h], x, o[h][NPB * t + n]);
+                    }
                 }
             }
         }
@@ -442,10 +467,13 @@ __global__ __launch_bounds__(64 * CW) void attn_chunk_kernel(const ChunkArgs a)
         }
     }
 #pragma unroll
-    for (int t = 0; t < DPL; t++) {
-        const int d = 64 * grp_v + 16 * sub_v + 16 * SUBS * t + jl;
+    for (int t = 0; t < NT; t++) {
 #pragma unroll
-        for (int h = 0; h < G; h++) so[wave][h][d] = o[h][t];
+        for (int n = 0; n < NPB; n++) {
+            const int d = DPC * (CPG * grp_v + sub_v + SUBS * t) + NPB * jl + n;
+#pragma unroll
+            for (int h = 0; h < G; h++) so[wave][h][d] = o[h][NPB * t + n];
+        }
     }
     __syncthreads();
 
@@ -579,6 +607,8 @@ extern "C" qsa_status qsa_kv_append(const qsa_pool *pools, int32_t n_pools, cons
     if (n_pools > QSA_MAX_POOLS) return QSA_ERR_UNSUPPORTED;
     for (int32_t p = 0; p < n_pools; p++)
         if ((st = check_pool(&pools[p], true)) != QSA_OK) return st;
+    const int vb = common_v_bits(pools, n_pools, dims.head_dim);
+    if (!vb) return QSA_ERR_UNSUPPORTED;
     if (n_rows == 0) return QSA_OK;
     if (n_rows > 65535) return QSA_ERR_UNSUPPORTED;
     AppendArgs a{};
@@ -589,10 +619,17 @@ extern "C" qsa_status qsa_kv_append(const qsa_pool *pools, int32_t n_pools, cons
     a.row_pool = row_pool; a.k_new = k_new; a.v_new = v_new; a.cells = cells; a.n_kv = dims.n_kv_heads;
     dim3 grid(n_rows, dims.n_kv_heads);
     hipStream_t s = (hipStream_t)stream;
+    switch (dims.head_dim * (vb == 4 ? -1 : 1)) {
+    case 64: append_encode_kernel<64, 8><<<grid, 64, 0, s>>>(a); break;
+    case 128: append_encode_kernel<128, 8><<<grid, 64, 0, s>>>(a); break;
+    case -128: append_encode_kernel<128, 4><<<grid, 64, 0, s>>>(a); break;
+    case -256: append_encode_kernel<256, 4><<<grid, 64, 0, s>>>(a); break;
+    default: append_encode_kernel<256, 8><<<grid, 64, 0, s>>>(a); break;
+    }
     switch (dims.head_dim) {
-    case 64: append_encode_kernel<64><<<grid, 64, 0, s>>>(a); append_index_kernel<64><<<grid, 64, 0, s>>>(a); break;
-    case 128: append_encode_kernel<128><<<grid, 64, 0, s>>>(a); append_index_kernel<128><<<grid, 64, 0, s>>>(a); break;
-    default: append_encode_kernel<256><<<grid, 64, 0, s>>>(a); append_index_kernel<256><<<grid, 64, 0, s>>>(a); break;
+    case 64: append_index_kernel<64><<<grid, 64, 0, s>>>(a); break;
+    case 128: append_index_kernel<128><<<grid, 64, 0, s>>>(a); break;
+    default: append_index_kernel<256><<<grid, 64, 0, s>>>(a); break;
     }
     return launch_status();
 }
@@ -623,27 +660,33 @@ extern "C" qsa_status qsa_block_scores(const float *q, const int32_t *pos, int32
 }
 
 namespace {
-template <int D>
+template <int D, int VB>
 void launch_chunk(int G, dim3 grid, hipStream_t s, const ChunkArgs &a)
 {
     switch (G) {
-    case 1: attn_chunk_kernel<D, 1><<<grid, 64 * CW, 0, s>>>(a); break;
-    case 2: attn_chunk_kernel<D, 2><<<grid, 64 * CW, 0, s>>>(a); break;
-    case 3: attn_chunk_kernel<D, 3><<<grid, 64 * CW, 0, s>>>(a); break;
-    case 4: attn_chunk_kernel<D, 4><<<grid, 64 * CW, 0, s>>>(a); break;
-    case 5: attn_chunk_kernel<D, 5><<<grid, 64 * CW, 0, s>>>(a); break;
-    case 6: attn_chunk_kernel<D, 6><<<grid, 64 * CW, 0, s>>>(a); break;
-    case 7: attn_chunk_kernel<D, 7><<<grid, 64 * CW, 0, s>>>(a); break;
-    default: attn_chunk_kernel<D, 8><<<grid, 64 * CW, 0, s>>>(a); break;
+    case 1: attn_chunk_kernel<D, 1, VB><<<grid, 64 * CW, 0, s>>>(a); break;
+    case 2: attn_chunk_kernel<D, 2, VB><<<grid, 64 * CW, 0, s>>>(a); break;
+    case 3: attn_chunk_kernel<D, 3, VB><<<grid, 64 * CW, 0, s>>>(a); break;
+    case 4: attn_chunk_kernel<D, 4, VB><<<grid, 64 * CW, 0, s>>>(a); break;
+    case 5: attn_chunk_kernel<D, 5, VB><<<grid, 64 * CW, 0, s>>>(a); break;
+    case 6: attn_chunk_kernel<D, 6, VB><<<grid, 64 * CW, 0, s>>>(a); break;
+    case 7: attn_chunk_kernel<D, 7, VB><<<grid, 64 * CW, 0, s>>>(a); break;
+    default: attn_chunk_kernel<D, 8, VB><<<grid, 64 * CW, 0, s>>>(a); break;
     }
 }
 
-void launch_chunk_d(int D, int G, dim3 grid, hipStream_t s, const ChunkArgs &a)
+// vb is the pools' common V width from common_v_bits (4 only with D >= 128).
+void launch_chunk_d(int D, int vb, int G, dim3 grid, hipStream_t s, const ChunkArgs &a)
 {
+    if (vb == 4) {
+        if (D == 128) launch_chunk<128, 4>(G, grid, s, a);
+        else launch_chunk<256, 4>(G, grid, s, a);
+        return;
+    }
     switch (D) {
-    case 64: launch_chunk<64>(G, grid, s, a); break;
-    case 128: launch_chunk<128>(G, grid, s, a); break;
-    default: launch_chunk<256>(G, grid, s, a); break;
+    case 64: launch_chunk<64, 8>(G, grid, s, a); break;
+    case 128: launch_chunk<128, 8>(G, grid, s, a); break;
+    default: launch_chunk<256, 8>(G, grid, s, a); break;
     }
 }
 }  // namespace
@@ -661,6 +704,8 @@ extern "C" qsa_status qsa_attn_chunk(const float *q, const int32_t *pos, int32_t
     if (n_pools > QSA_MAX_POOLS) return QSA_ERR_UNSUPPORTED;
     for (int32_t p = 0; p < n_pools; p++)
         if ((st = check_pool(&pools[p], true)) != QSA_OK) return st;
+    const int vb = common_v_bits(pools, n_pools, dims.head_dim);
+    if (!vb) return QSA_ERR_UNSUPPORTED;
     if (ids) {
         if (!counts) return QSA_ERR_NULL;
         if (k <= 0) return QSA_ERR_RANGE;
@@ -684,7 +729,7 @@ extern "C" qsa_status qsa_attn_chunk(const float *q, const int32_t *pos, int32_t
     a.qscale = sm_scale * LOG2E;
     dim3 grid(n_chunks, dims.n_kv_heads, n_rows);
     hipStream_t s = (hipStream_t)stream;
-    launch_chunk_d(dims.head_dim, a.G, grid, s, a);
+    launch_chunk_d(dims.head_dim, vb, a.G, grid, s, a);
     return launch_status();
 }
 
@@ -801,6 +846,8 @@ extern "C" qsa_status qsa_decode_layer(const float *q, const int32_t *pos, int32
     if (st != QSA_OK) return st;
     if (!out) return QSA_ERR_NULL;
     if (n_chunks < 1) return QSA_ERR_RANGE;
+    const int vb = common_v_bits(pools, n_pools, dims.head_dim);
+    if (!vb) return QSA_ERR_UNSUPPORTED;
     if (n_rows == 0) return QSA_OK;
     const LayerScratch lay = layer_layout(n_rows, dims, k, n_chunks);
     if (!scratch) return QSA_ERR_NULL;
@@ -824,7 +871,7 @@ extern "C" qsa_status qsa_decode_layer(const float *q, const int32_t *pos, int32
     a.n_qh = dims.n_q_heads; a.n_kv = dims.n_kv_heads; a.G = sa.G;
     a.topk = k; a.bpc = 0; a.n_chunks = n_chunks; a.max_chunks = n_chunks;
     a.qscale = sm_scale * LOG2E;
-    launch_chunk_d(dims.head_dim, a.G, dim3(n_chunks, dims.n_kv_heads, n_rows), s, a);
+    launch_chunk_d(dims.head_dim, vb, a.G, dim3(n_chunks, dims.n_kv_heads, n_rows), s, a);
     if ((st = launch_status()) != QSA_OK) return st;
     return merge_launch(a.m_out, a.l_out, a.o_out, a.empty_out, n_chunks, n_chunks, nullptr, n_rows, dims.n_q_heads,
                         dims.head_dim, out, lse, s);

@@ -37,7 +37,21 @@ inline qsa_status check_pool(const qsa_pool *p, bool need_v)
     if (need_v && (!p->v || !p->v_scale)) return QSA_ERR_NULL;
     if (p->capacity < 0 || p->n_valid < 0) return QSA_ERR_SHAPE;
     if (p->n_valid > p->capacity) return QSA_ERR_RANGE;
+    if (p->v_bits != 0 && p->v_bits != 8 && p->v_bits != 4) return QSA_ERR_UNSUPPORTED;
     return QSA_OK;
+}
+
+// V bits of a pool (0 means 8).
+inline int v_bits_of(const qsa_pool &p) { return p.v_bits == 4 ? 4 : 8; }
+
+// The V format shared by the pools of one call, or 0 when they differ or K8V4 meets an unsupported head_dim.
+inline int common_v_bits(const qsa_pool *pools, int32_t n_pools, int32_t head_dim)
+{
+    const int vb = v_bits_of(pools[0]);
+    for (int32_t p = 1; p < n_pools; p++)
+        if (v_bits_of(pools[p]) != vb) return 0;
+    if (vb == 4 && head_dim == 64) return 0;
+    return vb;
 }
 
 inline int32_t ceil_div(int32_t a, int32_t b) { return (a + b - 1) / b; }

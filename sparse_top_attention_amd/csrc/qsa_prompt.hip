@@ -497,7 +497,7 @@ extern "C" qsa_status qsa_prompt_attn(const float *q, int32_t n_q, int32_t pos0,
     if ((st = check_pool(pool, true)) != QSA_OK) return st;
     if (!q || !out) return QSA_ERR_NULL;
     if (n_q < 0 || pos0 < 0) return QSA_ERR_RANGE;
-    if (dims.head_dim != PD) return QSA_ERR_UNSUPPORTED;
+    if (dims.head_dim != PD || v_bits_of(*pool) != 8) return QSA_ERR_UNSUPPORTED;
     if (n_q == 0) return QSA_OK;
     const int64_t last = (int64_t)pos0 + n_q;
     const int32_t n_cells = (int32_t)(last < pool->n_valid ? last : pool->n_valid);

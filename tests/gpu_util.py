@@ -18,7 +18,7 @@ def dev(a, dtype=None):
 def to_device(pool):
     """synth.Pool (numpy) -> qsa.Pool on the GPU, with a block-index buffer allocated (not yet filled)."""
     n_kv, cap, d = pool.k.shape
-    p = qsa.Pool(dev(pool.k), dev(pool.ks), dev(pool.v), dev(pool.vs), pool.n_valid)
+    p = qsa.Pool(dev(pool.k), dev(pool.ks), dev(pool.v), dev(pool.vs), pool.n_valid, v_bits=pool.v_bits)
     p.index = torch.full((n_kv, -(-cap // BLOCK), d), float("nan"), dtype=torch.float32, device="cuda")
     return p
 

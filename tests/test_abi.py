@@ -48,8 +48,8 @@ def test_status_strings():
 D = qsa._Dims
 
 
-def _pool(k=1, ks=1, v=1, vs=1, index=1, cap=1024, n_valid=1024):
-    return qsa._Pool(k, ks, v, vs, index, cap, n_valid)
+def _pool(k=1, ks=1, v=1, vs=1, index=1, cap=1024, n_valid=1024, v_bits=8):
+    return qsa._Pool(k, ks, v, vs, index, cap, n_valid, v_bits)
 
 
 def _parts(max_chunks=8):
@@ -224,3 +224,19 @@ def test_kv_append_validation():
     bad = (qsa._Pool * 1)(_pool(n_valid=2000))
     assert L.qsa_kv_append(bad, 1, None, GOOD, 1, 1, 1, 4, None) == -5
     assert L.qsa_kv_append(pools, 2, 1, GOOD, 1, 1, 1, 0, None) == 0
+
+
+def test_v_bits_validation():
+    """V formats: 0/8 int8, 4 K8V4; anything else, mixed formats in one call, K8V4 at head_dim 64 and in the prompt
+    call are unsupported."""
+    L = qsa.lib_handle()
+    parts = _parts(8)
+
+    def chunk(pools, n, dims=GOOD):
+        return L.qsa_attn_chunk(1, 1, 4, pools, n, 1, dims, 1, 1, 32, 1, 8, 1.0, ctypes.byref(parts), None)
+    assert chunk((qsa._Pool * 1)(_pool(v_bits=3)), 1) == -3
+    assert chunk((qsa._Pool * 2)(_pool(v_bits=8), _pool(v_bits=4)), 2) == -3
+    assert chunk((qsa._Pool * 1)(_pool(v_bits=4)), 1, D(4, 4, 64, 64)) == -3
+    p4 = _pool(v_bits=4)
+    assert L.qsa_prompt_attn(1, 16, 0, ctypes.byref(p4), GOOD, 1.0, 1, 1, 1 << 30, None) == -3
+    assert L.qsa_kv_append((qsa._Pool * 1)(_pool(v_bits=4)), 1, None, D(4, 4, 64, 64), 1, 1, 1, 4, None) == -3

@@ -23,8 +23,8 @@ def dims_of(w):
     return qsa.Dims(w.n_q_heads, w.n_kv_heads, w.head_dim)
 
 
-def small_workload(seed, n_kv=2, G=3, d=128, cap=1400, n_valid=1290, rows=3, topk=7):
-    pool = synth.random_pool(seed, n_kv, cap, n_valid, d)
+def small_workload(seed, n_kv=2, G=3, d=128, cap=1400, n_valid=1290, rows=3, topk=7, v_bits=8):
+    pool = synth.random_pool(seed, n_kv, cap, n_valid, d, v_bits=v_bits)
     q = synth.random_q(seed + 1, rows, n_kv * G, d)
     pos = np.array([n_valid - rows + r for r in range(rows)], np.int32)
     return synth.Workload("small", n_kv * G, n_kv, d, [pool], q, pos, np.zeros(rows, np.int32), topk, 5, 1, 0, 1.0)
