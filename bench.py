@@ -178,15 +178,16 @@ def bench_decode(args):
 
     stream = torch.cuda.Stream()
 
-    def capture(fn_per_copy, n):
+    def capture(fn_per_copy, n, pools=None):
+        pools = pools or copies
         g = torch.cuda.CUDAGraph()
         with torch.cuda.stream(stream):
             for c in range(n):               # eager pass so every kernel is loaded before capture
-                fn_per_copy(copies[c % len(copies)])
+                fn_per_copy(pools[c % len(pools)])
         torch.cuda.synchronize()
         with torch.cuda.graph(g, stream=stream):
             for c in range(n):
-                fn_per_copy(copies[c % len(copies)])
+                fn_per_copy(pools[c % len(pools)])
         torch.cuda.synchronize()
         return g
 
@@ -213,8 +214,8 @@ def bench_decode(args):
     ms_per_step = ms_total / args.steps
 
     # ---- per-kernel average launch durations: graphs of L back-to-back launches of one kernel, one per copy
-    def kernel_avg_us(fn_per_copy, reps=20):
-        g = capture(fn_per_copy, L)
+    def kernel_avg_us(fn_per_copy, reps=20, pools=None):
+        g = capture(fn_per_copy, L, pools)
         with torch.cuda.stream(stream):
             g.replay()
             torch.cuda.synchronize()
@@ -254,6 +255,11 @@ def bench_decode(args):
         v_new = t(rng.standard_normal((n_rows, n_kv, D)).astype(np.float32))
         breakdown["kv_append"] = kernel_avg_us(lambda p: qsa.qsa_kv_append([p], dims, k_new, v_new, pos))
     chunk_key = "attn_chunk"
+    k8v4 = None
+    if not dense and D >= 128:
+        # the same workload in K8V4 (4-bit V): its K side draws the same numbers, so the selection is the same
+        k8v4 = bench_k8v4(args, w, dims, nb, S, q, pos, ids, counts, layer_scratch, out, lse, part,
+                          lambda fn, pools: kernel_avg_us(fn, pools=pools), L)
 
     # ---- algorithmic bytes
     ids_h, counts_h = ids.cpu().numpy(), counts.cpu().numpy()
@@ -292,6 +298,7 @@ def bench_decode(args):
         "kernels_us": {k2: round(v2, 3) for k2, v2 in breakdown.items()},
         "four_call_layer": separate,
         "capacity_wide": capacity_wide,
+        "k8v4": k8v4,
         "roofline": {"bound": "hbm", "kernel": chunk_key, "achieved": round(chunk_gbs, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(chunk_gbs / HBM_PEAK_GBS, 4),
                      "bytes_per_launch": int(chunk_bytes),
@@ -304,6 +311,43 @@ def bench_decode(args):
     del copies
     torch.cuda.empty_cache()
     return result
+
+
+def bench_k8v4(args, w, dims, nb, S, q, pos, ids, counts, layer_scratch, out, lse, part, kernel_avg_us, L):
+    """Layer and chunk-kernel times of the workload over K8V4 pool copies (int8 K, 4-bit V): K/V bytes per
+    (cell, KV head) drop from 272 to 208 at head_dim 128."""
+    import torch
+
+    import sparse_top_attention_amd as qsa
+    import synth
+
+    dev = q.device
+    p4 = synth.workload(args.workload, poison=False, v_bits=4).pools[0]
+
+    def t(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    base = qsa.Pool(t(p4.k), t(p4.ks), t(p4.v), t(p4.vs), p4.n_valid, v_bits=4)
+    base.index = torch.zeros(dims.n_kv_heads, -(-p4.capacity // BLOCK), dims.head_dim, dtype=torch.float32,
+                             device=dev)
+    qsa.qsa_block_index(base, dims, 0, p4.n_valid, base.index)
+    pools = [base] + [qsa.Pool(base.k.clone(), base.k_scale.clone(), base.v.clone(), base.v_scale.clone(),
+                               base.n_valid, base.index.clone(), v_bits=4) for _ in range(L - 1)]
+
+    def layer(p):
+        qsa.qsa_decode_layer(q, pos, [p], dims, nb, w.topk, S, out, lse, sm_scale=w.sm_scale, ids=ids, counts=counts,
+                             scratch=layer_scratch)
+
+    def attend(p):
+        qsa.qsa_attn_chunk(q, pos, [p], dims, part, S, w.sm_scale, ids=ids, counts=counts)
+    t_layer = kernel_avg_us(layer, pools)
+    t_chunk = kernel_avg_us(attend, pools)
+    ng = dims.head_dim // 64
+    per_cell = dims.head_dim + 4 * ng + dims.head_dim // 2 + 4 * ng
+    kv_cells = union_cells(ids.cpu().numpy(), counts.cpu().numpy(), w.pos, p4.n_valid, dims.n_kv_heads)
+    chunk_bytes = kv_cells * per_cell + w.q.nbytes
+    del pools
+    return {"us_per_layer": round(t_layer, 3), "attn_chunk_us": round(t_chunk, 3), "kv_bytes_per_cell_head": per_cell,
+            "attn_chunk_GBs": round(chunk_bytes / (t_chunk * 1e-6) / 1e9, 1)}
 
 
 def copy_calibration(nbytes=1 << 28, reps=4):

@@ -191,12 +191,21 @@ __global__ __launch_bounds__(64) void block_scores_kernel(const float *__restric
 #pragma unroll
             for (int e = 0; e < 8; e++) qt[rr][e] = 0.f;
             if (rr < nr) {
-                for (int32_t h = g * G; h < (g + 1) * G; h++) {
-                    const float4 *src =
-                        reinterpret_cast<const float4 *>(q + ((int64_t)(i0 + rr) * n_qh + h) * D + 8 * s);
-                    const float4 u = src[0], w = src[1];
-                    qt[rr][0] += u.x; qt[rr][1] += u.y; qt[rr][2] += u.z; qt[rr][3] += u.w;
-                    qt[rr][4] += w.x; qt[rr][5] += w.y; qt[rr][6] += w.z; qt[rr][7] += w.w;
+                // the row's G heads in head order; all 8 loads are issued together (heads past G re-read the last)
+                float4 u[8], w[8];
+#pragma unroll
+                for (int h = 0; h < 8; h++) {
+                    const float4 *src = reinterpret_cast<const float4 *>(
+                        q + ((int64_t)(i0 + rr) * n_qh + g * G + (h < G ? h : G - 1)) * D + 8 * s);
+                    u[h] = src[0];
+                    w[h] = src[1];
+                }
+#pragma unroll
+                for (int h = 0; h < 8; h++) {
+                    if (h < G) {
+                        qt[rr][0] += u[h].x; qt[rr][1] += u[h].y; qt[rr][2] += u[h].z; qt[rr][3] += u[h].w;
+                        qt[rr][4] += w[h].x; qt[rr][5] += w[h].y; qt[rr][6] += w[h].z; qt[rr][7] += w[h].w;
+                    }
                 }
             }
         }
@@ -360,9 +369,9 @@ __global__ __launch_bounds__(64 * CW) void attn_chunk_kernel(const ChunkArgs a)
         for (int q = 0; q < VCH; q++) {
             const int slot = 64 * q + lane, cell = slot / CHUNKS, pch = slot % CHUNKS;
             const int32_t c = min(cb + cell, limit);
-            __builtin_amdgcn_global_load_lds(vbase + (int64_t)c * RB + 16 * (pch ^ (cell & SWZ)),
-                                             (QSA_LDS void *)(svw + 1024 * q), 16, 0, 0);
+            load_lds16(vbase + (int64_t)c * RB + 16 * (pch ^ (cell & SWZ)), lds_addr(svw + 1024 * q));
         }
+        __builtin_amdgcn_sched_barrier(0);   // every copy is in flight before the logits start
 
         // ---- logits (base-2 units), masked past the limit
         float lg[STEPS][G];
@@ -477,32 +486,54 @@ __global__ __launch_bounds__(64 * CW) void attn_chunk_kernel(const ChunkArgs a)
     }
     __syncthreads();
 
-    // combine the CW waves: M = max m_w, out = sum e^(m_w - M) o_w (waves without a cell have m_w = -inf)
-    for (int idx = tid; idx < G * D; idx += 64 * CW) {
+    // combine the CW waves: M = max m_w, out = sum e^(m_w - M) o_w (waves without a cell have m_w = -inf). Every
+    // thread reads all the LDS values it needs at once and then combines them without branches; the (m, l, empty)
+    // of the G heads are written by the first G threads.
+    constexpr int NE = (G * D + 64 * CW - 1) / (64 * CW);   // output elements per thread
+    float smv[NE][CW], sov[NE][CW];
+#pragma unroll
+    for (int e = 0; e < NE; e++) {
+        const int idx = min(tid + 64 * CW * e, G * D - 1);
         const int h = idx / D, d = idx % D;
-        float M = sm[0][h];
 #pragma unroll
-        for (int w = 1; w < CW; w++) M = fmaxf(M, sm[w][h]);
-        float num = 0.f;
-        if (M != -INFINITY) {
-#pragma unroll
-            for (int w = 0; w < CW; w++)
-                if (sm[w][h] != -INFINITY) num = fmaf(__builtin_amdgcn_exp2f(sm[w][h] - M), so[w][h][d], num);
+        for (int w = 0; w < CW; w++) {
+            smv[e][w] = sm[w][h];
+            sov[e][w] = so[w][h][d];
         }
-        a.o_out[(((int64_t)i * a.n_qh + h0 + h) * a.max_chunks + j) * D + d] = num;
+    }
+    float hm[CW], hl[CW];
+    {
+        const int h = tid < G ? tid : 0;
+#pragma unroll
+        for (int w = 0; w < CW; w++) {
+            hm[w] = sm[w][h];
+            hl[w] = sl[w][h];
+        }
+    }
+    auto combine = [](const float (&mw)[CW], const float (&xw)[CW], float &M) {
+        M = mw[0];
+#pragma unroll
+        for (int w = 1; w < CW; w++) M = fmaxf(M, mw[w]);
+        float num = 0.f;
+#pragma unroll
+        for (int w = 0; w < CW; w++) {
+            const float t = fmaf(__builtin_amdgcn_exp2f(mw[w] - M), xw[w], num);
+            num = mw[w] != -INFINITY ? t : num;
+        }
+        return M != -INFINITY ? num : 0.f;
+    };
+    float *o_row = a.o_out + (((int64_t)i * a.n_qh + h0) * a.max_chunks + j) * D;
+#pragma unroll
+    for (int e = 0; e < NE; e++) {
+        const int idx = tid + 64 * CW * e;
+        float M;
+        const float num = combine(smv[e], sov[e], M);
+        if (idx < G * D) o_row[(int64_t)(idx / D) * a.max_chunks * D + idx % D] = num;
     }
     if (tid < G) {
-        const int h = tid;
-        float M = sm[0][h];
-#pragma unroll
-        for (int w = 1; w < CW; w++) M = fmaxf(M, sm[w][h]);
-        float L = 0.f;
-        if (M != -INFINITY) {
-#pragma unroll
-            for (int w = 0; w < CW; w++)
-                if (sm[w][h] != -INFINITY) L = fmaf(__builtin_amdgcn_exp2f(sm[w][h] - M), sl[w][h], L);
-        }
-        const int64_t idx = ((int64_t)i * a.n_qh + h0 + h) * a.max_chunks + j;
+        float M;
+        const float L = combine(hm, hl, M);
+        const int64_t idx = ((int64_t)i * a.n_qh + h0 + tid) * a.max_chunks + j;
         const bool empty = M == -INFINITY;
         a.m_out[idx] = empty ? -INFINITY : M * LN2;
         a.l_out[idx] = L;
@@ -511,9 +542,12 @@ __global__ __launch_bounds__(64 * CW) void attn_chunk_kernel(const ChunkArgs a)
 }
 
 // ---------------------------------------------------------------------------------------------------- merge
-// One workgroup of 4 waves per (row, q head). Pass 1 finds the max over the row's non-empty chunks, pass 2 adds
-// e^(m_j - M) l_j and e^(m_j - M) o_j; each wave takes a contiguous quarter of the chunks and the quarters are
-// combined through LDS. Lanes own D/64 consecutive dims.
+// One workgroup of 4 waves per (row, q head); each wave takes a contiguous quarter of the active chunks. A wave reads
+// the (m, l, empty) of up to 64 of its chunks at once, one chunk per lane, so the max M over the non-empty chunks,
+// the weights e^(m_j - M) and the weighted sum of l_j take one round of loads and a few cross-lane steps. The o_j
+// rows (lanes own D/64 consecutive dims) are loaded 8 chunks at a time with every load in flight before the first
+// use, and are added in chunk order with the weight read from the chunk's lane. Empty chunks are skipped by select,
+// never multiplied (their l and o may hold anything). The quarters are combined through LDS.
 template <int D>
 __global__ __launch_bounds__(256) void attn_merge_kernel(const float *__restrict__ m, const float *__restrict__ l,
                                                          const float *__restrict__ o, const uint8_t *__restrict__ em,
@@ -522,35 +556,93 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const float *__restrict
                                                          float *__restrict__ out, float *__restrict__ lse)
 {
     constexpr int VPL = D / 64;
+    constexpr int U = 8;                           // o rows in flight per batch
     __shared__ float sM[4], sL[4];
     __shared__ float sO[4][D];
-    const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
+    const int tid = threadIdx.x, lane = tid % 64;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
     const int32_t row = blockIdx.x;               // = i * n_qh + h
     const int32_t i = row / n_qh;
     int32_t na = n_active ? n_active[i] : n_chunks;
     na = na < 0 ? 0 : (na > n_chunks ? n_chunks : na);
     const int32_t j0 = (int32_t)(((int64_t)na * wave) / 4), j1 = (int32_t)(((int64_t)na * (wave + 1)) / 4);
     const int64_t base = (int64_t)row * max_chunks;
+    const int32_t nq = j1 - j0;                   // chunks of this wave
+    const int32_t jlast = n_chunks - 1;           // n_chunks >= 1: every clamped index is in bounds
+    auto clamp_j = [&](int32_t jj) { return jj < jlast ? jj : jlast; };
 
-    float M = -INFINITY;
-    for (int32_t jj = j0; jj < j1; jj++)
-        if (!em[base + jj]) M = fmaxf(M, m[base + jj]);
+    // the first batch (up to 64 chunks, one per lane, and the first U o rows), all loads before any wait
+    float ov0[U][VPL];
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+        const float *src = o + (base + clamp_j(j0 + (u < nq ? u : 0))) * D + VPL * lane;
+#pragma unroll
+        for (int e = 0; e < VPL; e++) ov0[u][e] = src[e];
+    }
+    const int32_t jc = clamp_j(j0 + (lane < nq ? lane : 0));
+    const float mv0 = m[base + jc], lv0 = l[base + jc];
+    const uint8_t ev0 = em[base + jc];
+    __builtin_amdgcn_sched_barrier(0);            // keep every load above ahead of the first wait
+    const bool live0 = lane < nq && !ev0;
+
+    // pass 1: M over the wave's non-empty chunks
+    float M = live0 ? mv0 : -INFINITY;
+    for (int32_t jb = j0 + 64; jb < j1; jb += 64) {
+        const int32_t jj = jb + lane;
+        const int32_t jcb = jj < j1 ? jj : jb;
+        const float mv = m[base + jcb];
+        const bool live = jj < j1 && !em[base + jcb];
+        M = live ? fmaxf(M, mv) : M;
+    }
+    M = group_max<64>(M);
     if (lane == 0) sM[wave] = M;
     __syncthreads();
     M = fmaxf(fmaxf(sM[0], sM[1]), fmaxf(sM[2], sM[3]));
 
+    // pass 2: L = sum e^(m_j - M) l_j and acc = sum e^(m_j - M) o_j, in chunk order; the first batch of 64 chunks
+    // uses the preloaded values
     float L = 0.f, acc[VPL];
 #pragma unroll
     for (int e = 0; e < VPL; e++) acc[e] = 0.f;
-    if (M != -INFINITY) {
-#pragma unroll 4
-        for (int32_t jj = j0; jj < j1; jj++) {
-            if (em[base + jj]) continue;
-            const float w = expf(m[base + jj] - M);
-            L = fmaf(w, l[base + jj], L);
-            const float *src = o + (base + jj) * D + VPL * lane;
+    auto add_rows = [&](const float (&ov)[U][VPL], int32_t c0, int32_t nb, int32_t flag, float wgt) {
 #pragma unroll
-            for (int e = 0; e < VPL; e++) acc[e] = fmaf(w, src[e], acc[e]);
+        for (int u = 0; u < U; u++) {
+            const int c = c0 + u;
+            if (c < nb && __builtin_amdgcn_readlane(flag, c)) {
+                const float wu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wgt), c));
+#pragma unroll
+                for (int e = 0; e < VPL; e++) acc[e] = fmaf(wu, ov[u][e], acc[e]);
+            }
+        }
+    };
+    auto batch = [&](int32_t jb, float mv, float lv, bool live, bool first) {
+        const int32_t nb = min(64, j1 - jb);
+        const float wgt = live ? expf(mv - M) : 0.f;
+        L += group_sum<64>(live ? wgt * lv : 0.f);
+        const int32_t flag = live ? 1 : 0;
+        int32_t c0 = 0;
+        if (first) {
+            add_rows(ov0, 0, nb, flag, wgt);
+            c0 = U;
+        }
+        for (; c0 < nb; c0 += U) {
+            float ov[U][VPL];
+#pragma unroll
+            for (int u = 0; u < U; u++) {
+                const float *src = o + (base + jb + min(c0 + u, nb - 1)) * D + VPL * lane;
+#pragma unroll
+                for (int e = 0; e < VPL; e++) ov[u][e] = src[e];
+            }
+            add_rows(ov, c0, nb, flag, wgt);
+        }
+    };
+    if (M != -INFINITY && nq > 0) {
+        batch(j0, mv0, lv0, live0, true);
+        for (int32_t jb = j0 + 64; jb < j1; jb += 64) {
+            const int32_t jcb = jb + lane < j1 ? jb + lane : jb;
+            const float mv = m[base + jcb], lv = l[base + jcb];
+            const bool live = jb + lane < j1 && !em[base + jcb];
+            batch(jb, mv, lv, live, false);
         }
     }
     if (lane == 0) sL[wave] = L;

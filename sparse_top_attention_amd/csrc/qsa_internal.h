@@ -100,6 +100,24 @@ typedef int32_t v4i __attribute__((ext_vector_type(4)));
 typedef int32_t v2i __attribute__((ext_vector_type(2)));
 #define QSA_LDS __attribute__((address_space(3)))
 
+// Global -> LDS copies (global_load_lds): lane l's bytes land at lds + size * l; lds must be wave-uniform. Written
+// as inline assembly so that the compiler does not track them: it would otherwise wait for every such load (and
+// for every vector load issued with them) before the next use of any loaded register or LDS byte. Kernels wait for
+// them themselves with s_waitcnt vmcnt; vector loads return in issue order, so a wait the compiler emits for its
+// own loads stays correct (it only becomes stricter) when these copies are in flight too.
+__device__ __forceinline__ void load_lds16(const void *src, uint32_t lds)
+{
+    asm volatile("global_load_lds_dwordx4 %0, off" : : "v"(src), "{m0}"(lds) : "memory");
+}
+__device__ __forceinline__ void load_lds4(const void *src, uint32_t lds)
+{
+    asm volatile("global_load_lds_dword %0, off" : : "v"(src), "{m0}"(lds) : "memory");
+}
+__device__ __forceinline__ uint32_t lds_addr(const void *p)
+{
+    return (uint32_t)(uintptr_t)(const QSA_LDS void *)p;
+}
+
 // DPP controls (gfx9 encoding).
 constexpr int DPP_QUAD_XOR1 = 0xB1;     // quad_perm [1,0,3,2]
 constexpr int DPP_QUAD_XOR2 = 0x4E;     // quad_perm [2,3,0,1]

@@ -59,21 +59,6 @@ __device__ __forceinline__ uint32_t bperm(uint32_t s0, uint32_t s1, uint32_t sel
     return __builtin_amdgcn_perm(s0, s1, sel);
 }
 
-// Global -> LDS copies (global_load_lds): lane l's bytes land at lds + size * l; lds must be wave-uniform. Written
-// as inline assembly so that the compiler does not track them: it would otherwise wait for every such load before
-// the next LDS read, which serialises the prefetch of the next tiles. The kernel waits for them itself (vmcnt).
-__device__ __forceinline__ void load_lds16(const void *src, uint32_t lds)
-{
-    asm volatile("global_load_lds_dwordx4 %0, off" : : "v"(src), "{m0}"(lds) : "memory");
-}
-__device__ __forceinline__ void load_lds4(const void *src, uint32_t lds)
-{
-    asm volatile("global_load_lds_dword %0, off" : : "v"(src), "{m0}"(lds) : "memory");
-}
-__device__ __forceinline__ uint32_t lds_addr(const void *p)
-{
-    return (uint32_t)(uintptr_t)(const QSA_LDS void *)p;
-}
 // s_waitcnt immediates (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
 constexpr int WAIT_VM0_LGKM0 = 0x0070;   // all vector memory and LDS operations done
 constexpr int WAIT_VM5_LGKM0 = 0x0075;   // all but the 5 newest vector memory operations done, LDS done

@@ -215,10 +215,17 @@ __global__ __launch_bounds__(256) void select_kernel(const SelectArgs a)
         }
     if (b_end > 0) load_batch(0);
 
-    // qsum over the row's q heads of g, summed in head order
+    // qsum over the row's q heads of g, summed in head order; the up to 8 loads are issued together (heads past G
+    // re-read the last head and are not added)
     for (int d = tid; d < D; d += 256) {
+        const float *qd = a.q + ((int64_t)i * a.n_qh + g * a.G) * D + d;
+        float v[8];
+#pragma unroll
+        for (int h = 0; h < 8; h++) v[h] = qd[(int64_t)(h < a.G ? h : a.G - 1) * D];
         float acc = 0.f;
-        for (int32_t h = g * a.G; h < (g + 1) * a.G; h++) acc += a.q[((int64_t)i * a.n_qh + h) * D + d];
+#pragma unroll
+        for (int h = 0; h < 8; h++)
+            if (h < a.G) acc += v[h];
         sqs[d] = acc;
     }
     __syncthreads();
