@@ -298,27 +298,16 @@ __global__ __launch_bounds__(64 * CW) void attn_chunk_kernel(const ChunkArgs a)
     const int32_t j = blockIdx.x, g = blockIdx.y, i = blockIdx.z;
     const int32_t h0 = g * G;
 
-    const int32_t pidx = a.row_pool ? a.row_pool[i] : 0;
-    const bool pool_ok = pidx >= 0 && pidx < a.n_pools;
-    const PoolArg P = a.pools[pool_ok ? pidx : 0];
-    const int32_t limit = pool_ok ? min(P.n_valid - 1, a.pos[i]) : -1;  // visible cells: c <= limit
-
-    int32_t n_blk, first;
-    const int32_t *blist = nullptr;
-    int32_t idv = 0;   // with k <= 64: the row's whole id list, one id per lane, loaded alongside its count
-    if (a.ids) {
-        blist = a.ids + ((int64_t)i * a.n_kv + g) * a.topk;
-        if (a.topk <= 64) idv = blist[lane < a.topk ? lane : 0];   // unconditional load: no wait at a branch end
-        int32_t cnt = a.counts[(int64_t)i * a.n_kv + g];
-        cnt = cnt < 0 ? 0 : (cnt > a.topk ? a.topk : cnt);
-        const int32_t base = cnt / a.n_chunks, rem = cnt % a.n_chunks;
-        n_blk = base + (j < rem ? 1 : 0);
-        first = j * base + (j < rem ? j : rem);
-    } else {
-        n_blk = a.bpc;
-        first = j * a.bpc;
-    }
-
+    // Prologue: the per-row words come in one vector load (lane 0 pos[i], lane 1 the pool index, lane 2 the block
+    // count; a missing row_pool or id list reads pos[i] instead, a valid word whose value is then ignored), issued
+    // with the id list and ahead of the q rows, so one round trip brings them all; the pool's fields follow.
+    const int64_t row_kv = (int64_t)i * a.n_kv + g;
+    const bool sel = a.ids != nullptr, mp = a.row_pool != nullptr;
+    const int32_t *p_pidx = mp ? a.row_pool + i : a.pos + i;
+    const int32_t *p_cnt = sel ? a.counts + row_kv : a.pos + i;
+    const int32_t *blist = sel ? a.ids + row_kv * a.topk : a.pos + i;
+    const int32_t words = *(lane == 1 ? p_pidx : (lane == 2 ? p_cnt : a.pos + i));
+    const int32_t idv = blist[sel && lane < a.topk ? lane : 0];   // k <= 64: the whole id list, one id per lane
     float qv[G][16];
 #pragma unroll
     for (int h = 0; h < G; h++) {
@@ -332,6 +321,17 @@ __global__ __launch_bounds__(64 * CW) void attn_chunk_kernel(const ChunkArgs a)
             qv[h][4 * jj + 3] = u.w;
         }
     }
+    const int32_t posi = __builtin_amdgcn_readlane(words, 0);
+    const int32_t pidx = mp ? __builtin_amdgcn_readlane(words, 1) : 0;
+    const int32_t cnt_raw = __builtin_amdgcn_readlane(words, 2);
+    const bool pool_ok = pidx >= 0 && pidx < a.n_pools;
+    const PoolArg P = a.pools[pool_ok ? pidx : 0];
+    const int32_t limit = pool_ok ? min(P.n_valid - 1, posi) : -1;  // visible cells: c <= limit
+    const int32_t cnt = cnt_raw < 0 ? 0 : (cnt_raw > a.topk ? a.topk : cnt_raw);
+    const int32_t base = sel ? cnt / a.n_chunks : a.bpc, rem = sel ? cnt % a.n_chunks : 0;
+    const int32_t n_blk = base + (j < rem ? 1 : 0);
+    const int32_t first = j * base + (j < rem ? j : rem);
+
     float mrun[G], lpart[G], o[G][DPL];
 #pragma unroll
     for (int h = 0; h < G; h++) {
@@ -350,7 +350,7 @@ __global__ __launch_bounds__(64 * CW) void attn_chunk_kernel(const ChunkArgs a)
 
     for (int32_t pc = wave; pc < n_blk * PPB; pc += CW) {
         const int32_t t_blk = first + pc / PPB;
-        const int32_t b = !blist ? t_blk : (a.topk <= 64 ? __builtin_amdgcn_readlane(idv, t_blk) : blist[t_blk]);
+        const int32_t b = !sel ? t_blk : (a.topk <= 64 ? __builtin_amdgcn_readlane(idv, t_blk) : blist[t_blk]);
         // negative id, or no visible valid cell in the piece (64-bit: ids past the pool may be huge)
         if (b < 0 || (int64_t)b * QSA_BLOCK + (pc % PPB) * PC > limit) continue;
         const int32_t cb = b * QSA_BLOCK + (pc % PPB) * PC;
