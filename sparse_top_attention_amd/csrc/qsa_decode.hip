@@ -322,10 +322,14 @@ __global__ __launch_bounds__(64 * CW) void attn_chunk_kernel(const ChunkArgs a)
         }
     }
     const int32_t posi = __builtin_amdgcn_readlane(words, 0);
-    const int32_t pidx = mp ? __builtin_amdgcn_readlane(words, 1) : 0;
     const int32_t cnt_raw = __builtin_amdgcn_readlane(words, 2);
-    const bool pool_ok = pidx >= 0 && pidx < a.n_pools;
-    const PoolArg P = a.pools[pool_ok ? pidx : 0];
+    bool pool_ok = true;
+    PoolArg P = a.pools[0];   // fixed argument offsets: read with the other arguments, no wait for the words
+    if (mp) {
+        const int32_t pidx = __builtin_amdgcn_readlane(words, 1);
+        pool_ok = pidx >= 0 && pidx < a.n_pools;
+        if (pool_ok && pidx != 0) P = a.pools[pidx];
+    }
     const int32_t limit = pool_ok ? min(P.n_valid - 1, posi) : -1;  // visible cells: c <= limit
     const int32_t cnt = cnt_raw < 0 ? 0 : (cnt_raw > a.topk ? a.topk : cnt_raw);
     const int32_t base = sel ? cnt / a.n_chunks : a.bpc, rem = sel ? cnt % a.n_chunks : 0;

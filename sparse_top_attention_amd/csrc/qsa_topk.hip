@@ -182,10 +182,26 @@ __global__ __launch_bounds__(256) void select_kernel(const SelectArgs a)
     __shared__ float ssc[256 * KPT];
     const int tid = threadIdx.x, lane = tid % 64, wave = tid / 64;
     const int32_t g = blockIdx.x, i = blockIdx.y;
-    const int32_t pidx = a.row_pool ? a.row_pool[i] : 0;
-    const bool pool_ok = pidx >= 0 && pidx < a.n_pools;
-    const PoolArg P = a.pools[pool_ok ? pidx : 0];
-    const int32_t p = a.pos[i];
+    // Loads first, in the order their values are needed: the per-row words (lane 0 pos[i], lane 1 the pool index;
+    // without row_pool lane 1 reads pos[i] too and the value is ignored) and the q rows of the sum, then the index
+    // rows. Without row_pool the pool is known from the arguments alone, so the index loads do not wait for a
+    // round trip.
+    const bool mp = a.row_pool != nullptr;
+    const int32_t words = *(lane == 1 && mp ? a.row_pool + i : a.pos + i);
+    float qh[8];
+    {
+        const int d = tid < D ? tid : 0;
+        const float *qd = a.q + ((int64_t)i * a.n_qh + g * a.G) * D + d;
+#pragma unroll
+        for (int h = 0; h < 8; h++) qh[h] = qd[(int64_t)(h < a.G ? h : a.G - 1) * D];
+    }
+    bool pool_ok = true;
+    PoolArg P = a.pools[0];   // fixed argument offsets: read with the other arguments, no wait for the words
+    if (mp) {
+        const int32_t pidx = __builtin_amdgcn_readlane(words, 1);
+        pool_ok = pidx >= 0 && pidx < a.n_pools;
+        if (pool_ok && pidx != 0) P = a.pools[pidx];
+    }
     const int32_t n_valid = pool_ok ? P.n_valid : 0;
     const int32_t stride = (P.capacity + QSA_BLOCK - 1) / QSA_BLOCK;
 
@@ -193,7 +209,7 @@ __global__ __launch_bounds__(256) void select_kernel(const SelectArgs a)
     const float *idx_g = P.index + (int64_t)g * stride * D + 8 * s;
     const int32_t n_live = min(a.width, (int32_t)((n_valid + QSA_BLOCK - 1) / QSA_BLOCK));
     // batches of NST steps of 4 * BPS blocks each. Loads are unconditional (a dead block reads block 0 and is zeroed
-    // afterwards) so a whole batch is in flight before the first wait; the first batch is issued before the q sums.
+    // afterwards) so a whole batch is in flight before the first wait.
     constexpr int NST = 16;
     float rv[NST][8];
     auto load_batch = [&](int32_t base) {
@@ -208,25 +224,21 @@ __global__ __launch_bounds__(256) void select_kernel(const SelectArgs a)
     };
     // only blocks below n_live hold a score; the rest of the row is -inf without a load
     const int32_t b_end = min(256 * KPT, (n_live + NST * 4 * BPS - 1) / (NST * 4 * BPS) * (NST * 4 * BPS));
+    if (b_end > 0) load_batch(0);
+    const int32_t p = __builtin_amdgcn_readlane(words, 0);
     for (int e = tid; e < 256 * KPT; e += 256)
         if (e >= b_end) {
             ssc[e] = -INFINITY;
             if (a.scores && e < a.width) a.scores[((int64_t)i * a.n_kv + g) * a.width + e] = -INFINITY;
         }
-    if (b_end > 0) load_batch(0);
 
-    // qsum over the row's q heads of g, summed in head order; the up to 8 loads are issued together (heads past G
-    // re-read the last head and are not added)
-    for (int d = tid; d < D; d += 256) {
-        const float *qd = a.q + ((int64_t)i * a.n_qh + g * a.G) * D + d;
-        float v[8];
-#pragma unroll
-        for (int h = 0; h < 8; h++) v[h] = qd[(int64_t)(h < a.G ? h : a.G - 1) * D];
+    // qsum over the row's q heads of g, summed in head order (heads past G re-read the last head, not added)
+    if (tid < D) {
         float acc = 0.f;
 #pragma unroll
         for (int h = 0; h < 8; h++)
-            if (h < a.G) acc += v[h];
-        sqs[d] = acc;
+            if (h < a.G) acc += qh[h];
+        sqs[tid] = acc;
     }
     __syncthreads();
     float qt[8];
