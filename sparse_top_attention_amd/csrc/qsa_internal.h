@@ -113,6 +113,15 @@ __device__ __forceinline__ void load_lds4(const void *src, uint32_t lds)
 {
     asm volatile("global_load_lds_dword %0, off" : : "v"(src), "{m0}"(lds) : "memory");
 }
+// The same copies from a wave-uniform base (scalar registers) plus a 32-bit per-lane byte offset.
+__device__ __forceinline__ void copy_lds16(const void *base, uint32_t off, uint32_t lds)
+{
+    asm volatile("global_load_lds_dwordx4 %0, %1" : : "v"(off), "s"(base), "{m0}"(lds) : "memory");
+}
+__device__ __forceinline__ void copy_lds4(const void *base, uint32_t off, uint32_t lds)
+{
+    asm volatile("global_load_lds_dword %0, %1" : : "v"(off), "s"(base), "{m0}"(lds) : "memory");
+}
 __device__ __forceinline__ uint32_t lds_addr(const void *p)
 {
     return (uint32_t)(uintptr_t)(const QSA_LDS void *)p;

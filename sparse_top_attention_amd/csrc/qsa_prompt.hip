@@ -238,22 +238,43 @@ __global__ __launch_bounds__(256, 2) void prompt_attn_kernel(const PromptArgs a)
     const int8_t *vg = P.v + (int64_t)g * P.capacity * PD;
     const float *ksg = P.ks + (int64_t)g * P.capacity * 2;
     const float *vsg = a.w + (int64_t)g * a.w_cells * 2;
+    // The tile's base address is wave-uniform (scalar registers); a lane's byte offset within a full tile is the
+    // same for every tile, and only a tile that runs past the last cell clamps its cells.
+    uint32_t koff[2], voff[2];
+#pragma unroll
+    for (int h = 0; h < 2; h++) {
+        const int slot = 128 * wave + 64 * h + lane;
+        const int cell = slot >> 3, pos = slot & 7;
+        koff[h] = cell * PD + 16 * (pos ^ swz_k(cell));
+        voff[h] = cell * PD + 16 * (pos ^ swz_v(cell));
+    }
+    const int se = 64 * (wave & 1) + lane;   // float se of the tile's [cell][grp] scales
     // (each wave issues 5 copies per tile)
     auto stage = [&](int32_t t, int buf) {
         const int32_t cb = t * PT;
         PromptTile &T = tile[buf];
+        const int8_t *kt = kg + (int64_t)cb * PD;
+        const int8_t *vt = vg + (int64_t)cb * PD;
+        const float *st = (wave < 2 ? ksg : vsg) + (int64_t)cb * 2;
+        float *sdst = (wave < 2 ? T.ks : T.vs) + 64 * (wave & 1);
+        const int32_t nfull = c_last - cb;   // cells past nfull re-read cell nfull
+        if (nfull >= PT - 1) {
 #pragma unroll
-        for (int h = 0; h < 2; h++) {
-            const int slot = 128 * wave + 64 * h + lane;
-            const int cell = slot >> 3, pos = slot & 7;
-            const int32_t c = min(cb + cell, c_last);
-            load_lds16(kg + (int64_t)c * PD + 16 * (pos ^ swz_k(cell)), lds_addr(T.k + 1024 * (2 * wave + h)));
-            load_lds16(vg + (int64_t)c * PD + 16 * (pos ^ swz_v(cell)), lds_addr(T.v + 1024 * (2 * wave + h)));
+            for (int h = 0; h < 2; h++) {
+                copy_lds16(kt, koff[h], lds_addr(T.k + 1024 * (2 * wave + h)));
+                copy_lds16(vt, voff[h], lds_addr(T.v + 1024 * (2 * wave + h)));
+            }
+            copy_lds4(st, 4 * se, lds_addr(sdst));
+        } else {
+#pragma unroll
+            for (int h = 0; h < 2; h++) {
+                const int slot = 128 * wave + 64 * h + lane;
+                const int cell = slot >> 3, pos = slot & 7, c = min(cell, nfull);
+                copy_lds16(kt, c * PD + 16 * (pos ^ swz_k(cell)), lds_addr(T.k + 1024 * (2 * wave + h)));
+                copy_lds16(vt, c * PD + 16 * (pos ^ swz_v(cell)), lds_addr(T.v + 1024 * (2 * wave + h)));
+            }
+            copy_lds4(st, 4 * (2 * min(se >> 1, nfull) + (se & 1)), lds_addr(sdst));
         }
-        const int e = 64 * (wave & 1) + lane;  // float e of the tile's [cell][grp] scales
-        const int32_t c = min(cb + (e >> 1), c_last);
-        if (wave < 2) load_lds4(ksg + (int64_t)c * 2 + (e & 1), lds_addr(T.ks + 64 * (wave & 1)));
-        else load_lds4(vsg + (int64_t)c * 2 + (e & 1), lds_addr(T.vs + 64 * (wave & 1)));
     };
 
     // Tiles are triple-buffered and prefetched two ahead: tile t lives in buffer (t - t0) % 3, and its copies are
