@@ -40,6 +40,7 @@ def parse():
     ap.add_argument("--workload", default="verify_window",
                     choices=["tiny_decode", "verify_window", "drafter", "prompt_chunk"])
     ap.add_argument("--no-prompt", action="store_true", help="skip the prompt-chunk measurement")
+    ap.add_argument("--no-other", action="store_true", help="skip the batch-window and drafter measurements")
     ap.add_argument("--prompt-steps", type=int, default=20)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of known size (to scale HBM byte counters)")
@@ -99,6 +100,8 @@ def main():
         res = bench_prompt(args, args.steps if args.steps != 1280 else args.prompt_steps, main_line=True)
     else:
         res = bench_decode(args)
+        if args.workload == "verify_window" and not args.no_other:
+            res["other_decode_workloads"] = bench_other_decode()
         if not args.no_prompt:
             res["prompt_chunk"] = bench_prompt(args, args.prompt_steps, main_line=False)
     print(json.dumps(res))
@@ -348,6 +351,124 @@ def bench_k8v4(args, w, dims, nb, S, q, pos, ids, counts, layer_scratch, out, ls
     del pools
     return {"us_per_layer": round(t_layer, 3), "attn_chunk_us": round(t_chunk, 3), "kv_bytes_per_cell_head": per_cell,
             "attn_chunk_GBs": round(chunk_bytes / (t_chunk * 1e-6) / 1e9, 1)}
+
+
+def bench_other_decode(copies=32):
+    """The batch window (2 slots x 2 rows, 65,536 valid cells per slot, top-64, one layer call over both pools) and
+    the drafter (dense attention over 300 active 64-cell chunks of a 512-chunk window, active-only merge): per-call
+    times and the chunk kernel's algorithmic bytes per launch over its time, against HBM peak. Pool copies rotate
+    so K/V come from HBM."""
+    import torch
+
+    import sparse_top_attention_amd as qsa
+    import synth
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.Stream()
+
+    def t(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    def avg_us(fn, n, reps=10):
+        with torch.cuda.stream(stream):
+            for c in range(n):
+                fn(c)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for c in range(n):
+                fn(c)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            g.replay()
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for _ in range(reps):
+                g.replay()
+            b.record(stream)
+            torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / (reps * n)
+
+    def dev_pool(pn, with_index, dims):
+        p = qsa.Pool(t(pn.k), t(pn.ks), t(pn.v), t(pn.vs), pn.n_valid)
+        if with_index:
+            p.index = torch.zeros(dims.n_kv_heads, -(-pn.capacity // BLOCK), dims.head_dim, dtype=torch.float32,
+                                  device=dev)
+            qsa.qsa_block_index(p, dims, 0, pn.n_valid, p.index)
+        return p
+
+    def clone(p):
+        return qsa.Pool(p.k.clone(), p.k_scale.clone(), p.v.clone(), p.v_scale.clone(), p.n_valid,
+                        None if p.index is None else p.index.clone())
+
+    res = {}
+    # ---- batch window
+    w = synth.workload("batch_window", poison=False)
+    dims = qsa.Dims(w.n_q_heads, w.n_kv_heads, w.head_dim)
+    n_rows, n_kv, D = w.q.shape[0], w.n_kv_heads, w.head_dim
+    base = [dev_pool(pn, True, dims) for pn in w.pools]
+    sets = [base] + [[clone(p) for p in base] for _ in range(copies - 1)]
+    nb = -(-w.pools[0].n_valid // BLOCK)
+    S = 20
+    q, pos, row_pool = t(w.q), t(w.pos), t(w.row_pool)
+    ids = torch.empty(n_rows, n_kv, w.topk, dtype=torch.int32, device=dev)
+    counts = torch.empty(n_rows, n_kv, dtype=torch.int32, device=dev)
+    out = torch.empty(n_rows, w.n_q_heads, D, dtype=torch.float32, device=dev)
+    lse = torch.empty(n_rows, w.n_q_heads, dtype=torch.float32, device=dev)
+    scratch = torch.empty(qsa.qsa_decode_layer_scratch_bytes(n_rows, dims, w.topk, S), dtype=torch.uint8, device=dev)
+    part = qsa.Partials.empty_like_shape(n_rows, w.n_q_heads, S, D, device=dev)
+
+    def layer(c):
+        qsa.qsa_decode_layer(q, pos, sets[c], dims, nb, w.topk, S, out, lse, sm_scale=w.sm_scale, row_pool=row_pool,
+                             ids=ids, counts=counts, scratch=scratch)
+
+    def chunk(c):
+        qsa.qsa_attn_chunk(q, pos, sets[c], dims, part, S, w.sm_scale, row_pool=row_pool, ids=ids, counts=counts)
+    t_layer = avg_us(layer, copies)
+    t_chunk = avg_us(chunk, copies)
+    ids_h, counts_h = ids.cpu().numpy(), counts.cpu().numpy()
+    cells = 0
+    for sidx in range(len(w.pools)):
+        rows = w.row_pool == sidx
+        cells += union_cells(ids_h[rows], counts_h[rows], w.pos[rows], w.pools[sidx].n_valid, n_kv)
+    cb = cells * KV_BYTES_PER_CELL_HEAD + w.q.nbytes
+    gbs = cb / (t_chunk * 1e-6) / 1e9
+    res["batch_window"] = {"us_per_layer": round(t_layer, 3), "attn_chunk_us": round(t_chunk, 3),
+                           "chunk_bytes_per_launch": int(cb), "attn_chunk_GBs": round(gbs, 1),
+                           "frac_of_hbm": round(gbs / HBM_PEAK_GBS, 4), "chunks": S}
+    del sets, base
+    torch.cuda.empty_cache()
+
+    # ---- drafter
+    w = synth.workload("drafter", poison=False)
+    dims = qsa.Dims(w.n_q_heads, w.n_kv_heads, w.head_dim)
+    pn = w.pools[0]
+    base = dev_pool(pn, False, dims)
+    pools = [base] + [clone(base) for _ in range(copies - 1)]
+    q, pos = t(w.q), t(w.pos)
+    part = qsa.Partials.empty_like_shape(1, w.n_q_heads, w.n_chunks, w.head_dim, device=dev)
+    out = torch.empty(1, w.n_q_heads, w.head_dim, dtype=torch.float32, device=dev)
+    lse = torch.empty(1, w.n_q_heads, dtype=torch.float32, device=dev)
+    n_active = t(np.array([w.n_active], np.int32))
+
+    def dchunk(c):
+        qsa.qsa_attn_chunk(q, pos, [pools[c]], dims, part, w.n_chunks, w.sm_scale, blocks_per_chunk=w.blocks_per_chunk)
+
+    def dlayer(c):
+        dchunk(c)
+        qsa.qsa_attn_merge(part, dims, w.n_chunks, out, lse, n_active=n_active)
+    t_chunk = avg_us(dchunk, copies)
+    t_layer = avg_us(dlayer, copies)
+    vis = min(pn.n_valid, int(w.pos[0]) + 1) * w.n_kv_heads
+    cb = vis * KV_BYTES_PER_CELL_HEAD + w.q.nbytes
+    gbs = cb / (t_chunk * 1e-6) / 1e9
+    res["drafter"] = {"us_per_call": round(t_layer, 3), "attn_chunk_us": round(t_chunk, 3),
+                      "chunk_bytes_per_launch": int(cb), "attn_chunk_GBs": round(gbs, 1),
+                      "frac_of_hbm": round(gbs / HBM_PEAK_GBS, 4), "chunks": w.n_chunks, "active": w.n_active}
+    del pools, base
+    torch.cuda.empty_cache()
+    return res
 
 
 def copy_calibration(nbytes=1 << 28, reps=4):

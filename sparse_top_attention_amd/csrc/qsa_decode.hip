@@ -252,9 +252,10 @@ struct ChunkArgs {
     float qscale;  // sm_scale * log2(e): logits are kept in base-2 units inside the kernel
 };
 
-// One workgroup of CW waves per (chunk j, KV head g, row i); every wave handles all G q heads of the KV head, so
-// each K/V byte is converted once for all of them. The chunk's blocks are cut into pieces of PC cells; wave w takes
-// pieces w, w + CW, ... and keeps a running (max, sum, output) per head over them.
+// One workgroup of CW waves per CW / wpc consecutive chunks of one (KV head g, row i), wpc waves per chunk; every
+// wave handles all G q heads of the KV head, so each K/V byte is converted once for all of them. A chunk's blocks
+// are cut into pieces of PC cells; its sub-wave s takes pieces s, s + wpc, ... and keeps a running (max, sum,
+// output) per head over them.
 //
 // q . k runs in the "cell x slice" layout (LPC lanes per cell, 16 dims each; a 3-4 step DPP sum finishes each
 // logit, after which all lanes of the cell hold it). p . v runs in a "lane owns dims" layout: the piece's V codes go
@@ -268,7 +269,7 @@ constexpr int CW = 4;
 // VB is the V code width: 8 (int8) or 4 (K8V4: two signed 4-bit codes per byte, dim 2j in the low nibble). A V row
 // is RB = D * VB / 8 bytes; a 16-byte chunk of it holds DPC = 128 / VB dims, so a transposing read gives each lane
 // 8 / VB dims of 8 cells and a lane makes NT = DPL * VB / 8 reads per 8 cells. The K side is the same for both.
-template <int D, int G, int VB>
+template <int D, int G, int VB, int WPC>
 __global__ __launch_bounds__(64 * CW) void attn_chunk_kernel(const ChunkArgs a)
 {
     static_assert(VB == 8 || (VB == 4 && D >= 128), "K8V4 needs head_dim >= 128");
@@ -295,7 +296,12 @@ __global__ __launch_bounds__(64 * CW) void attn_chunk_kernel(const ChunkArgs a)
     const int r = lane / LPC, s = lane % LPC, grp_s = s / (LPC / NG);
     const int G4 = lane >> 4, jl = lane & 15;
     const int grp_v = G4 / SUBS, sub_v = G4 % SUBS;  // the p . v lane's scale group and subgroup
-    const int32_t j = blockIdx.x, g = blockIdx.y, i = blockIdx.z;
+    // wave -> (chunk j of the workgroup's CW / wpc chunks, sub-wave sub of the chunk's wpc waves)
+    constexpr int wpc = WPC, cpw = CW / WPC;
+    const int sub = wave % wpc;
+    const int32_t j0c = blockIdx.x * cpw;                 // the workgroup's first chunk
+    const int32_t j = j0c + wave / wpc, g = blockIdx.y, i = blockIdx.z;
+    const bool chunk_ok = j < a.n_chunks;                 // the last workgroup may hold fewer chunks
     const int32_t h0 = g * G;
 
     // Prologue: the per-row words come in one vector load (lane 0 pos[i], lane 1 the pool index, lane 2 the block
@@ -333,7 +339,7 @@ __global__ __launch_bounds__(64 * CW) void attn_chunk_kernel(const ChunkArgs a)
     const int32_t limit = pool_ok ? min(P.n_valid - 1, posi) : -1;  // visible cells: c <= limit
     const int32_t cnt = cnt_raw < 0 ? 0 : (cnt_raw > a.topk ? a.topk : cnt_raw);
     const int32_t base = sel ? cnt / a.n_chunks : a.bpc, rem = sel ? cnt % a.n_chunks : 0;
-    const int32_t n_blk = base + (j < rem ? 1 : 0);
+    const int32_t n_blk = chunk_ok ? base + (j < rem ? 1 : 0) : 0;
     const int32_t first = j * base + (j < rem ? j : rem);
 
     float mrun[G], lpart[G], o[G][DPL];
@@ -352,7 +358,7 @@ __global__ __launch_bounds__(64 * CW) void attn_chunk_kernel(const ChunkArgs a)
     int8_t *svw = sv[wave];
     constexpr int PPB = QSA_BLOCK / PC;              // pieces per block
 
-    for (int32_t pc = wave; pc < n_blk * PPB; pc += CW) {
+    for (int32_t pc = sub; pc < n_blk * PPB; pc += wpc) {
         const int32_t t_blk = first + pc / PPB;
         const int32_t b = !sel ? t_blk : (a.topk <= 64 ? __builtin_amdgcn_readlane(idv, t_blk) : blist[t_blk]);
         // negative id, or no visible valid cell in the piece (64-bit: ids past the pool may be huge)
@@ -490,28 +496,20 @@ __global__ __launch_bounds__(64 * CW) void attn_chunk_kernel(const ChunkArgs a)
     }
     __syncthreads();
 
-    // combine the CW waves: M = max m_w, out = sum e^(m_w - M) o_w (waves without a cell have m_w = -inf). Every
-    // thread reads all the LDS values it needs at once and then combines them without branches; the (m, l, empty)
-    // of the G heads are written by the first G threads.
-    constexpr int NE = (G * D + 64 * CW - 1) / (64 * CW);   // output elements per thread
-    float smv[NE][CW], sov[NE][CW];
-#pragma unroll
-    for (int e = 0; e < NE; e++) {
-        const int idx = min(tid + 64 * CW * e, G * D - 1);
-        const int h = idx / D, d = idx % D;
-#pragma unroll
-        for (int w = 0; w < CW; w++) {
-            smv[e][w] = sm[w][h];
-            sov[e][w] = so[w][h][d];
-        }
-    }
+    // combine the wpc waves of each chunk: M = max m_w, out = sum e^(m_w - M) o_w (waves without a cell have
+    // m_w = -inf). Every thread reads all the LDS values it needs at once and then combines them without branches;
+    // the (m, l, empty) of the chunks' G heads are written by the first cpw * G threads.
+    constexpr int EB = 4;   // output elements per thread per round of LDS reads
+    constexpr int n_out = cpw * G * D;
+    constexpr int ROUNDS = (n_out + 64 * CW * EB - 1) / (64 * CW * EB);
     float hm[CW], hl[CW];
     {
-        const int h = tid < G ? tid : 0;
+        const int cc = tid < cpw * G ? tid / G : 0, h = tid < cpw * G ? tid % G : 0;
 #pragma unroll
-        for (int w = 0; w < CW; w++) {
-            hm[w] = sm[w][h];
-            hl[w] = sl[w][h];
+        for (int k = 0; k < CW; k++) {
+            const int w = min(cc * wpc + k, CW - 1);
+            hm[k] = k < wpc ? sm[w][h] : -INFINITY;
+            hl[k] = sl[w][h];
         }
     }
     auto combine = [](const float (&mw)[CW], const float (&xw)[CW], float &M) {
@@ -526,18 +524,36 @@ __global__ __launch_bounds__(64 * CW) void attn_chunk_kernel(const ChunkArgs a)
         }
         return M != -INFINITY ? num : 0.f;
     };
-    float *o_row = a.o_out + (((int64_t)i * a.n_qh + h0) * a.max_chunks + j) * D;
 #pragma unroll
-    for (int e = 0; e < NE; e++) {
-        const int idx = tid + 64 * CW * e;
-        float M;
-        const float num = combine(smv[e], sov[e], M);
-        if (idx < G * D) o_row[(int64_t)(idx / D) * a.max_chunks * D + idx % D] = num;
+    for (int e0 = 0; e0 < ROUNDS * EB; e0 += EB) {
+        float smv[EB][CW], sov[EB][CW];
+#pragma unroll
+        for (int e = 0; e < EB; e++) {
+            if ((e0 + e) * 64 * CW >= n_out) break;
+            const int idx = min(tid + 64 * CW * (e0 + e), n_out - 1);
+            const int cc = idx / (G * D), rem2 = idx % (G * D), h = rem2 / D, d = rem2 % D;
+#pragma unroll
+            for (int k = 0; k < CW; k++) {
+                const int w = min(cc * wpc + k, CW - 1);   // k >= wpc is masked
+                smv[e][k] = k < wpc ? sm[w][h] : -INFINITY;
+                sov[e][k] = so[w][h][d];
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < EB; e++) {
+            if ((e0 + e) * 64 * CW >= n_out) break;
+            const int idx = tid + 64 * CW * (e0 + e);
+            const int cc = idx / (G * D), rem2 = idx % (G * D);
+            float M;
+            const float num = combine(smv[e], sov[e], M);
+            if (idx < n_out && j0c + cc < a.n_chunks)
+                a.o_out[(((int64_t)i * a.n_qh + h0 + rem2 / D) * a.max_chunks + j0c + cc) * D + rem2 % D] = num;
+        }
     }
-    if (tid < G) {
+    if (tid < cpw * G && j0c + tid / G < a.n_chunks) {
         float M;
         const float L = combine(hm, hl, M);
-        const int64_t idx = ((int64_t)i * a.n_qh + h0 + tid) * a.max_chunks + j;
+        const int64_t idx = ((int64_t)i * a.n_qh + h0 + tid % G) * a.max_chunks + j0c + tid / G;
         const bool empty = M == -INFINITY;
         a.m_out[idx] = empty ? -INFINITY : M * LN2;
         a.l_out[idx] = L;
@@ -546,30 +562,29 @@ __global__ __launch_bounds__(64 * CW) void attn_chunk_kernel(const ChunkArgs a)
 }
 
 // ---------------------------------------------------------------------------------------------------- merge
-// One workgroup of 4 waves per (row, q head); each wave takes a contiguous quarter of the active chunks. A wave reads
+// One workgroup of NW waves per (row, q head); each wave takes a contiguous 1/NW of the active chunks. A wave reads
 // the (m, l, empty) of up to 64 of its chunks at once, one chunk per lane, so the max M over the non-empty chunks,
 // the weights e^(m_j - M) and the weighted sum of l_j take one round of loads and a few cross-lane steps. The o_j
-// rows (lanes own D/64 consecutive dims) are loaded 8 chunks at a time with every load in flight before the first
+// rows (lanes own D/64 consecutive dims) are loaded U chunks at a time with every load in flight before the first
 // use, and are added in chunk order with the weight read from the chunk's lane. Empty chunks are skipped by select,
-// never multiplied (their l and o may hold anything). The quarters are combined through LDS.
-template <int D>
-__global__ __launch_bounds__(256) void attn_merge_kernel(const float *__restrict__ m, const float *__restrict__ l,
+// never multiplied (their l and o may hold anything). The waves' parts are combined through LDS.
+template <int D, int NW, int U>
+__global__ __launch_bounds__(64 * NW) void attn_merge_kernel(const float *__restrict__ m, const float *__restrict__ l,
                                                          const float *__restrict__ o, const uint8_t *__restrict__ em,
                                                          int32_t max_chunks, int32_t n_chunks,
                                                          const int32_t *__restrict__ n_active, int32_t n_qh,
                                                          float *__restrict__ out, float *__restrict__ lse)
 {
     constexpr int VPL = D / 64;
-    constexpr int U = 8;                           // o rows in flight per batch
-    __shared__ float sM[4], sL[4];
-    __shared__ float sO[4][D];
+    __shared__ float sM[NW], sL[NW];
+    __shared__ float sO[NW][D];
     const int tid = threadIdx.x, lane = tid % 64;
     const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
     const int32_t row = blockIdx.x;               // = i * n_qh + h
     const int32_t i = row / n_qh;
     int32_t na = n_active ? n_active[i] : n_chunks;
     na = na < 0 ? 0 : (na > n_chunks ? n_chunks : na);
-    const int32_t j0 = (int32_t)(((int64_t)na * wave) / 4), j1 = (int32_t)(((int64_t)na * (wave + 1)) / 4);
+    const int32_t j0 = (int32_t)(((int64_t)na * wave) / NW), j1 = (int32_t)(((int64_t)na * (wave + 1)) / NW);
     const int64_t base = (int64_t)row * max_chunks;
     const int32_t nq = j1 - j0;                   // chunks of this wave
     const int32_t jlast = n_chunks - 1;           // n_chunks >= 1: every clamped index is in bounds
@@ -601,7 +616,9 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const float *__restrict
     M = group_max<64>(M);
     if (lane == 0) sM[wave] = M;
     __syncthreads();
-    M = fmaxf(fmaxf(sM[0], sM[1]), fmaxf(sM[2], sM[3]));
+    M = sM[0];
+#pragma unroll
+    for (int w = 1; w < NW; w++) M = fmaxf(M, sM[w]);
 
     // pass 2: L = sum e^(m_j - M) l_j and acc = sum e^(m_j - M) o_j, in chunk order; the first batch of 64 chunks
     // uses the preloaded values
@@ -654,12 +671,16 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const float *__restrict
     for (int e = 0; e < VPL; e++) sO[wave][VPL * lane + e] = acc[e];
     __syncthreads();
     if (wave == 0) {
-        const float Lt = (sL[0] + sL[1]) + (sL[2] + sL[3]);
+        float Lt = sL[0];
+#pragma unroll
+        for (int w = 1; w < NW; w++) Lt += sL[w];
         const bool none = M == -INFINITY;
 #pragma unroll
         for (int e = 0; e < VPL; e++) {
             const int d = VPL * lane + e;
-            const float num = (sO[0][d] + sO[1][d]) + (sO[2][d] + sO[3][d]);
+            float num = sO[0][d];
+#pragma unroll
+            for (int w = 1; w < NW; w++) num += sO[w][d];
             out[(int64_t)row * D + d] = none ? 0.f : num / Lt;
         }
         if (lse && lane == 0) lse[row] = none ? -INFINITY : M + logf(Lt);
@@ -756,33 +777,53 @@ extern "C" qsa_status qsa_block_scores(const float *q, const int32_t *pos, int32
 }
 
 namespace {
-template <int D, int VB>
-void launch_chunk(int G, dim3 grid, hipStream_t s, const ChunkArgs &a)
+template <int D, int VB, int W>
+void launch_chunk_g(int G, dim3 grid, hipStream_t s, const ChunkArgs &a)
 {
     switch (G) {
-    case 1: attn_chunk_kernel<D, 1, VB><<<grid, 64 * CW, 0, s>>>(a); break;
-    case 2: attn_chunk_kernel<D, 2, VB><<<grid, 64 * CW, 0, s>>>(a); break;
-    case 3: attn_chunk_kernel<D, 3, VB><<<grid, 64 * CW, 0, s>>>(a); break;
-    case 4: attn_chunk_kernel<D, 4, VB><<<grid, 64 * CW, 0, s>>>(a); break;
-    case 5: attn_chunk_kernel<D, 5, VB><<<grid, 64 * CW, 0, s>>>(a); break;
-    case 6: attn_chunk_kernel<D, 6, VB><<<grid, 64 * CW, 0, s>>>(a); break;
-    case 7: attn_chunk_kernel<D, 7, VB><<<grid, 64 * CW, 0, s>>>(a); break;
-    default: attn_chunk_kernel<D, 8, VB><<<grid, 64 * CW, 0, s>>>(a); break;
+    case 1: attn_chunk_kernel<D, 1, VB, W><<<grid, 64 * CW, 0, s>>>(a); break;
+    case 2: attn_chunk_kernel<D, 2, VB, W><<<grid, 64 * CW, 0, s>>>(a); break;
+    case 3: attn_chunk_kernel<D, 3, VB, W><<<grid, 64 * CW, 0, s>>>(a); break;
+    case 4: attn_chunk_kernel<D, 4, VB, W><<<grid, 64 * CW, 0, s>>>(a); break;
+    case 5: attn_chunk_kernel<D, 5, VB, W><<<grid, 64 * CW, 0, s>>>(a); break;
+    case 6: attn_chunk_kernel<D, 6, VB, W><<<grid, 64 * CW, 0, s>>>(a); break;
+    case 7: attn_chunk_kernel<D, 7, VB, W><<<grid, 64 * CW, 0, s>>>(a); break;
+    default: attn_chunk_kernel<D, 8, VB, W><<<grid, 64 * CW, 0, s>>>(a); break;
     }
 }
 
+template <int D, int VB>
+void launch_chunk(int G, int wpc, dim3 grid, hipStream_t s, const ChunkArgs &a)
+{
+    if (wpc == CW) launch_chunk_g<D, VB, CW>(G, grid, s, a);
+    else if (wpc == 2) launch_chunk_g<D, VB, 2>(G, grid, s, a);
+    else launch_chunk_g<D, VB, 1>(G, grid, s, a);
+}
+
+// Waves per chunk: CW when a chunk is expected to hold at least CW pieces of 32 cells (16 at d = 256); otherwise
+// small chunks (a dense 64-cell chunk is two pieces) share a workgroup instead of leaving waves idle: 2 waves per
+// chunk while the grid fits the chip in one round of two workgroups per CU (the kernel's register use), else 1, so
+// that a wave walks its chunk's pieces itself rather than waiting for a second round.
+int chunk_wpc(int32_t D, int64_t blocks_per_chunk, int64_t n_chunks, int64_t n_groups)
+{
+    const int64_t pieces = blocks_per_chunk * (QSA_BLOCK / (D <= 128 ? 32 : 16));
+    if (pieces >= CW) return CW;
+    const int64_t wgs = (n_chunks + 1) / 2 * n_groups;   // workgroups with 2 waves per chunk
+    return wgs <= 2 * 256 ? 2 : 1;
+}
+
 // vb is the pools' common V width from common_v_bits (4 only with D >= 128).
-void launch_chunk_d(int D, int vb, int G, dim3 grid, hipStream_t s, const ChunkArgs &a)
+void launch_chunk_d(int D, int vb, int G, int wpc, dim3 grid, hipStream_t s, const ChunkArgs &a)
 {
     if (vb == 4) {
-        if (D == 128) launch_chunk<128, 4>(G, grid, s, a);
-        else launch_chunk<256, 4>(G, grid, s, a);
+        if (D == 128) launch_chunk<128, 4>(G, wpc, grid, s, a);
+        else launch_chunk<256, 4>(G, wpc, grid, s, a);
         return;
     }
     switch (D) {
-    case 64: launch_chunk<64, 8>(G, grid, s, a); break;
-    case 128: launch_chunk<128, 8>(G, grid, s, a); break;
-    default: launch_chunk<256, 8>(G, grid, s, a); break;
+    case 64: launch_chunk<64, 8>(G, wpc, grid, s, a); break;
+    case 128: launch_chunk<128, 8>(G, wpc, grid, s, a); break;
+    default: launch_chunk<256, 8>(G, wpc, grid, s, a); break;
     }
 }
 }  // namespace
@@ -823,9 +864,11 @@ extern "C" qsa_status qsa_attn_chunk(const float *q, const int32_t *pos, int32_t
     a.n_qh = dims.n_q_heads; a.n_kv = dims.n_kv_heads; a.G = dims.n_q_heads / dims.n_kv_heads;
     a.topk = k; a.bpc = blocks_per_chunk; a.n_chunks = n_chunks; a.max_chunks = out->max_chunks;
     a.qscale = sm_scale * LOG2E;
-    dim3 grid(n_chunks, dims.n_kv_heads, n_rows);
+    const int wpc = chunk_wpc(dims.head_dim, ids ? ceil_div(k, n_chunks) : blocks_per_chunk, n_chunks,
+                              (int64_t)dims.n_kv_heads * n_rows);
+    dim3 grid(ceil_div(n_chunks, CW / wpc), dims.n_kv_heads, n_rows);
     hipStream_t s = (hipStream_t)stream;
-    launch_chunk_d(dims.head_dim, vb, a.G, grid, s, a);
+    launch_chunk_d(dims.head_dim, vb, a.G, wpc, grid, s, a);
     return launch_status();
 }
 
@@ -834,7 +877,16 @@ qsa_status qsa::merge_launch(const float *m, const float *l, const float *o, con
                              int32_t head_dim, float *out, float *lse, hipStream_t s)
 {
     dim3 grid((uint32_t)n_rows * (uint32_t)n_qh);
-#define QSA_MERGE(DD) attn_merge_kernel<DD><<<grid, 256, 0, s>>>(m, l, o, empty, max_chunks, n_chunks, n_active, n_qh, out, lse)
+    // a few chunks: 4 waves, 8 rows in flight each; many (a dense window): 16 waves, 16 rows in flight each
+#define QSA_MERGE(DD)                                                                                              \
+    do {                                                                                                           \
+        if (n_chunks <= 64)                                                                                        \
+            attn_merge_kernel<DD, 4, 8><<<grid, 256, 0, s>>>(m, l, o, empty, max_chunks, n_chunks, n_active, n_qh, \
+                                                             out, lse);                                           \
+        else                                                                                                       \
+            attn_merge_kernel<DD, 16, 16><<<grid, 1024, 0, s>>>(m, l, o, empty, max_chunks, n_chunks, n_active,     \
+                                                                n_qh, out, lse);                                  \
+    } while (0)
     switch (head_dim) {
     case 64: QSA_MERGE(64); break;
     case 128: QSA_MERGE(128); break;
@@ -967,7 +1019,8 @@ extern "C" qsa_status qsa_decode_layer(const float *q, const int32_t *pos, int32
     a.n_qh = dims.n_q_heads; a.n_kv = dims.n_kv_heads; a.G = sa.G;
     a.topk = k; a.bpc = 0; a.n_chunks = n_chunks; a.max_chunks = n_chunks;
     a.qscale = sm_scale * LOG2E;
-    launch_chunk_d(dims.head_dim, vb, a.G, dim3(n_chunks, dims.n_kv_heads, n_rows), s, a);
+    const int wpc = chunk_wpc(dims.head_dim, ceil_div(k, n_chunks), n_chunks, (int64_t)dims.n_kv_heads * n_rows);
+    launch_chunk_d(dims.head_dim, vb, a.G, wpc, dim3(ceil_div(n_chunks, CW / wpc), dims.n_kv_heads, n_rows), s, a);
     if ((st = launch_status()) != QSA_OK) return st;
     return merge_launch(a.m_out, a.l_out, a.o_out, a.empty_out, n_chunks, n_chunks, nullptr, n_rows, dims.n_q_heads,
                         dims.head_dim, out, lse, s);

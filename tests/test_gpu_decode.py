@@ -355,3 +355,25 @@ def test_repeat_runs_are_bitwise_identical():
     b = decode_layer(w, p, dims, n_chunks=16)
     for key in ("scores", "ids", "out", "lse", "m", "l", "o"):
         assert np.array_equal(a[key], b[key]), key
+
+
+@pytest.mark.parametrize("n_chunks,rows", [(301, 2), (7, 3)])
+def test_dense_partials_one_and_two_waves_per_chunk(n_chunks, rows):
+    """Dense 64-cell chunks: with many chunks a wave walks a whole chunk (one wave per chunk, four chunks per
+    workgroup, the last workgroup partly empty); with few, two waves share one. Partials against the oracle's."""
+    cap = 64 * n_chunks + 100
+    w = small_workload(61 + n_chunks, n_kv=2, G=3, cap=cap, n_valid=cap - 150, rows=rows, topk=4)
+    dims = dims_of(w)
+    q, pos = dev(w.q), dev(w.pos)
+    part = qsa.Partials.empty_like_shape(rows, dims.n_q_heads, n_chunks + 1, dims.head_dim)
+    qsa.qsa_attn_chunk(q, pos, [to_device(w.pools[0])], dims, part, n_chunks, w.sm_scale, blocks_per_chunk=1)
+    torch.cuda.synchronize()
+    gm, gl, go, ge = (t.cpu().numpy()[:, :, :n_chunks] for t in (part.m, part.l, part.o, part.empty))
+    rm, rl, ro, re = oracle.chunk_partials(w.q, w.pos, w.pools[0], w.n_kv_heads, n_chunks, bpc=1)
+    assert np.array_equal(ge, re)
+    full = ~re.astype(bool)
+    assert np.all(gm[~full] == -np.inf) and np.all(gl[~full] == 0) and np.all(go[~full] == 0)
+    lse_g = gm[full].astype(np.float64) + np.log(gl[full].astype(np.float64))
+    lse_r = rm[full] + np.log(rl[full])
+    assert np.abs(lse_g - lse_r).max() <= TOL
+    assert rel_err_rows(go[full] / gl[full][:, None], ro[full] / rl[full][:, None]).max() <= TOL
