@@ -170,3 +170,30 @@ def test_capacity_wide_selection():
     assert np.array_equal(wide["ids"], narrow["ids"]) and np.array_equal(wide["counts"], narrow["counts"])
     assert np.array_equal(wide["out"], narrow["out"])
     _check_end_to_end(w, narrow)
+
+
+@pytest.mark.parametrize("n_valid,topk", [(25_000, 20), (60_000, 64), (16_384, 256)])
+def test_select_one_wave_topk_widths(n_valid, topk):
+    """Score rows of 391 and 938 blocks (the one-wave top-k with 8 and 16 keys per lane), a row whose k equals its
+    eligible count and a row of equal scores: the fused selection picks exactly what the separate score and top-k
+    calls pick, and what the oracle's top-k of those scores picks."""
+    pool = synth.random_pool(660 + topk, 2, n_valid + 64, n_valid, 128, poison=False)
+    q = synth.random_q(661 + topk, 3, 12, 128)
+    q[2, :6] = 0.0                      # row 2, KV head 0: every score is zero, a row of ties
+    pos = np.array([n_valid - 1, n_valid // 2, 300], np.int32)
+    dims = qsa.Dims(12, 2, 128)
+    p = build_index(to_device(pool), dims)
+    nb = -(-n_valid // BLOCK)
+    qd, posd = dev(q), dev(pos)
+    s_sep = torch.empty(3, 2, nb, dtype=torch.float32, device="cuda")
+    qsa.qsa_block_scores(qd, posd, p, dims, nb, s_sep)
+    i_sep = torch.empty(3, 2, topk, dtype=torch.int32, device="cuda")
+    c_sep = torch.empty(3, 2, dtype=torch.int32, device="cuda")
+    qsa.qsa_topk(s_sep, topk, i_sep, c_sep)
+    i = torch.empty_like(i_sep)
+    c = torch.empty_like(c_sep)
+    qsa.qsa_decode_select(qd, posd, [p], dims, nb, topk, i, c)
+    torch.cuda.synchronize()
+    assert np.array_equal(i.cpu().numpy(), i_sep.cpu().numpy()) and np.array_equal(c.cpu().numpy(), c_sep.cpu().numpy())
+    ref, cnt = oracle.topk(s_sep.cpu().numpy().astype(np.float64).reshape(-1, nb), topk)
+    assert np.array_equal(i.cpu().numpy().reshape(-1, topk), ref) and np.array_equal(c.cpu().numpy().reshape(-1), cnt)
