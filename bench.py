@@ -353,7 +353,7 @@ def bench_k8v4(args, w, dims, nb, S, q, pos, ids, counts, layer_scratch, out, ls
             "attn_chunk_GBs": round(chunk_bytes / (t_chunk * 1e-6) / 1e9, 1)}
 
 
-def bench_other_decode(copies=32):
+def bench_other_decode(copies=32, bw_chunks=32):
     """The batch window (2 slots x 2 rows, 65,536 valid cells per slot, top-64, one layer call over both pools) and
     the drafter (dense attention over 300 active 64-cell chunks of a 512-chunk window, active-only merge): per-call
     times and the chunk kernel's algorithmic bytes per launch over its time, against HBM peak. Pool copies rotate
@@ -410,7 +410,7 @@ def bench_other_decode(copies=32):
     base = [dev_pool(pn, True, dims) for pn in w.pools]
     sets = [base] + [[clone(p) for p in base] for _ in range(copies - 1)]
     nb = -(-w.pools[0].n_valid // BLOCK)
-    S = 20
+    S = bw_chunks
     q, pos, row_pool = t(w.q), t(w.pos), t(w.row_pool)
     ids = torch.empty(n_rows, n_kv, w.topk, dtype=torch.int32, device=dev)
     counts = torch.empty(n_rows, n_kv, dtype=torch.int32, device=dev)

@@ -1,8 +1,9 @@
 // Radix top-k over block-score rows for gfx950.
 //
-// One workgroup of 256 threads per row; thread t owns the KPT consecutive entries [t*KPT, t*KPT + KPT) so that the
-// final compaction runs in index order. Scores become order-preserving uint32 keys (-0.0 folded onto +0.0; -inf
-// and a key of 0 mark an ineligible entry). Four passes find the k-th largest key one 8-bit digit at a time, each
+// One workgroup of 64 * NW threads per row (4 waves up to 256 entries, else 16 for qsa_topk and 8 for the fused
+// selection); thread t owns the KPT consecutive entries [t*KPT, t*KPT + KPT) so that the final compaction runs in
+// index order. Scores become order-preserving uint32 keys (-0.0 folded onto +0.0; -inf and a key of 0 mark an
+// ineligible entry). Four passes find the k-th largest key one 8-bit digit at a time, each
 // with a 256-bin LDS histogram and a workgroup prefix scan over the bins (no serial walk over the bins). Keys
 // above that threshold are all kept; keys equal to it are kept lowest index first until k are taken.
 #include "qsa_internal.h"
@@ -31,7 +32,8 @@ __device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t x)
     return (uint32_t)v;
 }
 
-// Exclusive prefix sum over the 256 threads of the workgroup; `total` receives the sum over all threads.
+// Exclusive prefix sum over the NW waves of the workgroup; `total` receives the sum over all threads.
+template <int NW>
 __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t *sh_wave, uint32_t &total)
 {
     const int lane = threadIdx.x % 64, wave = threadIdx.x / 64;
@@ -40,7 +42,7 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t *s
     __syncthreads();
     uint32_t before = 0, all = 0;
 #pragma unroll
-    for (int w = 0; w < 4; w++) {
+    for (int w = 0; w < NW; w++) {
         const uint32_t t = sh_wave[w];
         before += (w < wave) ? t : 0u;
         all += t;
@@ -51,13 +53,15 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t *s
 }
 
 // Top-k over one row of keys held KPT per thread (thread t owns entries [t KPT, t KPT + KPT)); writes the k ids
-// (index order, -1 padded) and the count. Every thread of the 256-thread workgroup must call it.
-template <int KPT>
+// (index order, -1 padded) and the count. Every thread of the 64 * NW-thread workgroup must call it.
+template <int KPT, int NW>
 __device__ __forceinline__ void radix_topk(const uint32_t (&key)[KPT], int32_t k, int32_t *__restrict__ dst,
                                            int32_t *__restrict__ count)
 {
+    static_assert(NW >= 4, "the 256 histogram bins are cleared one per thread");
+    constexpr int NTH = 64 * NW;
     __shared__ uint32_t hist[2][256];
-    __shared__ uint32_t sh_wave[4];
+    __shared__ uint32_t sh_wave[NW];
     __shared__ uint32_t sh_digit, sh_remaining;
     __shared__ bool sh_whole;
     const int tid = threadIdx.x;
@@ -67,7 +71,7 @@ __device__ __forceinline__ void radix_topk(const uint32_t (&key)[KPT], int32_t k
 #pragma unroll
     for (int e = 0; e < KPT; e++) mine += key[e] != 0u;
     uint32_t n_elig;
-    block_exclusive_scan(mine, sh_wave, n_elig);
+    block_exclusive_scan<NW>(mine, sh_wave, n_elig);
     const uint32_t kk = n_elig < (uint32_t)k ? n_elig : (uint32_t)k;
 
     uint32_t T, take_eq = 0;
@@ -78,7 +82,7 @@ __device__ __forceinline__ void radix_topk(const uint32_t (&key)[KPT], int32_t k
     } else {
         uint32_t prefix = 0, mask = 0, remaining = kk;
         bool done_early = false;
-        hist[0][tid] = 0;
+        if (tid < 256) hist[0][tid] = 0;
         __syncthreads();
         // Two histograms alternate (the next one is cleared while the current one fills), and one wave scans the 256
         // bins, so a pass costs two barriers.
@@ -89,7 +93,7 @@ __device__ __forceinline__ void radix_topk(const uint32_t (&key)[KPT], int32_t k
 #pragma unroll
             for (int e = 0; e < KPT; e++)
                 if (key[e] != 0u && (key[e] & mask) == prefix) atomicAdd(&hc[(key[e] >> shift) & 255u], 1u);
-            hist[(pass + 1) & 1][tid] = 0;
+            if (tid < 256) hist[(pass + 1) & 1][tid] = 0;
             __syncthreads();
             if (tid < 64) {
                 // lane l holds digits 255 - 4l - e (e = 0..3), highest first; cum counts the matching keys whose digit
@@ -134,7 +138,7 @@ __device__ __forceinline__ void radix_topk(const uint32_t (&key)[KPT], int32_t k
 #pragma unroll
     for (int e = 0; e < KPT; e++) n_eq += (key[e] != 0u && key[e] == T);
     uint32_t tot_eq;
-    uint32_t eq_rank = block_exclusive_scan(n_eq, sh_wave, tot_eq);
+    uint32_t eq_rank = block_exclusive_scan<NW>(n_eq, sh_wave, tot_eq);
     bool sel[KPT];
     uint32_t n_sel = 0;
 #pragma unroll
@@ -145,16 +149,16 @@ __device__ __forceinline__ void radix_topk(const uint32_t (&key)[KPT], int32_t k
         n_sel += sel[e];
     }
     uint32_t tot_sel;
-    uint32_t at = block_exclusive_scan(n_sel, sh_wave, tot_sel);
+    uint32_t at = block_exclusive_scan<NW>(n_sel, sh_wave, tot_sel);
 #pragma unroll
     for (int e = 0; e < KPT; e++)
         if (sel[e]) dst[at++] = i0 + e;
-    for (int32_t jj = (int32_t)kk + tid; jj < k; jj += 256) dst[jj] = -1;
+    for (int32_t jj = (int32_t)kk + tid; jj < k; jj += NTH) dst[jj] = -1;
     if (tid == 0) *count = (int32_t)kk;
 }
 
-template <int KPT>
-__global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ scores, int32_t width, int32_t k,
+template <int KPT, int NW>
+__global__ __launch_bounds__(64 * NW) void topk_kernel(const float *__restrict__ scores, int32_t width, int32_t k,
                                                    int32_t *__restrict__ ids, int32_t *__restrict__ counts)
 {
     const int64_t row = blockIdx.x;
@@ -166,20 +170,24 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ sco
         const int32_t idx = i0 + e;
         key[e] = idx < width ? score_key(src[idx]) : 0u;
     }
-    radix_topk<KPT>(key, k, ids + row * k, counts + row);
+    radix_topk<KPT, NW>(key, k, ids + row * k, counts + row);
 }
 
 // ------------------------------------------------------------------------------- fused block scores + top-k
-// One 256-thread workgroup per (KV head g, row i) of a decode layer: the row's q heads of g are summed, every
+// One workgroup of NW waves per (KV head g, row i) of a decode layer: the row's q heads of g are summed, every
 // block's score qsum . index[g][b] is computed (the same arithmetic, in the same order, as the block-score kernel:
 // 8-dim fmaf chains per lane, then a DPP sum over the D/8 lanes of a block) into LDS, and the radix top-k selects
-// from them.
-template <int D, int KPT>
-__global__ __launch_bounds__(256) void select_kernel(const SelectArgs a)
+// from them. The index rows are fetched in batches whose loads are all in flight before the first wait (16 steps of
+// NW * BPS blocks), so a wide row (more than 256 blocks) takes 8 waves: twice the bytes in flight per batch of a
+// 4-wave workgroup.
+template <int D, int KPT, int NW>
+__global__ __launch_bounds__(64 * NW) void select_kernel(const SelectArgs a)
 {
     constexpr int LPB = D / 8, BPS = 64 / LPB;       // lanes per block, blocks per wave step
+    constexpr int T = 64 * NW, SB = NW * BPS;         // threads, blocks per workgroup step
+    static_assert(T >= D, "one thread per dim sums q");
     __shared__ float sqs[D];
-    __shared__ float ssc[256 * KPT];
+    __shared__ float ssc[T * KPT];
     const int tid = threadIdx.x, lane = tid % 64, wave = tid / 64;
     const int32_t g = blockIdx.x, i = blockIdx.y;
     // Loads first, in the order their values are needed: the per-row words (lane 0 pos[i], lane 1 the pool index;
@@ -208,25 +216,25 @@ __global__ __launch_bounds__(256) void select_kernel(const SelectArgs a)
     const int rb = lane / LPB, s = lane % LPB;
     const float *idx_g = P.index + (int64_t)g * stride * D + 8 * s;
     const int32_t n_live = min(a.width, (int32_t)((n_valid + QSA_BLOCK - 1) / QSA_BLOCK));
-    // batches of NST steps of 4 * BPS blocks each. Loads are unconditional (a dead block reads block 0 and is zeroed
+    // batches of NST steps of SB blocks each. Loads are unconditional (a dead block reads block 0 and is zeroed
     // afterwards) so a whole batch is in flight before the first wait.
     constexpr int NST = 16;
     float rv[NST][8];
-    auto load_batch = [&](int32_t base) {
-#pragma unroll
-        for (int st = 0; st < NST; st++) {
-            const int32_t b = base + st * 4 * BPS + wave * BPS + rb;
-            const float4 *src = reinterpret_cast<const float4 *>(idx_g + (int64_t)(b < n_live ? b : 0) * D);
-            const float4 u = src[0], w = src[1];
-            rv[st][0] = u.x; rv[st][1] = u.y; rv[st][2] = u.z; rv[st][3] = u.w;
-            rv[st][4] = w.x; rv[st][5] = w.y; rv[st][6] = w.z; rv[st][7] = w.w;
-        }
+    auto load_step = [&](int32_t base, int st) {
+        const int32_t b = base + st * SB + wave * BPS + rb;
+        const float4 *src = reinterpret_cast<const float4 *>(idx_g + (int64_t)(b < n_live ? b : 0) * D);
+        const float4 u = src[0], w = src[1];
+        rv[st][0] = u.x; rv[st][1] = u.y; rv[st][2] = u.z; rv[st][3] = u.w;
+        rv[st][4] = w.x; rv[st][5] = w.y; rv[st][6] = w.z; rv[st][7] = w.w;
     };
     // only blocks below n_live hold a score; the rest of the row is -inf without a load
-    const int32_t b_end = min(256 * KPT, (n_live + NST * 4 * BPS - 1) / (NST * 4 * BPS) * (NST * 4 * BPS));
-    if (b_end > 0) load_batch(0);
+    const int32_t b_end = min(T * KPT, (n_live + NST * SB - 1) / (NST * SB) * (NST * SB));
+    if (b_end > 0) {
+#pragma unroll
+        for (int st = 0; st < NST; st++) load_step(0, st);
+    }
     const int32_t p = __builtin_amdgcn_readlane(words, 0);
-    for (int e = tid; e < 256 * KPT; e += 256)
+    for (int e = tid; e < T * KPT; e += T)
         if (e >= b_end) {
             ssc[e] = -INFINITY;
             if (a.scores && e < a.width) a.scores[((int64_t)i * a.n_kv + g) * a.width + e] = -INFINITY;
@@ -244,22 +252,26 @@ __global__ __launch_bounds__(256) void select_kernel(const SelectArgs a)
     float qt[8];
 #pragma unroll
     for (int e = 0; e < 8; e++) qt[e] = sqs[8 * s + e];
-    for (int32_t base = 0; base < b_end; base += NST * 4 * BPS) {
-        if (base > 0) load_batch(base);
+    // one batch of index rows in registers at a time: each step's registers take the next batch's rows as soon as
+    // its score is done
+#pragma unroll 1
+    for (int32_t base = 0; base < b_end; base += NST * SB) {
+        const int32_t next = base + NST * SB;
 #pragma unroll
         for (int st = 0; st < NST; st++) {
-            const int32_t b = base + st * 4 * BPS + wave * BPS + rb;
+            const int32_t b = base + st * SB + wave * BPS + rb;
             const bool live = b < n_live;
             float dot = 0.f;
 #pragma unroll
             for (int e = 0; e < 8; e++) dot = fmaf(qt[e], live ? rv[st][e] : 0.f, dot);
             dot = group_sum<LPB>(dot);
-            if (s == 0 && b < 256 * KPT) {
+            if (s == 0 && b < T * KPT) {
                 const int64_t first = (int64_t)b * QSA_BLOCK;
                 const float sc = (b < a.width && first <= p && first < n_valid) ? dot : -INFINITY;
                 ssc[b] = sc;
                 if (a.scores && b < a.width) a.scores[((int64_t)i * a.n_kv + g) * a.width + b] = sc;
             }
+            if (next < b_end) load_step(next, st);
         }
     }
     __syncthreads();
@@ -267,7 +279,7 @@ __global__ __launch_bounds__(256) void select_kernel(const SelectArgs a)
 #pragma unroll
     for (int e = 0; e < KPT; e++) key[e] = score_key(ssc[tid * KPT + e]);   // past the width: -inf, key 0
     const int64_t row = (int64_t)i * a.n_kv + g;
-    radix_topk<KPT>(key, a.k, a.ids + row * a.k, a.counts + row);
+    radix_topk<KPT, NW>(key, a.k, a.ids + row * a.k, a.counts + row);
 }
 
 }  // namespace qsa
@@ -277,17 +289,18 @@ using namespace qsa;
 qsa_status qsa::select_launch(const SelectArgs &a, int32_t n_rows, int32_t n_kv, int32_t head_dim, hipStream_t s)
 {
     dim3 grid(n_kv, n_rows);
-    const int kpt = (a.width + 255) / 256;
-#define QSA_SEL(DD, K) select_kernel<DD, K><<<grid, 256, 0, s>>>(a)
+    // up to 256 columns: 4 waves, one column per thread; wider rows: 8 waves, KPT = 1..32 columns per thread
+    const int kpt = (a.width + 511) / 512;
+#define QSA_SEL(DD, K, W) select_kernel<DD, K, W><<<grid, 64 * W, 0, s>>>(a)
 #define QSA_SEL_D(DD)                                                                                               \
     do {                                                                                                          \
-        if (kpt <= 1) QSA_SEL(DD, 1);                                                                             \
-        else if (kpt <= 2) QSA_SEL(DD, 2);                                                                        \
-        else if (kpt <= 4) QSA_SEL(DD, 4);                                                                        \
-        else if (kpt <= 8) QSA_SEL(DD, 8);                                                                        \
-        else if (kpt <= 16) QSA_SEL(DD, 16);                                                                      \
-        else if (kpt <= 32) QSA_SEL(DD, 32);                                                                      \
-        else QSA_SEL(DD, 64);                                                                                     \
+        if (a.width <= 256) QSA_SEL(DD, 1, 4);                                                                    \
+        else if (kpt <= 1) QSA_SEL(DD, 1, 8);                                                                     \
+        else if (kpt <= 2) QSA_SEL(DD, 2, 8);                                                                     \
+        else if (kpt <= 4) QSA_SEL(DD, 4, 8);                                                                     \
+        else if (kpt <= 8) QSA_SEL(DD, 8, 8);                                                                     \
+        else if (kpt <= 16) QSA_SEL(DD, 16, 8);                                                                   \
+        else QSA_SEL(DD, 32, 8);                                                                                  \
     } while (0)
     switch (head_dim) {
     case 64: QSA_SEL_D(64); break;
@@ -316,15 +329,14 @@ extern "C" qsa_status qsa_topk(const float *scores, int32_t n_rows, int32_t widt
     if (n_rows == 0) return QSA_OK;
     hipStream_t s = (hipStream_t)stream;
     dim3 grid(n_rows);
-    const int kpt = (width + 255) / 256;
-#define QSA_TOPK(K) topk_kernel<K><<<grid, 256, 0, s>>>(scores, width, k, ids, counts)
-    if (kpt <= 1) QSA_TOPK(1);
-    else if (kpt <= 2) QSA_TOPK(2);
-    else if (kpt <= 4) QSA_TOPK(4);
-    else if (kpt <= 8) QSA_TOPK(8);
-    else if (kpt <= 16) QSA_TOPK(16);
-    else if (kpt <= 32) QSA_TOPK(32);
-    else QSA_TOPK(64);
+    const int kpt = (width + 1023) / 1024;
+#define QSA_TOPK(K, W) topk_kernel<K, W><<<grid, 64 * W, 0, s>>>(scores, width, k, ids, counts)
+    if (width <= 256) QSA_TOPK(1, 4);
+    else if (kpt <= 1) QSA_TOPK(1, 16);
+    else if (kpt <= 2) QSA_TOPK(2, 16);
+    else if (kpt <= 4) QSA_TOPK(4, 16);
+    else if (kpt <= 8) QSA_TOPK(8, 16);
+    else QSA_TOPK(16, 16);
 #undef QSA_TOPK
     return launch_status();
 }
