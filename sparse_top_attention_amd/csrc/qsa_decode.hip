@@ -291,6 +291,7 @@ __global__ __launch_bounds__(64 * CW) void attn_chunk_kernel(const ChunkArgs a)
     __shared__ __align__(16) float sp[CW][PC][NG][GP];
     __shared__ float sm[CW][G], sl[CW][G];
     __shared__ float so[CW][G][D];
+    __shared__ __align__(16) float sq[G * D];        // the G q rows of (row i, KV head g)
     const int tid = threadIdx.x, lane = tid % 64;
     const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
     const int r = lane / LPC, s = lane % LPC, grp_s = s / (LPC / NG);
@@ -304,9 +305,21 @@ __global__ __launch_bounds__(64 * CW) void attn_chunk_kernel(const ChunkArgs a)
     const bool chunk_ok = j < a.n_chunks;                 // the last workgroup may hold fewer chunks
     const int32_t h0 = g * G;
 
-    // Prologue: the per-row words come in one vector load (lane 0 pos[i], lane 1 the pool index, lane 2 the block
-    // count; a missing row_pool or id list reads pos[i] instead, a valid word whose value is then ignored), issued
-    // with the id list and ahead of the q rows, so one round trip brings them all; the pool's fields follow.
+    // Prologue: the workgroup's G q rows (one 16-byte load per thread), then the per-row words in one vector load
+    // (lane 0 pos[i], lane 1 the pool index, lane 2 the block count; a missing row_pool or id list reads pos[i]
+    // instead, a valid word whose value is then ignored) and the id list, so one round trip brings them all. The q
+    // rows go through LDS: every wave needs all of them, and one copy per workgroup keeps them off the load-return
+    // path that the K and V bytes take. The pool's fields follow.
+    constexpr int QV4 = G * D / 4, QPT = (QV4 + 64 * CW - 1) / (64 * CW);
+    float4 qld[QPT];
+    {
+        const float4 *qsrc = reinterpret_cast<const float4 *>(a.q + ((int64_t)i * a.n_qh + h0) * D);
+#pragma unroll
+        for (int u = 0; u < QPT; u++) {
+            const int e = tid + 64 * CW * u;
+            qld[u] = qsrc[e < QV4 ? e : 0];
+        }
+    }
     const int64_t row_kv = (int64_t)i * a.n_kv + g;
     const bool sel = a.ids != nullptr, mp = a.row_pool != nullptr;
     const int32_t *p_pidx = mp ? a.row_pool + i : a.pos + i;
@@ -314,10 +327,16 @@ __global__ __launch_bounds__(64 * CW) void attn_chunk_kernel(const ChunkArgs a)
     const int32_t *blist = sel ? a.ids + row_kv * a.topk : a.pos + i;
     const int32_t words = *(lane == 1 ? p_pidx : (lane == 2 ? p_cnt : a.pos + i));
     const int32_t idv = blist[sel && lane < a.topk ? lane : 0];   // k <= 64: the whole id list, one id per lane
+#pragma unroll
+    for (int u = 0; u < QPT; u++) {
+        const int e = tid + 64 * CW * u;
+        if (e < QV4) reinterpret_cast<float4 *>(sq)[e] = qld[u];
+    }
+    __syncthreads();
     float qv[G][16];
 #pragma unroll
     for (int h = 0; h < G; h++) {
-        const float4 *src = reinterpret_cast<const float4 *>(a.q + ((int64_t)i * a.n_qh + h0 + h) * D + 16 * s);
+        const float4 *src = reinterpret_cast<const float4 *>(sq + h * D + 16 * s);
 #pragma unroll
         for (int jj = 0; jj < 4; jj++) {
             const float4 u = src[jj];
@@ -475,9 +494,40 @@ __global__ __launch_bounds__(64 * CW) void attn_chunk_kernel(const ChunkArgs a)
         }
     }
 
-    // ---- hand the wave's partial to LDS: lane 0 the maxima and sums, every lane its own dims of o
 #pragma unroll
     for (int h = 0; h < G; h++) lpart[h] = strided_sum<LPC>(lpart[h]);
+    if constexpr (WPC == 1) {
+        // one wave per chunk: its partial is the chunk's, stored straight from registers (no LDS fold, no barrier;
+        // the same values the fold would produce, since a single term's weight is 2^0 = 1)
+        if (!chunk_ok) return;
+        const int64_t row0 = ((int64_t)i * a.n_qh + h0) * a.max_chunks + j;
+#pragma unroll
+        for (int t = 0; t < NT; t++) {
+#pragma unroll
+            for (int n = 0; n < NPB; n++) {
+                const int d = DPC * (CPG * grp_v + sub_v + SUBS * t) + NPB * jl + n;
+#pragma unroll
+                for (int h = 0; h < G; h++)
+                    a.o_out[(row0 + (int64_t)h * a.max_chunks) * D + d] = mrun[h] != -INFINITY ? o[h][NPB * t + n] : 0.f;
+            }
+        }
+        if (lane < G) {
+            float mh = mrun[0], lh = lpart[0];
+#pragma unroll
+            for (int h = 1; h < G; h++) {
+                mh = lane == h ? mrun[h] : mh;
+                lh = lane == h ? lpart[h] : lh;
+            }
+            const int64_t idx = row0 + (int64_t)lane * a.max_chunks;
+            const bool empty = mh == -INFINITY;
+            a.m_out[idx] = empty ? -INFINITY : mh * LN2;
+            a.l_out[idx] = empty ? 0.f : lh;
+            a.empty_out[idx] = empty ? 1 : 0;
+        }
+        return;
+    }
+
+    // ---- hand the wave's partial to LDS: lane 0 the maxima and sums, every lane its own dims of o
     if (lane == 0) {
 #pragma unroll
         for (int h = 0; h < G; h++) {
