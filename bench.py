@@ -46,6 +46,8 @@ def parse():
                     help="only run a plain device copy of known size (to scale HBM byte counters)")
     ap.add_argument("--copies", type=int, default=64, help="pool copies the steps rotate over")
     ap.add_argument("--chunks", type=int, default=0, help="split count (0 = the library default for the shape)")
+    ap.add_argument("--scale", action="store_true",
+                    help="only measure the chunk kernel on 1, 2, 4 and 8 verify-window slots in one launch")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     return ap.parse_args()
@@ -95,6 +97,10 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         print(json.dumps(copy_calibration()))
+        return
+    if args.scale:
+        for line in bench_scale():
+            print(json.dumps(line), flush=True)
         return
     if args.workload == "prompt_chunk":
         res = bench_prompt(args, args.steps if args.steps != 1280 else args.prompt_steps, main_line=True)
@@ -469,6 +475,91 @@ def bench_other_decode(copies=32, bw_chunks=32):
     del pools, base
     torch.cuda.empty_cache()
     return res
+
+
+def bench_scale(slot_counts=(1, 2, 4, 8), chunk_counts=(4, 16)):
+    """The verify window repeated over 1-8 slots (4 rows each, one 16,384-cell pool per slot) in one layer call:
+    the chunk kernel's algorithmic bytes over its time as the launch grows, for a few chunk counts. Pool copies
+    rotate so that about 450 MB of selected K/V separates two reads of the same bytes (they come from HBM)."""
+    import torch
+
+    import sparse_top_attention_amd as qsa
+    import synth
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.Stream()
+
+    def t(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    def avg_us(fn, n, reps=10):
+        with torch.cuda.stream(stream):
+            for c in range(n):
+                fn(c)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for c in range(n):
+                fn(c)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            g.replay()
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for _ in range(reps):
+                g.replay()
+            b.record(stream)
+            torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / (reps * n)
+
+    out = []
+    for slots in slot_counts:
+        w = synth.workload("verify_window", poison=False, slots=slots)
+        dims = qsa.Dims(w.n_q_heads, w.n_kv_heads, w.head_dim)
+        copies = max(2, 64 // slots)
+
+        def dev_pool(pn):
+            p = qsa.Pool(t(pn.k), t(pn.ks), t(pn.v), t(pn.vs), pn.n_valid)
+            p.index = torch.zeros(dims.n_kv_heads, -(-pn.capacity // BLOCK), dims.head_dim, dtype=torch.float32,
+                                  device=dev)
+            qsa.qsa_block_index(p, dims, 0, pn.n_valid, p.index)
+            return p
+        base = [dev_pool(pn) for pn in w.pools]
+        sets = [base] + [[qsa.Pool(p.k.clone(), p.k_scale.clone(), p.v.clone(), p.v_scale.clone(), p.n_valid,
+                                   p.index.clone()) for p in base] for _ in range(copies - 1)]
+        n_rows = w.q.shape[0]
+        nb = -(-w.pools[0].n_valid // BLOCK)
+        q, pos, rp = t(w.q), t(w.pos), t(w.row_pool)
+        ids = torch.empty(n_rows, w.n_kv_heads, w.topk, dtype=torch.int32, device=dev)
+        counts = torch.empty(n_rows, w.n_kv_heads, dtype=torch.int32, device=dev)
+        out_t = torch.empty(n_rows, w.n_q_heads, w.head_dim, dtype=torch.float32, device=dev)
+        lse = torch.empty(n_rows, w.n_q_heads, dtype=torch.float32, device=dev)
+        qsa.qsa_decode_select(q, pos, sets[0], dims, nb, w.topk, ids, counts, row_pool=rp)
+        torch.cuda.synchronize()
+        ih, ch = ids.cpu().numpy(), counts.cpu().numpy()
+        cells = sum(union_cells(ih[w.row_pool == s], ch[w.row_pool == s], w.pos[w.row_pool == s],
+                                w.pools[s].n_valid, w.n_kv_heads) for s in range(slots))
+        cb = cells * KV_BYTES_PER_CELL_HEAD + w.q.nbytes
+        for S in chunk_counts:
+            scratch = torch.empty(qsa.qsa_decode_layer_scratch_bytes(n_rows, dims, w.topk, S), dtype=torch.uint8,
+                                  device=dev)
+            part = qsa.Partials.empty_like_shape(n_rows, w.n_q_heads, S, w.head_dim, device=dev)
+
+            def layer(c):
+                qsa.qsa_decode_layer(q, pos, sets[c], dims, nb, w.topk, S, out_t, lse, sm_scale=w.sm_scale,
+                                     row_pool=rp, ids=ids, counts=counts, scratch=scratch)
+
+            def chunk(c):
+                qsa.qsa_attn_chunk(q, pos, sets[c], dims, part, S, w.sm_scale, row_pool=rp, ids=ids, counts=counts)
+            tl, tc = avg_us(layer, copies), avg_us(chunk, copies)
+            gbs = cb / (tc * 1e-6) / 1e9
+            out.append({"workload": "verify_window x slots", "slots": slots, "rows": n_rows, "chunks": S,
+                        "layer_us": round(tl, 2), "attn_chunk_us": round(tc, 2), "chunk_bytes_per_launch": int(cb),
+                        "attn_chunk_GBs": round(gbs, 1), "frac_of_hbm": round(gbs / HBM_PEAK_GBS, 4)})
+        del sets, base
+        torch.cuda.empty_cache()
+    return out
 
 
 def copy_calibration(nbytes=1 << 28, reps=4):
