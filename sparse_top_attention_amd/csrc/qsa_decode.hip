@@ -29,6 +29,34 @@ __device__ __forceinline__ void unpack16(const int4 w, float (&x)[16])
     }
 }
 
+// Reduce-scatter over the LPC lanes of a cell (LPC = 4, 8 or 16, lane bits = s): every lane enters with NV partial
+// values, value v belonging to slot v, and lane s leaves with the sums over the LPC lanes of slots s, s + LPC, ...
+// in v[0], v[LPC], ... Stage m pairs the positions p and p | m: the lane whose bit m is set keeps slot p | m, the
+// other slot p, each adding what its partner (bit m flipped, the bits above m equal: the quad swaps below 4, the
+// 8- and 16-lane mirrors at 4 and 8) sends for it, and the result goes to position p.
+template <int LPC, int NV>
+__device__ __forceinline__ void reduce_scatter(float (&v)[NV], int s)
+{
+#pragma unroll
+    for (int m = LPC / 2; m >= 1; m /= 2) {
+        // the per-lane choice is a bit select on a lane mask held in a vector register (no scalar lane masks)
+        const uint32_t hi = (s & m) ? 0xFFFFFFFFu : 0u;
+#pragma unroll
+        for (int p = 0; p < NV; p++) {
+            if ((p & m) || (p & (LPC - 1) & ~(2 * m - 1))) continue;   // not the low position of a live pair
+            const uint32_t lo_b = __float_as_uint(v[p]), hi_b = __float_as_uint(v[p | m]);
+            const float keep = __uint_as_float((hi_b & hi) | (lo_b & ~hi));
+            const float send = __uint_as_float((lo_b & hi) | (hi_b & ~hi));
+            float recv;
+            if (m == 8) recv = dpp_f<DPP_ROW_MIRROR>(send);
+            else if (m == 4) recv = dpp_f<DPP_ROW_HALF_MIRROR>(send);
+            else if (m == 2) recv = dpp_f<DPP_QUAD_XOR2>(send);
+            else recv = dpp_f<DPP_QUAD_XOR1>(send);
+            v[p] = keep + recv;
+        }
+    }
+}
+
 // --------------------------------------------------------------------------------------------- block index
 // index[g][b][:] = mean of the dequantised keys of block b's valid cells, computed by one wave.
 template <int D>
@@ -361,19 +389,24 @@ __global__ __launch_bounds__(64 * CW) void attn_chunk_kernel(const ChunkArgs a)
     const int32_t n_blk = chunk_ok ? base + (j < rem ? 1 : 0) : 0;
     const int32_t first = j * base + (j < rem ? j : rem);
 
-    float mrun[G], lpart[G], o[G][DPL];
+    // after the logits' reduce-scatter lane (r, s) holds heads s, s + LPC, ... (HPL slots) of its cell; the running
+    // max and sum of head h live in the lanes of slot h, the output accumulators in every lane
+    constexpr int HPL = (G + LPC - 1) / LPC, NV = HPL * LPC;
+    float mrun[HPL], lpart[HPL], o[G][DPL];
 #pragma unroll
-    for (int h = 0; h < G; h++) {
-        mrun[h] = -INFINITY;
-        lpart[h] = 0.f;
+    for (int k = 0; k < HPL; k++) {
+        mrun[k] = -INFINITY;
+        lpart[k] = 0.f;
+    }
+#pragma unroll
+    for (int h = 0; h < G; h++)
 #pragma unroll
         for (int t = 0; t < DPL; t++) o[h][t] = 0.f;
-    }
 
     const int8_t *kbase = P.k + (int64_t)g * P.capacity * D + 16 * s;
     const int8_t *vbase = P.v + (int64_t)g * P.capacity * RB;
     const float *ksbase = P.ks + (int64_t)g * P.capacity * NG + grp_s;
-    const float *vsbase = P.vs + (int64_t)g * P.capacity * NG + (s < NG ? s : 0);
+    const float *vsbase = P.vs + (int64_t)g * P.capacity * NG;
     int8_t *svw = sv[wave];
     constexpr int PPB = QSA_BLOCK / PC;              // pieces per block
 
@@ -386,13 +419,22 @@ __global__ __launch_bounds__(64 * CW) void attn_chunk_kernel(const ChunkArgs a)
 
         // ---- loads: K slices and scales into registers, the V piece into LDS
         int4 kw[STEPS];
-        float ksc[STEPS], vsc[STEPS];
+        float ksc[STEPS], vsc[STEPS][NG];
 #pragma unroll
         for (int st = 0; st < STEPS; st++) {
             const int32_t c = min(cb + st * CPS + r, limit);
             kw[st] = *reinterpret_cast<const int4 *>(kbase + (int64_t)c * D);
             ksc[st] = ksbase[(int64_t)c * NG] * a.qscale;   // sm_scale * log2(e) rides on the key scale
-            vsc[st] = vsbase[(int64_t)c * NG];
+            const float *vsrc = vsbase + (int64_t)c * NG;   // all NG group scales of the cell, one load
+            if constexpr (NG == 4) {
+                const float4 u = *reinterpret_cast<const float4 *>(vsrc);
+                vsc[st][0] = u.x; vsc[st][1] = u.y; vsc[st][2] = u.z; vsc[st][3] = u.w;
+            } else if constexpr (NG == 2) {
+                const float2 u = *reinterpret_cast<const float2 *>(vsrc);
+                vsc[st][0] = u.x; vsc[st][1] = u.y;
+            } else {
+                vsc[st][0] = vsrc[0];
+            }
         }
 #pragma unroll
         for (int q = 0; q < VCH; q++) {
@@ -402,57 +444,66 @@ __global__ __launch_bounds__(64 * CW) void attn_chunk_kernel(const ChunkArgs a)
         }
         __builtin_amdgcn_sched_barrier(0);   // every copy is in flight before the logits start
 
-        // ---- logits (base-2 units), masked past the limit
-        float lg[STEPS][G];
+        // ---- logits (base-2 units), masked past the limit: the G dot products of the lane's 16 dims, then a
+        // reduce-scatter over the cell's lanes, so each (cell, head) logit is finished in one lane only
+        float lg[STEPS][HPL];
 #pragma unroll
         for (int st = 0; st < STEPS; st++) {
             const bool vis = cb + st * CPS + r <= limit;
             float x[16];
             unpack16(kw[st], x);
+            float d[NV];
 #pragma unroll
-            for (int h = 0; h < G; h++) {
+            for (int h = 0; h < NV; h++) {
                 float dot = 0.f;
+                if (h < G) {
 #pragma unroll
-                for (int e = 0; e < 16; e++) dot = fmaf(qv[h][e], x[e], dot);
-                dot = group_sum<LPC>(dot * ksc[st]);
-                lg[st][h] = vis ? dot : -INFINITY;
+                    for (int e = 0; e < 16; e++) dot = fmaf(qv[h < G ? h : 0][e], x[e], dot);
+                }
+                d[h] = dot * ksc[st];
             }
+            reduce_scatter<LPC, NV>(d, s);
+#pragma unroll
+            for (int k = 0; k < HPL; k++) lg[st][k] = vis ? d[LPC * k] : -INFINITY;
         }
 
-        // ---- running max per head; p = 2^(logit - max); p * v_scale to LDS by the first NG lanes of each cell
+        // ---- running max per head over the piece's cells (lanes of one slot), p = 2^(logit - max); the output
+        // accumulators take every head's rescale, read from the head's slot lane
+        float alpha[HPL];
 #pragma unroll
-        for (int h = 0; h < G; h++) {
-            float mb = lg[0][h];
+        for (int k = 0; k < HPL; k++) {
+            float mb = lg[0][k];
 #pragma unroll
-            for (int st = 1; st < STEPS; st++) mb = fmaxf(mb, lg[st][h]);
+            for (int st = 1; st < STEPS; st++) mb = fmaxf(mb, lg[st][k]);
             mb = strided_max<LPC>(mb);            // the piece holds a visible cell, so mb is finite
-            const float mnew = fmaxf(mrun[h], mb);
-            const float alpha = __builtin_amdgcn_exp2f(mrun[h] - mnew);  // 0 on the first piece
-            mrun[h] = mnew;
-            lpart[h] *= alpha;
-#pragma unroll
-            for (int t = 0; t < DPL; t++) o[h][t] *= alpha;
+            const float mnew = fmaxf(mrun[k], mb);
+            alpha[k] = __builtin_amdgcn_exp2f(mrun[k] - mnew);  // 0 on the first piece
+            mrun[k] = mnew;
+            lpart[k] *= alpha[k];
 #pragma unroll
             for (int st = 0; st < STEPS; st++) {
-                const float p = __builtin_amdgcn_exp2f(lg[st][h] - mnew);   // masked cells: 2^-inf = 0
-                lpart[h] += p;
-                lg[st][h] = p;
+                const float p = __builtin_amdgcn_exp2f(lg[st][k] - mnew);   // masked cells: 2^-inf = 0
+                lpart[k] += p;
+                lg[st][k] = p;
             }
         }
-        if (s < NG) {
 #pragma unroll
-            for (int st = 0; st < STEPS; st++) {
-                float *dst = &sp[wave][st * CPS + r][s][0];
-                // masked cells have p = 0 but their v_scale may be anything (even NaN): their rows are zeroed
-                const float w = cb + st * CPS + r <= limit ? vsc[st] : 0.f;
+        for (int h = 0; h < G; h++) {
+            const float ah = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha[h / LPC]), h % LPC));
 #pragma unroll
-                for (int h4 = 0; h4 < GP; h4 += 4) {
-                    float4 v4;
-                    v4.x = h4 + 0 < G ? lg[st][h4 + 0 < G ? h4 + 0 : 0] * w : 0.f;
-                    v4.y = h4 + 1 < G ? lg[st][h4 + 1 < G ? h4 + 1 : 0] * w : 0.f;
-                    v4.z = h4 + 2 < G ? lg[st][h4 + 2 < G ? h4 + 2 : 0] * w : 0.f;
-                    v4.w = h4 + 3 < G ? lg[st][h4 + 3 < G ? h4 + 3 : 0] * w : 0.f;
-                    *reinterpret_cast<float4 *>(dst + h4) = v4;
+            for (int t = 0; t < DPL; t++) o[h][t] *= ah;
+        }
+        // p * v_scale per (cell, scale group, head) to LDS, written by the head's slot lane of each cell; masked
+        // cells have p = 0 but their v_scale may be anything (even NaN): their entries are zeroed
+#pragma unroll
+        for (int st = 0; st < STEPS; st++) {
+            const bool vis = cb + st * CPS + r <= limit;
+#pragma unroll
+            for (int k = 0; k < HPL; k++) {
+                const int h = s + LPC * k;
+                if (h < G) {
+#pragma unroll
+                    for (int gi = 0; gi < NG; gi++) sp[wave][st * CPS + r][gi][h] = vis ? lg[st][k] * vsc[st][gi] : 0.f;
                 }
             }
         }
@@ -495,7 +546,7 @@ __global__ __launch_bounds__(64 * CW) void attn_chunk_kernel(const ChunkArgs a)
     }
 
 #pragma unroll
-    for (int h = 0; h < G; h++) lpart[h] = strided_sum<LPC>(lpart[h]);
+    for (int k = 0; k < HPL; k++) lpart[k] = strided_sum<LPC>(lpart[k]);
     if constexpr (WPC == 1) {
         // one wave per chunk: its partial is the chunk's, stored straight from registers (no LDS fold, no barrier;
         // the same values the fold would produce, since a single term's weight is 2^0 = 1)
@@ -511,28 +562,28 @@ __global__ __launch_bounds__(64 * CW) void attn_chunk_kernel(const ChunkArgs a)
                     a.o_out[(row0 + (int64_t)h * a.max_chunks) * D + d] = mrun[h] != -INFINITY ? o[h][NPB * t + n] : 0.f;
             }
         }
-        if (lane < G) {
-            float mh = mrun[0], lh = lpart[0];
 #pragma unroll
-            for (int h = 1; h < G; h++) {
-                mh = lane == h ? mrun[h] : mh;
-                lh = lane == h ? lpart[h] : lh;
+        for (int k = 0; k < HPL; k++) {
+            const int h = lane + LPC * k;   // lanes 0 .. LPC - 1 (the first cell's) hold every head once
+            if (lane < LPC && h < G) {
+                const int64_t idx = row0 + (int64_t)h * a.max_chunks;
+                const bool empty = mrun[k] == -INFINITY;
+                a.m_out[idx] = empty ? -INFINITY : mrun[k] * LN2;
+                a.l_out[idx] = empty ? 0.f : lpart[k];
+                a.empty_out[idx] = empty ? 1 : 0;
             }
-            const int64_t idx = row0 + (int64_t)lane * a.max_chunks;
-            const bool empty = mh == -INFINITY;
-            a.m_out[idx] = empty ? -INFINITY : mh * LN2;
-            a.l_out[idx] = empty ? 0.f : lh;
-            a.empty_out[idx] = empty ? 1 : 0;
         }
         return;
     }
 
-    // ---- hand the wave's partial to LDS: lane 0 the maxima and sums, every lane its own dims of o
-    if (lane == 0) {
+    // ---- hand the wave's partial to LDS: the first cell's slot lanes the maxima and sums, every lane its own dims
+    // of o
 #pragma unroll
-        for (int h = 0; h < G; h++) {
-            sm[wave][h] = mrun[h];
-            sl[wave][h] = lpart[h];
+    for (int k = 0; k < HPL; k++) {
+        const int h = lane + LPC * k;
+        if (lane < LPC && h < G) {
+            sm[wave][h] = mrun[k];
+            sl[wave][h] = lpart[k];
         }
     }
 #pragma unroll
