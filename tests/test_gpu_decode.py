@@ -150,7 +150,8 @@ def test_chunk_partials_short_selection_and_bad_ids():
     _partials_vs_oracle(w, to_device(w.pools[0]), dims, 4, ids, ref_counts, gpu_counts=neg)
 
 
-@pytest.mark.parametrize("d,G", [(64, 1), (64, 4), (128, 2), (128, 5), (128, 8), (256, 3), (256, 6), (256, 8)])
+@pytest.mark.parametrize("d,G", [(64, 1), (64, 4), (64, 6), (64, 8), (128, 1), (128, 2), (128, 5), (128, 8),
+                                 (256, 1), (256, 3), (256, 6), (256, 8)])
 def test_decode_head_dims_and_group_sizes(d, G):
     w = small_workload(31 + d + G, n_kv=2, G=G, d=d, cap=2100, n_valid=2010, rows=2, topk=9)
     dims = dims_of(w)
