@@ -509,37 +509,51 @@ __global__ __launch_bounds__(64 * CW) void attn_chunk_kernel(const ChunkArgs a)
         }
         __builtin_amdgcn_s_waitcnt(0);   // the V piece has landed and the p rows are written (this wave only)
 
-        // ---- o[h][dim] += sum over cells of (p * v_scale)[cell][h] * v[cell][dim]
+        // ---- o[h][dim] += sum over cells of (p * v_scale)[cell][h] * v[cell][dim]. Each cell's p * v_scale row
+        // feeds only G * DPL FMAs, so the rows are read PWD cells ahead (a ring of registers) and the next 8-cell
+        // block's transposing V reads are issued half a block early: the LDS latency stays behind the FMAs.
         const int i8 = jl >> 1, hh = jl & 1;
+        constexpr int PWD = 3;                           // p * v_scale rows in flight
+        constexpr int GR = (G + 3) / 4;                  // float4 reads per row (heads past G are not read)
+        auto read_row = [&](int c, float4 (&dst)[GR]) {
+            const float *prow = &sp[wave][c][grp_v][0];
 #pragma unroll
-        for (int co = 0; co < PC / 8; co++) {
-            v2i vb[NT];
+            for (int u = 0; u < GR; u++) dst[u] = *reinterpret_cast<const float4 *>(prow + 4 * u);
+        };
+        auto read_v = [&](int co, v2i (&dst)[NT]) {
 #pragma unroll
             for (int t = 0; t < NT; t++) {
                 const int lc = CPG * grp_v + sub_v + SUBS * t;   // logical 16-byte chunk of the lane's dims
                 const int cell = 8 * co + i8;
-                vb[t] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                dst[t] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
                     (QSA_LDS v2i *)(svw + cell * RB + 16 * (lc ^ (cell & SWZ)) + 8 * hh));
             }
+        };
+        float4 ring[PWD][GR];
+        v2i vb[2][NT];
+        read_v(0, vb[0]);
 #pragma unroll
-            for (int ci = 0; ci < 8; ci++) {
-                const float *prow = &sp[wave][8 * co + ci][grp_v][0];
-                float pw[GP];
+        for (int c = 0; c < PWD - 1; c++) read_row(c, ring[c]);
 #pragma unroll
-                for (int h4 = 0; h4 < GP; h4 += 4) {
-                    const float4 v4 = *reinterpret_cast<const float4 *>(prow + h4);
-                    pw[h4] = v4.x; pw[h4 + 1] = v4.y; pw[h4 + 2] = v4.z; pw[h4 + 3] = v4.w;
-                }
+        for (int c = 0; c < PC; c++) {
+            const int co = c / 8, ci = c % 8;
+            if (c + PWD - 1 < PC) read_row(c + PWD - 1, ring[(c + PWD - 1) % PWD]);
+            if (ci == 4 && co + 1 < PC / 8) read_v(co + 1, vb[(co + 1) & 1]);
+            float pw[4 * GR];
 #pragma unroll
-                for (int t = 0; t < NT; t++) {
-                    const int32_t word = ci < 4 ? vb[t][0] : vb[t][1];
+            for (int u = 0; u < GR; u++) {
+                pw[4 * u] = ring[c % PWD][u].x; pw[4 * u + 1] = ring[c % PWD][u].y;
+                pw[4 * u + 2] = ring[c % PWD][u].z; pw[4 * u + 3] = ring[c % PWD][u].w;
+            }
 #pragma unroll
-                    for (int n = 0; n < NPB; n++) {
-                        // signed field of VB bits at bit 8 * (ci & 3) + VB * n
-                        const float x = (float)((word << (32 - VB - 8 * (ci & 3) - VB * n)) >> (32 - VB));
+            for (int t = 0; t < NT; t++) {
+                const int32_t word = ci < 4 ? vb[co & 1][t][0] : vb[co & 1][t][1];
 #pragma unroll
-                        for (int h = 0; h < G; h++) o[h][NPB * t + n] = fmaf(pw[h], x, o[h][NPB * t + n]);
-                    }
+                for (int n = 0; n < NPB; n++) {
+                    // signed field of VB bits at bit 8 * (ci & 3) + VB * n
+                    const float x = (float)((word << (32 - VB - 8 * (ci & 3) - VB * n)) >> (32 - VB));
+#pragma unroll
+                    for (int h = 0; h < G; h++) o[h][NPB * t + n] = fmaf(pw[h], x, o[h][NPB * t + n]);
                 }
             }
         }
