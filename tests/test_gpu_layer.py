@@ -70,14 +70,29 @@ def test_layer_repeated_calls_reuse_scratch():
         _check_end_to_end(w, got)
 
 
-def test_layer_batch_window_two_pools():
-    """Both slots' rows in one call through row_pool; each slot checked against the oracle on its own pool."""
+@pytest.mark.parametrize("S", [20, 32])
+def test_layer_batch_window_two_pools(S):
+    """Both slots' rows in one call through row_pool (32 chunks is the split the benchmark times); each slot checked
+    against the oracle on its own pool."""
     w = synth.workload("batch_window")
     dims = dims_of(w)
     pdevs = [build_index(to_device(pl), dims) for pl in w.pools]
-    got = run_layer(w, pdevs, dims, 20, row_pool=dev(w.row_pool))
+    got = run_layer(w, pdevs, dims, S, row_pool=dev(w.row_pool))
     for sidx in range(2):
         rows = slice(2 * sidx, 2 * sidx + 2)
+        sub = {k: v[rows] for k, v in got.items()}
+        _check_end_to_end(w, sub, pool=w.pools[sidx], rows=rows)
+
+
+def test_layer_verify_window_four_slots_four_chunks():
+    """Four verify-window slots (one 200,000-cell pool each) in one call with 4 chunks per row, the launch shape of
+    the benchmark's scale measurement: every wave of the chunk kernel takes several pieces."""
+    w = synth.workload("verify_window", slots=4)
+    dims = dims_of(w)
+    pdevs = [build_index(to_device(pl), dims) for pl in w.pools]
+    got = run_layer(w, pdevs, dims, 4, row_pool=dev(w.row_pool))
+    for sidx in range(4):
+        rows = slice(4 * sidx, 4 * sidx + 4)
         sub = {k: v[rows] for k, v in got.items()}
         _check_end_to_end(w, sub, pool=w.pools[sidx], rows=rows)
 
