@@ -29,11 +29,14 @@ def _host(p):
             p.index.cpu().numpy())
 
 
-@pytest.mark.parametrize("d", [64, 128, 256])
-def test_append_matches_oracle_bitwise(d):
+@pytest.mark.parametrize("d,many", [(64, False), (128, False), (256, False), (64, True), (128, True)])
+def test_append_matches_oracle_bitwise(d, many):
+    """6 or 12 new rows (12 rows: six more cells in the same two blocks) against the oracle's encoder, bit for bit."""
     n_kv, cap, n_old = 2, 700, 600
     pool = synth.random_pool(1000 + d, n_kv, cap, n_old, d, poison=False)
     cells = np.array([600, 601, 640, 605, 699, 650], np.int32)   # rows share blocks; 699 >= n_valid: skipped
+    if many:
+        cells = np.concatenate([cells, np.array([602, 603, 641, 651, 659, 604], np.int32)])
     n_new = 660                                                    # n_valid after the append
     kn, vn = _new_rows(1001 + d, len(cells), n_kv, d, zero_group=True)
     dims = qsa.Dims(n_kv * 3, n_kv, d)
