@@ -663,6 +663,33 @@ def bench_prompt(args, steps, main_line):
     return res
 
 
+def host_cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+class one_core:
+    """Pins this process to one of its allowed cores while the oracle is timed (it is single-threaded), then
+    restores the affinity; a no-op where affinity cannot be set."""
+    def __enter__(self):
+        self.saved = None
+        try:
+            self.saved = os.sched_getaffinity(0)
+            os.sched_setaffinity(0, {min(self.saved)})
+        except (AttributeError, OSError):
+            self.saved = None
+        return self
+
+    def __exit__(self, *exc):
+        if self.saved is not None:
+            os.sched_setaffinity(0, self.saved)
+
+
 def cpu_baseline(w, layer_bytes, budget_s):
     """The FP64 oracle (single thread) on the same workload: scores, top-k and attention of one layer, repeated
     for about budget_s seconds; reported in the bench's unit (algorithmic bytes per layer / time per layer)."""
@@ -673,23 +700,25 @@ def cpu_baseline(w, layer_bytes, budget_s):
     r = oracle.block_index(pool)          # append-time step, outside the timed sample as on the GPU
     dense = w.topk == 0
     n = 0
-    t0 = time.perf_counter()
-    while True:
-        if dense:
-            oracle.attn(w.q, w.pos, pool, n_kv)
-        else:
-            s = oracle.block_scores(w.q, w.pos, r, n_kv, pool.n_valid, nb)
-            ids, cnt = oracle.topk(s.reshape(-1, nb), w.topk)
-            oracle.attn(w.q, w.pos, pool, n_kv, ids=ids.reshape(len(w.pos), n_kv, -1),
-                        counts=cnt.reshape(len(w.pos), n_kv))
-        n += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s:
-            break
+    with one_core():
+        t0 = time.perf_counter()
+        while True:
+            if dense:
+                oracle.attn(w.q, w.pos, pool, n_kv)
+            else:
+                s = oracle.block_scores(w.q, w.pos, r, n_kv, pool.n_valid, nb)
+                ids, cnt = oracle.topk(s.reshape(-1, nb), w.topk)
+                oracle.attn(w.q, w.pos, pool, n_kv, ids=ids.reshape(len(w.pos), n_kv, -1),
+                            counts=cnt.reshape(len(w.pos), n_kv))
+            n += 1
+            el = time.perf_counter() - t0
+            if el >= budget_s:
+                break
     per_layer = el / n
     return {"value": round(layer_bytes / per_layer / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"{n} full {w.name} layers (scores, top-k, attention; FP64, one thread) in {el:.1f} s, "
-                      f"{per_layer * 1e3:.1f} ms per layer", "host_cpus": os.cpu_count()}
+                      f"{per_layer * 1e3:.1f} ms per layer, pinned to one core", "host_cpus": os.cpu_count(),
+            "host_cpu": host_cpu_model()}
 
 
 def cpu_baseline_prompt(w, ops, vis, budget_s):
@@ -700,21 +729,22 @@ def cpu_baseline_prompt(w, ops, vis, budget_s):
     rng = np.random.default_rng(0)
     n_q = w.q.shape[0]
     done_cells, n = 0, 0
-    t0 = time.perf_counter()
-    while True:
-        i, h = int(rng.integers(0, n_q)), int(rng.integers(0, w.n_q_heads))
-        oracle.attn_one(w.q, w.pos, i, h, pool, w.n_kv_heads)
-        done_cells += min(pool.n_valid, int(w.pos[i]) + 1)
-        n += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s:
-            break
+    with one_core():
+        t0 = time.perf_counter()
+        while True:
+            i, h = int(rng.integers(0, n_q)), int(rng.integers(0, w.n_q_heads))
+            oracle.attn_one(w.q, w.pos, i, h, pool, w.n_kv_heads)
+            done_cells += min(pool.n_valid, int(w.pos[i]) + 1)
+            n += 1
+            el = time.perf_counter() - t0
+            if el >= budget_s:
+                break
     per_cell = el / done_cells
     full_s = per_cell * vis * w.n_q_heads
     return {"value": round(ops / full_s / 1e12, 6), "unit": "TOPS", "cores": 1, "kind": "oracle",
             "sample": f"{n} random (query, head) rows of the prompt chunk (FP64 dense attention, one thread) in "
                       f"{el:.1f} s; scaled to the chunk's {vis * w.n_q_heads} (row, cell) pairs: {full_s:.0f} s "
-                      f"per chunk", "host_cpus": os.cpu_count()}
+                      f"per chunk, pinned to one core", "host_cpus": os.cpu_count(), "host_cpu": host_cpu_model()}
 
 
 if __name__ == "__main__":
