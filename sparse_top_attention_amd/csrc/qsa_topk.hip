@@ -3,7 +3,7 @@
 // One workgroup of 64 * NW threads per row (4 waves up to 256 entries, else 16 for qsa_topk and 8 for the fused
 // selection); thread t owns the KPT consecutive entries [t*KPT, t*KPT + KPT) so that the final compaction runs in
 // index order. Scores become order-preserving uint32 keys (-0.0 folded onto +0.0; -inf and a key of 0 mark an
-// ineligible entry). Four passes find the k-th largest key one 8-bit digit at a time, each
+// ineligible entry). Up to four passes find the k-th largest key one 8-bit digit at a time, each
 // with a 256-bin LDS histogram and a workgroup prefix scan over the bins (no serial walk over the bins). Keys
 // above that threshold are all kept; keys equal to it are kept lowest index first until k are taken.
 #include "qsa_internal.h"
@@ -62,97 +62,100 @@ __device__ __forceinline__ void radix_topk(const uint32_t (&key)[KPT], int32_t k
     constexpr int NTH = 64 * NW;
     __shared__ uint32_t hist[2][256];
     __shared__ uint32_t sh_wave[NW];
-    __shared__ uint32_t sh_digit, sh_remaining;
-    __shared__ bool sh_whole;
+    __shared__ uint32_t sh_digit, sh_remaining, sh_kk;
+    __shared__ bool sh_whole, sh_all;
     const int tid = threadIdx.x;
     const int32_t i0 = tid * KPT;
 
-    uint32_t mine = 0;
-#pragma unroll
-    for (int e = 0; e < KPT; e++) mine += key[e] != 0u;
-    uint32_t n_elig;
-    block_exclusive_scan<NW>(mine, sh_wave, n_elig);
-    const uint32_t kk = n_elig < (uint32_t)k ? n_elig : (uint32_t)k;
-
-    uint32_t T, take_eq = 0;
-    if (kk == 0) {
-        T = 0xFFFFFFFFu;  // nothing is above it
-    } else if (kk == n_elig) {
-        T = 0u;           // every eligible key is above it
-    } else {
-        uint32_t prefix = 0, mask = 0, remaining = kk;
-        bool done_early = false;
-        if (tid < 256) hist[0][tid] = 0;
-        __syncthreads();
-        // Two histograms alternate (the next one is cleared while the current one fills), and one wave scans the 256
-        // bins, so a pass costs two barriers.
+    // The first digit pass counts every eligible key, so its histogram total is the eligible count: kk = min(count,
+    // k) comes out of that pass, and when every eligible key is kept (or none exists) no threshold is needed.
+    uint32_t prefix = 0, mask = 0, remaining = 0, kk = 0, T = 0, take_eq = 0;
+    bool settled = false;
+    if (tid < 256) hist[0][tid] = 0;
+    __syncthreads();
+    // Two histograms alternate (the next one is cleared while the current one fills), and one wave scans the 256
+    // bins, so a pass costs two barriers.
 #pragma unroll 1
-        for (int pass = 0; pass < 4; pass++) {
-            const int shift = 24 - 8 * pass;
-            uint32_t *hc = hist[pass & 1];
+    for (int pass = 0; pass < 4; pass++) {
+        const int shift = 24 - 8 * pass;
+        uint32_t *hc = hist[pass & 1];
 #pragma unroll
-            for (int e = 0; e < KPT; e++)
-                if (key[e] != 0u && (key[e] & mask) == prefix) atomicAdd(&hc[(key[e] >> shift) & 255u], 1u);
-            if (tid < 256) hist[(pass + 1) & 1][tid] = 0;
-            __syncthreads();
-            if (tid < 64) {
-                // lane l holds digits 255 - 4l - e (e = 0..3), highest first; cum counts the matching keys whose digit
-                // is at least the current one
-                uint32_t c[4];
+        for (int e = 0; e < KPT; e++)
+            if (key[e] != 0u && (key[e] & mask) == prefix) atomicAdd(&hc[(key[e] >> shift) & 255u], 1u);
+        if (tid < 256) hist[(pass + 1) & 1][tid] = 0;
+        __syncthreads();
+        if (tid < 64) {
+            // lane l holds digits 255 - 4l - e (e = 0..3), highest first; cum counts the matching keys whose digit
+            // is at least the current one
+            uint32_t c[4];
 #pragma unroll
-                for (int e = 0; e < 4; e++) c[e] = hc[255 - 4 * tid - e];
-                const uint32_t lsum = (c[0] + c[1]) + (c[2] + c[3]);
-                const uint32_t incl = wave_inclusive_scan(lsum);
-                uint32_t cum = incl - lsum;
-#pragma unroll
-                for (int e = 0; e < 4; e++) {
-                    const uint32_t before = cum;
-                    cum += c[e];
-                    if (cum >= remaining && before < remaining) {
-                        sh_digit = 255u - 4u * (uint32_t)tid - (uint32_t)e;
-                        sh_remaining = remaining - before;
-                        sh_whole = (remaining - before) == c[e];   // the whole bin is taken
-                    }
+            for (int e = 0; e < 4; e++) c[e] = hc[255 - 4 * tid - e];
+            const uint32_t lsum = (c[0] + c[1]) + (c[2] + c[3]);
+            const uint32_t incl = wave_inclusive_scan(lsum);
+            uint32_t rem = remaining;
+            if (pass == 0) {
+                const uint32_t n_elig = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+                rem = n_elig < (uint32_t)k ? n_elig : (uint32_t)k;
+                if (tid == 0) {
+                    sh_kk = rem;
+                    sh_all = rem == n_elig;
                 }
             }
-            __syncthreads();
-            prefix |= sh_digit << shift;
-            mask |= 255u << shift;
-            remaining = sh_remaining;
-            if (sh_whole) {  // every key with this prefix is kept: keep all keys >= prefix, no tie to break
-                done_early = true;
+            uint32_t cum = incl - lsum;
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                const uint32_t before = cum;
+                cum += c[e];
+                if (cum >= rem && before < rem) {
+                    sh_digit = 255u - 4u * (uint32_t)tid - (uint32_t)e;
+                    sh_remaining = rem - before;
+                    sh_whole = (rem - before) == c[e];   // the whole bin is taken
+                }
+            }
+        }
+        __syncthreads();
+        if (pass == 0) {
+            kk = sh_kk;
+            if (sh_all) {   // keep every eligible key: nothing (kk = 0) or everything is above the threshold
+                T = kk == 0 ? 0xFFFFFFFFu : 0u;
+                settled = true;
                 break;
             }
         }
-        if (done_early) {
+        prefix |= sh_digit << shift;
+        mask |= 255u << shift;
+        remaining = sh_remaining;
+        if (sh_whole) {  // every key with this prefix is kept: keep all keys >= prefix, no tie to break
             T = prefix == 0u ? 0u : prefix - 1u;
-            take_eq = 0;
-        } else {
-            T = prefix;
-            take_eq = remaining;
+            settled = true;
+            break;
         }
     }
+    if (!settled) {
+        T = prefix;
+        take_eq = remaining;
+    }
 
-    // compaction in index order: keys > T, then the first take_eq keys == T
-    uint32_t n_eq = 0;
-#pragma unroll
-    for (int e = 0; e < KPT; e++) n_eq += (key[e] != 0u && key[e] == T);
-    uint32_t tot_eq;
-    uint32_t eq_rank = block_exclusive_scan<NW>(n_eq, sh_wave, tot_eq);
-    bool sel[KPT];
-    uint32_t n_sel = 0;
+    // compaction in index order: every key > T, then the first take_eq keys == T. One scan of the packed per-thread
+    // counts (greater << 16 | equal; a row has at most 16,384 keys, so neither field carries) gives each thread the
+    // number of greater and of equal keys before its own; the position of a kept key is the greater keys before it
+    // plus the kept equal keys before it.
+    uint32_t n_gt = 0, n_eq = 0;
 #pragma unroll
     for (int e = 0; e < KPT; e++) {
-        const bool eq = key[e] != 0u && key[e] == T;
-        sel[e] = (key[e] != 0u && key[e] > T) || (eq && eq_rank < take_eq);
-        eq_rank += eq;
-        n_sel += sel[e];
+        n_gt += key[e] != 0u && key[e] > T;
+        n_eq += key[e] != 0u && key[e] == T;
     }
-    uint32_t tot_sel;
-    uint32_t at = block_exclusive_scan<NW>(n_sel, sh_wave, tot_sel);
+    uint32_t tot;
+    const uint32_t pre = block_exclusive_scan<NW>((n_gt << 16) | n_eq, sh_wave, tot);
+    uint32_t gt_b = pre >> 16, eq_b = pre & 0xFFFFu;
 #pragma unroll
-    for (int e = 0; e < KPT; e++)
-        if (sel[e]) dst[at++] = i0 + e;
+    for (int e = 0; e < KPT; e++) {
+        const bool gt = key[e] != 0u && key[e] > T, eq = key[e] != 0u && key[e] == T;
+        if (gt || (eq && eq_b < take_eq)) dst[gt_b + (eq_b < take_eq ? eq_b : take_eq)] = i0 + e;
+        gt_b += gt;
+        eq_b += eq;
+    }
     for (int32_t jj = (int32_t)kk + tid; jj < k; jj += NTH) dst[jj] = -1;
     if (tid == 0) *count = (int32_t)kk;
 }
