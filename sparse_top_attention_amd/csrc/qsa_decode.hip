@@ -318,7 +318,7 @@ __global__ __launch_bounds__(64 * CW) void attn_chunk_kernel(const ChunkArgs a)
     __shared__ __align__(16) int8_t sv[CW][PC * RB]; // the wave's V piece: [cell][RB], chunk c of row r at c ^ (r & SWZ)
     __shared__ __align__(16) float sp[CW][PC][NG][GP];
     __shared__ float sm[CW][G], sl[CW][G];
-    __shared__ float so[CW][G][D];
+    __shared__ __align__(16) float so[CW][G][D];
     __shared__ __align__(16) float sq[G * D];        // the G q rows of (row i, KV head g)
     const int tid = threadIdx.x, lane = tid % 64;
     const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
@@ -612,11 +612,11 @@ __global__ __launch_bounds__(64 * CW) void attn_chunk_kernel(const ChunkArgs a)
     __syncthreads();
 
     // combine the wpc waves of each chunk: M = max m_w, out = sum e^(m_w - M) o_w (waves without a cell have
-    // m_w = -inf). Every thread reads all the LDS values it needs at once and then combines them without branches;
-    // the (m, l, empty) of the chunks' G heads are written by the first cpw * G threads.
-    constexpr int EB = 4;   // output elements per thread per round of LDS reads
-    constexpr int n_out = cpw * G * D;
-    constexpr int ROUNDS = (n_out + 64 * CW * EB - 1) / (64 * CW * EB);
+    // m_w = -inf). A thread takes four consecutive dims of one (chunk, head), so their weights are computed once and
+    // the values move as 16-byte LDS reads and stores; every LDS value a round needs is read before the arithmetic,
+    // which runs without branches. The (m, l, empty) of the chunks' G heads are written by the first cpw * G threads.
+    constexpr int n_out4 = cpw * G * D / 4;   // float4 outputs
+    constexpr int ROUNDS = (n_out4 + 64 * CW - 1) / (64 * CW);
     float hm[CW], hl[CW];
     {
         const int cc = tid < cpw * G ? tid / G : 0, h = tid < cpw * G ? tid % G : 0;
@@ -640,30 +640,35 @@ __global__ __launch_bounds__(64 * CW) void attn_chunk_kernel(const ChunkArgs a)
         return M != -INFINITY ? num : 0.f;
     };
 #pragma unroll
-    for (int e0 = 0; e0 < ROUNDS * EB; e0 += EB) {
-        float smv[EB][CW], sov[EB][CW];
+    for (int r0 = 0; r0 < ROUNDS; r0++) {
+        const int q4 = tid + 64 * CW * r0;
+        const int qq = min(q4, n_out4 - 1);
+        const int cc = qq / (G * D / 4), rem4 = qq % (G * D / 4), h = rem4 / (D / 4), d4 = rem4 % (D / 4);
+        float mw[CW];
+        float4 ow[CW];
 #pragma unroll
-        for (int e = 0; e < EB; e++) {
-            if ((e0 + e) * 64 * CW >= n_out) break;
-            const int idx = min(tid + 64 * CW * (e0 + e), n_out - 1);
-            const int cc = idx / (G * D), rem2 = idx % (G * D), h = rem2 / D, d = rem2 % D;
-#pragma unroll
-            for (int k = 0; k < CW; k++) {
-                const int w = min(cc * wpc + k, CW - 1);   // k >= wpc is masked
-                smv[e][k] = k < wpc ? sm[w][h] : -INFINITY;
-                sov[e][k] = so[w][h][d];
-            }
+        for (int k = 0; k < CW; k++) {
+            const int w = min(cc * wpc + k, CW - 1);   // k >= wpc is masked
+            mw[k] = k < wpc ? sm[w][h] : -INFINITY;
+            ow[k] = *reinterpret_cast<const float4 *>(&so[w][h][4 * d4]);
         }
+        float M = mw[0];
 #pragma unroll
-        for (int e = 0; e < EB; e++) {
-            if ((e0 + e) * 64 * CW >= n_out) break;
-            const int idx = tid + 64 * CW * (e0 + e);
-            const int cc = idx / (G * D), rem2 = idx % (G * D);
-            float M;
-            const float num = combine(smv[e], sov[e], M);
-            if (idx < n_out && j0c + cc < a.n_chunks)
-                a.o_out[(((int64_t)i * a.n_qh + h0 + rem2 / D) * a.max_chunks + j0c + cc) * D + rem2 % D] = num;
+        for (int k = 1; k < CW; k++) M = fmaxf(M, mw[k]);
+        float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int k = 0; k < CW; k++) {
+            const float wk = __builtin_amdgcn_exp2f(mw[k] - M);
+            const bool live = mw[k] != -INFINITY;
+            num.x = live ? fmaf(wk, ow[k].x, num.x) : num.x;
+            num.y = live ? fmaf(wk, ow[k].y, num.y) : num.y;
+            num.z = live ? fmaf(wk, ow[k].z, num.z) : num.z;
+            num.w = live ? fmaf(wk, ow[k].w, num.w) : num.w;
         }
+        if (M == -INFINITY) num = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (q4 < n_out4 && j0c + cc < a.n_chunks)
+            *reinterpret_cast<float4 *>(
+                a.o_out + (((int64_t)i * a.n_qh + h0 + h) * a.max_chunks + j0c + cc) * D + 4 * d4) = num;
     }
     if (tid < cpw * G && j0c + tid / G < a.n_chunks) {
         float M;
