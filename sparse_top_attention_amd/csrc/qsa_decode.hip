@@ -5,8 +5,9 @@
 //
 // Lane layout shared by the index and chunk kernels ("cell x slice"): a cell's D dims are cut into D/16 slices of
 // 16 dims (one 16-byte load of int8 codes), so a wave covers 64 / (D/16) cells per step; lane = cell_slot * LPC +
-// slice. A slice never straddles a 64-dim scale group. Per-cell dot products are finished by a DPP sum over the
-// LPC lanes of the cell, after which every lane of the cell holds the same logit.
+// slice. A slice never straddles a 64-dim scale group. The index kernel finishes its per-cell sums with a DPP sum
+// over the LPC lanes of the cell; the chunk kernel finishes its G per-cell dot products with a reduce-scatter over
+// those lanes, so that each (cell, head) logit ends in one lane.
 #include "qsa_internal.h"
 
 #include <math.h>
@@ -285,12 +286,13 @@ struct ChunkArgs {
 // are cut into pieces of PC cells; its sub-wave s takes pieces s, s + wpc, ... and keeps a running (max, sum,
 // output) per head over them.
 //
-// q . k runs in the "cell x slice" layout (LPC lanes per cell, 16 dims each; a 3-4 step DPP sum finishes each
-// logit, after which all lanes of the cell hold it). p . v runs in a "lane owns dims" layout: the piece's V codes go
-// from HBM straight into the wave's LDS (global_load_lds, 16-byte chunks swizzled by cell), and ds_read_b64_tr_b8
-// hands each lane 8 cells of one dim per read; p * v_scale per (cell, scale group, head) is written to LDS by the
-// q . k lanes and read back as a broadcast. Each lane then owns D/64 output dims of every head, so nothing is summed
-// across lanes at the end; the CW waves are combined through LDS with a log-sum-exp rescale.
+// q . k runs in the "cell x slice" layout (LPC lanes per cell, 16 dims each), and a reduce-scatter over the cell's
+// lanes leaves the logit of head s in the cell's lane s, so the softmax work runs once per (cell, head). p . v runs
+// in a "lane owns dims" layout: the piece's V codes go from HBM straight into the wave's LDS (global_load_lds,
+// 16-byte chunks swizzled by cell), and ds_read_b64_tr_b8 hands each lane 8 cells of one dim per read; p * v_scale
+// per (cell, scale group, head) is written to LDS by the head's lane of the cell and read back as a broadcast. Each
+// lane then owns D/64 output dims of every head, so nothing is summed across lanes at the end; the waves of a chunk
+// are combined through LDS with a log-sum-exp rescale (a one-wave chunk stores its partial directly).
 constexpr int CW = 4;
 
 //
