@@ -690,19 +690,24 @@ __global__ __launch_bounds__(64 * CW) void attn_chunk_kernel(const ChunkArgs a)
 // rows (lanes own D/64 consecutive dims) are loaded U chunks at a time with every load in flight before the first
 // use, and are added in chunk order with the weight read from the chunk's lane. Empty chunks are skipped by select,
 // never multiplied (their l and o may hold anything). The waves' parts are combined through LDS.
-template <int D, int NW, int U>
+template <int D, int NW, int U, int DS>
 __global__ __launch_bounds__(64 * NW) void attn_merge_kernel(const float *__restrict__ m, const float *__restrict__ l,
                                                          const float *__restrict__ o, const uint8_t *__restrict__ em,
                                                          int32_t max_chunks, int32_t n_chunks,
                                                          const int32_t *__restrict__ n_active, int32_t n_qh,
                                                          float *__restrict__ out, float *__restrict__ lse)
 {
-    constexpr int VPL = D / 64;
+    constexpr int DW = D / DS;                    // dims of this workgroup's slice of the row
+    static_assert(DW % 64 == 0, "lanes own whole dims");
+    constexpr int VPL = DW / 64;
     __shared__ float sM[NW], sL[NW];
-    __shared__ float sO[NW][D];
+    __shared__ float sO[NW][DW];
     const int tid = threadIdx.x, lane = tid % 64;
     const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
     const int32_t row = blockIdx.x;               // = i * n_qh + h
+    const int32_t dsl = blockIdx.y;               // dim slice: dims [dsl * DW, dsl * DW + DW)
+    o += dsl * DW;
+    out += dsl * DW;
     const int32_t i = row / n_qh;
     int32_t na = n_active ? n_active[i] : n_chunks;
     na = na < 0 ? 0 : (na > n_chunks ? n_chunks : na);
@@ -805,7 +810,7 @@ __global__ __launch_bounds__(64 * NW) void attn_merge_kernel(const float *__rest
             for (int w = 1; w < NW; w++) num += sO[w][d];
             out[(int64_t)row * D + d] = none ? 0.f : num / Lt;
         }
-        if (lse && lane == 0) lse[row] = none ? -INFINITY : M + logf(Lt);
+        if (lse && lane == 0 && dsl == 0) lse[row] = none ? -INFINITY : M + logf(Lt);
     }
 }
 
@@ -998,16 +1003,18 @@ qsa_status qsa::merge_launch(const float *m, const float *l, const float *o, con
                              int32_t n_chunks, const int32_t *n_active, int32_t n_rows, int32_t n_qh,
                              int32_t head_dim, float *out, float *lse, hipStream_t s)
 {
-    dim3 grid((uint32_t)n_rows * (uint32_t)n_qh);
-    // a few chunks: 4 waves, 8 rows in flight each; many (a dense window): 16 waves, 16 rows in flight each
+    const uint32_t rows = (uint32_t)n_rows * (uint32_t)n_qh;
+    // a few chunks: 4 waves, 8 rows in flight each, one workgroup per (row, head); many (a dense window): 16 waves,
+    // 16 rows in flight each, and the head's dims split over D/64 workgroups, so more CUs stream the o rows (each
+    // re-reads the chunks' m, l and empty marks)
 #define QSA_MERGE(DD)                                                                                              \
     do {                                                                                                           \
         if (n_chunks <= 64)                                                                                        \
-            attn_merge_kernel<DD, 4, 8><<<grid, 256, 0, s>>>(m, l, o, empty, max_chunks, n_chunks, n_active, n_qh, \
-                                                             out, lse);                                           \
+            attn_merge_kernel<DD, 4, 8, 1><<<dim3(rows, 1), 256, 0, s>>>(m, l, o, empty, max_chunks, n_chunks,      \
+                                                                       n_active, n_qh, out, lse);                 \
         else                                                                                                       \
-            attn_merge_kernel<DD, 16, 16><<<grid, 1024, 0, s>>>(m, l, o, empty, max_chunks, n_chunks, n_active,     \
-                                                                n_qh, out, lse);                                  \
+            attn_merge_kernel<DD, 16, 16, DD / 64><<<dim3(rows, DD / 64), 1024, 0, s>>>(                          \
+                m, l, o, empty, max_chunks, n_chunks, n_active, n_qh, out, lse);                                  \
     } while (0)
     switch (head_dim) {
     case 64: QSA_MERGE(64); break;
