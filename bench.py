@@ -431,6 +431,13 @@ def bench_other_decode(copies=32, bw_chunks=32):
 
     def chunk(c):
         qsa.qsa_attn_chunk(q, pos, sets[c], dims, part, S, w.sm_scale, row_pool=row_pool, ids=ids, counts=counts)
+
+    # the layer's selection: with rows this wide it is the score launch then the top-k launch over a score buffer
+    sel_scores = torch.empty(n_rows, n_kv, nb, dtype=torch.float32, device=dev)
+
+    def select(c):
+        qsa.qsa_decode_select(q, pos, sets[c], dims, nb, w.topk, ids, counts, scores=sel_scores, row_pool=row_pool)
+    t_select = avg_us(select, copies)
     t_layer = avg_us(layer, copies)
     t_chunk = avg_us(chunk, copies)
     ids_h, counts_h = ids.cpu().numpy(), counts.cpu().numpy()
@@ -440,7 +447,8 @@ def bench_other_decode(copies=32, bw_chunks=32):
         cells += union_cells(ids_h[rows], counts_h[rows], w.pos[rows], w.pools[sidx].n_valid, n_kv)
     cb = cells * KV_BYTES_PER_CELL_HEAD + w.q.nbytes
     gbs = cb / (t_chunk * 1e-6) / 1e9
-    res["batch_window"] = {"us_per_layer": round(t_layer, 3), "attn_chunk_us": round(t_chunk, 3),
+    res["batch_window"] = {"us_per_layer": round(t_layer, 3), "select_us": round(t_select, 3),
+                           "attn_chunk_us": round(t_chunk, 3),
                            "chunk_bytes_per_launch": int(cb), "attn_chunk_GBs": round(gbs, 1),
                            "frac_of_hbm": round(gbs / HBM_PEAK_GBS, 4), "chunks": S}
     del sets, base

@@ -258,6 +258,74 @@ __global__ __launch_bounds__(64) void block_scores_kernel(const float *__restric
     }
 }
 
+// The score rows of a whole decode window in one launch, for the two-launch selection of wide rows (the fused kernel
+// streams a row's index through one CU): the block-score kernel's arithmetic, in the same order, over every pool of
+// the window. Workgroup (block range, g, p) scores the rows whose row_pool is p against pool p's index rows; pool 0's
+// workgroups also write -inf rows for the rows whose pool index is out of range, which then select nothing.
+template <int D>
+__global__ __launch_bounds__(64) void select_scores_kernel(const SelectArgs a, int32_t n_rows)
+{
+    constexpr int LPB = D / 8, BPS = 64 / LPB, NSTEP = 4;
+    const int lane = threadIdx.x, rb = lane / LPB, s = lane % LPB;
+    const int32_t g = blockIdx.y, pidx = blockIdx.z;
+    const PoolArg P = a.pools[pidx];
+    const int32_t stride = (P.capacity + QSA_BLOCK - 1) / QSA_BLOCK;
+    const int32_t bw = blockIdx.x * (BPS * NSTEP);
+    const int32_t n_live = min(a.width, (int32_t)(((int64_t)P.n_valid + QSA_BLOCK - 1) / QSA_BLOCK));
+    float rv[NSTEP][8];
+    int32_t bidx[NSTEP];
+#pragma unroll
+    for (int st = 0; st < NSTEP; st++) {
+        const int32_t b = bw + st * BPS + rb;
+        bidx[st] = b;
+        const bool live = b < n_live;
+        const float4 *src =
+            reinterpret_cast<const float4 *>(P.index + ((int64_t)g * stride + (live ? b : 0)) * D + 8 * s);
+        const float4 u = src[0], w = src[1];
+        rv[st][0] = u.x; rv[st][1] = u.y; rv[st][2] = u.z; rv[st][3] = u.w;
+        rv[st][4] = w.x; rv[st][5] = w.y; rv[st][6] = w.z; rv[st][7] = w.w;
+#pragma unroll
+        for (int e = 0; e < 8; e++) rv[st][e] = live ? rv[st][e] : 0.f;
+    }
+    for (int32_t i = 0; i < n_rows; i++) {
+        const int32_t rp = a.row_pool ? a.row_pool[i] : 0;
+        const bool bad = rp < 0 || rp >= a.n_pools;
+        if (!(rp == pidx || (bad && pidx == 0))) continue;   // wave-uniform
+        // the row's G q heads of g summed in head order (heads past G re-read the last one and are not added)
+        float qt[8];
+#pragma unroll
+        for (int e = 0; e < 8; e++) qt[e] = 0.f;
+        float4 u[8], w[8];
+#pragma unroll
+        for (int h = 0; h < 8; h++) {
+            const float4 *src = reinterpret_cast<const float4 *>(
+                a.q + ((int64_t)i * a.n_qh + g * a.G + (h < a.G ? h : a.G - 1)) * D + 8 * s);
+            u[h] = src[0];
+            w[h] = src[1];
+        }
+#pragma unroll
+        for (int h = 0; h < 8; h++) {
+            if (h < a.G) {
+                qt[0] += u[h].x; qt[1] += u[h].y; qt[2] += u[h].z; qt[3] += u[h].w;
+                qt[4] += w[h].x; qt[5] += w[h].y; qt[6] += w[h].z; qt[7] += w[h].w;
+            }
+        }
+        const int32_t p = a.pos[i];
+#pragma unroll
+        for (int st = 0; st < NSTEP; st++) {
+            float dot = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; e++) dot = fmaf(qt[e], rv[st][e], dot);
+            dot = group_sum<LPB>(dot);
+            const int32_t b = bidx[st];
+            const int64_t first = (int64_t)b * QSA_BLOCK;
+            if (s == 0 && b < a.width)
+                a.scores[((int64_t)i * a.n_kv + g) * a.width + b] =
+                    (!bad && first <= p && first < P.n_valid) ? dot : -INFINITY;
+        }
+    }
+}
+
 // ---------------------------------------------------------------------------------------- chunk attention
 struct ChunkArgs {
     const float *q;
@@ -878,6 +946,19 @@ extern "C" qsa_status qsa_kv_append(const qsa_pool *pools, int32_t n_pools, cons
     return launch_status();
 }
 
+qsa_status qsa::select_scores_launch(const SelectArgs &a, int32_t n_rows, int32_t n_kv, int32_t head_dim,
+                                     hipStream_t s)
+{
+    const int32_t per_wave = (64 / (head_dim / 8)) * 4;
+    dim3 grid(ceil_div(a.width, per_wave), n_kv, a.n_pools);
+    switch (head_dim) {
+    case 64: select_scores_kernel<64><<<grid, 64, 0, s>>>(a, n_rows); break;
+    case 128: select_scores_kernel<128><<<grid, 64, 0, s>>>(a, n_rows); break;
+    default: select_scores_kernel<256><<<grid, 64, 0, s>>>(a, n_rows); break;
+    }
+    return launch_status();
+}
+
 extern "C" qsa_status qsa_block_scores(const float *q, const int32_t *pos, int32_t n_rows, const qsa_pool *pool,
                                        qsa_dims dims, int32_t n_blocks, float *scores, qsa_stream_t stream)
 {
@@ -1135,6 +1216,11 @@ extern "C" qsa_status qsa_decode_layer(const float *q, const int32_t *pos, int32
     sa.ids = ids ? ids : reinterpret_cast<int32_t *>(base + lay.ids);
     sa.counts = counts ? counts : reinterpret_cast<int32_t *>(base + lay.counts);
     sa.scores = scores;
+    // Without a caller's score buffer, wide rows still take the two-launch selection when their score rows fit in
+    // the chunk partials' region, which the chunk kernel writes only after the selection has read them.
+    if (!scores && select_splits(sa) &&
+        (size_t)n_rows * dims.n_kv_heads * n_blocks * sizeof(float) <= lay.ids - lay.m)
+        sa.scores = reinterpret_cast<float *>(base + lay.m);
     if ((st = select_launch(sa, n_rows, dims.n_kv_heads, dims.head_dim, s)) != QSA_OK) return st;
 
     ChunkArgs a{};

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "qsa.h"
 
 #define QSA_BLOCK 64  // cells per selection block
@@ -89,6 +91,20 @@ struct SelectArgs {
     float *scores;       // optional [n_rows][n_kv][width]
 };
 qsa_status select_launch(const SelectArgs &a, int32_t n_rows, int32_t n_kv, int32_t head_dim, hipStream_t s);
+// The score rows alone (all pools, one launch) and the radix top-k over score rows: the two launches that replace the
+// fused selection kernel when a score buffer is at hand and some pool has more than SELECT_SPLIT_WIDTH live blocks
+// (blocks below both the row width and the pool's valid cells; the fused kernel loads no others).
+constexpr int32_t SELECT_SPLIT_WIDTH = 256;
+inline bool select_splits(const SelectArgs &a)
+{
+    int32_t live = 0;
+    for (int32_t p = 0; p < a.n_pools; p++)
+        live = std::max(live, std::min(a.width, ceil_div(a.pools[p].n_valid, QSA_BLOCK)));
+    return live > SELECT_SPLIT_WIDTH;
+}
+qsa_status select_scores_launch(const SelectArgs &a, int32_t n_rows, int32_t n_kv, int32_t head_dim, hipStream_t s);
+qsa_status topk_launch(const float *scores, int32_t n_rows, int32_t width, int32_t k, int32_t *ids, int32_t *counts,
+                       hipStream_t s);
 
 // Launches the log-sum-exp merge of chunk partials laid out [n_rows][n_qh][max_chunks] (+[head_dim] for o).
 qsa_status merge_launch(const float *m, const float *l, const float *o, const uint8_t *empty, int32_t max_chunks,

@@ -289,8 +289,31 @@ __global__ __launch_bounds__(64 * NW) void select_kernel(const SelectArgs a)
 
 using namespace qsa;
 
+qsa_status qsa::topk_launch(const float *scores, int32_t n_rows, int32_t width, int32_t k, int32_t *ids,
+                            int32_t *counts, hipStream_t s)
+{
+    dim3 grid(n_rows);
+    const int kpt = (width + 1023) / 1024;
+#define QSA_TOPK(K, W) topk_kernel<K, W><<<grid, 64 * W, 0, s>>>(scores, width, k, ids, counts)
+    if (width <= 256) QSA_TOPK(1, 4);
+    else if (kpt <= 1) QSA_TOPK(1, 16);
+    else if (kpt <= 2) QSA_TOPK(2, 16);
+    else if (kpt <= 4) QSA_TOPK(4, 16);
+    else if (kpt <= 8) QSA_TOPK(8, 16);
+    else QSA_TOPK(16, 16);
+#undef QSA_TOPK
+    return launch_status();
+}
+
 qsa_status qsa::select_launch(const SelectArgs &a, int32_t n_rows, int32_t n_kv, int32_t head_dim, hipStream_t s)
 {
+    if (a.scores && select_splits(a)) {
+        // wide rows: the score rows in one launch spread over many CUs, then the top-k over them (the fused kernel
+        // would stream each row's index rows through a single CU)
+        const qsa_status st = select_scores_launch(a, n_rows, n_kv, head_dim, s);
+        if (st != QSA_OK) return st;
+        return topk_launch(a.scores, n_rows * n_kv, a.width, a.k, a.ids, a.counts, s);
+    }
     dim3 grid(n_kv, n_rows);
     // up to 256 columns: 4 waves, one column per thread; wider rows: 8 waves, KPT = 1..32 columns per thread
     const int kpt = (a.width + 511) / 512;
@@ -330,16 +353,5 @@ extern "C" qsa_status qsa_topk(const float *scores, int32_t n_rows, int32_t widt
     if (k < 1 || k > width) return QSA_ERR_RANGE;
     if (width > 256 * 64) return QSA_ERR_UNSUPPORTED;
     if (n_rows == 0) return QSA_OK;
-    hipStream_t s = (hipStream_t)stream;
-    dim3 grid(n_rows);
-    const int kpt = (width + 1023) / 1024;
-#define QSA_TOPK(K, W) topk_kernel<K, W><<<grid, 64 * W, 0, s>>>(scores, width, k, ids, counts)
-    if (width <= 256) QSA_TOPK(1, 4);
-    else if (kpt <= 1) QSA_TOPK(1, 16);
-    else if (kpt <= 2) QSA_TOPK(2, 16);
-    else if (kpt <= 4) QSA_TOPK(4, 16);
-    else if (kpt <= 8) QSA_TOPK(8, 16);
-    else QSA_TOPK(16, 16);
-#undef QSA_TOPK
-    return launch_status();
+    return topk_launch(scores, n_rows, width, k, ids, counts, (hipStream_t)stream);
 }

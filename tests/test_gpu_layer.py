@@ -14,7 +14,7 @@ pytestmark = pytest.mark.gpu
 TOL = 1e-5
 
 
-def run_layer(w, pdevs, dims, n_chunks, row_pool=None, nb=None, scratch=None, q=None):
+def run_layer(w, pdevs, dims, n_chunks, row_pool=None, nb=None, scratch=None, q=None, with_scores=True):
     n_rows = w.q.shape[0]
     nb = nb or -(-w.pools[0].n_valid // BLOCK)
     q = dev(w.q) if q is None else q
@@ -27,9 +27,10 @@ def run_layer(w, pdevs, dims, n_chunks, row_pool=None, nb=None, scratch=None, q=
         scratch = torch.empty(qsa.qsa_decode_layer_scratch_bytes(n_rows, dims, w.topk, n_chunks), dtype=torch.uint8,
                               device="cuda")
     qsa.qsa_decode_layer(q, dev(w.pos), pdevs, dims, nb, w.topk, n_chunks, out, lse, sm_scale=w.sm_scale,
-                         row_pool=row_pool, scores=scores, ids=ids, counts=counts, scratch=scratch)
+                         row_pool=row_pool, scores=scores if with_scores else None, ids=ids, counts=counts,
+                         scratch=scratch)
     torch.cuda.synchronize()
-    return dict(scores=scores.cpu().numpy(), ids=ids.cpu().numpy(), counts=counts.cpu().numpy(),
+    return dict(scores=scores.cpu().numpy() if with_scores else None, ids=ids.cpu().numpy(), counts=counts.cpu().numpy(),
                 out=out.cpu().numpy(), lse=lse.cpu().numpy())
 
 
@@ -82,6 +83,40 @@ def test_layer_batch_window_two_pools(S):
         rows = slice(2 * sidx, 2 * sidx + 2)
         sub = {k: v[rows] for k, v in got.items()}
         _check_end_to_end(w, sub, pool=w.pools[sidx], rows=rows)
+
+
+def test_wide_rows_split_selection_matches_fused():
+    """Rows of 1,024 blocks over two pools, one row with an out-of-range pool index: the selection through a score
+    buffer (score rows in one launch, then the top-k) picks the ids and counts of the fused one-launch selection, and
+    the layer gives the same bits with or without a caller's score buffer."""
+    w = synth.workload("batch_window")
+    dims = dims_of(w)
+    pdevs = [build_index(to_device(pl), dims) for pl in w.pools]
+    rp = w.row_pool.copy()
+    rp[1] = 7
+    rpd = dev(rp)
+    nb = -(-w.pools[0].n_valid // BLOCK)
+    assert nb > 256
+    q, pos = dev(w.q), dev(w.pos)
+    n_rows = w.q.shape[0]
+    res = []
+    for with_scores in (False, True):
+        s = torch.full((n_rows, dims.n_kv_heads, nb), float("nan"), dtype=torch.float32, device="cuda")
+        i = torch.empty(n_rows, dims.n_kv_heads, w.topk, dtype=torch.int32, device="cuda")
+        c = torch.empty(n_rows, dims.n_kv_heads, dtype=torch.int32, device="cuda")
+        qsa.qsa_decode_select(q, pos, pdevs, dims, nb, w.topk, i, c, row_pool=rpd, scores=s if with_scores else None)
+        torch.cuda.synchronize()
+        res.append((i.cpu().numpy(), c.cpu().numpy(), s.cpu().numpy()))
+    assert np.array_equal(res[0][0], res[1][0]) and np.array_equal(res[0][1], res[1][1])
+    assert np.all(res[1][1][1] == 0) and np.all(np.isneginf(res[1][2][1]))
+    # the split path's ids: the oracle's top-k of its own fp32 score rows
+    ids2, cnt2 = oracle.topk(res[1][2].astype(np.float64).reshape(-1, nb), w.topk)
+    assert np.array_equal(res[1][0].reshape(-1, w.topk), ids2) and np.array_equal(res[1][1].reshape(-1), cnt2)
+    with_buf = run_layer(w, pdevs, dims, 32, row_pool=rpd)
+    without = run_layer(w, pdevs, dims, 32, row_pool=rpd, with_scores=False)
+    for key in ("ids", "counts", "out", "lse"):
+        assert np.array_equal(with_buf[key], without[key]), key
+    assert np.array_equal(with_buf["ids"], res[1][0])
 
 
 def test_layer_verify_window_four_slots_four_chunks():
