@@ -61,6 +61,7 @@ GOOD = D(24, 4, 128, 64)
 
 @pytest.mark.parametrize("dims,expect", [
     (D(24, 4, 96, 64), -3),    # head_dim not supported
+    (D(24, 4, 192, 64), -3),   # 64-dim groups, but 12 lanes per cell: not supported
     (D(24, 4, 128, 32), -3),   # block size not 64
     (D(24, 5, 128, 64), -2),   # q heads not a multiple of KV heads
     (D(40, 4, 128, 64), -3),   # more than 8 q heads per KV head
