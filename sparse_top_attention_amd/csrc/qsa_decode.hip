@@ -1,7 +1,8 @@
 // Decode-path kernels of libqsa for gfx950: block index, block scores, split-K chunk attention and the
-// log-sum-exp merge. All four stream int8 codes / fp32 rows from HBM with 16-byte coalesced loads and use the
-// VALU only (no matrix cores): per cell the work is a few hundred FMAs against 272 bytes, so HBM and the fp32 VALU
-// are the ceilings.
+// log-sum-exp merge. All four stream int8 codes / fp32 rows from HBM with 16-byte coalesced loads; per cell the
+// work is a few hundred FMAs against 272 bytes, so HBM and the fp32 VALU are the ceilings. The chunk kernel's p . v
+// product runs on the matrix cores (fp16 MFMA with exact V codes and a two-term split of p * v_scale) for 4 to 6 q
+// heads per KV head at d = 128, on the VALU otherwise.
 //
 // Lane layout shared by the index and chunk kernels ("cell x slice"): a cell's D dims are cut into D/16 slices of
 // 16 dims (one 16-byte load of int8 codes), so a wave covers 64 / (D/16) cells per step; lane = cell_slot * LPC +
@@ -28,6 +29,35 @@ __device__ __forceinline__ void unpack16(const int4 w, float (&x)[16])
         x[4 * j + 2] = sbyte_f<2>(ws[j]);
         x[4 * j + 3] = sbyte_f<3>(ws[j]);
     }
+}
+
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef float f4v __attribute__((ext_vector_type(4)));
+
+// Eight signed int8 codes (two dwords, byte j of the pair = element j) as exact fp16: the byte b + 128 is put under
+// the fp16 exponent of 1024 (0x64 high byte, spacing 1), giving 1024 + 128 + b, and 1152 is subtracted.
+__device__ __forceinline__ h8 codes_h8(const v2i w)
+{
+    h8 r;
+    const h2 bias = {(_Float16)-1152.0f, (_Float16)-1152.0f};
+#pragma unroll
+    for (int q = 0; q < 2; q++) {
+        const uint32_t u = (uint32_t)w[q] ^ 0x80808080u;
+        const h2 a = __builtin_bit_cast(h2, __builtin_amdgcn_perm(0x64646464u, u, 0x04010400u)) + bias;
+        const h2 b = __builtin_bit_cast(h2, __builtin_amdgcn_perm(0x64646464u, u, 0x04030402u)) + bias;
+        r[4 * q] = a[0]; r[4 * q + 1] = a[1]; r[4 * q + 2] = b[0]; r[4 * q + 3] = b[1];
+    }
+    return r;
+}
+
+// x = hi + lo with hi, lo fp16 (22 significant bits): hi is x with its float mantissa cut to 10 bits (exact in fp16
+// when |x| is in fp16's normal range), lo the exact remainder rounded to fp16.
+__device__ __forceinline__ void split_h2(const float x, _Float16 &hi, _Float16 &lo)
+{
+    const float xh = __uint_as_float(__float_as_uint(x) & 0xFFFFE000u);
+    hi = (_Float16)xh;
+    lo = (_Float16)(x - xh);
 }
 
 // Reduce-scatter over the LPC lanes of a cell (LPC = 4, 8 or 16, lane bits = s): every lane enters with NV partial
@@ -359,8 +389,10 @@ struct ChunkArgs {
 // in a "lane owns dims" layout: the piece's V codes go from HBM straight into the wave's LDS (global_load_lds,
 // 16-byte chunks swizzled by cell), and ds_read_b64_tr_b8 hands each lane 8 cells of one dim per read; p * v_scale
 // per (cell, scale group, head) is written to LDS by the head's lane of the cell and read back as a broadcast. Each
-// lane then owns D/64 output dims of every head, so nothing is summed across lanes at the end; the waves of a chunk
-// are combined through LDS with a log-sum-exp rescale (a one-wave chunk stores its partial directly).
+// lane then owns D/64 output dims of every head, so nothing is summed across lanes at the end. In the MFMA form
+// (MPV below) the same transposing reads are the B operands, the p * v_scale columns the A operands, and a lane owns
+// one dim of 4 heads per 16-dim tile. The waves of a chunk are combined through LDS with a log-sum-exp rescale (a
+// one-wave chunk stores its partial directly).
 constexpr int CW = 4;
 
 //
@@ -385,10 +417,19 @@ __global__ __launch_bounds__(64 * CW) void attn_chunk_kernel(const ChunkArgs a)
     constexpr int VCH = PC * RB / 1024;              // 1 KB global -> LDS copies per piece
     constexpr int GP = (G + 3) & ~3;                 // p * v_scale row padded to float4s
     static_assert(CPG == SUBS * NT && VCH * 1024 == PC * RB, "p . v lane layout");
+    // p . v on the matrix cores (int8 V, d = 128, 4 to 6 heads; more would pass 256 registers): per 16-dim tile T of the output,
+    // O[head][dim] += P[head][cell] V[cell][dim] over the piece's 32 cells with v_mfma_f32_16x16x32_f16. V codes are
+    // exact in fp16, and p * v_scale goes in as two fp16 terms (hi + lo, 22 bits) scaled by a power of two per piece
+    // so that the largest fits fp16's range; both terms accumulate into the same fp32 tile.
+    constexpr bool MPV = VB == 8 && D == 128 && G >= 4 && G <= 6;
+    constexpr int NTL = D / 16;                      // 16-dim output tiles (MPV)
+    constexpr int SPS = PC + 4;                      // MPV: p * v_scale column stride (banks shift between heads)
+    constexpr int SPN = MPV ? NG * G * SPS : PC * NG * GP;
     __shared__ __align__(16) int8_t sv[CW][PC * RB]; // the wave's V piece: [cell][RB], chunk c of row r at c ^ (r & SWZ)
-    __shared__ __align__(16) float sp[CW][PC][NG][GP];
+    // p * v_scale: [cell][group][head] rows for the VALU p . v, [group][head][cell] columns for the MFMA form
+    __shared__ __align__(16) float sp[CW][SPN];
     __shared__ float sm[CW][G], sl[CW][G];
-    __shared__ __align__(16) float so[CW][G][D];
+    __shared__ __align__(16) float so[CW][G + (MPV ? 1 : 0)][D];   // MPV: row G takes the padding heads' stores
     __shared__ __align__(16) float sq[G * D];        // the G q rows of (row i, KV head g)
     const int tid = threadIdx.x, lane = tid % 64;
     const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
@@ -472,6 +513,12 @@ __global__ __launch_bounds__(64 * CW) void attn_chunk_kernel(const ChunkArgs a)
     for (int h = 0; h < G; h++)
 #pragma unroll
         for (int t = 0; t < DPL; t++) o[h][t] = 0.f;
+    // MFMA form: tile T's accumulator; lane (G4, jl) holds dim 16 T + jl of heads 4 G4 .. 4 G4 + 3, in units of
+    // 2^-srun (srun only decreases, so a rescale never grows the accumulators)
+    f4v oacc[NTL];
+#pragma unroll
+    for (int t = 0; t < NTL; t++) oacc[t] = f4v{0.f, 0.f, 0.f, 0.f};
+    int32_t srun = 1000;
 
     const int8_t *kbase = P.k + (int64_t)g * P.capacity * D + 16 * s;
     const int8_t *vbase = P.v + (int64_t)g * P.capacity * RB;
@@ -557,73 +604,157 @@ __global__ __launch_bounds__(64 * CW) void attn_chunk_kernel(const ChunkArgs a)
                 lg[st][k] = p;
             }
         }
+        if constexpr (MPV) {
+            // the piece's power-of-two scale: 2^snew times its largest |v_scale| (visible cells) stays below 2^14;
+            // srun only decreases, and the accumulators take the change with the heads' rescale
+            float vmax = 0.f;
 #pragma unroll
-        for (int h = 0; h < G; h++) {
-            const float ah = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha[h / LPC]), h % LPC));
+            for (int st = 0; st < STEPS; st++) {
+                const bool vis = cb + st * CPS + r <= limit;
 #pragma unroll
-            for (int t = 0; t < DPL; t++) o[h][t] *= ah;
-        }
-        // p * v_scale per (cell, scale group, head) to LDS, written by the head's slot lane of each cell; masked
-        // cells have p = 0 but their v_scale may be anything (even NaN): their entries are zeroed
+                for (int gi = 0; gi < NG; gi++) vmax = fmaxf(vmax, vis ? fabsf(vsc[st][gi]) : 0.f);
+            }
+            vmax = group_max<64>(vmax);
+            const int32_t snew = __builtin_amdgcn_readfirstlane(min(srun, 14 - __builtin_amdgcn_frexp_expf(vmax)));
+            const int32_t dsh = snew - srun;   // <= 0
+            const bool first = srun == 1000;   // the accumulators are still 0
+            srun = snew;
+            // rescale, when some head's max or the scale moved (a wave-uniform test): lane (G4, jl) holds heads
+            // 4 G4 + i; heads past G (padding rows) get 0
+            float ah[G];
+            bool moved = dsh != 0;
 #pragma unroll
-        for (int st = 0; st < STEPS; st++) {
-            const bool vis = cb + st * CPS + r <= limit;
+            for (int h = 0; h < G; h++) {
+                ah[h] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha[h / LPC]), h % LPC));
+                moved = moved || ah[h] != 1.f;
+            }
+            if (!first && moved) {
+                float fac[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int k = 0; k < HPL; k++) {
-                const int h = s + LPC * k;
-                if (h < G) {
+                for (int h = 0; h < G; h++) {
+                    const float f = __builtin_amdgcn_ldexpf(ah[h], dsh);
+                    if (h < 4) fac[h] = G4 == 0 ? f : fac[h];
+                    else fac[h - 4] = G4 == 1 ? f : fac[h - 4];
+                }
 #pragma unroll
-                    for (int gi = 0; gi < NG; gi++) sp[wave][st * CPS + r][gi][h] = vis ? lg[st][k] * vsc[st][gi] : 0.f;
+                for (int t = 0; t < NTL; t++)
+#pragma unroll
+                    for (int e = 0; e < 4; e++) oacc[t][e] *= fac[e];
+            }
+            // scaled p * v_scale per (group, head, cell) to LDS by the head's slot lane of each cell; masked cells
+            // are zeroed (their v_scale may be anything)
+            float *spw = sp[wave];
+#pragma unroll
+            for (int st = 0; st < STEPS; st++) {
+                const bool vis = cb + st * CPS + r <= limit;
+#pragma unroll
+                for (int k = 0; k < HPL; k++) {
+                    const int h = s + LPC * k;
+                    if (h < G) {
+#pragma unroll
+                        for (int gi = 0; gi < NG; gi++)
+                            spw[(gi * G + h) * SPS + st * CPS + r] =
+                                vis ? __builtin_amdgcn_ldexpf(lg[st][k] * vsc[st][gi], snew) : 0.f;
+                    }
                 }
             }
-        }
-        __builtin_amdgcn_s_waitcnt(0);   // the V piece has landed and the p rows are written (this wave only)
+            __builtin_amdgcn_s_waitcnt(0);   // the V piece has landed and the p columns are written (this wave only)
 
-        // ---- o[h][dim] += sum over cells of (p * v_scale)[cell][h] * v[cell][dim]. Each cell's p * v_scale row
-        // feeds only G * DPL FMAs, so the rows are read PWD cells ahead (a ring of registers) and the next 8-cell
-        // block's transposing V reads are issued half a block early: the LDS latency stays behind the FMAs.
-        const int i8 = jl >> 1, hh = jl & 1;
-        constexpr int PWD = 3;                           // p * v_scale rows in flight
-        constexpr int GR = (G + 3) / 4;                  // float4 reads per row (heads past G are not read)
-        auto read_row = [&](int c, float4 (&dst)[GR]) {
-            const float *prow = &sp[wave][c][grp_v][0];
+            // A operands: lane (G4, jl) holds head jl's (padding rows repeat head G - 1) scaled p * v_scale for cells
+            // 8 G4 .. 8 G4 + 7 of each scale group, as hi + lo fp16. B operands: the transposing read of chunk T
+            // gives lane jl dim 16 T + jl of the same 8 cells, so element e of both is cell 8 G4 + e.
+            const int ha = jl < G ? jl : G - 1;
+            h8 ahi[NG], alo[NG];
 #pragma unroll
-            for (int u = 0; u < GR; u++) dst[u] = *reinterpret_cast<const float4 *>(prow + 4 * u);
-        };
-        auto read_v = [&](int co, v2i (&dst)[NT]) {
+            for (int gi = 0; gi < NG; gi++) {
+                const float4 *src = reinterpret_cast<const float4 *>(spw + (gi * G + ha) * SPS + 8 * G4);
+                const float4 u0 = src[0], u1 = src[1];
+                const float xs[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
 #pragma unroll
-            for (int t = 0; t < NT; t++) {
-                const int lc = CPG * grp_v + sub_v + SUBS * t;   // logical 16-byte chunk of the lane's dims
-                const int cell = 8 * co + i8;
-                dst[t] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-                    (QSA_LDS v2i *)(svw + cell * RB + 16 * (lc ^ (cell & SWZ)) + 8 * hh));
+                for (int e = 0; e < 8; e++) {
+                    _Float16 hi, lo;
+                    split_h2(xs[e], hi, lo);
+                    ahi[gi][e] = hi;
+                    alo[gi][e] = lo;
+                }
             }
-        };
-        float4 ring[PWD][GR];
-        v2i vb[2][NT];
-        read_v(0, vb[0]);
+            const int cell = 8 * G4 + (jl >> 1);
 #pragma unroll
-        for (int c = 0; c < PWD - 1; c++) read_row(c, ring[c]);
-#pragma unroll
-        for (int c = 0; c < PC; c++) {
-            const int co = c / 8, ci = c % 8;
-            if (c + PWD - 1 < PC) read_row(c + PWD - 1, ring[(c + PWD - 1) % PWD]);
-            if (ci == 4 && co + 1 < PC / 8) read_v(co + 1, vb[(co + 1) & 1]);
-            float pw[4 * GR];
-#pragma unroll
-            for (int u = 0; u < GR; u++) {
-                pw[4 * u] = ring[c % PWD][u].x; pw[4 * u + 1] = ring[c % PWD][u].y;
-                pw[4 * u + 2] = ring[c % PWD][u].z; pw[4 * u + 3] = ring[c % PWD][u].w;
+            for (int t = 0; t < NTL; t++) {
+                const h8 bv = codes_h8(__builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                    (QSA_LDS v2i *)(svw + cell * RB + 16 * (t ^ (cell & SWZ)) + 8 * (jl & 1))));
+                oacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi[t / (NTL / NG)], bv, oacc[t], 0, 0, 0);
+                oacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo[t / (NTL / NG)], bv, oacc[t], 0, 0, 0);
             }
+        } else {
 #pragma unroll
-            for (int t = 0; t < NT; t++) {
-                const int32_t word = ci < 4 ? vb[co & 1][t][0] : vb[co & 1][t][1];
+            for (int h = 0; h < G; h++) {
+                const float ah = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha[h / LPC]), h % LPC));
 #pragma unroll
-                for (int n = 0; n < NPB; n++) {
-                    // signed field of VB bits at bit 8 * (ci & 3) + VB * n
-                    const float x = (float)((word << (32 - VB - 8 * (ci & 3) - VB * n)) >> (32 - VB));
+                for (int t = 0; t < DPL; t++) o[h][t] *= ah;
+            }
+            // p * v_scale per (cell, scale group, head) to LDS, written by the head's slot lane of each cell; masked
+            // cells have p = 0 but their v_scale may be anything (even NaN): their entries are zeroed
 #pragma unroll
-                    for (int h = 0; h < G; h++) o[h][NPB * t + n] = fmaf(pw[h], x, o[h][NPB * t + n]);
+            for (int st = 0; st < STEPS; st++) {
+                const bool vis = cb + st * CPS + r <= limit;
+#pragma unroll
+                for (int k = 0; k < HPL; k++) {
+                    const int h = s + LPC * k;
+                    if (h < G) {
+#pragma unroll
+                        for (int gi = 0; gi < NG; gi++) sp[wave][((st * CPS + r) * NG + gi) * GP + h] = vis ? lg[st][k] * vsc[st][gi] : 0.f;
+                    }
+                }
+            }
+            __builtin_amdgcn_s_waitcnt(0);   // the V piece has landed and the p rows are written (this wave only)
+
+            // ---- o[h][dim] += sum over cells of (p * v_scale)[cell][h] * v[cell][dim]. Each cell's p * v_scale row
+            // feeds only G * DPL FMAs, so the rows are read PWD cells ahead (a ring of registers) and the next 8-cell
+            // block's transposing V reads are issued half a block early: the LDS latency stays behind the FMAs.
+            const int i8 = jl >> 1, hh = jl & 1;
+            constexpr int PWD = 3;                           // p * v_scale rows in flight
+            constexpr int GR = (G + 3) / 4;                  // float4 reads per row (heads past G are not read)
+            auto read_row = [&](int c, float4 (&dst)[GR]) {
+                const float *prow = &sp[wave][(c * NG + grp_v) * GP];
+#pragma unroll
+                for (int u = 0; u < GR; u++) dst[u] = *reinterpret_cast<const float4 *>(prow + 4 * u);
+            };
+            auto read_v = [&](int co, v2i (&dst)[NT]) {
+#pragma unroll
+                for (int t = 0; t < NT; t++) {
+                    const int lc = CPG * grp_v + sub_v + SUBS * t;   // logical 16-byte chunk of the lane's dims
+                    const int cell = 8 * co + i8;
+                    dst[t] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                        (QSA_LDS v2i *)(svw + cell * RB + 16 * (lc ^ (cell & SWZ)) + 8 * hh));
+                }
+            };
+            float4 ring[PWD][GR];
+            v2i vb[2][NT];
+            read_v(0, vb[0]);
+#pragma unroll
+            for (int c = 0; c < PWD - 1; c++) read_row(c, ring[c]);
+#pragma unroll
+            for (int c = 0; c < PC; c++) {
+                const int co = c / 8, ci = c % 8;
+                if (c + PWD - 1 < PC) read_row(c + PWD - 1, ring[(c + PWD - 1) % PWD]);
+                if (ci == 4 && co + 1 < PC / 8) read_v(co + 1, vb[(co + 1) & 1]);
+                float pw[4 * GR];
+#pragma unroll
+                for (int u = 0; u < GR; u++) {
+                    pw[4 * u] = ring[c % PWD][u].x; pw[4 * u + 1] = ring[c % PWD][u].y;
+                    pw[4 * u + 2] = ring[c % PWD][u].z; pw[4 * u + 3] = ring[c % PWD][u].w;
+                }
+#pragma unroll
+                for (int t = 0; t < NT; t++) {
+                    const int32_t word = ci < 4 ? vb[co & 1][t][0] : vb[co & 1][t][1];
+#pragma unroll
+                    for (int n = 0; n < NPB; n++) {
+                        // signed field of VB bits at bit 8 * (ci & 3) + VB * n
+                        const float x = (float)((word << (32 - VB - 8 * (ci & 3) - VB * n)) >> (32 - VB));
+#pragma unroll
+                        for (int h = 0; h < G; h++) o[h][NPB * t + n] = fmaf(pw[h], x, o[h][NPB * t + n]);
+                    }
                 }
             }
         }
@@ -636,14 +767,28 @@ __global__ __launch_bounds__(64 * CW) void attn_chunk_kernel(const ChunkArgs a)
         // the same values the fold would produce, since a single term's weight is 2^0 = 1)
         if (!chunk_ok) return;
         const int64_t row0 = ((int64_t)i * a.n_qh + h0) * a.max_chunks + j;
+        // a chunk without a visible cell ran no piece, so its accumulators are still 0
+        if constexpr (MPV) {
 #pragma unroll
-        for (int t = 0; t < NT; t++) {
+            for (int t = 0; t < NTL; t++) {
 #pragma unroll
-            for (int n = 0; n < NPB; n++) {
-                const int d = DPC * (CPG * grp_v + sub_v + SUBS * t) + NPB * jl + n;
+                for (int e = 0; e < 4; e++) {
+                    const int h = 4 * G4 + e;
+                    if (h < G)
+                        a.o_out[(row0 + (int64_t)h * a.max_chunks) * D + 16 * t + jl] =
+                            __builtin_amdgcn_ldexpf(oacc[t][e], -srun);
+                }
+            }
+        } else {
 #pragma unroll
-                for (int h = 0; h < G; h++)
-                    a.o_out[(row0 + (int64_t)h * a.max_chunks) * D + d] = mrun[h] != -INFINITY ? o[h][NPB * t + n] : 0.f;
+            for (int t = 0; t < NT; t++) {
+#pragma unroll
+                for (int n = 0; n < NPB; n++) {
+                    const int d = DPC * (CPG * grp_v + sub_v + SUBS * t) + NPB * jl + n;
+#pragma unroll
+                    for (int h = 0; h < G; h++)
+                        a.o_out[(row0 + (int64_t)h * a.max_chunks) * D + d] = o[h][NPB * t + n];
+                }
             }
         }
 #pragma unroll
@@ -670,13 +815,24 @@ __global__ __launch_bounds__(64 * CW) void attn_chunk_kernel(const ChunkArgs a)
             sl[wave][h] = lpart[k];
         }
     }
+    if constexpr (MPV) {
 #pragma unroll
-    for (int t = 0; t < NT; t++) {
+        for (int t = 0; t < NTL; t++) {
 #pragma unroll
-        for (int n = 0; n < NPB; n++) {
-            const int d = DPC * (CPG * grp_v + sub_v + SUBS * t) + NPB * jl + n;
+            for (int e = 0; e < 4; e++) {
+                const int h = 4 * G4 + e;
+                so[wave][h < G ? h : G][16 * t + jl] = __builtin_amdgcn_ldexpf(oacc[t][e], -srun);
+            }
+        }
+    } else {
 #pragma unroll
-            for (int h = 0; h < G; h++) so[wave][h][d] = o[h][NPB * t + n];
+        for (int t = 0; t < NT; t++) {
+#pragma unroll
+            for (int n = 0; n < NPB; n++) {
+                const int d = DPC * (CPG * grp_v + sub_v + SUBS * t) + NPB * jl + n;
+#pragma unroll
+                for (int h = 0; h < G; h++) so[wave][h][d] = o[h][NPB * t + n];
+            }
         }
     }
     __syncthreads();
