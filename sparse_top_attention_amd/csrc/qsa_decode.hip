@@ -1,8 +1,8 @@
 // Decode-path kernels of libqsa for gfx950: block index, block scores, split-K chunk attention and the
 // log-sum-exp merge. All four stream int8 codes / fp32 rows from HBM with 16-byte coalesced loads; per cell the
-// work is a few hundred FMAs against 272 bytes, so HBM and the fp32 VALU are the ceilings. The chunk kernel's p . v
-// product runs on the matrix cores (fp16 MFMA with exact V codes and a two-term split of p * v_scale) for 4 to 6 q
-// heads per KV head at d = 128, on the VALU otherwise.
+// work is a few hundred FMAs against 272 bytes, so HBM and the fp32 VALU are the ceilings. With 4 or more q heads
+// per KV head at d = 128 the chunk kernel runs both of its products on the matrix cores (fp16 MFMA with exact K and V
+// codes and two-term splits of q and p * v_scale), on the VALU otherwise.
 //
 // Lane layout shared by the index and chunk kernels ("cell x slice"): a cell's D dims are cut into D/16 slices of
 // 16 dims (one 16-byte load of int8 codes), so a wave covers 64 / (D/16) cells per step; lane = cell_slot * LPC +
@@ -390,9 +390,10 @@ struct ChunkArgs {
 // 16-byte chunks swizzled by cell), and ds_read_b64_tr_b8 hands each lane 8 cells of one dim per read; p * v_scale
 // per (cell, scale group, head) is written to LDS by the head's lane of the cell and read back as a broadcast. Each
 // lane then owns D/64 output dims of every head, so nothing is summed across lanes at the end. In the MFMA form
-// (MPV below) the same transposing reads are the B operands, the p * v_scale columns the A operands, and a lane owns
-// one dim of 4 heads per 16-dim tile. The waves of a chunk are combined through LDS with a log-sum-exp rescale (a
-// one-wave chunk stores its partial directly).
+// (MPV below) a lane of 16-lane group G4 holds one head's logits of 8 cells, which are its A operand for p . v, the
+// transposing reads of the same cells are the B operands, and a lane owns one dim of 4 heads per 16-dim tile. The
+// waves of a chunk are combined through LDS with a log-sum-exp rescale (a one-wave chunk stores its partial
+// directly).
 constexpr int CW = 4;
 
 //
@@ -417,19 +418,22 @@ __global__ __launch_bounds__(64 * CW) void attn_chunk_kernel(const ChunkArgs a)
     constexpr int VCH = PC * RB / 1024;              // 1 KB global -> LDS copies per piece
     constexpr int GP = (G + 3) & ~3;                 // p * v_scale row padded to float4s
     static_assert(CPG == SUBS * NT && VCH * 1024 == PC * RB, "p . v lane layout");
-    // p . v on the matrix cores (int8 V, d = 128, 4 to 6 heads; more would pass 256 registers): per 16-dim tile T of the output,
-    // O[head][dim] += P[head][cell] V[cell][dim] over the piece's 32 cells with v_mfma_f32_16x16x32_f16. V codes are
-    // exact in fp16, and p * v_scale goes in as two fp16 terms (hi + lo, 22 bits) scaled by a power of two per piece
-    // so that the largest fits fp16's range; both terms accumulate into the same fp32 tile.
-    constexpr bool MPV = VB == 8 && D == 128 && G >= 4 && G <= 6;
+    // Both products on the matrix cores (int8 K and V, d = 128, 4 or more heads; MPV): the logits of the piece's 32
+    // cells as S[cell][head] = K q^T per 64-dim scale group, and per 16-dim output tile O[head][dim] +=
+    // P[head][cell] V[cell][dim], all with v_mfma_f32_16x16x32_f16 (heads padded to 16 rows). K and V codes are exact
+    // in fp16; q and p * v_scale go in as two fp16 terms (hi + lo, 22 significant bits) scaled by powers of two that
+    // keep them in fp16's range, both terms accumulating into the same fp32 tile.
+    constexpr bool MPV = VB == 8 && D == 128 && G >= 4;
     constexpr int NTL = D / 16;                      // 16-dim output tiles (MPV)
-    constexpr int SPS = PC + 4;                      // MPV: p * v_scale column stride (banks shift between heads)
-    constexpr int SPN = MPV ? NG * G * SPS : PC * NG * GP;
-    __shared__ __align__(16) int8_t sv[CW][PC * RB]; // the wave's V piece: [cell][RB], chunk c of row r at c ^ (r & SWZ)
-    // p * v_scale: [cell][group][head] rows for the VALU p . v, [group][head][cell] columns for the MFMA form
-    __shared__ __align__(16) float sp[CW][SPN];
+    static_assert(!MPV || (NG == 2 && PC == 32 && CHUNKS == 8), "MFMA form: d = 128, 32-cell pieces");
+    __shared__ __align__(16) int8_t sv[CW][PC * RB]; // the wave's V piece: [cell][RB], chunk c of row r at c ^ swizzle(r)
+    // p * v_scale rows [cell][group][head] of the VALU p . v (the MFMA form keeps p in registers)
+    __shared__ __align__(16) float sp[CW][MPV ? 4 : PC * NG * GP];
     __shared__ float sm[CW][G], sl[CW][G];
     __shared__ __align__(16) float so[CW][G + (MPV ? 1 : 0)][D];   // MPV: row G takes the padding heads' stores
+    // MPV's V swizzle: the 8 rows of one transposing read (cells 4 G4 + e and 16 + 4 G4 + e) land on 8 distinct
+    // 16-byte positions
+    auto mswz = [](int c) { return (c + 4 * (c >> 4)) & 7; };
     __shared__ __align__(16) float sq[G * D];        // the G q rows of (row i, KV head g)
     const int tid = threadIdx.x, lane = tid % 64;
     const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
@@ -485,6 +489,44 @@ __global__ __launch_bounds__(64 * CW) void attn_chunk_kernel(const ChunkArgs a)
             qv[h][4 * jj + 3] = u.w;
         }
     }
+    // MFMA form: q as B operands of the logits' products, lane (G4, jl): head jl (0 for the padding heads past G),
+    // dims 64 gi + 16 G4 + 8 ks + e, times 2^sqe (per head: its largest |q| times 2^sqe stays below 2^14) as hi + lo
+    // fp16; qsh = sm_scale log2(e) 2^-sqe undoes the scale on the logits
+    h8 qb[NG][2][2];   // [scale group][k step][hi, lo]
+    float qsh = 0.f;
+    if constexpr (MPV) {
+        float qx[NG][16];
+        float qmax = 0.f;
+        const int hq = jl < G ? jl : G - 1;
+#pragma unroll
+        for (int gi = 0; gi < NG; gi++) {
+            const float4 *src = reinterpret_cast<const float4 *>(sq + hq * D + 64 * gi + 16 * G4);
+#pragma unroll
+            for (int jj = 0; jj < 4; jj++) {
+                const float4 u = src[jj];
+                const float uu[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    qx[gi][4 * jj + e] = jl < G ? uu[e] : 0.f;
+                    qmax = fmaxf(qmax, fabsf(qx[gi][4 * jj + e]));
+                }
+            }
+        }
+        qmax = max32(max16(qmax));
+        const int sqe = 14 - __builtin_amdgcn_frexp_expf(qmax);
+        qsh = __builtin_amdgcn_ldexpf(a.qscale, -sqe);
+#pragma unroll
+        for (int gi = 0; gi < NG; gi++)
+#pragma unroll
+            for (int ks = 0; ks < 2; ks++)
+#pragma unroll
+                for (int e = 0; e < 8; e++) {
+                    _Float16 hi, lo;
+                    split_h2(__builtin_amdgcn_ldexpf(qx[gi][8 * ks + e], sqe), hi, lo);
+                    qb[gi][ks][0][e] = hi;
+                    qb[gi][ks][1][e] = lo;
+                }
+    }
     const int32_t posi = __builtin_amdgcn_readlane(words, 0);
     const int32_t cnt_raw = __builtin_amdgcn_readlane(words, 2);
     bool pool_ok = true;
@@ -524,6 +566,8 @@ __global__ __launch_bounds__(64 * CW) void attn_chunk_kernel(const ChunkArgs a)
     const int8_t *vbase = P.v + (int64_t)g * P.capacity * RB;
     const float *ksbase = P.ks + (int64_t)g * P.capacity * NG + grp_s;
     const float *vsbase = P.vs + (int64_t)g * P.capacity * NG;
+    const int8_t *kmb = P.k + (int64_t)g * P.capacity * D + 16 * G4;   // MFMA form: the lane's 16 dims of a group
+    const float *ksm = P.ks + (int64_t)g * P.capacity * NG;
     int8_t *svw = sv[wave];
     constexpr int PPB = QSA_BLOCK / PC;              // pieces per block
 
@@ -534,101 +578,98 @@ __global__ __launch_bounds__(64 * CW) void attn_chunk_kernel(const ChunkArgs a)
         if (b < 0 || (int64_t)b * QSA_BLOCK + (pc % PPB) * PC > limit) continue;
         const int32_t cb = b * QSA_BLOCK + (pc % PPB) * PC;
 
-        // ---- loads: K slices and scales into registers, the V piece into LDS
-        int4 kw[STEPS];
-        float ksc[STEPS], vsc[STEPS][NG];
-#pragma unroll
-        for (int st = 0; st < STEPS; st++) {
-            const int32_t c = min(cb + st * CPS + r, limit);
-            kw[st] = *reinterpret_cast<const int4 *>(kbase + (int64_t)c * D);
-            ksc[st] = ksbase[(int64_t)c * NG] * a.qscale;   // sm_scale * log2(e) rides on the key scale
-            const float *vsrc = vsbase + (int64_t)c * NG;   // all NG group scales of the cell, one load
-            if constexpr (NG == 4) {
-                const float4 u = *reinterpret_cast<const float4 *>(vsrc);
-                vsc[st][0] = u.x; vsc[st][1] = u.y; vsc[st][2] = u.z; vsc[st][3] = u.w;
-            } else if constexpr (NG == 2) {
-                const float2 u = *reinterpret_cast<const float2 *>(vsrc);
-                vsc[st][0] = u.x; vsc[st][1] = u.y;
-            } else {
-                vsc[st][0] = vsrc[0];
-            }
-        }
-#pragma unroll
-        for (int q = 0; q < VCH; q++) {
-            const int slot = 64 * q + lane, cell = slot / CHUNKS, pch = slot % CHUNKS;
-            const int32_t c = min(cb + cell, limit);
-            load_lds16(vbase + (int64_t)c * RB + 16 * (pch ^ (cell & SWZ)), lds_addr(svw + 1024 * q));
-        }
-        __builtin_amdgcn_sched_barrier(0);   // every copy is in flight before the logits start
-
-        // ---- logits (base-2 units), masked past the limit: the G dot products of the lane's 16 dims, then a
-        // reduce-scatter over the cell's lanes, so each (cell, head) logit is finished in one lane only
-        float lg[STEPS][HPL];
-#pragma unroll
-        for (int st = 0; st < STEPS; st++) {
-            const bool vis = cb + st * CPS + r <= limit;
-            float x[16];
-            unpack16(kw[st], x);
-            float d[NV];
-#pragma unroll
-            for (int h = 0; h < NV; h++) {
-                float dot = 0.f;
-                if (h < G) {
-#pragma unroll
-                    for (int e = 0; e < 16; e++) dot = fmaf(qv[h < G ? h : 0][e], x[e], dot);
-                }
-                d[h] = dot * ksc[st];
-            }
-            reduce_scatter<LPC, NV>(d, s);
-#pragma unroll
-            for (int k = 0; k < HPL; k++) lg[st][k] = vis ? d[LPC * k] : -INFINITY;
-        }
-
-        // ---- running max per head over the piece's cells (lanes of one slot), p = 2^(logit - max); the output
-        // accumulators take every head's rescale, read from the head's slot lane
-        float alpha[HPL];
-#pragma unroll
-        for (int k = 0; k < HPL; k++) {
-            float mb = lg[0][k];
-#pragma unroll
-            for (int st = 1; st < STEPS; st++) mb = fmaxf(mb, lg[st][k]);
-            mb = strided_max<LPC>(mb);            // the piece holds a visible cell, so mb is finite
-            const float mnew = fmaxf(mrun[k], mb);
-            alpha[k] = __builtin_amdgcn_exp2f(mrun[k] - mnew);  // 0 on the first piece
-            mrun[k] = mnew;
-            lpart[k] *= alpha[k];
-#pragma unroll
-            for (int st = 0; st < STEPS; st++) {
-                const float p = __builtin_amdgcn_exp2f(lg[st][k] - mnew);   // masked cells: 2^-inf = 0
-                lpart[k] += p;
-                lg[st][k] = p;
-            }
-        }
         if constexpr (MPV) {
-            // the piece's power-of-two scale: 2^snew times its largest |v_scale| (visible cells) stays below 2^14;
-            // srun only decreases, and the accumulators take the change with the heads' rescale
+            // ---- loads: the K rows as A operands (lane (G4, jl): cell 16 ct + jl, dims 64 gi + 16 G4 .. + 15), the
+            // key and value scales of the lane's logit cells 16 ct + 4 G4 + e, the V piece into LDS
+            int4 kq[2][NG];
+            float2 ksv[2][4], vsv[2][4];
+#pragma unroll
+            for (int ct = 0; ct < 2; ct++) {
+                const int32_t ck = min(cb + 16 * ct + jl, limit);
+#pragma unroll
+                for (int gi = 0; gi < NG; gi++)
+                    kq[ct][gi] = *reinterpret_cast<const int4 *>(kmb + (int64_t)ck * D + 64 * gi);
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    const int32_t cs = min(cb + 16 * ct + 4 * G4 + e, limit);
+                    ksv[ct][e] = *reinterpret_cast<const float2 *>(ksm + (int64_t)cs * NG);
+                    vsv[ct][e] = *reinterpret_cast<const float2 *>(vsbase + (int64_t)cs * NG);
+                }
+            }
+#pragma unroll
+            for (int q = 0; q < VCH; q++) {
+                const int slot = 64 * q + lane, cell = slot / CHUNKS, pch = slot % CHUNKS;
+                const int32_t c = min(cb + cell, limit);
+                load_lds16(vbase + (int64_t)c * RB + 16 * (pch ^ mswz(cell)), lds_addr(svw + 1024 * q));
+            }
+            __builtin_amdgcn_sched_barrier(0);   // every copy is in flight before the logits start
+
+            // ---- logits: S[cell][head] per scale group on the matrix cores (both q terms into one tile), then
+            // t = sum over groups of k_scale * S in base-2 units; lane (G4, jl) ends with head jl's logits of cells
+            // 16 ct + 4 G4 + e (masked past the limit)
+            float t[2][4];
+            float mb = -INFINITY;
+#pragma unroll
+            for (int ct = 0; ct < 2; ct++) {
+                f4v sacc[NG];
+#pragma unroll
+                for (int gi = 0; gi < NG; gi++) {
+                    const h8 k0 = codes_h8(v2i{kq[ct][gi].x, kq[ct][gi].y});
+                    const h8 k1 = codes_h8(v2i{kq[ct][gi].z, kq[ct][gi].w});
+                    f4v acc = {0.f, 0.f, 0.f, 0.f};
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(k0, qb[gi][0][0], acc, 0, 0, 0);
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(k1, qb[gi][1][0], acc, 0, 0, 0);
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(k0, qb[gi][0][1], acc, 0, 0, 0);
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(k1, qb[gi][1][1], acc, 0, 0, 0);
+                    sacc[gi] = acc;
+                }
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    const bool vis = cb + 16 * ct + 4 * G4 + e <= limit;
+                    const float x = fmaf(ksv[ct][e].y, sacc[1][e], ksv[ct][e].x * sacc[0][e]) * qsh;
+                    t[ct][e] = vis ? x : -INFINITY;
+                    mb = fmaxf(mb, t[ct][e]);
+                }
+            }
+            // ---- running max of head jl over the piece (the 4 lane groups), p = 2^(t - max)
+            mb = max32(max16(mb));                // the piece holds a visible cell, so mb is finite
+            const float mnew = fmaxf(mrun[0], mb);
+            const float alpha = __builtin_amdgcn_exp2f(mrun[0] - mnew);  // 0 on the first piece
+            mrun[0] = mnew;
+            lpart[0] *= alpha;
+#pragma unroll
+            for (int ct = 0; ct < 2; ct++)
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    t[ct][e] = __builtin_amdgcn_exp2f(t[ct][e] - mnew);   // masked cells: 2^-inf = 0
+                    lpart[0] += t[ct][e];
+                }
+
+            // ---- the piece's power-of-two scale: 2^snew times its largest |v_scale| (visible cells) stays below
+            // 2^14; srun only decreases, and the accumulators take the change with the heads' rescale
             float vmax = 0.f;
 #pragma unroll
-            for (int st = 0; st < STEPS; st++) {
-                const bool vis = cb + st * CPS + r <= limit;
+            for (int ct = 0; ct < 2; ct++)
 #pragma unroll
-                for (int gi = 0; gi < NG; gi++) vmax = fmaxf(vmax, vis ? fabsf(vsc[st][gi]) : 0.f);
-            }
-            vmax = group_max<64>(vmax);
+                for (int e = 0; e < 4; e++) {
+                    const bool vis = cb + 16 * ct + 4 * G4 + e <= limit;
+                    vmax = fmaxf(vmax, vis ? fmaxf(fabsf(vsv[ct][e].x), fabsf(vsv[ct][e].y)) : 0.f);
+                }
+            vmax = max32(max16(vmax));
             const int32_t snew = __builtin_amdgcn_readfirstlane(min(srun, 14 - __builtin_amdgcn_frexp_expf(vmax)));
             const int32_t dsh = snew - srun;   // <= 0
-            const bool first = srun == 1000;   // the accumulators are still 0
+            const bool fresh = srun == 1000;   // the accumulators are still 0
             srun = snew;
-            // rescale, when some head's max or the scale moved (a wave-uniform test): lane (G4, jl) holds heads
-            // 4 G4 + i; heads past G (padding rows) get 0
+            // rescale, when some head's max or the scale moved (a wave-uniform test): head h's factor is in lane h;
+            // lane (G4, jl) holds heads 4 G4 + e, and heads past G (padding rows) get 0
             float ah[G];
             bool moved = dsh != 0;
 #pragma unroll
             for (int h = 0; h < G; h++) {
-                ah[h] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha[h / LPC]), h % LPC));
+                ah[h] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), h));
                 moved = moved || ah[h] != 1.f;
             }
-            if (!first && moved) {
+            if (!fresh && moved) {
                 float fac[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int h = 0; h < G; h++) {
@@ -637,56 +678,109 @@ __global__ __launch_bounds__(64 * CW) void attn_chunk_kernel(const ChunkArgs a)
                     else fac[h - 4] = G4 == 1 ? f : fac[h - 4];
                 }
 #pragma unroll
-                for (int t = 0; t < NTL; t++)
+                for (int tt = 0; tt < NTL; tt++)
 #pragma unroll
-                    for (int e = 0; e < 4; e++) oacc[t][e] *= fac[e];
+                    for (int e = 0; e < 4; e++) oacc[tt][e] *= fac[e];
             }
-            // scaled p * v_scale per (group, head, cell) to LDS by the head's slot lane of each cell; masked cells
-            // are zeroed (their v_scale may be anything)
-            float *spw = sp[wave];
+
+            // ---- p . v: A operands are the lane's own p values (head jl; element 4 ct + e = cell 16 ct + 4 G4 + e)
+            // times v_scale of each group and 2^snew, as hi + lo fp16 (masked cells 0: their v_scale may be
+            // anything); the B operands come from transposing reads whose 8 rows are those same cells
+            h8 ahi[NG], alo[NG];
+#pragma unroll
+            for (int e8 = 0; e8 < 8; e8++) {
+                const int ct = e8 >> 2, e = e8 & 3;
+                const bool vis = cb + 16 * ct + 4 * G4 + e <= limit;
+#pragma unroll
+                for (int gi = 0; gi < NG; gi++) {
+                    const float x = vis ? __builtin_amdgcn_ldexpf(t[ct][e] * (gi ? vsv[ct][e].y : vsv[ct][e].x), snew) : 0.f;
+                    _Float16 hi, lo;
+                    split_h2(x, hi, lo);
+                    ahi[gi][e8] = hi;
+                    alo[gi][e8] = lo;
+                }
+            }
+            __builtin_amdgcn_s_waitcnt(0);   // the V piece has landed (this wave's copies)
+            const int i8 = jl >> 1;
+            const int vcell = 4 * G4 + (i8 & 3) + 16 * (i8 >> 2);
+#pragma unroll
+            for (int tt = 0; tt < NTL; tt++) {
+                const h8 bv = codes_h8(__builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                    (QSA_LDS v2i *)(svw + vcell * RB + 16 * (tt ^ mswz(vcell)) + 8 * (jl & 1))));
+                oacc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi[tt / (NTL / NG)], bv, oacc[tt], 0, 0, 0);
+                oacc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo[tt / (NTL / NG)], bv, oacc[tt], 0, 0, 0);
+            }
+        } else {
+            // ---- loads: K slices and scales into registers, the V piece into LDS
+            int4 kw[STEPS];
+            float ksc[STEPS], vsc[STEPS][NG];
+#pragma unroll
+            for (int st = 0; st < STEPS; st++) {
+                const int32_t c = min(cb + st * CPS + r, limit);
+                kw[st] = *reinterpret_cast<const int4 *>(kbase + (int64_t)c * D);
+                ksc[st] = ksbase[(int64_t)c * NG] * a.qscale;   // sm_scale * log2(e) rides on the key scale
+                const float *vsrc = vsbase + (int64_t)c * NG;   // all NG group scales of the cell, one load
+                if constexpr (NG == 4) {
+                    const float4 u = *reinterpret_cast<const float4 *>(vsrc);
+                    vsc[st][0] = u.x; vsc[st][1] = u.y; vsc[st][2] = u.z; vsc[st][3] = u.w;
+                } else if constexpr (NG == 2) {
+                    const float2 u = *reinterpret_cast<const float2 *>(vsrc);
+                    vsc[st][0] = u.x; vsc[st][1] = u.y;
+                } else {
+                    vsc[st][0] = vsrc[0];
+                }
+            }
+#pragma unroll
+            for (int q = 0; q < VCH; q++) {
+                const int slot = 64 * q + lane, cell = slot / CHUNKS, pch = slot % CHUNKS;
+                const int32_t c = min(cb + cell, limit);
+                load_lds16(vbase + (int64_t)c * RB + 16 * (pch ^ (cell & SWZ)), lds_addr(svw + 1024 * q));
+            }
+            __builtin_amdgcn_sched_barrier(0);   // every copy is in flight before the logits start
+
+            // ---- logits (base-2 units), masked past the limit: the G dot products of the lane's 16 dims, then a
+            // reduce-scatter over the cell's lanes, so each (cell, head) logit is finished in one lane only
+            float lg[STEPS][HPL];
 #pragma unroll
             for (int st = 0; st < STEPS; st++) {
                 const bool vis = cb + st * CPS + r <= limit;
+                float x[16];
+                unpack16(kw[st], x);
+                float d[NV];
 #pragma unroll
-                for (int k = 0; k < HPL; k++) {
-                    const int h = s + LPC * k;
+                for (int h = 0; h < NV; h++) {
+                    float dot = 0.f;
                     if (h < G) {
 #pragma unroll
-                        for (int gi = 0; gi < NG; gi++)
-                            spw[(gi * G + h) * SPS + st * CPS + r] =
-                                vis ? __builtin_amdgcn_ldexpf(lg[st][k] * vsc[st][gi], snew) : 0.f;
+                        for (int e = 0; e < 16; e++) dot = fmaf(qv[h < G ? h : 0][e], x[e], dot);
                     }
+                    d[h] = dot * ksc[st];
                 }
+                reduce_scatter<LPC, NV>(d, s);
+#pragma unroll
+                for (int k = 0; k < HPL; k++) lg[st][k] = vis ? d[LPC * k] : -INFINITY;
             }
-            __builtin_amdgcn_s_waitcnt(0);   // the V piece has landed and the p columns are written (this wave only)
 
-            // A operands: lane (G4, jl) holds head jl's (padding rows repeat head G - 1) scaled p * v_scale for cells
-            // 8 G4 .. 8 G4 + 7 of each scale group, as hi + lo fp16. B operands: the transposing read of chunk T
-            // gives lane jl dim 16 T + jl of the same 8 cells, so element e of both is cell 8 G4 + e.
-            const int ha = jl < G ? jl : G - 1;
-            h8 ahi[NG], alo[NG];
+            // ---- running max per head over the piece's cells (lanes of one slot), p = 2^(logit - max); the output
+            // accumulators take every head's rescale, read from the head's slot lane
+            float alpha[HPL];
 #pragma unroll
-            for (int gi = 0; gi < NG; gi++) {
-                const float4 *src = reinterpret_cast<const float4 *>(spw + (gi * G + ha) * SPS + 8 * G4);
-                const float4 u0 = src[0], u1 = src[1];
-                const float xs[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+            for (int k = 0; k < HPL; k++) {
+                float mb = lg[0][k];
 #pragma unroll
-                for (int e = 0; e < 8; e++) {
-                    _Float16 hi, lo;
-                    split_h2(xs[e], hi, lo);
-                    ahi[gi][e] = hi;
-                    alo[gi][e] = lo;
+                for (int st = 1; st < STEPS; st++) mb = fmaxf(mb, lg[st][k]);
+                mb = strided_max<LPC>(mb);            // the piece holds a visible cell, so mb is finite
+                const float mnew = fmaxf(mrun[k], mb);
+                alpha[k] = __builtin_amdgcn_exp2f(mrun[k] - mnew);  // 0 on the first piece
+                mrun[k] = mnew;
+                lpart[k] *= alpha[k];
+#pragma unroll
+                for (int st = 0; st < STEPS; st++) {
+                    const float p = __builtin_amdgcn_exp2f(lg[st][k] - mnew);   // masked cells: 2^-inf = 0
+                    lpart[k] += p;
+                    lg[st][k] = p;
                 }
             }
-            const int cell = 8 * G4 + (jl >> 1);
-#pragma unroll
-            for (int t = 0; t < NTL; t++) {
-                const h8 bv = codes_h8(__builtin_amdgcn_ds_read_tr8_b64_v2i32(
-                    (QSA_LDS v2i *)(svw + cell * RB + 16 * (t ^ (cell & SWZ)) + 8 * (jl & 1))));
-                oacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi[t / (NTL / NG)], bv, oacc[t], 0, 0, 0);
-                oacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo[t / (NTL / NG)], bv, oacc[t], 0, 0, 0);
-            }
-        } else {
 #pragma unroll
             for (int h = 0; h < G; h++) {
                 const float ah = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha[h / LPC]), h % LPC));
@@ -760,8 +854,10 @@ __global__ __launch_bounds__(64 * CW) void attn_chunk_kernel(const ChunkArgs a)
         }
     }
 
+    // the sum of a head over its lanes: the cell's slot lanes, or in the MFMA form the head's 4 lane groups; either
+    // way lane h (< G) then holds head h's max and sum in slot 0
 #pragma unroll
-    for (int k = 0; k < HPL; k++) lpart[k] = strided_sum<LPC>(lpart[k]);
+    for (int k = 0; k < HPL; k++) lpart[k] = MPV ? strided_sum<16>(lpart[k]) : strided_sum<LPC>(lpart[k]);
     if constexpr (WPC == 1) {
         // one wave per chunk: its partial is the chunk's, stored straight from registers (no LDS fold, no barrier;
         // the same values the fold would produce, since a single term's weight is 2^0 = 1)
