@@ -494,7 +494,8 @@ __global__ __launch_bounds__(64 * CW) void attn_chunk_kernel(const ChunkArgs a)
     // fp16; qsh = sm_scale log2(e) 2^-sqe undoes the scale on the logits
     h8 qb[NG][2][2];   // [scale group][k step][hi, lo]
     float qsh = 0.f;
-    if constexpr (MPV) {
+    // (made on the wave's first piece, after its loads are issued, so that this work overlaps their latency)
+    auto make_qb = [&]() {
         float qx[NG][16];
         float qmax = 0.f;
         const int hq = jl < G ? jl : G - 1;
@@ -526,7 +527,8 @@ __global__ __launch_bounds__(64 * CW) void attn_chunk_kernel(const ChunkArgs a)
                     qb[gi][ks][0][e] = hi;
                     qb[gi][ks][1][e] = lo;
                 }
-    }
+    };
+    bool qready = false;
     const int32_t posi = __builtin_amdgcn_readlane(words, 0);
     const int32_t cnt_raw = __builtin_amdgcn_readlane(words, 2);
     bool pool_ok = true;
@@ -566,7 +568,7 @@ __global__ __launch_bounds__(64 * CW) void attn_chunk_kernel(const ChunkArgs a)
     const int8_t *vbase = P.v + (int64_t)g * P.capacity * RB;
     const float *ksbase = P.ks + (int64_t)g * P.capacity * NG + grp_s;
     const float *vsbase = P.vs + (int64_t)g * P.capacity * NG;
-    const int8_t *kmb = P.k + (int64_t)g * P.capacity * D + 16 * G4;   // MFMA form: the lane's 16 dims of a group
+    const int8_t *kmu = P.k + (int64_t)g * P.capacity * D;   // MFMA form: K and key scales of KV head g
     const float *ksm = P.ks + (int64_t)g * P.capacity * NG;
     int8_t *svw = sv[wave];
     constexpr int PPB = QSA_BLOCK / PC;              // pieces per block
@@ -581,28 +583,38 @@ __global__ __launch_bounds__(64 * CW) void attn_chunk_kernel(const ChunkArgs a)
         if constexpr (MPV) {
             // ---- loads: the K rows as A operands (lane (G4, jl): cell 16 ct + jl, dims 64 gi + 16 G4 .. + 15), the
             // key and value scales of the lane's logit cells 16 ct + 4 G4 + e, the V piece into LDS
+            // (64-bit bases of the piece in scalar registers, 32-bit lane offsets from them; cells past the limit
+            // read the last visible cell)
             int4 kq[2][NG];
             float2 ksv[2][4], vsv[2][4];
+            const int32_t lr = limit - cb;   // >= 0: the piece holds a visible cell
+            const int8_t *kp = kmu + (int64_t)cb * D;
+            const float *ksp = ksm + (int64_t)cb * NG, *vsp = vsbase + (int64_t)cb * NG;
+            const int8_t *vp = vbase + (int64_t)cb * RB;
 #pragma unroll
             for (int ct = 0; ct < 2; ct++) {
-                const int32_t ck = min(cb + 16 * ct + jl, limit);
+                const uint32_t ck = min(16 * ct + jl, lr);
 #pragma unroll
                 for (int gi = 0; gi < NG; gi++)
-                    kq[ct][gi] = *reinterpret_cast<const int4 *>(kmb + (int64_t)ck * D + 64 * gi);
+                    kq[ct][gi] = *reinterpret_cast<const int4 *>(kp + (ck * D + 64 * gi + 16 * G4));
 #pragma unroll
                 for (int e = 0; e < 4; e++) {
-                    const int32_t cs = min(cb + 16 * ct + 4 * G4 + e, limit);
-                    ksv[ct][e] = *reinterpret_cast<const float2 *>(ksm + (int64_t)cs * NG);
-                    vsv[ct][e] = *reinterpret_cast<const float2 *>(vsbase + (int64_t)cs * NG);
+                    const uint32_t cs = min(16 * ct + 4 * G4 + e, lr);
+                    ksv[ct][e] = *reinterpret_cast<const float2 *>(reinterpret_cast<const char *>(ksp) + cs * 8u);
+                    vsv[ct][e] = *reinterpret_cast<const float2 *>(reinterpret_cast<const char *>(vsp) + cs * 8u);
                 }
             }
 #pragma unroll
             for (int q = 0; q < VCH; q++) {
                 const int slot = 64 * q + lane, cell = slot / CHUNKS, pch = slot % CHUNKS;
-                const int32_t c = min(cb + cell, limit);
-                load_lds16(vbase + (int64_t)c * RB + 16 * (pch ^ mswz(cell)), lds_addr(svw + 1024 * q));
+                const uint32_t c = min(cell, lr);
+                load_lds16(vp + (c * RB + 16 * (pch ^ mswz(cell))), lds_addr(svw + 1024 * q));
             }
             __builtin_amdgcn_sched_barrier(0);   // every copy is in flight before the logits start
+            if (!qready) {
+                make_qb();
+                qready = true;
+            }
 
             // ---- logits: S[cell][head] per scale group on the matrix cores (both q terms into one tile), then
             // t = sum over groups of k_scale * S in base-2 units; lane (G4, jl) ends with head jl's logits of cells
