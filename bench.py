@@ -148,8 +148,10 @@ def bench_decode(args):
     ids = torch.empty(n_rows, n_kv, k, dtype=torch.int32, device=dev)
     counts = torch.empty(n_rows, n_kv, dtype=torch.int32, device=dev)
     part = qsa.Partials.empty_like_shape(n_rows, w.n_q_heads, S, D, device=dev)
-    layer_scratch = None if dense else torch.empty(qsa.qsa_decode_layer_scratch_bytes(n_rows, dims, k, S),
-                                                   dtype=torch.uint8, device=dev)
+    # sized for the capacity-wide score rows too (the widest call below)
+    layer_scratch = None if dense else torch.empty(
+        qsa.qsa_decode_layer_scratch_bytes(n_rows, dims, -(-pool_np.capacity // BLOCK), k, S), dtype=torch.uint8,
+        device=dev)
     out = torch.empty(n_rows, w.n_q_heads, D, dtype=torch.float32, device=dev)
     lse = torch.empty(n_rows, w.n_q_heads, dtype=torch.float32, device=dev)
     n_active = t(np.full(n_rows, w.n_active, np.int32)) if dense else None
@@ -422,7 +424,8 @@ def bench_other_decode(copies=32, bw_chunks=32):
     counts = torch.empty(n_rows, n_kv, dtype=torch.int32, device=dev)
     out = torch.empty(n_rows, w.n_q_heads, D, dtype=torch.float32, device=dev)
     lse = torch.empty(n_rows, w.n_q_heads, dtype=torch.float32, device=dev)
-    scratch = torch.empty(qsa.qsa_decode_layer_scratch_bytes(n_rows, dims, w.topk, S), dtype=torch.uint8, device=dev)
+    scratch = torch.empty(qsa.qsa_decode_layer_scratch_bytes(n_rows, dims, nb, w.topk, S), dtype=torch.uint8,
+                          device=dev)
     part = qsa.Partials.empty_like_shape(n_rows, w.n_q_heads, S, D, device=dev)
 
     def layer(c):
@@ -550,8 +553,8 @@ def bench_scale(slot_counts=(1, 2, 4, 8), chunk_counts=(4, 16)):
                                 w.pools[s].n_valid, w.n_kv_heads) for s in range(slots))
         cb = cells * KV_BYTES_PER_CELL_HEAD + w.q.nbytes
         for S in chunk_counts:
-            scratch = torch.empty(qsa.qsa_decode_layer_scratch_bytes(n_rows, dims, w.topk, S), dtype=torch.uint8,
-                                  device=dev)
+            scratch = torch.empty(qsa.qsa_decode_layer_scratch_bytes(n_rows, dims, nb, w.topk, S),
+                                  dtype=torch.uint8, device=dev)
             part = qsa.Partials.empty_like_shape(n_rows, w.n_q_heads, S, w.head_dim, device=dev)
 
             def layer(c):

@@ -186,19 +186,21 @@ qsa_status qsa_decode_select(const float *q, const int32_t *pos, int32_t n_rows,
                              int32_t n_pools, const int32_t *row_pool, qsa_dims dims, int32_t n_blocks, int32_t k,
                              float *scores, int32_t *ids, int32_t *counts, qsa_stream_t stream);
 
-/* Scratch bytes qsa_decode_layer needs (0 if the arguments are invalid). */
-size_t qsa_decode_layer_scratch_bytes(int32_t n_rows, qsa_dims dims, int32_t k, int32_t n_chunks);
+/* Scratch bytes qsa_decode_layer needs for score rows of n_blocks columns (0 if the arguments are invalid). */
+size_t qsa_decode_layer_scratch_bytes(int32_t n_rows, qsa_dims dims, int32_t n_blocks, int32_t k, int32_t n_chunks);
 
-/* One decode layer in three launches: qsa_decode_select, then qsa_attn_chunk in sparse mode with n_chunks, then
- * qsa_attn_merge over all n_chunks ([2806] Summary: fewer, shorter launches per layer). For every row i (pool
+/* One decode layer in three launches ([2806] Summary: fewer, shorter launches per layer): the selection, then
+ * qsa_attn_chunk in sparse mode with n_chunks, then qsa_attn_merge over all n_chunks. With n_blocks <= 1,024 and
+ * k <= 256 the first launch writes the score rows only and every chunk workgroup takes its row's top-k itself;
+ * otherwise the first launch is qsa_decode_select. For every row i (pool
  * pools[row_pool[i]], row_pool NULL = pool 0) and KV head g it computes the same scores, ids and counts as
  * qsa_block_scores + qsa_topk, and the same output as qsa_attn_chunk + qsa_attn_merge on them:
  *   out [n_rows][n_q_heads][head_dim]; lse [n_rows][n_q_heads] (may be NULL).
  * scores [n_rows][n_kv][n_blocks], ids [n_rows][n_kv][k] and counts [n_rows][n_kv] are optional outputs (NULL:
  * kept in scratch). Requires every pool to carry K, V, both scales and an index, 1 <= k <= n_blocks <= 16,384,
  * n_blocks <= ceil(capacity / 64) for every pool, n_chunks >= 1, and scratch_bytes >=
- * qsa_decode_layer_scratch_bytes (QSA_ERR_SCRATCH); scratch holds the chunk partials (and ids and counts when they
- * are not asked for). Calls sharing one scratch buffer must be ordered on one stream. */
+ * qsa_decode_layer_scratch_bytes for n_blocks (QSA_ERR_SCRATCH); scratch holds the chunk partials (and scores, ids
+ * and counts when they are not asked for). Calls sharing one scratch buffer must be ordered on one stream. */
 qsa_status qsa_decode_layer(const float *q, const int32_t *pos, int32_t n_rows, const qsa_pool *pools, int32_t n_pools,
                             const int32_t *row_pool, qsa_dims dims, int32_t n_blocks, int32_t k, int32_t n_chunks,
                             float sm_scale, float *out, float *lse, float *scores, int32_t *ids, int32_t *counts,

@@ -71,7 +71,7 @@ def _lib():
         L.qsa_prompt_attn.argtypes = [P, I32, I32, PP, PD, ctypes.c_float, P, P, SZ, P]
         L.qsa_kv_append.argtypes = [PP, I32, P, PD, P, P, P, I32, P]
         L.qsa_decode_select.argtypes = [P, P, I32, PP, I32, P, PD, I32, I32, P, P, P, P]
-        L.qsa_decode_layer_scratch_bytes.argtypes = [I32, PD, I32, I32]
+        L.qsa_decode_layer_scratch_bytes.argtypes = [I32, PD, I32, I32, I32]
         L.qsa_decode_layer_scratch_bytes.restype = SZ
         L.qsa_decode_layer.argtypes = [P, P, I32, PP, I32, P, PD, I32, I32, I32, ctypes.c_float, P, P, P, P, P, P,
                                        SZ, P]
@@ -245,8 +245,8 @@ def qsa_decode_select(q, pos, pools: Sequence[Pool], dims: Dims, n_blocks: int, 
     return ids, counts
 
 
-def qsa_decode_layer_scratch_bytes(n_rows, dims: Dims, k, n_chunks):
-    return _lib().qsa_decode_layer_scratch_bytes(n_rows, dims.c(), k, n_chunks)
+def qsa_decode_layer_scratch_bytes(n_rows, dims: Dims, n_blocks, k, n_chunks):
+    return _lib().qsa_decode_layer_scratch_bytes(n_rows, dims.c(), n_blocks, k, n_chunks)
 
 
 def qsa_decode_layer(q, pos, pools: Sequence[Pool], dims: Dims, n_blocks: int, k: int, n_chunks: int, out, lse=None,

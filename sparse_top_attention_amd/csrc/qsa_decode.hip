@@ -10,6 +10,7 @@
 // over the LPC lanes of the cell; the chunk kernel finishes its G per-cell dot products with a reduce-scatter over
 // those lanes, so that each (cell, head) logit ends in one lane.
 #include "qsa_internal.h"
+#include "qsa_radix.h"
 
 #include <math.h>
 
@@ -293,66 +294,63 @@ __global__ __launch_bounds__(64) void block_scores_kernel(const float *__restric
 // the window. Workgroup (block range, g, p) scores the rows whose row_pool is p against pool p's index rows; pool 0's
 // workgroups also write -inf rows for the rows whose pool index is out of range, which then select nothing.
 template <int D>
-__global__ __launch_bounds__(64) void select_scores_kernel(const SelectArgs a, int32_t n_rows)
+__global__ __launch_bounds__(64) void select_scores_kernel(const SelectArgs a)
 {
+    // one wave per (tile of BPS * NSTEP blocks, KV head g, row i): the row's words and q rows, then the tile's index
+    // rows of the row's pool (the block-score arithmetic: 8-dim fmaf chains per lane, a DPP sum over the block's
+    // lanes); blocks past the pool's valid cells, and every block of a row whose pool index is out of range, are -inf
     constexpr int LPB = D / 8, BPS = 64 / LPB, NSTEP = 4;
     const int lane = threadIdx.x, rb = lane / LPB, s = lane % LPB;
-    const int32_t g = blockIdx.y, pidx = blockIdx.z;
-    const PoolArg P = a.pools[pidx];
-    const int32_t stride = (P.capacity + QSA_BLOCK - 1) / QSA_BLOCK;
+    const int32_t g = blockIdx.y, i = blockIdx.z;
     const int32_t bw = blockIdx.x * (BPS * NSTEP);
-    const int32_t n_live = min(a.width, (int32_t)(((int64_t)P.n_valid + QSA_BLOCK - 1) / QSA_BLOCK));
+    const int32_t rp = a.row_pool ? a.row_pool[i] : 0;
+    const int32_t p = a.pos[i];
+    // the row's G q heads of g summed in head order (heads past G re-read the last one and are not added)
+    float4 u[8], w[8];
+#pragma unroll
+    for (int h = 0; h < 8; h++) {
+        const float4 *src = reinterpret_cast<const float4 *>(
+            a.q + ((int64_t)i * a.n_qh + g * a.G + (h < a.G ? h : a.G - 1)) * D + 8 * s);
+        u[h] = src[0];
+        w[h] = src[1];
+    }
+    const bool bad = rp < 0 || rp >= a.n_pools;
+    const PoolArg P = a.pools[bad ? 0 : rp];
+    const int32_t stride = (P.capacity + QSA_BLOCK - 1) / QSA_BLOCK;
+    const int32_t n_live = bad ? 0 : min(a.width, (int32_t)(((int64_t)P.n_valid + QSA_BLOCK - 1) / QSA_BLOCK));
     float rv[NSTEP][8];
-    int32_t bidx[NSTEP];
 #pragma unroll
     for (int st = 0; st < NSTEP; st++) {
         const int32_t b = bw + st * BPS + rb;
-        bidx[st] = b;
         const bool live = b < n_live;
         const float4 *src =
             reinterpret_cast<const float4 *>(P.index + ((int64_t)g * stride + (live ? b : 0)) * D + 8 * s);
-        const float4 u = src[0], w = src[1];
-        rv[st][0] = u.x; rv[st][1] = u.y; rv[st][2] = u.z; rv[st][3] = u.w;
-        rv[st][4] = w.x; rv[st][5] = w.y; rv[st][6] = w.z; rv[st][7] = w.w;
+        const float4 x = src[0], y = src[1];
+        rv[st][0] = x.x; rv[st][1] = x.y; rv[st][2] = x.z; rv[st][3] = x.w;
+        rv[st][4] = y.x; rv[st][5] = y.y; rv[st][6] = y.z; rv[st][7] = y.w;
 #pragma unroll
         for (int e = 0; e < 8; e++) rv[st][e] = live ? rv[st][e] : 0.f;
     }
-    for (int32_t i = 0; i < n_rows; i++) {
-        const int32_t rp = a.row_pool ? a.row_pool[i] : 0;
-        const bool bad = rp < 0 || rp >= a.n_pools;
-        if (!(rp == pidx || (bad && pidx == 0))) continue;   // wave-uniform
-        // the row's G q heads of g summed in head order (heads past G re-read the last one and are not added)
-        float qt[8];
+    float qt[8];
 #pragma unroll
-        for (int e = 0; e < 8; e++) qt[e] = 0.f;
-        float4 u[8], w[8];
+    for (int e = 0; e < 8; e++) qt[e] = 0.f;
 #pragma unroll
-        for (int h = 0; h < 8; h++) {
-            const float4 *src = reinterpret_cast<const float4 *>(
-                a.q + ((int64_t)i * a.n_qh + g * a.G + (h < a.G ? h : a.G - 1)) * D + 8 * s);
-            u[h] = src[0];
-            w[h] = src[1];
+    for (int h = 0; h < 8; h++) {
+        if (h < a.G) {
+            qt[0] += u[h].x; qt[1] += u[h].y; qt[2] += u[h].z; qt[3] += u[h].w;
+            qt[4] += w[h].x; qt[5] += w[h].y; qt[6] += w[h].z; qt[7] += w[h].w;
         }
+    }
 #pragma unroll
-        for (int h = 0; h < 8; h++) {
-            if (h < a.G) {
-                qt[0] += u[h].x; qt[1] += u[h].y; qt[2] += u[h].z; qt[3] += u[h].w;
-                qt[4] += w[h].x; qt[5] += w[h].y; qt[6] += w[h].z; qt[7] += w[h].w;
-            }
-        }
-        const int32_t p = a.pos[i];
+    for (int st = 0; st < NSTEP; st++) {
+        float dot = 0.f;
 #pragma unroll
-        for (int st = 0; st < NSTEP; st++) {
-            float dot = 0.f;
-#pragma unroll
-            for (int e = 0; e < 8; e++) dot = fmaf(qt[e], rv[st][e], dot);
-            dot = group_sum<LPB>(dot);
-            const int32_t b = bidx[st];
-            const int64_t first = (int64_t)b * QSA_BLOCK;
-            if (s == 0 && b < a.width)
-                a.scores[((int64_t)i * a.n_kv + g) * a.width + b] =
-                    (!bad && first <= p && first < P.n_valid) ? dot : -INFINITY;
-        }
+        for (int e = 0; e < 8; e++) dot = fmaf(qt[e], rv[st][e], dot);
+        dot = group_sum<LPB>(dot);
+        const int32_t b = bw + st * BPS + rb;
+        const int64_t first = (int64_t)b * QSA_BLOCK;
+        if (s == 0 && b < a.width)
+            a.scores[((int64_t)i * a.n_kv + g) * a.width + b] = (b < n_live && first <= p) ? dot : -INFINITY;
     }
 }
 
@@ -377,6 +375,13 @@ struct ChunkArgs {
     int32_t n_chunks;
     int32_t max_chunks;
     float qscale;  // sm_scale * log2(e): logits are kept in base-2 units inside the kernel
+    // fused selection (scores != NULL): every workgroup takes the top-k of its (row, KV head)'s score row of `width`
+    // columns itself (ids and counts are not read); the first chunk's workgroup stores them in ids_out and
+    // counts_out when those are given
+    int32_t width;
+    const float *scores;
+    int32_t *ids_out;
+    int32_t *counts_out;
 };
 
 // One workgroup of CW waves per CW / wpc consecutive chunks of one (KV head g, row i), wpc waves per chunk; every
@@ -464,18 +469,44 @@ __global__ __launch_bounds__(64 * CW) void attn_chunk_kernel(const ChunkArgs a)
         }
     }
     const int64_t row_kv = (int64_t)i * a.n_kv + g;
-    const bool sel = a.ids != nullptr, mp = a.row_pool != nullptr;
+    const bool fz = a.scores != nullptr;                  // fused selection (workgroup-uniform)
+    const bool sel = a.ids != nullptr || fz, mp = a.row_pool != nullptr;
     const int32_t *p_pidx = mp ? a.row_pool + i : a.pos + i;
-    const int32_t *p_cnt = sel ? a.counts + row_kv : a.pos + i;
-    const int32_t *blist = sel ? a.ids + row_kv * a.topk : a.pos + i;
+    const int32_t *p_cnt = sel && !fz ? a.counts + row_kv : a.pos + i;
+    const int32_t *blist = sel && !fz ? a.ids + row_kv * a.topk : a.pos + i;
     const int32_t words = *(lane == 1 ? p_pidx : (lane == 2 ? p_cnt : a.pos + i));
-    const int32_t idv = blist[sel && lane < a.topk ? lane : 0];   // k <= 64: the whole id list, one id per lane
+    const int32_t idv = blist[sel && !fz && lane < a.topk ? lane : 0];   // k <= 64: the whole id list, one per lane
+    // fused selection: the score row's keys, 4 consecutive columns per thread (rows of up to 1,024 columns)
+    __shared__ int32_t s_ids[FUSED_TOPK_MAX_K];
+    __shared__ int32_t s_cnt;
+    uint32_t key[4];
+    if (fz) {
+        const float *srow = a.scores + row_kv * a.width;
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+            const int32_t c = 4 * tid + e;
+            key[e] = c < a.width ? score_key(srow[c]) : 0u;
+        }
+    }
 #pragma unroll
     for (int u = 0; u < QPT; u++) {
         const int e = tid + 64 * CW * u;
         if (e < QV4) reinterpret_cast<float4 *>(sq)[e] = qld[u];
     }
     __syncthreads();
+    int32_t cnt_fz = 0;
+    if (fz) {
+        // the same top-k as the selection kernels (the result is unique: the k largest keys, ties to the lower
+        // column, in column order), into LDS; the first chunk's workgroup also stores it
+        radix_topk<4, CW>(key, a.topk, s_ids, &s_cnt);
+        __syncthreads();
+        cnt_fz = __builtin_amdgcn_readfirstlane(s_cnt);
+        if (blockIdx.x == 0) {
+            if (a.ids_out)
+                for (int e = tid; e < a.topk; e += 64 * CW) a.ids_out[row_kv * a.topk + e] = s_ids[e];
+            if (a.counts_out && tid == 0) a.counts_out[row_kv] = cnt_fz;
+        }
+    }
     float qv[G][16];
 #pragma unroll
     for (int h = 0; h < G; h++) {
@@ -530,7 +561,7 @@ __global__ __launch_bounds__(64 * CW) void attn_chunk_kernel(const ChunkArgs a)
     };
     bool qready = false;
     const int32_t posi = __builtin_amdgcn_readlane(words, 0);
-    const int32_t cnt_raw = __builtin_amdgcn_readlane(words, 2);
+    const int32_t cnt_raw = fz ? cnt_fz : __builtin_amdgcn_readlane(words, 2);
     bool pool_ok = true;
     PoolArg P = a.pools[0];   // fixed argument offsets: read with the other arguments, no wait for the words
     if (mp) {
@@ -575,7 +606,9 @@ __global__ __launch_bounds__(64 * CW) void attn_chunk_kernel(const ChunkArgs a)
 
     for (int32_t pc = sub; pc < n_blk * PPB; pc += wpc) {
         const int32_t t_blk = first + pc / PPB;
-        const int32_t b = !sel ? t_blk : (a.topk <= 64 ? __builtin_amdgcn_readlane(idv, t_blk) : blist[t_blk]);
+        const int32_t b = !sel ? t_blk
+                                : fz ? __builtin_amdgcn_readfirstlane(s_ids[t_blk])
+                                     : (a.topk <= 64 ? __builtin_amdgcn_readlane(idv, t_blk) : blist[t_blk]);
         // negative id, or no visible valid cell in the piece (64-bit: ids past the pool may be huge)
         if (b < 0 || (int64_t)b * QSA_BLOCK + (pc % PPB) * PC > limit) continue;
         const int32_t cb = b * QSA_BLOCK + (pc % PPB) * PC;
@@ -1214,11 +1247,11 @@ qsa_status qsa::select_scores_launch(const SelectArgs &a, int32_t n_rows, int32_
                                      hipStream_t s)
 {
     const int32_t per_wave = (64 / (head_dim / 8)) * 4;
-    dim3 grid(ceil_div(a.width, per_wave), n_kv, a.n_pools);
+    dim3 grid(ceil_div(a.width, per_wave), n_kv, n_rows);
     switch (head_dim) {
-    case 64: select_scores_kernel<64><<<grid, 64, 0, s>>>(a, n_rows); break;
-    case 128: select_scores_kernel<128><<<grid, 64, 0, s>>>(a, n_rows); break;
-    default: select_scores_kernel<256><<<grid, 64, 0, s>>>(a, n_rows); break;
+    case 64: select_scores_kernel<64><<<grid, 64, 0, s>>>(a); break;
+    case 128: select_scores_kernel<128><<<grid, 64, 0, s>>>(a); break;
+    default: select_scores_kernel<256><<<grid, 64, 0, s>>>(a); break;
     }
     return launch_status();
 }
@@ -1358,7 +1391,7 @@ qsa_status qsa::merge_launch(const float *m, const float *l, const float *o, con
             attn_merge_kernel<DD, 4, 8, 1><<<dim3(rows, 1), 256, 0, s>>>(m, l, o, empty, max_chunks, n_chunks,      \
                                                                        n_active, n_qh, out, lse);                 \
         else                                                                                                       \
-            attn_merge_kernel<DD, 16, 16, DD / 64><<<dim3(rows, DD / 64), 1024, 0, s>>>(                          \
+            attn_merge_kernel<DD, 16, 32, DD / 64><<<dim3(rows, DD / 64), 1024, 0, s>>>(                          \
                 m, l, o, empty, max_chunks, n_chunks, n_active, n_qh, out, lse);                                  \
     } while (0)
     switch (head_dim) {
@@ -1387,10 +1420,10 @@ extern "C" qsa_status qsa_attn_merge(const qsa_partials *in, int32_t n_rows, qsa
 // ======================================================================================= fused decode layer
 namespace {
 struct LayerScratch {
-    size_t m, l, e, o, ids, counts, total;
+    size_t m, l, e, o, ids, counts, scores, total;
 };
 
-LayerScratch layer_layout(int32_t n_rows, const qsa_dims &d, int32_t k, int32_t n_chunks)
+LayerScratch layer_layout(int32_t n_rows, const qsa_dims &d, int32_t n_blocks, int32_t k, int32_t n_chunks)
 {
     auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
     const size_t rh = (size_t)n_rows * d.n_q_heads * n_chunks;
@@ -1403,6 +1436,7 @@ LayerScratch layer_layout(int32_t n_rows, const qsa_dims &d, int32_t k, int32_t 
     s.o = off; off += al(rh * d.head_dim * sizeof(float));
     s.ids = off; off += al(rk * k * sizeof(int32_t));
     s.counts = off; off += al(rk * sizeof(int32_t));
+    s.scores = off; off += al(rk * n_blocks * sizeof(float));
     s.total = off;
     return s;
 }
@@ -1451,10 +1485,11 @@ extern "C" qsa_status qsa_decode_select(const float *q, const int32_t *pos, int3
     return select_launch(sa, n_rows, dims.n_kv_heads, dims.head_dim, (hipStream_t)stream);
 }
 
-extern "C" size_t qsa_decode_layer_scratch_bytes(int32_t n_rows, qsa_dims dims, int32_t k, int32_t n_chunks)
+extern "C" size_t qsa_decode_layer_scratch_bytes(int32_t n_rows, qsa_dims dims, int32_t n_blocks, int32_t k,
+                                                 int32_t n_chunks)
 {
-    if (n_rows <= 0 || k <= 0 || n_chunks <= 0 || check_dims(dims) != QSA_OK) return 0;
-    return layer_layout(n_rows, dims, k, n_chunks).total;
+    if (n_rows <= 0 || n_blocks <= 0 || k <= 0 || n_chunks <= 0 || check_dims(dims) != QSA_OK) return 0;
+    return layer_layout(n_rows, dims, n_blocks, k, n_chunks).total;
 }
 
 extern "C" qsa_status qsa_decode_layer(const float *q, const int32_t *pos, int32_t n_rows, const qsa_pool *pools,
@@ -1471,7 +1506,7 @@ extern "C" qsa_status qsa_decode_layer(const float *q, const int32_t *pos, int32
     const int vb = common_v_bits(pools, n_pools, dims.head_dim);
     if (!vb) return QSA_ERR_UNSUPPORTED;
     if (n_rows == 0) return QSA_OK;
-    const LayerScratch lay = layer_layout(n_rows, dims, k, n_chunks);
+    const LayerScratch lay = layer_layout(n_rows, dims, n_blocks, k, n_chunks);
     if (!scratch) return QSA_ERR_NULL;
     if (scratch_bytes < lay.total) return QSA_ERR_SCRATCH;
     char *base = static_cast<char *>(scratch);
@@ -1479,16 +1514,23 @@ extern "C" qsa_status qsa_decode_layer(const float *q, const int32_t *pos, int32
 
     sa.ids = ids ? ids : reinterpret_cast<int32_t *>(base + lay.ids);
     sa.counts = counts ? counts : reinterpret_cast<int32_t *>(base + lay.counts);
-    sa.scores = scores;
-    // Without a caller's score buffer, wide rows still take the two-launch selection when their score rows fit in
-    // the chunk partials' region, which the chunk kernel writes only after the selection has read them.
-    if (!scores && select_splits(sa) &&
-        (size_t)n_rows * dims.n_kv_heads * n_blocks * sizeof(float) <= lay.ids - lay.m)
-        sa.scores = reinterpret_cast<float *>(base + lay.m);
-    if ((st = select_launch(sa, n_rows, dims.n_kv_heads, dims.head_dim, s)) != QSA_OK) return st;
+    // Rows of up to FUSED_TOPK_MAX_WIDTH columns: the score rows in one launch over many CUs, and every chunk
+    // workgroup takes its row's top-k itself (no selection launch of one workgroup per row). Wider rows: the
+    // selection launches (through the score rows when they have many live blocks), then the chunks read the ids.
+    const bool fuse = n_blocks <= FUSED_TOPK_MAX_WIDTH && k <= FUSED_TOPK_MAX_K;
+    sa.scores = scores ? scores : reinterpret_cast<float *>(base + lay.scores);
+    if (!fuse && !scores && !select_splits(sa)) sa.scores = nullptr;
+    if (fuse) st = select_scores_launch(sa, n_rows, dims.n_kv_heads, dims.head_dim, s);
+    else st = select_launch(sa, n_rows, dims.n_kv_heads, dims.head_dim, s);
+    if (st != QSA_OK) return st;
 
     ChunkArgs a{};
-    a.q = q; a.pos = pos; a.row_pool = row_pool; a.ids = sa.ids; a.counts = sa.counts;
+    a.q = q; a.pos = pos; a.row_pool = row_pool;
+    if (fuse) {
+        a.scores = sa.scores; a.width = n_blocks; a.ids_out = ids; a.counts_out = counts;
+    } else {
+        a.ids = sa.ids; a.counts = sa.counts;
+    }
     a.m_out = reinterpret_cast<float *>(base + lay.m);
     a.l_out = reinterpret_cast<float *>(base + lay.l);
     a.o_out = reinterpret_cast<float *>(base + lay.o);

@@ -95,6 +95,9 @@ qsa_status select_launch(const SelectArgs &a, int32_t n_rows, int32_t n_kv, int3
 // fused selection kernel when a score buffer is at hand and some pool has more than SELECT_SPLIT_WIDTH live blocks
 // (blocks below both the row width and the pool's valid cells; the fused kernel loads no others).
 constexpr int32_t SELECT_SPLIT_WIDTH = 256;
+// The decode layer's chunk kernel takes the top-k itself (from score rows written by the score launch) for rows of
+// up to FUSED_TOPK_MAX_WIDTH columns and k up to FUSED_TOPK_MAX_K.
+constexpr int32_t FUSED_TOPK_MAX_WIDTH = 1024, FUSED_TOPK_MAX_K = 256;
 inline bool select_splits(const SelectArgs &a)
 {
     int32_t live = 0;

@@ -176,10 +176,13 @@ def test_prompt_scratch_sizing_and_checks():
 def test_decode_layer_validation():
     L = qsa.lib_handle()
     pools = (qsa._Pool * 2)(_pool(), _pool())
-    need = L.qsa_decode_layer_scratch_bytes(4, GOOD, 8, 4)
+    need = L.qsa_decode_layer_scratch_bytes(4, GOOD, 16, 8, 4)
     assert need >= 4 * 24 * 4 * (128 * 4 + 9)             # the partials at least
-    assert L.qsa_decode_layer_scratch_bytes(0, GOOD, 8, 4) == 0
-    assert L.qsa_decode_layer_scratch_bytes(4, GOOD, 0, 4) == 0
+    assert need >= 4 * 24 * 4 * (128 * 4 + 9) + 4 * 4 * 16 * 4   # and the score rows of 16 columns
+    assert L.qsa_decode_layer_scratch_bytes(4, GOOD, 1024, 8, 4) >= need + 4 * 4 * (1024 - 16) * 4 - 256
+    assert L.qsa_decode_layer_scratch_bytes(0, GOOD, 16, 8, 4) == 0
+    assert L.qsa_decode_layer_scratch_bytes(4, GOOD, 16, 0, 4) == 0
+    assert L.qsa_decode_layer_scratch_bytes(4, GOOD, 0, 8, 4) == 0
     args = dict(q=1, pos=1, n_rows=4, pools=pools, n_pools=2, row_pool=1, dims=GOOD, nb=16, k=8, S=4, sm=1.0,
                 out=1, lse=None, scores=None, ids=None, counts=None, scratch=1, nbytes=need, stream=None)
 

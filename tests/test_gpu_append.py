@@ -111,7 +111,7 @@ def test_append_then_decode_layer():
     scores = torch.empty(n_rows, dims.n_kv_heads, nb, dtype=torch.float32, device="cuda")
     ids = torch.empty(n_rows, dims.n_kv_heads, w.topk, dtype=torch.int32, device="cuda")
     counts = torch.empty(n_rows, dims.n_kv_heads, dtype=torch.int32, device="cuda")
-    scratch = torch.empty(qsa.qsa_decode_layer_scratch_bytes(n_rows, dims, w.topk, 16), dtype=torch.uint8,
+    scratch = torch.empty(qsa.qsa_decode_layer_scratch_bytes(n_rows, dims, nb, w.topk, 16), dtype=torch.uint8,
                           device="cuda")
     qsa.qsa_decode_layer(dev(w.q), dev(w.pos), [p], dims, nb, w.topk, 16, out, lse, sm_scale=w.sm_scale,
                          scores=scores, ids=ids, counts=counts, scratch=scratch)

@@ -24,7 +24,7 @@ def run_layer(w, pdevs, dims, n_chunks, row_pool=None, nb=None, scratch=None, q=
     ids = torch.empty(n_rows, dims.n_kv_heads, w.topk, dtype=torch.int32, device="cuda")
     counts = torch.empty(n_rows, dims.n_kv_heads, dtype=torch.int32, device="cuda")
     if scratch is None:
-        scratch = torch.empty(qsa.qsa_decode_layer_scratch_bytes(n_rows, dims, w.topk, n_chunks), dtype=torch.uint8,
+        scratch = torch.empty(qsa.qsa_decode_layer_scratch_bytes(n_rows, dims, nb, w.topk, n_chunks), dtype=torch.uint8,
                               device="cuda")
     qsa.qsa_decode_layer(q, dev(w.pos), pdevs, dims, nb, w.topk, n_chunks, out, lse, sm_scale=w.sm_scale,
                          row_pool=row_pool, scores=scores if with_scores else None, ids=ids, counts=counts,
@@ -64,7 +64,7 @@ def test_layer_repeated_calls_reuse_scratch():
     w = small_workload(611, n_kv=2, G=6, rows=3, topk=8)
     dims = dims_of(w)
     p = build_index(to_device(w.pools[0]), dims)
-    scratch = torch.empty(qsa.qsa_decode_layer_scratch_bytes(3, dims, w.topk, 4), dtype=torch.uint8, device="cuda")
+    scratch = torch.empty(qsa.qsa_decode_layer_scratch_bytes(3, dims, -(-w.pools[0].n_valid // BLOCK), w.topk, 4), dtype=torch.uint8, device="cuda")
     for rep in range(3):
         w.q = synth.random_q(700 + rep, 3, dims.n_q_heads, dims.head_dim)
         got = run_layer(w, [p], dims, 4, scratch=scratch)
