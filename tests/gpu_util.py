@@ -69,11 +69,12 @@ def topk_margin_ok(s_ref, k, scale, tol=1e-5):
     return ok
 
 
-def decode_layer(w, p_dev, dims, n_chunks, ids_override=None):
-    """scores -> topk -> chunk -> merge for a one-pool workload; returns a dict of host arrays."""
+def decode_layer(w, p_dev, dims, n_chunks, ids_override=None, nb=None):
+    """scores -> topk -> chunk -> merge for a one-pool workload (score rows of nb columns, default the valid
+    blocks); returns a dict of host arrays."""
     pool = p_dev
     n_rows = w.q.shape[0]
-    nb = -(-w.pools[0].n_valid // BLOCK)
+    nb = nb or -(-w.pools[0].n_valid // BLOCK)
     q = dev(w.q)
     pos = dev(w.pos)
     scores = torch.empty(n_rows, dims.n_kv_heads, nb, dtype=torch.float32, device="cuda")

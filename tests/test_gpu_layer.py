@@ -119,6 +119,24 @@ def test_wide_rows_split_selection_matches_fused():
     assert np.array_equal(with_buf["ids"], res[1][0])
 
 
+@pytest.mark.parametrize("d,G,topk,n_valid,extra", [(128, 6, 200, 15_000, 0), (128, 2, 100, 15_000, 0),
+                                                    (64, 4, 256, 60_000, 0), (128, 6, 40, 15_000, 900)])
+def test_layer_large_k_and_width_limits(d, G, topk, n_valid, extra):
+    """Selections past 64 ids (read from LDS by the chunk workgroups), k at the fused limit of 256, and rows just past
+    the fused width limit (1,135 columns: the selection launch, then the chunks read the ids): the same ids, counts
+    and output as the separate calls."""
+    w = small_workload(900 + topk + G, n_kv=2, G=G, d=d, cap=n_valid + 64 * extra + 64, n_valid=n_valid, rows=3,
+                       topk=topk)
+    dims = dims_of(w)
+    p = build_index(to_device(w.pools[0]), dims)
+    nb = -(-n_valid // BLOCK) + extra
+    sep = decode_layer(w, p, dims, n_chunks=5, nb=nb)
+    got = run_layer(w, [p], dims, 5, nb=nb)
+    assert np.array_equal(got["scores"], sep["scores"])
+    assert np.array_equal(got["ids"], sep["ids"]) and np.array_equal(got["counts"], sep["counts"])
+    assert rel_err_rows(got["out"], sep["out"]).max() <= TOL
+
+
 def test_layer_verify_window_four_slots_four_chunks():
     """Four verify-window slots (one 200,000-cell pool each) in one call with 4 chunks per row, the launch shape of
     the benchmark's scale measurement: every wave of the chunk kernel takes several pieces."""
