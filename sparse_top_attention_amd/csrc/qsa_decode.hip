@@ -52,6 +52,25 @@ __device__ __forceinline__ h8 codes_h8(const v2i w)
     return r;
 }
 
+// Eight bytes of signed 4-bit code pairs (byte j: the codes of two adjacent dims of element j, the even dim in the
+// low nibble) as two sets of exact fp16, the even dims and the odd dims (the nibble n ^ 8 under the exponent of
+// 1024, minus 1032).
+__device__ __forceinline__ void nibbles_h8(const v2i w, h8 &even, h8 &odd)
+{
+    const h2 bias = {(_Float16)-1032.0f, (_Float16)-1032.0f};
+#pragma unroll
+    for (int q = 0; q < 2; q++) {
+        const uint32_t u = (uint32_t)w[q] ^ 0x88888888u;
+        const uint32_t ev = u & 0x0F0F0F0Fu, od = (u >> 4) & 0x0F0F0F0Fu;
+        const h2 e0 = __builtin_bit_cast(h2, __builtin_amdgcn_perm(0x64646464u, ev, 0x04010400u)) + bias;
+        const h2 e1 = __builtin_bit_cast(h2, __builtin_amdgcn_perm(0x64646464u, ev, 0x04030402u)) + bias;
+        const h2 o0 = __builtin_bit_cast(h2, __builtin_amdgcn_perm(0x64646464u, od, 0x04010400u)) + bias;
+        const h2 o1 = __builtin_bit_cast(h2, __builtin_amdgcn_perm(0x64646464u, od, 0x04030402u)) + bias;
+        even[4 * q] = e0[0]; even[4 * q + 1] = e0[1]; even[4 * q + 2] = e1[0]; even[4 * q + 3] = e1[1];
+        odd[4 * q] = o0[0]; odd[4 * q + 1] = o0[1]; odd[4 * q + 2] = o1[0]; odd[4 * q + 3] = o1[1];
+    }
+}
+
 // x = hi + lo with hi, lo fp16 (22 significant bits): hi is x with its float mantissa cut to 10 bits (exact in fp16
 // when |x| is in fp16's normal range), lo the exact remainder rounded to fp16.
 __device__ __forceinline__ void split_h2(const float x, _Float16 &hi, _Float16 &lo)
@@ -428,9 +447,12 @@ __global__ __launch_bounds__(64 * CW) void attn_chunk_kernel(const ChunkArgs a)
     // P[head][cell] V[cell][dim], all with v_mfma_f32_16x16x32_f16 (heads padded to 16 rows). K and V codes are exact
     // in fp16; q and p * v_scale go in as two fp16 terms (hi + lo, 22 significant bits) scaled by powers of two that
     // keep them in fp16's range, both terms accumulating into the same fp32 tile.
-    constexpr bool MPV = VB == 8 && D == 128 && G >= 4;
+    constexpr bool MPV = D == 128 && G >= 4;
     constexpr int NTL = D / 16;                      // 16-dim output tiles (MPV)
-    static_assert(!MPV || (NG == 2 && PC == 32 && CHUNKS == 8), "MFMA form: d = 128, 32-cell pieces");
+    static_assert(!MPV || (NG == 2 && PC == 32), "MFMA form: d = 128, 32-cell pieces");
+    // MFMA form: output tile t's lane jl holds dim 16 t + jl (int8 V); with 4-bit V a transposing read of 16-byte
+    // chunk c gives dims 32 c + 2 jl (low nibbles, tile 2 c) and 32 c + 2 jl + 1 (high nibbles, tile 2 c + 1)
+    auto tile_dim = [](int t, int l) { return VB == 8 ? 16 * t + l : 32 * (t >> 1) + 2 * l + (t & 1); };
     __shared__ __align__(16) int8_t sv[CW][PC * RB]; // the wave's V piece: [cell][RB], chunk c of row r at c ^ swizzle(r)
     // p * v_scale rows [cell][group][head] of the VALU p . v (the MFMA form keeps p in registers)
     __shared__ __align__(16) float sp[CW][MPV ? 4 : PC * NG * GP];
@@ -438,7 +460,7 @@ __global__ __launch_bounds__(64 * CW) void attn_chunk_kernel(const ChunkArgs a)
     __shared__ __align__(16) float so[CW][G + (MPV ? 1 : 0)][D];   // MPV: row G takes the padding heads' stores
     // MPV's V swizzle: the 8 rows of one transposing read (cells 4 G4 + e and 16 + 4 G4 + e) land on 8 distinct
     // 16-byte positions
-    auto mswz = [](int c) { return (c + 4 * (c >> 4)) & 7; };
+    auto mswz = [](int c) { return (c + 4 * (c >> 4)) & SWZ; };
     __shared__ __align__(16) float sq[G * D];        // the G q rows of (row i, KV head g)
     const int tid = threadIdx.x, lane = tid % 64;
     const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
@@ -748,12 +770,27 @@ __global__ __launch_bounds__(64 * CW) void attn_chunk_kernel(const ChunkArgs a)
             __builtin_amdgcn_s_waitcnt(0);   // the V piece has landed (this wave's copies)
             const int i8 = jl >> 1;
             const int vcell = 4 * G4 + (i8 & 3) + 16 * (i8 >> 2);
+            if constexpr (VB == 8) {
 #pragma unroll
-            for (int tt = 0; tt < NTL; tt++) {
-                const h8 bv = codes_h8(__builtin_amdgcn_ds_read_tr8_b64_v2i32(
-                    (QSA_LDS v2i *)(svw + vcell * RB + 16 * (tt ^ mswz(vcell)) + 8 * (jl & 1))));
-                oacc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi[tt / (NTL / NG)], bv, oacc[tt], 0, 0, 0);
-                oacc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo[tt / (NTL / NG)], bv, oacc[tt], 0, 0, 0);
+                for (int tt = 0; tt < NTL; tt++) {
+                    const h8 bv = codes_h8(__builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                        (QSA_LDS v2i *)(svw + vcell * RB + 16 * (tt ^ mswz(vcell)) + 8 * (jl & 1))));
+                    oacc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi[tt / (NTL / NG)], bv, oacc[tt], 0, 0, 0);
+                    oacc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo[tt / (NTL / NG)], bv, oacc[tt], 0, 0, 0);
+                }
+            } else {
+#pragma unroll
+                for (int c = 0; c < CHUNKS; c++) {
+                    h8 bv0, bv1;
+                    nibbles_h8(__builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                                   (QSA_LDS v2i *)(svw + vcell * RB + 16 * (c ^ mswz(vcell)) + 8 * (jl & 1))),
+                               bv0, bv1);
+                    const int t0 = 2 * c, t1 = 2 * c + 1;
+                    oacc[t0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi[t0 / (NTL / NG)], bv0, oacc[t0], 0, 0, 0);
+                    oacc[t1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi[t1 / (NTL / NG)], bv1, oacc[t1], 0, 0, 0);
+                    oacc[t0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo[t0 / (NTL / NG)], bv0, oacc[t0], 0, 0, 0);
+                    oacc[t1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo[t1 / (NTL / NG)], bv1, oacc[t1], 0, 0, 0);
+                }
             }
         } else {
             // ---- loads: K slices and scales into registers, the V piece into LDS
@@ -916,7 +953,7 @@ __global__ __launch_bounds__(64 * CW) void attn_chunk_kernel(const ChunkArgs a)
                 for (int e = 0; e < 4; e++) {
                     const int h = 4 * G4 + e;
                     if (h < G)
-                        a.o_out[(row0 + (int64_t)h * a.max_chunks) * D + 16 * t + jl] =
+                        a.o_out[(row0 + (int64_t)h * a.max_chunks) * D + tile_dim(t, jl)] =
                             __builtin_amdgcn_ldexpf(oacc[t][e], -srun);
                 }
             }
@@ -962,7 +999,7 @@ __global__ __launch_bounds__(64 * CW) void attn_chunk_kernel(const ChunkArgs a)
 #pragma unroll
             for (int e = 0; e < 4; e++) {
                 const int h = 4 * G4 + e;
-                so[wave][h < G ? h : G][16 * t + jl] = __builtin_amdgcn_ldexpf(oacc[t][e], -srun);
+                so[wave][h < G ? h : G][tile_dim(t, jl)] = __builtin_amdgcn_ldexpf(oacc[t][e], -srun);
             }
         }
     } else {
