@@ -1100,8 +1100,11 @@ __global__ __launch_bounds__(64 * NW) void attn_merge_kernel(const float *__rest
                                                          float *__restrict__ out, float *__restrict__ lse)
 {
     constexpr int DW = D / DS;                    // dims of this workgroup's slice of the row
-    static_assert(DW % 64 == 0, "lanes own whole dims");
-    constexpr int VPL = DW / 64;
+    static_assert(DW % 64 == 0 || DW == 32, "lanes own whole dims");
+    // a slice of 32 dims: lanes 0-31 take the even chunks of each row step, lanes 32-63 the odd ones
+    constexpr int CPL = DW < 64 ? 2 : 1;          // chunks per row step
+    constexpr int VPL = DW < 64 ? 1 : DW / 64;
+    const int sub = CPL == 2 ? (int)(threadIdx.x % 64) / 32 : 0, dl = (int)(threadIdx.x % 64) % (64 / CPL);
     __shared__ float sM[NW], sL[NW];
     __shared__ float sO[NW][DW];
     const int tid = threadIdx.x, lane = tid % 64;
@@ -1119,11 +1122,12 @@ __global__ __launch_bounds__(64 * NW) void attn_merge_kernel(const float *__rest
     const int32_t jlast = n_chunks - 1;           // n_chunks >= 1: every clamped index is in bounds
     auto clamp_j = [&](int32_t jj) { return jj < jlast ? jj : jlast; };
 
-    // the first batch (up to 64 chunks, one per lane, and the first U o rows), all loads before any wait
+    // the first batch (up to 64 chunks, one per lane, and the first U row steps of o), all loads before any wait
     float ov0[U][VPL];
 #pragma unroll
     for (int u = 0; u < U; u++) {
-        const float *src = o + (base + clamp_j(j0 + (u < nq ? u : 0))) * D + VPL * lane;
+        const int c = CPL * u + sub;
+        const float *src = o + (base + clamp_j(j0 + (c < nq ? c : 0))) * D + VPL * dl;
 #pragma unroll
         for (int e = 0; e < VPL; e++) ov0[u][e] = src[e];
     }
@@ -1157,11 +1161,26 @@ __global__ __launch_bounds__(64 * NW) void attn_merge_kernel(const float *__rest
     auto add_rows = [&](const float (&ov)[U][VPL], int32_t c0, int32_t nb, int32_t flag, float wgt) {
 #pragma unroll
         for (int u = 0; u < U; u++) {
-            const int c = c0 + u;
-            if (c < nb && __builtin_amdgcn_readlane(flag, c)) {
-                const float wu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wgt), c));
+            if constexpr (CPL == 1) {
+                const int c = c0 + u;
+                if (c < nb && __builtin_amdgcn_readlane(flag, c)) {
+                    const float wu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wgt), c));
 #pragma unroll
-                for (int e = 0; e < VPL; e++) acc[e] = fmaf(wu, ov[u][e], acc[e]);
+                    for (int e = 0; e < VPL; e++) acc[e] = fmaf(wu, ov[u][e], acc[e]);
+                }
+            } else {
+                // the even and the odd chunk of the step; a lane takes its half's, and skips it by select when it
+                // is past the batch or empty (an empty chunk's row may hold anything)
+                const int c = c0 + 2 * u;
+                if (c < nb) {
+                    const int c1 = c + 1 < 64 ? c + 1 : 63;
+                    const bool l0 = __builtin_amdgcn_readlane(flag, c) != 0;
+                    const bool l1 = c + 1 < nb && __builtin_amdgcn_readlane(flag, c1) != 0;
+                    const float w0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wgt), c));
+                    const float w1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wgt), c1));
+                    const float t = fmaf(sub ? w1 : w0, ov[u][0], acc[0]);
+                    acc[0] = (sub ? l1 : l0) ? t : acc[0];
+                }
             }
         }
     };
@@ -1173,13 +1192,13 @@ __global__ __launch_bounds__(64 * NW) void attn_merge_kernel(const float *__rest
         int32_t c0 = 0;
         if (first) {
             add_rows(ov0, 0, nb, flag, wgt);
-            c0 = U;
+            c0 = CPL * U;
         }
-        for (; c0 < nb; c0 += U) {
+        for (; c0 < nb; c0 += CPL * U) {
             float ov[U][VPL];
 #pragma unroll
             for (int u = 0; u < U; u++) {
-                const float *src = o + (base + jb + min(c0 + u, nb - 1)) * D + VPL * lane;
+                const float *src = o + (base + jb + min(c0 + CPL * u + sub, nb - 1)) * D + VPL * dl;
 #pragma unroll
                 for (int e = 0; e < VPL; e++) ov[u][e] = src[e];
             }
@@ -1196,8 +1215,10 @@ __global__ __launch_bounds__(64 * NW) void attn_merge_kernel(const float *__rest
         }
     }
     if (lane == 0) sL[wave] = L;
+    if constexpr (CPL == 2) acc[0] = sum32(acc[0]);   // the even and odd chunks' sums of dim dl
 #pragma unroll
-    for (int e = 0; e < VPL; e++) sO[wave][VPL * lane + e] = acc[e];
+    for (int e = 0; e < VPL; e++)
+        if (sub == 0) sO[wave][VPL * dl + e] = acc[e];
     __syncthreads();
     if (wave == 0) {
         float Lt = sL[0];
@@ -1206,11 +1227,11 @@ __global__ __launch_bounds__(64 * NW) void attn_merge_kernel(const float *__rest
         const bool none = M == -INFINITY;
 #pragma unroll
         for (int e = 0; e < VPL; e++) {
-            const int d = VPL * lane + e;
+            const int d = VPL * dl + e;
             float num = sO[0][d];
 #pragma unroll
             for (int w = 1; w < NW; w++) num += sO[w][d];
-            out[(int64_t)row * D + d] = none ? 0.f : num / Lt;
+            if (sub == 0) out[(int64_t)row * D + d] = none ? 0.f : num / Lt;
         }
         if (lse && lane == 0 && dsl == 0) lse[row] = none ? -INFINITY : M + logf(Lt);
     }
@@ -1420,15 +1441,15 @@ qsa_status qsa::merge_launch(const float *m, const float *l, const float *o, con
 {
     const uint32_t rows = (uint32_t)n_rows * (uint32_t)n_qh;
     // a few chunks: 4 waves, 8 rows in flight each, one workgroup per (row, head); many (a dense window): 16 waves,
-    // 16 rows in flight each, and the head's dims split over D/64 workgroups, so more CUs stream the o rows (each
-    // re-reads the chunks' m, l and empty marks)
+    // 16 steps of two chunks in flight each, and the head's dims split over D/32 workgroups of 32 dims, so more CUs
+    // stream the o rows (each re-reads the chunks' m, l and empty marks)
 #define QSA_MERGE(DD)                                                                                              \
     do {                                                                                                           \
         if (n_chunks <= 64)                                                                                        \
             attn_merge_kernel<DD, 4, 8, 1><<<dim3(rows, 1), 256, 0, s>>>(m, l, o, empty, max_chunks, n_chunks,      \
                                                                        n_active, n_qh, out, lse);                 \
         else                                                                                                       \
-            attn_merge_kernel<DD, 16, 32, DD / 64><<<dim3(rows, DD / 64), 1024, 0, s>>>(                          \
+            attn_merge_kernel<DD, 16, 16, DD / 32><<<dim3(rows, DD / 32), 1024, 0, s>>>(                          \
                 m, l, o, empty, max_chunks, n_chunks, n_active, n_qh, out, lse);                                  \
     } while (0)
     switch (head_dim) {

@@ -181,6 +181,29 @@ def test_merge_active_and_garbage():
     assert np.abs(lse.cpu().numpy() - ref_lse).max() <= TOL * np.abs(ref_lse).max()
 
 
+@pytest.mark.parametrize("S,n_act", [(150, None), (97, np.array([97, 65, 3], np.int32))])
+def test_merge_many_chunks_skips_empty_garbage(S, n_act):
+    """More than 64 chunks (the merge's split-dims form, two chunks per row step): chunks marked empty hold NaN in
+    m, l and o and change nothing; an odd number of active chunks leaves the last step's second chunk unused."""
+    w = small_workload(47)
+    pool = w.pools[0]
+    dims = dims_of(w)
+    m, l, o, e = oracle.chunk_partials(w.q, w.pos, pool, 2, S, bpc=1)
+    assert e[:, :, 30:].all() and not e[:, :, :5].any()
+    m32, l32, o32 = m.astype(np.float32), l.astype(np.float32), o.astype(np.float32)
+    m32[e.astype(bool)] = np.nan
+    l32[e.astype(bool)] = np.nan
+    o32[e.astype(bool)] = np.nan
+    part = qsa.Partials(dev(m32), dev(l32), dev(o32), dev(e))
+    out = torch.empty(3, 6, 128, dtype=torch.float32, device="cuda")
+    lse = torch.empty(3, 6, dtype=torch.float32, device="cuda")
+    qsa.qsa_attn_merge(part, dims, S, out, lse, n_active=None if n_act is None else dev(n_act))
+    torch.cuda.synchronize()
+    ref, ref_lse = oracle.merge(m, l, o, e, n_active=n_act)
+    assert rel_err_rows(out.cpu().numpy(), ref).max() <= TOL
+    assert np.abs(lse.cpu().numpy() - ref_lse).max() <= TOL * np.abs(ref_lse).max()
+
+
 def test_merge_of_oracle_partials():
     """The merge alone, fed FP64-computed partials rounded to fp32."""
     w = small_workload(43)
