@@ -498,15 +498,17 @@ __global__ __launch_bounds__(64 * CW) void attn_chunk_kernel(const ChunkArgs a)
     const int32_t *blist = sel && !fz ? a.ids + row_kv * a.topk : a.pos + i;
     const int32_t words = *(lane == 1 ? p_pidx : (lane == 2 ? p_cnt : a.pos + i));
     const int32_t idv = blist[sel && !fz && lane < a.topk ? lane : 0];   // k <= 64: the whole id list, one per lane
-    // fused selection: the score row's keys, 4 consecutive columns per thread (rows of up to 1,024 columns)
+    // fused selection: the score row's keys, one column per thread up to 256 columns, else 4 consecutive columns
+    // per thread (rows of up to 1,024 columns)
     __shared__ int32_t s_ids[FUSED_TOPK_MAX_K];
     __shared__ int32_t s_cnt;
     uint32_t key[4];
+    const bool one_key = a.width <= 64 * CW;
     if (fz) {
         const float *srow = a.scores + row_kv * a.width;
 #pragma unroll
         for (int e = 0; e < 4; e++) {
-            const int32_t c = 4 * tid + e;
+            const int32_t c = one_key ? (e == 0 ? tid : a.width) : 4 * tid + e;
             key[e] = c < a.width ? score_key(srow[c]) : 0u;
         }
     }
@@ -520,7 +522,12 @@ __global__ __launch_bounds__(64 * CW) void attn_chunk_kernel(const ChunkArgs a)
     if (fz) {
         // the same top-k as the selection kernels (the result is unique: the k largest keys, ties to the lower
         // column, in column order), into LDS; the first chunk's workgroup also stores it
-        radix_topk<4, CW>(key, a.topk, s_ids, &s_cnt);
+        if (one_key) {
+            const uint32_t key1[1] = {key[0]};
+            radix_topk<1, CW>(key1, a.topk, s_ids, &s_cnt);
+        } else {
+            radix_topk<4, CW>(key, a.topk, s_ids, &s_cnt);
+        }
         __syncthreads();
         cnt_fz = __builtin_amdgcn_readfirstlane(s_cnt);
         if (blockIdx.x == 0) {
