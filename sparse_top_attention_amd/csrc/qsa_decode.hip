@@ -312,13 +312,15 @@ __global__ __launch_bounds__(64) void block_scores_kernel(const float *__restric
 // streams a row's index through one CU): the block-score kernel's arithmetic, in the same order, over every pool of
 // the window. Workgroup (block range, g, p) scores the rows whose row_pool is p against pool p's index rows; pool 0's
 // workgroups also write -inf rows for the rows whose pool index is out of range, which then select nothing.
+constexpr int SCORE_STEPS = 2;   // steps of blocks per wave of the score-row kernel (more waves beat fewer, wider)
+
 template <int D>
 __global__ __launch_bounds__(64) void select_scores_kernel(const SelectArgs a)
 {
     // one wave per (tile of BPS * NSTEP blocks, KV head g, row i): the row's words and q rows, then the tile's index
     // rows of the row's pool (the block-score arithmetic: 8-dim fmaf chains per lane, a DPP sum over the block's
     // lanes); blocks past the pool's valid cells, and every block of a row whose pool index is out of range, are -inf
-    constexpr int LPB = D / 8, BPS = 64 / LPB, NSTEP = 4;
+    constexpr int LPB = D / 8, BPS = 64 / LPB, NSTEP = SCORE_STEPS;
     const int lane = threadIdx.x, rb = lane / LPB, s = lane % LPB;
     const int32_t g = blockIdx.y, i = blockIdx.z;
     const int32_t bw = blockIdx.x * (BPS * NSTEP);
@@ -1311,7 +1313,7 @@ extern "C" qsa_status qsa_kv_append(const qsa_pool *pools, int32_t n_pools, cons
 qsa_status qsa::select_scores_launch(const SelectArgs &a, int32_t n_rows, int32_t n_kv, int32_t head_dim,
                                      hipStream_t s)
 {
-    const int32_t per_wave = (64 / (head_dim / 8)) * 4;
+    const int32_t per_wave = (64 / (head_dim / 8)) * SCORE_STEPS;
     dim3 grid(ceil_div(a.width, per_wave), n_kv, n_rows);
     switch (head_dim) {
     case 64: select_scores_kernel<64><<<grid, 64, 0, s>>>(a); break;
