@@ -238,7 +238,9 @@ def bench_decode(args):
             torch.cuda.synchronize()
         return a.elapsed_time(b) * 1e3 / (reps * L)
 
-    # each kernel alone, back to back over the pool copies (the layer runs them one after the other)
+    # each call alone, back to back over the pool copies: the one-launch selection of qsa_decode_select (the layer
+    # itself writes score rows in one launch and takes the top-k inside its chunk launch for rows of up to 1,024
+    # blocks), the chunk kernel from given ids (the roofline's kernel) and the merge
     breakdown = {}
     separate = None
     if not dense:
