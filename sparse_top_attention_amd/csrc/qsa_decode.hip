@@ -426,8 +426,8 @@ constexpr int CW = 4;
 // VB is the V code width: 8 (int8) or 4 (K8V4: two signed 4-bit codes per byte, dim 2j in the low nibble). A V row
 // is RB = D * VB / 8 bytes; a 16-byte chunk of it holds DPC = 128 / VB dims, so a transposing read gives each lane
 // 8 / VB dims of 8 cells and a lane makes NT = DPL * VB / 8 reads per 8 cells. The K side is the same for both.
-template <int D, int G, int VB, int WPC>
-__global__ __launch_bounds__(64 * CW) void attn_chunk_kernel(const ChunkArgs a)
+template <int D, int G, int VB, int WPC, bool FZ>
+__device__ __forceinline__ void attn_chunk_body(const ChunkArgs &a)
 {
     static_assert(VB == 8 || (VB == 4 && D >= 128), "K8V4 needs head_dim >= 128");
     constexpr int PC = D <= 128 ? 32 : 16;           // cells per piece
@@ -493,7 +493,7 @@ __global__ __launch_bounds__(64 * CW) void attn_chunk_kernel(const ChunkArgs a)
         }
     }
     const int64_t row_kv = (int64_t)i * a.n_kv + g;
-    const bool fz = a.scores != nullptr;                  // fused selection (workgroup-uniform)
+    constexpr bool fz = FZ;                               // fused selection: a.scores holds the score rows
     const bool sel = a.ids != nullptr || fz, mp = a.row_pool != nullptr;
     const int32_t *p_pidx = mp ? a.row_pool + i : a.pos + i;
     const int32_t *p_cnt = sel && !fz ? a.counts + row_kv : a.pos + i;
@@ -1094,6 +1094,20 @@ __global__ __launch_bounds__(64 * CW) void attn_chunk_kernel(const ChunkArgs a)
     }
 }
 
+// The chunk kernel from given ids (or dense), and the decode layer's form that takes each row's top-k itself from its
+// score row: two kernels, so that neither carries the other's code.
+template <int D, int G, int VB, int WPC>
+__global__ __launch_bounds__(64 * CW) void attn_chunk_kernel(const ChunkArgs a)
+{
+    attn_chunk_body<D, G, VB, WPC, false>(a);
+}
+
+template <int D, int G, int VB, int WPC>
+__global__ __launch_bounds__(64 * CW) void attn_chunk_select_kernel(const ChunkArgs a)
+{
+    attn_chunk_body<D, G, VB, WPC, true>(a);
+}
+
 // ---------------------------------------------------------------------------------------------------- merge
 // One workgroup of NW waves per (row, q head); each wave takes a contiguous 1/NW of the active chunks. A wave reads
 // the (m, l, empty) of up to 64 of its chunks at once, one chunk per lane, so the max M over the non-empty chunks,
@@ -1352,16 +1366,22 @@ namespace {
 template <int D, int VB, int W>
 void launch_chunk_g(int G, dim3 grid, hipStream_t s, const ChunkArgs &a)
 {
+#define QSA_CHUNK(GG)                                                                                              \
+    do {                                                                                                           \
+        if (a.scores) attn_chunk_select_kernel<D, GG, VB, W><<<grid, 64 * CW, 0, s>>>(a);                          \
+        else attn_chunk_kernel<D, GG, VB, W><<<grid, 64 * CW, 0, s>>>(a);                                          \
+    } while (0)
     switch (G) {
-    case 1: attn_chunk_kernel<D, 1, VB, W><<<grid, 64 * CW, 0, s>>>(a); break;
-    case 2: attn_chunk_kernel<D, 2, VB, W><<<grid, 64 * CW, 0, s>>>(a); break;
-    case 3: attn_chunk_kernel<D, 3, VB, W><<<grid, 64 * CW, 0, s>>>(a); break;
-    case 4: attn_chunk_kernel<D, 4, VB, W><<<grid, 64 * CW, 0, s>>>(a); break;
-    case 5: attn_chunk_kernel<D, 5, VB, W><<<grid, 64 * CW, 0, s>>>(a); break;
-    case 6: attn_chunk_kernel<D, 6, VB, W><<<grid, 64 * CW, 0, s>>>(a); break;
-    case 7: attn_chunk_kernel<D, 7, VB, W><<<grid, 64 * CW, 0, s>>>(a); break;
-    default: attn_chunk_kernel<D, 8, VB, W><<<grid, 64 * CW, 0, s>>>(a); break;
+    case 1: QSA_CHUNK(1); break;
+    case 2: QSA_CHUNK(2); break;
+    case 3: QSA_CHUNK(3); break;
+    case 4: QSA_CHUNK(4); break;
+    case 5: QSA_CHUNK(5); break;
+    case 6: QSA_CHUNK(6); break;
+    case 7: QSA_CHUNK(7); break;
+    default: QSA_CHUNK(8); break;
     }
+#undef QSA_CHUNK
 }
 
 template <int D, int VB>
