@@ -10,7 +10,9 @@ exceed the 256 MB Infinity Cache, so K/V come from HBM; the layers are replayed 
 
 Prints one JSON line. `value` = algorithmic bytes of a layer / time per layer (GB/s); `roofline` reports the chunk
 kernel (the dominant one): its algorithmic bytes per launch / its average launch duration, timed with HIP events
-around graphs of back-to-back launches on the stream the kernels run on.
+around graphs of back-to-back launches on the stream the kernels run on. The prompt chunk's roofline counts useful
+ops (4 x head_dim per visible (query, q head, cell) pair) against the int8 peak; the digit-plane and issued int8
+MFMA op counts are reported beside it under their own keys.
 """
 from __future__ import annotations
 
@@ -589,11 +591,26 @@ def copy_calibration(nbytes=1 << 28, reps=4):
 
 
 def prompt_ops(w):
-    """Algorithmic int8 ops of one prompt chunk: for every (query, q head) and every visible cell, 128 multiply-adds
-    for q.k and 128 for p.v, each done on three digit planes, 2 ops per multiply-add."""
+    """Ops of one prompt chunk, per visible (query, q head, cell) pair:
+    useful   -- the attention itself: d multiply-adds for q.k and d for p.v, 2 ops each (4 d per pair);
+    planes   -- the same products on the pages' three 8-bit digit planes each (12 d per pair), the int8 work the
+                pages' 24-bit split method implies;
+    issued   -- the int8 MFMA ops the kernel actually issues: per 64-row block of a KV head and per 64-cell tile up
+                to the block's last visible cell, 4 waves x (24 + 32) v_mfma_i32_16x16x64_i8 of 16*16*64*2 ops
+                (3 q digit planes x 2 groups x 4 cell blocks for S^T, 4 p.w digit planes x 8 dim tiles for O^T);
+                masked cells and padding rows included."""
     n_valid = w.pools[0].n_valid
     vis = sum(min(n_valid, int(p) + 1) for p in w.pos)
-    return vis * w.n_q_heads * w.head_dim * 2 * 3 * 2, vis
+    pairs = vis * w.n_q_heads
+    G = w.n_q_heads // w.n_kv_heads
+    R = len(w.pos) * G
+    tiles = 0
+    for rb in range(-(-R // 64)):
+        rlast = min(rb * 64 + 63, R - 1)
+        c_end = min(n_valid, w.pos0 + rlast // G + 1)
+        tiles += -(-c_end // 64)
+    issued = tiles * w.n_kv_heads * 4 * (24 + 32) * 16 * 16 * 64 * 2
+    return {"useful": pairs * w.head_dim * 4, "planes": pairs * w.head_dim * 12, "issued": issued}, vis
 
 
 def bench_prompt(args, steps, main_line):
@@ -648,16 +665,28 @@ def bench_prompt(args, steps, main_line):
         torch.cuda.synchronize()
     n_calls = reps * n_copies
     ms = e0.elapsed_time(e1) / n_calls
-    ops, vis = prompt_ops(w)
+    opc, vis = prompt_ops(w)
+    ops = opc["useful"]
     tops = ops / (ms * 1e-3) / 1e12
+
+    def frac(n):
+        return round(n / (ms * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4)
+
     res = {
         "workload": "prompt_chunk", "queries": n_q, "pos0": w.pos0, "n_valid": pool_np.n_valid,
         "q_heads": w.n_q_heads, "kv_heads": w.n_kv_heads, "head_dim": w.head_dim,
-        "ms_per_call": round(ms, 4), "calls_timed": n_calls, "int8_ops_per_call": int(ops),
+        "ms_per_call": round(ms, 4), "calls_timed": n_calls,
         "roofline": {"bound": "mfma", "kernel": "qsa_prompt_attn (q split + attention + chunk merge)",
                      "achieved": round(tops, 1), "peak": INT8_PEAK_TOPS, "unit": "TOPS",
                      "frac": round(tops / INT8_PEAK_TOPS, 4), "ops_per_launch": int(ops),
+                     "ops": "useful: 4 x head_dim per visible (query, q head, cell) pair (q.k and p.v)",
                      "traffic": measured_traffic("prompt_attn_prompt_chunk")},
+        "digit_plane_ops": {"ops_per_call": int(opc["planes"]), "frac_of_int8_peak": frac(opc["planes"]),
+                            "about": "the useful products on three 8-bit digit planes each (the pages' 24-bit "
+                                     "split): 3x the useful ops"},
+        "issued_int8_mfma_ops": {"ops_per_call": int(opc["issued"]), "frac_of_int8_peak": frac(opc["issued"]),
+                                 "about": "int8 MFMA ops the kernel issues (3 q planes + 4 p.w planes, whole "
+                                          "64-cell tiles, padded rows): the matrix cores' busy share"},
     }
     if main_line:
         res = {

@@ -1,7 +1,7 @@
 """Python binding of libqsa (QSA attention over an int8 KV cache, MI355X / gfx950).
 
-Argument marshalling only: every function checks dtypes, devices and contiguity of torch tensors, passes their
-device pointers and the current HIP stream to the C ABI declared in include/qsa.h, and raises QSAError on a
+Argument marshalling only: every function checks dtypes, devices, contiguity and sizes of torch tensors (the sizes
+against the dims, row counts, k, n_blocks and max_chunks the C side will index them by), passes their device pointers and the current HIP stream to the C ABI declared in include/qsa.h, and raises QSAError on a
 non-zero status. No torch operator runs on the compute path; PyTorch supplies device memory and streams.
 
 The library is the in-tree ``libqsa.so``; importing this package raises if it has not been built (there is no
@@ -104,6 +104,39 @@ def _ptr(t: Optional[torch.Tensor], dtype, name, allow_none=False):
     return t.data_ptr()
 
 
+def _need(t: Optional[torch.Tensor], n: int, name: str):
+    """The C side indexes t as n elements (its size cannot be checked on the device): refuse a smaller tensor."""
+    if t is not None and t.numel() < n:
+        raise ValueError(f"{name}: the call reads or writes {n} elements, the tensor holds {t.numel()}")
+
+
+def _shape(t: Optional[torch.Tensor], shape, name: str):
+    if t is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _rows_of(q: torch.Tensor, dims: "Dims", name="q"):
+    """q is [n_rows][n_q_heads][head_dim] (or [n_rows][n_q_heads * head_dim])."""
+    if q.dim() < 1:
+        raise ValueError(f"{name}: expected [n_rows][n_q_heads][head_dim]")
+    n = q.shape[0]
+    _need(q, n * dims.n_q_heads * dims.head_dim, name)
+    if q.numel() != n * dims.n_q_heads * dims.head_dim:
+        raise ValueError(f"{name}: expected {n} x {dims.n_q_heads} x {dims.head_dim} elements, got {q.numel()}")
+    return n
+
+
+def _check_pools(pools: Sequence["Pool"], dims: "Dims", need_index=False):
+    if len(pools) == 0:
+        raise ValueError("at least one pool is required")
+    for p in pools:
+        p.check(dims, need_index)
+
+
+def _pool_array(pools: Sequence["Pool"]):
+    return (_Pool * len(pools))(*[p.c() for p in pools])
+
+
 def _stream(stream):
     if stream is None:
         stream = torch.cuda.current_stream()
@@ -143,6 +176,21 @@ class Pool:
     def capacity(self):
         return self.k.shape[1]
 
+    def check(self, dims: "Dims", need_index=False):
+        """Every tensor's shape against dims and the capacity k implies (the kernels index them by those)."""
+        if self.k.dim() != 3:
+            raise ValueError("k: expected [n_kv_heads][capacity][head_dim]")
+        n_kv, cap, d = dims.n_kv_heads, self.capacity, dims.head_dim
+        _shape(self.k, (n_kv, cap, d), "k")
+        _shape(self.k_scale, (n_kv, cap, max(d // 64, 1)), "k_scale")
+        _shape(self.v, (n_kv, cap, d if self.v_bits in (0, 8) else d // 2), "v")
+        _shape(self.v_scale, (n_kv, cap, max(d // 64, 1)), "v_scale")
+        _shape(self.index, (n_kv, -(-cap // BLOCK), d), "index")
+        if need_index and self.index is None:
+            raise ValueError("index: the selection calls need the pool's block index")
+        if not 0 <= self.n_valid <= cap:
+            raise ValueError(f"n_valid {self.n_valid} outside [0, capacity {cap}]")
+
     def c(self):
         return _Pool(_ptr(self.k, torch.int8, "k"), _ptr(self.k_scale, torch.float32, "k_scale"),
                      _ptr(self.v, torch.int8, "v"), _ptr(self.v_scale, torch.float32, "v_scale"),
@@ -169,6 +217,14 @@ class Partials:
                         torch.empty(n_rows, n_q_heads, max_chunks, head_dim, dtype=torch.float32, device=device),
                         torch.empty(n_rows, n_q_heads, max_chunks, dtype=torch.uint8, device=device))
 
+    def check(self, n_rows: int, dims: "Dims"):
+        """m, l, empty [>= n_rows][n_q_heads][max_chunks] and o [...][head_dim], the strides the kernels use."""
+        mc = self.max_chunks
+        _need(self.m, n_rows * dims.n_q_heads * mc, "partials m")
+        _need(self.l, n_rows * dims.n_q_heads * mc, "partials l")
+        _need(self.empty, n_rows * dims.n_q_heads * mc, "partials empty")
+        _need(self.o, n_rows * dims.n_q_heads * mc * dims.head_dim, "partials o")
+
     def c(self):
         return _Partials(_ptr(self.m, torch.float32, "m"), _ptr(self.l, torch.float32, "l"),
                          _ptr(self.o, torch.float32, "o"), _ptr(self.empty, torch.uint8, "empty"), self.max_chunks)
@@ -176,6 +232,8 @@ class Partials:
 
 # --------------------------------------------------------------------------------------------- the calls
 def qsa_block_index(pool: Pool, dims: Dims, cell_begin: int, cell_end: int, index: torch.Tensor, stream=None):
+    pool.check(dims)
+    _shape(index, (dims.n_kv_heads, -(-pool.capacity // BLOCK), dims.head_dim), "index")
     p = pool.c()
     _check("qsa_block_index", _lib().qsa_block_index(ctypes.byref(p), dims.c(), cell_begin, cell_end,
                                                      _ptr(index, torch.float32, "index"), _stream(stream)))
@@ -183,9 +241,13 @@ def qsa_block_index(pool: Pool, dims: Dims, cell_begin: int, cell_end: int, inde
 
 
 def qsa_block_scores(q, pos, pool: Pool, dims: Dims, n_blocks: int, scores, stream=None):
+    pool.check(dims, need_index=True)
+    n = _rows_of(q, dims)
+    _need(pos, n, "pos")
+    _need(scores, n * dims.n_kv_heads * n_blocks, "scores")
     p = pool.c()
     _check("qsa_block_scores", _lib().qsa_block_scores(_ptr(q, torch.float32, "q"), _ptr(pos, torch.int32, "pos"),
-                                                       q.shape[0], ctypes.byref(p), dims.c(), n_blocks,
+                                                       n, ctypes.byref(p), dims.c(), n_blocks,
                                                        _ptr(scores, torch.float32, "scores"), _stream(stream)))
     return scores
 
@@ -197,6 +259,8 @@ def qsa_topk_scratch_bytes(n_rows, width, k):
 def qsa_topk(scores, k, ids, counts, scratch=None, stream=None):
     width = scores.shape[-1]
     n_rows = scores.numel() // width if width else 0
+    _need(ids, n_rows * k, "ids")
+    _need(counts, n_rows, "counts")
     sp = None if scratch is None else _ptr(scratch, torch.uint8, "scratch")
     nbytes = 0 if scratch is None else scratch.numel()
     _check("qsa_topk", _lib().qsa_topk(_ptr(scores, torch.float32, "scores"), n_rows, width, k,
@@ -207,11 +271,18 @@ def qsa_topk(scores, k, ids, counts, scratch=None, stream=None):
 
 def qsa_attn_chunk(q, pos, pools: Sequence[Pool], dims: Dims, out: Partials, n_chunks: int, sm_scale: float = 1.0,
                    row_pool=None, ids=None, counts=None, blocks_per_chunk: int = 1, stream=None):
-    arr = (_Pool * len(pools))(*[p.c() for p in pools])
+    _check_pools(pools, dims)
+    n = _rows_of(q, dims)
     k = ids.shape[-1] if ids is not None else 0
+    _need(pos, n, "pos")
+    _need(row_pool, n, "row_pool")
+    _need(ids, n * dims.n_kv_heads * k, "ids")
+    _need(counts, n * dims.n_kv_heads, "counts")
+    out.check(n, dims)
     part = out.c()
+    arr = _pool_array(pools)
     _check("qsa_attn_chunk", _lib().qsa_attn_chunk(
-        _ptr(q, torch.float32, "q"), _ptr(pos, torch.int32, "pos"), q.shape[0], arr, len(pools),
+        _ptr(q, torch.float32, "q"), _ptr(pos, torch.int32, "pos"), n, arr, len(pools),
         _ptr(row_pool, torch.int32, "row_pool", allow_none=True), dims.c(),
         _ptr(ids, torch.int32, "ids", allow_none=True), _ptr(counts, torch.int32, "counts", allow_none=True), k,
         blocks_per_chunk, n_chunks, sm_scale, ctypes.byref(part), _stream(stream)))
@@ -219,15 +290,26 @@ def qsa_attn_chunk(q, pos, pools: Sequence[Pool], dims: Dims, out: Partials, n_c
 
 
 def qsa_attn_merge(part: Partials, dims: Dims, n_chunks: int, out, lse=None, n_active=None, stream=None):
+    n = part.m.shape[0]
+    part.check(n, dims)
+    _need(out, n * dims.n_q_heads * dims.head_dim, "out")
+    _need(lse, n * dims.n_q_heads, "lse")
+    _need(n_active, n, "n_active")
     pc = part.c()
     _check("qsa_attn_merge", _lib().qsa_attn_merge(
-        ctypes.byref(pc), part.m.shape[0], dims.c(), n_chunks, _ptr(n_active, torch.int32, "n_active", True),
+        ctypes.byref(pc), n, dims.c(), n_chunks, _ptr(n_active, torch.int32, "n_active", True),
         _ptr(out, torch.float32, "out"), _ptr(lse, torch.float32, "lse", allow_none=True), _stream(stream)))
     return out
 
 
 def qsa_kv_append(pools: Sequence[Pool], dims: Dims, k_new, v_new, cells, row_pool=None, stream=None):
-    arr = (_Pool * len(pools))(*[p.c() for p in pools])
+    _check_pools(pools, dims)
+    n = k_new.shape[0]
+    _need(k_new, n * dims.n_kv_heads * dims.head_dim, "k_new")
+    _need(v_new, n * dims.n_kv_heads * dims.head_dim, "v_new")
+    _need(cells, n, "cells")
+    _need(row_pool, n, "row_pool")
+    arr = _pool_array(pools)
     _check("qsa_kv_append", _lib().qsa_kv_append(
         arr, len(pools), _ptr(row_pool, torch.int32, "row_pool", allow_none=True), dims.c(),
         _ptr(k_new, torch.float32, "k_new"), _ptr(v_new, torch.float32, "v_new"), _ptr(cells, torch.int32, "cells"),
@@ -236,9 +318,16 @@ def qsa_kv_append(pools: Sequence[Pool], dims: Dims, k_new, v_new, cells, row_po
 
 def qsa_decode_select(q, pos, pools: Sequence[Pool], dims: Dims, n_blocks: int, k: int, ids, counts, scores=None,
                       row_pool=None, stream=None):
-    arr = (_Pool * len(pools))(*[p.c() for p in pools])
+    _check_pools(pools, dims, need_index=True)
+    n = _rows_of(q, dims)
+    _need(pos, n, "pos")
+    _need(row_pool, n, "row_pool")
+    _need(ids, n * dims.n_kv_heads * k, "ids")
+    _need(counts, n * dims.n_kv_heads, "counts")
+    _need(scores, n * dims.n_kv_heads * n_blocks, "scores")
+    arr = _pool_array(pools)
     _check("qsa_decode_select", _lib().qsa_decode_select(
-        _ptr(q, torch.float32, "q"), _ptr(pos, torch.int32, "pos"), q.shape[0], arr, len(pools),
+        _ptr(q, torch.float32, "q"), _ptr(pos, torch.int32, "pos"), n, arr, len(pools),
         _ptr(row_pool, torch.int32, "row_pool", allow_none=True), dims.c(), n_blocks, k,
         _ptr(scores, torch.float32, "scores", allow_none=True), _ptr(ids, torch.int32, "ids"),
         _ptr(counts, torch.int32, "counts"), _stream(stream)))
@@ -252,11 +341,20 @@ def qsa_decode_layer_scratch_bytes(n_rows, dims: Dims, n_blocks, k, n_chunks):
 def qsa_decode_layer(q, pos, pools: Sequence[Pool], dims: Dims, n_blocks: int, k: int, n_chunks: int, out, lse=None,
                      sm_scale: float = 1.0, row_pool=None, scores=None, ids=None, counts=None, scratch=None,
                      stream=None):
-    arr = (_Pool * len(pools))(*[p.c() for p in pools])
+    _check_pools(pools, dims, need_index=True)
+    n = _rows_of(q, dims)
+    _need(pos, n, "pos")
+    _need(row_pool, n, "row_pool")
+    _need(out, n * dims.n_q_heads * dims.head_dim, "out")
+    _need(lse, n * dims.n_q_heads, "lse")
+    _need(scores, n * dims.n_kv_heads * n_blocks, "scores")
+    _need(ids, n * dims.n_kv_heads * k, "ids")
+    _need(counts, n * dims.n_kv_heads, "counts")
     sp = None if scratch is None else _ptr(scratch, torch.uint8, "scratch")
     nbytes = 0 if scratch is None else scratch.numel()
+    arr = _pool_array(pools)
     _check("qsa_decode_layer", _lib().qsa_decode_layer(
-        _ptr(q, torch.float32, "q"), _ptr(pos, torch.int32, "pos"), q.shape[0], arr, len(pools),
+        _ptr(q, torch.float32, "q"), _ptr(pos, torch.int32, "pos"), n, arr, len(pools),
         _ptr(row_pool, torch.int32, "row_pool", allow_none=True), dims.c(), n_blocks, k, n_chunks, sm_scale,
         _ptr(out, torch.float32, "out"), _ptr(lse, torch.float32, "lse", allow_none=True),
         _ptr(scores, torch.float32, "scores", allow_none=True), _ptr(ids, torch.int32, "ids", allow_none=True),
@@ -269,10 +367,13 @@ def qsa_prompt_scratch_bytes(n_q, pos0, dims: Dims):
 
 
 def qsa_prompt_attn(q, pos0: int, pool: Pool, dims: Dims, out, sm_scale: float = 1.0, scratch=None, stream=None):
+    pool.check(dims)
+    n = _rows_of(q, dims)
+    _need(out, n * dims.n_q_heads * dims.head_dim, "out")
     p = pool.c()
     sp = None if scratch is None else _ptr(scratch, torch.uint8, "scratch")
     nbytes = 0 if scratch is None else scratch.numel()
-    _check("qsa_prompt_attn", _lib().qsa_prompt_attn(_ptr(q, torch.float32, "q"), q.shape[0], pos0,
+    _check("qsa_prompt_attn", _lib().qsa_prompt_attn(_ptr(q, torch.float32, "q"), n, pos0,
                                                      ctypes.byref(p), dims.c(), sm_scale,
                                                      _ptr(out, torch.float32, "out"), sp, nbytes, _stream(stream)))
     return out

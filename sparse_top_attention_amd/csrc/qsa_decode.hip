@@ -1497,7 +1497,8 @@ extern "C" qsa_status qsa_attn_merge(const qsa_partials *in, int32_t n_rows, qsa
     if (st != QSA_OK) return st;
     if (!in || !out) return QSA_ERR_NULL;
     if (!in->m || !in->l || !in->o || !in->empty) return QSA_ERR_NULL;
-    if (n_rows < 0 || n_chunks < 0) return QSA_ERR_SHAPE;
+    if (n_rows < 0) return QSA_ERR_SHAPE;
+    if (n_chunks < 1) return QSA_ERR_RANGE;   // the merge kernel reads chunk n_chunks - 1 as its clamp target
     if (n_chunks > in->max_chunks) return QSA_ERR_SCRATCH;
     if (n_rows == 0) return QSA_OK;
     return merge_launch(in->m, in->l, in->o, in->empty, in->max_chunks, n_chunks, n_active, n_rows, dims.n_q_heads,

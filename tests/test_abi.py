@@ -147,6 +147,10 @@ def test_merge_validation():
     assert L.qsa_attn_merge(None, 4, GOOD, 8, None, 1, None, None) == -1
     assert L.qsa_attn_merge(ctypes.byref(parts), 4, GOOD, 8, None, None, None, None) == -1
     assert L.qsa_attn_merge(ctypes.byref(parts), 0, GOOD, 8, None, 1, None, None) == 0
+    # no chunks to fold: refused before any launch (the kernel's clamp target would be chunk -1)
+    assert L.qsa_attn_merge(ctypes.byref(parts), 4, GOOD, 0, None, 1, None, None) == -5
+    assert L.qsa_attn_merge(ctypes.byref(parts), 0, GOOD, 0, None, 1, None, None) == -5
+    assert L.qsa_attn_merge(ctypes.byref(parts), 4, GOOD, -1, None, 1, None, None) == -5
 
 
 def test_prompt_validation():
@@ -244,3 +248,77 @@ def test_v_bits_validation():
     p4 = _pool(v_bits=4)
     assert L.qsa_prompt_attn(1, 16, 0, ctypes.byref(p4), GOOD, 1.0, 1, 1, 1 << 30, None) == -3
     assert L.qsa_kv_append((qsa._Pool * 1)(_pool(v_bits=4)), 1, None, D(4, 4, 64, 64), 1, 1, 1, 4, None) == -3
+
+
+# ------------------------------------------------------------------ the binding's size checks (CPU tensors)
+# The C side cannot see the size of a device buffer, so the binding checks every tensor against the sizes the call
+# will index it by, before any pointer is taken. CPU tensors suffice: a size error is raised before the device check.
+import torch  # noqa: E402
+
+
+def _cpu_pool(n_kv=2, cap=300, d=128, v_bits=8, index=True):
+    g = max(d // 64, 1)
+    return qsa.Pool(torch.zeros(n_kv, cap, d, dtype=torch.int8), torch.zeros(n_kv, cap, g),
+                    torch.zeros(n_kv, cap, d if v_bits == 8 else d // 2, dtype=torch.int8), torch.zeros(n_kv, cap, g),
+                    cap, torch.zeros(n_kv, -(-cap // 64), d) if index else None, v_bits)
+
+
+SIZE_ERR = r"expected shape|reads or writes|elements|n_valid|index"
+
+
+def test_binding_rejects_pool_shapes():
+    dims = qsa.Dims(12, 2, 128)
+    good = _cpu_pool()
+    good.check(dims, need_index=True)
+    bad_scale = _cpu_pool()
+    bad_scale.k_scale = torch.zeros(2, 300, 1)
+    bad_v = _cpu_pool()
+    bad_v.v = torch.zeros(2, 299, 128, dtype=torch.int8)
+    bad_index = _cpu_pool()
+    bad_index.index = torch.zeros(2, 4, 128)
+    bad_n = _cpu_pool()
+    bad_n.n_valid = 301
+    for p in (bad_scale, bad_v, bad_index, bad_n):
+        with pytest.raises(ValueError, match=SIZE_ERR):
+            p.check(dims)
+    with pytest.raises(ValueError, match=SIZE_ERR):
+        _cpu_pool(index=False).check(dims, need_index=True)
+    with pytest.raises(ValueError, match=SIZE_ERR):          # pools for another head count
+        good.check(qsa.Dims(12, 3, 128))
+    _cpu_pool(v_bits=4).check(dims)                          # K8V4: v holds two codes per byte
+
+
+def test_binding_rejects_short_buffers():
+    dims = qsa.Dims(12, 2, 128)
+    p = _cpu_pool()
+    q = torch.zeros(3, 12, 128)
+    pos = torch.zeros(3, dtype=torch.int32)
+    with pytest.raises(ValueError, match=SIZE_ERR):          # pos of 2 rows for 3 rows of q
+        qsa.qsa_block_scores(q, pos[:2], p, dims, 5, torch.zeros(3, 2, 5))
+    with pytest.raises(ValueError, match=SIZE_ERR):          # score rows narrower than n_blocks
+        qsa.qsa_block_scores(q, pos, p, dims, 5, torch.zeros(3, 2, 4))
+    with pytest.raises(ValueError, match=SIZE_ERR):          # q with the wrong head count
+        qsa.qsa_block_scores(torch.zeros(3, 10, 128), pos, p, dims, 5, torch.zeros(3, 2, 5))
+    part = qsa.Partials.empty_like_shape(3, 12, 4, 128, device="cpu")
+    ids = torch.zeros(3, 2, 6, dtype=torch.int32)
+    with pytest.raises(ValueError, match=SIZE_ERR):          # counts of 2 rows
+        qsa.qsa_attn_chunk(q, pos, [p], dims, part, 4, ids=ids, counts=torch.zeros(2, 2, dtype=torch.int32))
+    short = qsa.Partials(part.m, part.l, part.o[:2], part.empty)
+    with pytest.raises(ValueError, match=SIZE_ERR):          # o of 2 rows of partials
+        qsa.qsa_attn_chunk(q, pos, [p], dims, short, 4, blocks_per_chunk=1)
+    with pytest.raises(ValueError, match=SIZE_ERR):          # merge output of 2 rows
+        qsa.qsa_attn_merge(part, dims, 4, torch.zeros(2, 12, 128))
+    with pytest.raises(ValueError, match=SIZE_ERR):
+        qsa.qsa_attn_merge(part, dims, 4, torch.zeros(3, 12, 128), lse=torch.zeros(3, 11))
+    with pytest.raises(ValueError, match=SIZE_ERR):          # layer ids narrower than k
+        qsa.qsa_decode_layer(q, pos, [p], dims, 5, 3, 2, torch.zeros(3, 12, 128), ids=torch.zeros(3, 2, 2))
+    with pytest.raises(ValueError, match=SIZE_ERR):
+        qsa.qsa_decode_select(q, pos, [p], dims, 5, 3, torch.zeros(3, 2, 3, dtype=torch.int32),
+                              torch.zeros(3, dtype=torch.int32))
+    with pytest.raises(ValueError, match=SIZE_ERR):          # cells of 1 row for 2 new rows
+        qsa.qsa_kv_append([p], dims, torch.zeros(2, 2, 128), torch.zeros(2, 2, 128), torch.zeros(1, dtype=torch.int32))
+    with pytest.raises(ValueError, match=SIZE_ERR):          # prompt output of 2 queries for 3
+        qsa.qsa_prompt_attn(q, 10, p, dims, torch.zeros(2, 12, 128))
+    with pytest.raises(ValueError, match=SIZE_ERR):          # top-k ids narrower than k
+        qsa.qsa_topk(torch.zeros(4, 16), 5, torch.zeros(4, 4, dtype=torch.int32), torch.zeros(4, dtype=torch.int32))
+

@@ -69,6 +69,26 @@ def test_prompt_single_chunk_path():
             assert rel_err_rows(got[i, h][None], ref[None]).max() <= TOL, (i, h)
 
 
+def test_prompt_forced_fold_past_1024_tiles():
+    """One cell chunk longer than 1,024 tiles of 64 cells: the PV int32 sums are folded into fp32 every 1,024
+    tiles whether or not the row max moved (8 KV heads x 4,096 queries fill the chip without splitting the cells,
+    and pos0 = 66,000 gives every workgroup at least 1,032 tiles). Checked on sampled rows."""
+    n_kv, G, n_q, pos0 = 8, 1, 4096, 66000
+    n_valid = pos0 + n_q
+    dims = qsa.Dims(n_kv * G, n_kv, 128)
+    pool = synth.random_pool(341, n_kv, n_valid + 40, n_valid, 128)
+    q = synth.random_q(342, n_q, n_kv * G, 128)
+    got = run_prompt(q, pos0, to_device(pool), dims)
+    assert np.all(np.isfinite(got))
+    pos = (pos0 + np.arange(n_q)).astype(np.int32)
+    rng = np.random.default_rng(9)
+    picks = [(0, 0), (63, 3), (64, 4), (4095, 7), (4032, 1)]
+    picks += [(int(i), int(h)) for i, h in zip(rng.integers(0, n_q, 11), rng.integers(0, n_kv, 11))]
+    for i, h in picks:
+        ref, _ = oracle.attn_one(q, pos, i, h, pool, n_kv)
+        assert rel_err_rows(got[i, h][None], ref[None]).max() <= TOL, (i, h)
+
+
 def test_prompt_chunk_full_size_sampled():
     """The 2,048-query prompt chunk at the end of a 32,768-cell context, checked on sampled rows."""
     w = synth.workload("prompt_chunk")
