@@ -207,6 +207,24 @@ qsa_status qsa_decode_layer(const float *q, const int32_t *pos, int32_t n_rows, 
                             float sm_scale, float *out, float *lse, float *scores, int32_t *ids, int32_t *counts,
                             void *scratch, size_t scratch_bytes, qsa_stream_t stream);
 
+/* Bytes of device scratch qsa_decode_layer_noalloc may use: qsa_decode_layer_scratch_bytes of its arguments must not
+ * exceed this (8 MiB: the verify window's 4 rows at 16 chunks need 0.8 MiB, 32 rows of 24 heads at 16 chunks 6.3 MiB). */
+#define QSA_NOALLOC_SCRATCH_BYTES (8u << 20)
+
+/* qsa_decode_layer for callers that cannot allocate device memory (code under HIP graph capture, serving loops or
+ * harnesses that forbid hipMalloc): the same launches, arithmetic and outputs, with the scratch taken from a
+ * file-scope device array of QSA_NOALLOC_SCRATCH_BYTES that each GPU holds from the first call on it until the
+ * process ends. The caller still passes every input and output. Calls no hipMalloc/hipFree or allocating routine.
+ * Returns QSA_ERR_SCRATCH, having launched nothing, when qsa_decode_layer_scratch_bytes(n_rows, dims, n_blocks, k,
+ * n_chunks) > QSA_NOALLOC_SCRATCH_BYTES; QSA_ERR_LAUNCH if the array's device address cannot be obtained. Every
+ * call on one GPU shares that GPU's array (it keeps the last call's contents; nothing in it must start at zero):
+ * calls that may overlap on one GPU -- on different streams, or from different threads -- race and must be ordered
+ * by the caller. The library's otherwise stateless convention does not hold for this call. */
+qsa_status qsa_decode_layer_noalloc(const float *q, const int32_t *pos, int32_t n_rows, const qsa_pool *pools,
+                                    int32_t n_pools, const int32_t *row_pool, qsa_dims dims, int32_t n_blocks,
+                                    int32_t k, int32_t n_chunks, float sm_scale, float *out, float *lse,
+                                    float *scores, int32_t *ids, int32_t *counts, qsa_stream_t stream);
+
 /* Static, human-readable name of a status code. */
 const char *qsa_status_str(qsa_status status);
 

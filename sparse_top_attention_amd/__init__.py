@@ -23,6 +23,7 @@ QSA_OK = 0
 STATUS_NAMES = {0: "QSA_OK", -1: "QSA_ERR_NULL", -2: "QSA_ERR_SHAPE", -3: "QSA_ERR_UNSUPPORTED",
                 -4: "QSA_ERR_SCRATCH", -5: "QSA_ERR_RANGE", -6: "QSA_ERR_LAUNCH"}
 BLOCK = 64
+NOALLOC_SCRATCH_BYTES = 8 << 20   # QSA_NOALLOC_SCRATCH_BYTES in include/qsa.h
 
 
 class QSAError(RuntimeError):
@@ -75,10 +76,13 @@ def _lib():
         L.qsa_decode_layer_scratch_bytes.restype = SZ
         L.qsa_decode_layer.argtypes = [P, P, I32, PP, I32, P, PD, I32, I32, I32, ctypes.c_float, P, P, P, P, P, P,
                                        SZ, P]
+        L.qsa_decode_layer_noalloc.argtypes = [P, P, I32, PP, I32, P, PD, I32, I32, I32, ctypes.c_float, P, P, P, P,
+                                               P, P]
         L.qsa_status_str.argtypes = [I32]
         L.qsa_status_str.restype = ctypes.c_char_p
         for fn in ("qsa_block_index", "qsa_block_scores", "qsa_topk", "qsa_attn_chunk", "qsa_attn_merge",
-                   "qsa_prompt_attn", "qsa_decode_layer", "qsa_decode_select", "qsa_kv_append"):
+                   "qsa_prompt_attn", "qsa_decode_layer", "qsa_decode_select", "qsa_kv_append",
+                   "qsa_decode_layer_noalloc"):
             getattr(L, fn).restype = I32
         _L = L
     return _L
@@ -362,6 +366,29 @@ def qsa_decode_layer(q, pos, pools: Sequence[Pool], dims: Dims, n_blocks: int, k
     return out
 
 
+def qsa_decode_layer_noalloc(q, pos, pools: Sequence[Pool], dims: Dims, n_blocks: int, k: int, n_chunks: int, out,
+                             lse=None, sm_scale: float = 1.0, row_pool=None, scores=None, ids=None, counts=None,
+                             stream=None):
+    """qsa_decode_layer with the library's per-device static scratch (no scratch argument, nothing allocated)."""
+    _check_pools(pools, dims, need_index=True)
+    n = _rows_of(q, dims)
+    _need(pos, n, "pos")
+    _need(row_pool, n, "row_pool")
+    _need(out, n * dims.n_q_heads * dims.head_dim, "out")
+    _need(lse, n * dims.n_q_heads, "lse")
+    _need(scores, n * dims.n_kv_heads * n_blocks, "scores")
+    _need(ids, n * dims.n_kv_heads * k, "ids")
+    _need(counts, n * dims.n_kv_heads, "counts")
+    arr = _pool_array(pools)
+    _check("qsa_decode_layer_noalloc", _lib().qsa_decode_layer_noalloc(
+        _ptr(q, torch.float32, "q"), _ptr(pos, torch.int32, "pos"), n, arr, len(pools),
+        _ptr(row_pool, torch.int32, "row_pool", allow_none=True), dims.c(), n_blocks, k, n_chunks, sm_scale,
+        _ptr(out, torch.float32, "out"), _ptr(lse, torch.float32, "lse", allow_none=True),
+        _ptr(scores, torch.float32, "scores", allow_none=True), _ptr(ids, torch.int32, "ids", allow_none=True),
+        _ptr(counts, torch.int32, "counts", allow_none=True), _stream(stream)))
+    return out
+
+
 def qsa_prompt_scratch_bytes(n_q, pos0, dims: Dims):
     return _lib().qsa_prompt_scratch_bytes(n_q, pos0, dims.c())
 
@@ -385,5 +412,6 @@ def qsa_status_str(status: int) -> str:
 
 __all__ = ["Dims", "Pool", "Partials", "QSAError", "qsa_block_index", "qsa_block_scores", "qsa_topk_scratch_bytes",
            "qsa_topk", "qsa_attn_chunk", "qsa_attn_merge", "qsa_prompt_scratch_bytes", "qsa_prompt_attn",
-           "qsa_decode_select", "qsa_decode_layer_scratch_bytes", "qsa_decode_layer", "qsa_kv_append",
+           "qsa_decode_select", "qsa_decode_layer_scratch_bytes", "qsa_decode_layer", "qsa_decode_layer_noalloc",
+           "qsa_kv_append",
            "qsa_status_str", "lib_handle"]

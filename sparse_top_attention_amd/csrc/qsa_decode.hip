@@ -14,6 +14,8 @@
 
 #include <math.h>
 
+#include <mutex>
+
 namespace qsa {
 
 constexpr float LOG2E = 1.4426950408889634f;
@@ -1580,25 +1582,29 @@ extern "C" size_t qsa_decode_layer_scratch_bytes(int32_t n_rows, qsa_dims dims, 
     return layer_layout(n_rows, dims, n_blocks, k, n_chunks).total;
 }
 
-extern "C" qsa_status qsa_decode_layer(const float *q, const int32_t *pos, int32_t n_rows, const qsa_pool *pools,
-                                       int32_t n_pools, const int32_t *row_pool, qsa_dims dims, int32_t n_blocks,
-                                       int32_t k, int32_t n_chunks, float sm_scale, float *out, float *lse,
-                                       float *scores, int32_t *ids, int32_t *counts, void *scratch,
-                                       size_t scratch_bytes, qsa_stream_t stream)
+namespace {
+// Host-side checks of qsa_decode_layer's arguments (everything but the scratch buffer); fills sa and vb.
+qsa_status layer_setup(const float *q, const int32_t *pos, int32_t n_rows, const qsa_pool *pools, int32_t n_pools,
+                       const int32_t *row_pool, const qsa_dims &dims, int32_t n_blocks, int32_t k, int32_t n_chunks,
+                       const float *out, SelectArgs &sa, int &vb)
 {
-    SelectArgs sa;
     qsa_status st = select_setup(q, pos, n_rows, pools, n_pools, row_pool, dims, n_blocks, k, sa);
     if (st != QSA_OK) return st;
     if (!out) return QSA_ERR_NULL;
     if (n_chunks < 1) return QSA_ERR_RANGE;
-    const int vb = common_v_bits(pools, n_pools, dims.head_dim);
+    vb = common_v_bits(pools, n_pools, dims.head_dim);
     if (!vb) return QSA_ERR_UNSUPPORTED;
-    if (n_rows == 0) return QSA_OK;
+    return QSA_OK;
+}
+
+// The three launches of the decode layer over a scratch region `base` already checked to hold layer_layout's total.
+qsa_status layer_launch(const float *q, const int32_t *pos, int32_t n_rows, const qsa_pool *pools, int32_t n_pools,
+                        const int32_t *row_pool, const qsa_dims &dims, int32_t n_blocks, int32_t k, int32_t n_chunks,
+                        float sm_scale, float *out, float *lse, float *scores, int32_t *ids, int32_t *counts,
+                        SelectArgs &sa, int vb, char *base, hipStream_t s)
+{
+    qsa_status st;
     const LayerScratch lay = layer_layout(n_rows, dims, n_blocks, k, n_chunks);
-    if (!scratch) return QSA_ERR_NULL;
-    if (scratch_bytes < lay.total) return QSA_ERR_SCRATCH;
-    char *base = static_cast<char *>(scratch);
-    hipStream_t s = (hipStream_t)stream;
 
     sa.ids = ids ? ids : reinterpret_cast<int32_t *>(base + lay.ids);
     sa.counts = counts ? counts : reinterpret_cast<int32_t *>(base + lay.counts);
@@ -1633,6 +1639,70 @@ extern "C" qsa_status qsa_decode_layer(const float *q, const int32_t *pos, int32
     if ((st = launch_status()) != QSA_OK) return st;
     return merge_launch(a.m_out, a.l_out, a.o_out, a.empty_out, n_chunks, n_chunks, nullptr, n_rows, dims.n_q_heads,
                         dims.head_dim, out, lse, s);
+}
+}  // namespace
+
+extern "C" qsa_status qsa_decode_layer(const float *q, const int32_t *pos, int32_t n_rows, const qsa_pool *pools,
+                                       int32_t n_pools, const int32_t *row_pool, qsa_dims dims, int32_t n_blocks,
+                                       int32_t k, int32_t n_chunks, float sm_scale, float *out, float *lse,
+                                       float *scores, int32_t *ids, int32_t *counts, void *scratch,
+                                       size_t scratch_bytes, qsa_stream_t stream)
+{
+    SelectArgs sa;
+    int vb = 0;
+    qsa_status st = layer_setup(q, pos, n_rows, pools, n_pools, row_pool, dims, n_blocks, k, n_chunks, out, sa, vb);
+    if (st != QSA_OK) return st;
+    if (n_rows == 0) return QSA_OK;
+    if (!scratch) return QSA_ERR_NULL;
+    if (scratch_bytes < layer_layout(n_rows, dims, n_blocks, k, n_chunks).total) return QSA_ERR_SCRATCH;
+    return layer_launch(q, pos, n_rows, pools, n_pools, row_pool, dims, n_blocks, k, n_chunks, sm_scale, out, lse,
+                        scores, ids, counts, sa, vb, static_cast<char *>(scratch), (hipStream_t)stream);
+}
+
+// ============================================================================ decode layer without allocation
+// The scratch of qsa_decode_layer_noalloc: one file-scope device array, so callers that cannot allocate (code under
+// graph capture, serving loops that forbid it) pass only their inputs and outputs. Each GPU the library runs on holds
+// its own copy for the life of the process. On the host the array's name is a stand-in, not a device address: the
+// device address comes from hipGetSymbolAddress, once per device, and only that address is handed to kernels.
+namespace {
+static __device__ __align__(256) char layer_scratch_static[QSA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int MAX_DEVICES = 64;
+std::mutex static_scratch_mutex;
+char *static_scratch_ptr[MAX_DEVICES];   // per device, set on the first call on that device
+
+qsa_status static_scratch(char **ptr)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return QSA_ERR_LAUNCH;
+    std::lock_guard<std::mutex> lock(static_scratch_mutex);
+    if (!static_scratch_ptr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(layer_scratch_static)) != hipSuccess || !p) return QSA_ERR_LAUNCH;
+        static_scratch_ptr[dev] = static_cast<char *>(p);
+    }
+    *ptr = static_scratch_ptr[dev];
+    return QSA_OK;
+}
+}  // namespace
+
+extern "C" qsa_status qsa_decode_layer_noalloc(const float *q, const int32_t *pos, int32_t n_rows,
+                                               const qsa_pool *pools, int32_t n_pools, const int32_t *row_pool,
+                                               qsa_dims dims, int32_t n_blocks, int32_t k, int32_t n_chunks,
+                                               float sm_scale, float *out, float *lse, float *scores, int32_t *ids,
+                                               int32_t *counts, qsa_stream_t stream)
+{
+    SelectArgs sa;
+    int vb = 0;
+    qsa_status st = layer_setup(q, pos, n_rows, pools, n_pools, row_pool, dims, n_blocks, k, n_chunks, out, sa, vb);
+    if (st != QSA_OK) return st;
+    if (n_rows == 0) return QSA_OK;
+    if (layer_layout(n_rows, dims, n_blocks, k, n_chunks).total > (size_t)QSA_NOALLOC_SCRATCH_BYTES)
+        return QSA_ERR_SCRATCH;
+    char *base = nullptr;
+    if ((st = static_scratch(&base)) != QSA_OK) return st;
+    return layer_launch(q, pos, n_rows, pools, n_pools, row_pool, dims, n_blocks, k, n_chunks, sm_scale, out, lse,
+                        scores, ids, counts, sa, vb, base, (hipStream_t)stream);
 }
 
 extern "C" const char *qsa_status_str(qsa_status status)

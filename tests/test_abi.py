@@ -24,7 +24,8 @@ def test_header_declares_the_calls():
     names = declared_functions()
     for fn in ["qsa_block_index", "qsa_block_scores", "qsa_topk", "qsa_topk_scratch_bytes", "qsa_attn_chunk",
                "qsa_attn_merge", "qsa_prompt_attn", "qsa_prompt_scratch_bytes", "qsa_decode_layer",
-               "qsa_decode_layer_scratch_bytes", "qsa_decode_select", "qsa_kv_append", "qsa_status_str"]:
+               "qsa_decode_layer_scratch_bytes", "qsa_decode_select", "qsa_kv_append", "qsa_status_str",
+               "qsa_decode_layer_noalloc"]:
         assert fn in names
 
 
@@ -322,3 +323,23 @@ def test_binding_rejects_short_buffers():
     with pytest.raises(ValueError, match=SIZE_ERR):          # top-k ids narrower than k
         qsa.qsa_topk(torch.zeros(4, 16), 5, torch.zeros(4, 4, dtype=torch.int32), torch.zeros(4, dtype=torch.int32))
 
+
+def test_noalloc_layer_refuses_oversized_scratch_before_any_hip_call():
+    """qsa_decode_layer_noalloc checks its scratch need against the static array's size (QSA_NOALLOC_SCRATCH_BYTES)
+    on the host, before touching the device: an oversized layer is refused here, where there is no GPU."""
+    L = qsa.lib_handle()
+    text = open(HEADER).read()
+    assert re.search(r"#define QSA_NOALLOC_SCRATCH_BYTES \(8u << 20\)", text)
+    assert qsa.NOALLOC_SCRATCH_BYTES == 8 << 20
+    pools = (qsa._Pool * 1)(_pool(cap=200_000, n_valid=65_536))
+    need = L.qsa_decode_layer_scratch_bytes(64, GOOD, 1024, 64, 64)
+    assert need > qsa.NOALLOC_SCRATCH_BYTES
+    st = L.qsa_decode_layer_noalloc(1, 1, 64, pools, 1, None, GOOD, 1024, 64, 64, 1.0, 1, None, None, None, None, None)
+    assert st == -4
+    # the usual argument checks come first
+    assert L.qsa_decode_layer_noalloc(1, 1, 64, pools, 1, None, GOOD, 1024, 64, 0, 1.0, 1, None, None, None, None,
+                                      None) == -5
+    assert L.qsa_decode_layer_noalloc(1, 1, 64, pools, 1, None, GOOD, 1024, 64, 4, 1.0, None, None, None, None, None,
+                                      None) == -1
+    assert L.qsa_decode_layer_noalloc(1, 1, 0, pools, 1, None, GOOD, 1024, 64, 4, 1.0, 1, None, None, None, None,
+                                      None) == 0
