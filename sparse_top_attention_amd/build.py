@@ -10,7 +10,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libqsa.so")
-SOURCES = ["qsa_decode.hip", "qsa_topk.hip", "qsa_prompt.hip"]
+SOURCES = ["qsa_decode.hip", "qsa_topk.hip", "qsa_prompt.hip", "qsa_chunk_d64_v8.hip", "qsa_chunk_d128_v8.hip",
+           "qsa_chunk_d128_v4.hip", "qsa_chunk_d256_v8.hip", "qsa_chunk_d256_v4.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # Packed-FP32 VALU ops are switched off on purpose (-packed-fp32-ops): the kernels use scalar fp32 FMAs only.
@@ -21,7 +22,7 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-u
 
 # The decode chunk kernel's matrix-core accumulators are rescaled by the VALU between products: keeping them in
 # ordinary VGPRs saves the copies to and from the accumulation registers.
-EXTRA = {"qsa_decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+EXTRA = {src: ["-mllvm", "-amdgpu-mfma-vgpr-form"] for src in SOURCES if src.startswith("qsa_chunk_")}
 
 
 def _compile(src):
@@ -35,7 +36,7 @@ def _compile(src):
 
 def build(verbose=False):
     os.makedirs(BUILD, exist_ok=True)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(int(os.environ.get("MAX_JOBS", "8")), len(SOURCES))) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIB + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
