@@ -55,10 +55,19 @@ def parse():
     return ap.parse_args()
 
 
-def measured_traffic(key):
-    """Per-launch HBM bytes (read + write) measured with rocprofv3 byte counters for this kernel source, or None
-    once the source has changed since the counters were taken."""
+def sources_hash(paths):
+    """sha256 (first 16 hex digits) of the concatenated contents of the kernel's source files."""
     import hashlib
+    h = hashlib.sha256()
+    for rel in paths:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(key):
+    """Per-launch HBM bytes (read + write) measured with rocprofv3 byte counters for this kernel's sources, or None
+    once a source has changed since the counters were taken."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
@@ -66,10 +75,33 @@ def measured_traffic(key):
         entry = json.load(f).get(key)
     if not entry:
         return None
-    with open(os.path.join(ROOT, entry["source"]), "rb") as f:
-        if hashlib.sha256(f.read()).hexdigest()[:16] != entry["sha256_16"]:
+    srcs = entry.get("sources") or [entry.get("source")]
+    try:
+        if sources_hash(srcs) != entry["sha256_16"]:
             return None
+    except (OSError, TypeError, KeyError):
+        return None
     return int(entry["read_bytes"] + entry["write_bytes"])
+
+
+def measured_hbm_gbs(nbytes=1 << 30, reps=10):
+    """HBM bandwidth a plain device-to-device copy reaches on this GPU (bytes read + written per second): the
+    measured peak printed beside the datasheet's."""
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    gbs = 2 * nbytes * reps / (a.elapsed_time(b) * 1e-3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    return round(gbs, 1)
 
 
 def union_cells(ids, counts, pos, n_valid, n_kv):
@@ -225,6 +257,7 @@ def bench_decode(args):
         torch.cuda.synchronize()
     ms_total = e0.elapsed_time(e1)
     ms_per_step = ms_total / args.steps
+    hbm_gbs = measured_hbm_gbs()
 
     # ---- per-kernel average launch durations: graphs of L back-to-back launches of one kernel, one per copy
     def kernel_avg_us(fn_per_copy, reps=20, pools=None):
@@ -317,7 +350,8 @@ def bench_decode(args):
         "roofline": {"bound": "hbm", "kernel": chunk_key, "achieved": round(chunk_gbs, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(chunk_gbs / HBM_PEAK_GBS, 4),
                      "bytes_per_launch": int(chunk_bytes),
-                     "traffic": measured_traffic(f"{chunk_key}_{args.workload}") if args.chunks == 0 else None},
+                     "traffic": measured_traffic(f"{chunk_key}_{args.workload}") if args.chunks == 0 else None,
+                     "measured_peak": hbm_gbs, "frac_of_measured_peak": round(chunk_gbs / hbm_gbs, 4)},
         "cpu_baseline": None,
     }
 
