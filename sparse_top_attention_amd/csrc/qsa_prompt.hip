@@ -369,10 +369,9 @@ __global__ __launch_bounds__(256, 2) void prompt_attn_kernel(const PromptArgs a)
             }
         const int i = n16 >> 1, hh = n16 & 1;
         const int c0 = 16 * G4 + i, c1 = c0 + 8;   // (c & 7) == i for both
-        __builtin_amdgcn_s_setprio(1);
+        v4i pd[2][4];   // [group][digit plane d3, d2, d1, d0] of the lane's 16 cells
 #pragma unroll
         for (int grp = 0; grp < 2; grp++) {
-            v4i pd[4];   // digit planes d3, d2, d1, d0 of the lane's 16 cells
 #pragma unroll
             for (int b = 0; b < 4; b++) {
                 const int cl0 = 16 * G4 + 4 * b;
@@ -384,11 +383,19 @@ __global__ __launch_bounds__(256, 2) void prompt_attn_kernel(const PromptArgs a)
                 for (int v = 0; v < 4; v++) u[v] = (uint32_t)fmaf(p[b][v], wv[v], PBIAS);
                 const uint32_t A01 = bperm(u[1], u[0], 0x05010400u), B01 = bperm(u[1], u[0], 0x07030602u);
                 const uint32_t A23 = bperm(u[3], u[2], 0x05010400u), B23 = bperm(u[3], u[2], 0x07030602u);
-                pd[3][b] = (int32_t)(bperm(A23, A01, 0x05040100u) ^ 0x80808080u);
-                pd[2][b] = (int32_t)(bperm(A23, A01, 0x07060302u) ^ 0x80808080u);
-                pd[1][b] = (int32_t)(bperm(B23, B01, 0x05040100u) ^ 0x80808080u);
-                pd[0][b] = (int32_t)bperm(B23, B01, 0x07060302u);
+                pd[grp][3][b] = (int32_t)(bperm(A23, A01, 0x05040100u) ^ 0x80808080u);
+                pd[grp][2][b] = (int32_t)(bperm(A23, A01, 0x07060302u) ^ 0x80808080u);
+                pd[grp][1][b] = (int32_t)(bperm(B23, B01, 0x05040100u) ^ 0x80808080u);
+                pd[grp][0][b] = (int32_t)bperm(B23, B01, 0x07060302u);
             }
+        }
+        // Both groups' splits first, then the 32 MFMAs as one burst: MFMA and VALU work of one wave do not overlap on
+        // this chip, those of two waves on a SIMD do, so a long MFMA run gives the SIMD's other wave room to issue
+        // its VALU work meanwhile.
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+        for (int grp = 0; grp < 2; grp++) {
 #pragma unroll
             for (int dq = 0; dq < 4; dq++) {
                 const int db = 4 * grp + dq, ch = 2 * db + hh;   // 8-byte chunk of the cell's 128-byte row
@@ -399,7 +406,7 @@ __global__ __launch_bounds__(256, 2) void prompt_attn_kernel(const PromptArgs a)
                 const v4i va = v4i{lo[0], lo[1], hi[0], hi[1]};
 #pragma unroll
                 for (int pl = 0; pl < 4; pl++)
-                    acc[pl][db] = __builtin_amdgcn_mfma_i32_16x16x64_i8(va, pd[pl], acc[pl][db], 0, 0, 0);
+                    acc[pl][db] = __builtin_amdgcn_mfma_i32_16x16x64_i8(va, pd[grp][pl], acc[pl][db], 0, 0, 0);
             }
         }
 
