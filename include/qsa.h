@@ -67,8 +67,8 @@ typedef struct {
  * int8 (#1888, "What changed": formats left alone; #2075, "Bit for bit": parity cases per KV format) without its
  * layout -- V codes are signed 4-bit integers (-7..7), two per byte (dim 2j in the low nibble, 2j + 1 in the high
  * one), v is [n_kv_heads][capacity][head_dim / 2] bytes, and v_scale is as for int8. K8V4 is supported by the decode
- * calls at head_dim 128 and 256 (QSA_ERR_UNSUPPORTED otherwise and in qsa_prompt_attn); the pools of one call must
- * share a format. */
+ * calls and the prompt call at head_dim 128 and 256 (QSA_ERR_UNSUPPORTED otherwise); the pools of one call must share
+ * a format. */
 typedef struct {
     const int8_t *k;
     const float *k_scale;
@@ -164,16 +164,19 @@ qsa_status qsa_attn_chunk(const float *q, const int32_t *pos, int32_t n_rows, co
 qsa_status qsa_attn_merge(const qsa_partials *in, int32_t n_rows, qsa_dims dims, int32_t n_chunks,
                           const int32_t *n_active, float *out, float *lse, qsa_stream_t stream);
 
-/* Scratch bytes qsa_prompt_attn needs for n_q queries starting at position pos0 (0 if the arguments are invalid or
- * head_dim has no prompt kernel). Covers any pool: the call sees at most pos0 + n_q cells. */
+/* Scratch bytes qsa_prompt_attn needs for n_q queries starting at position pos0 (0 if the arguments are invalid).
+ * Covers any pool and V format: the call sees at most pos0 + n_q cells. */
 size_t qsa_prompt_scratch_bytes(int32_t n_q, int32_t pos0, qsa_dims dims);
 
 /* Prompt-chunk attention on int8 matrix cores ([1367] "What it does"): dense causal attention for n_q queries at
- * positions pos0 .. pos0 + n_q - 1 over the pool's cells c <= pos (and c < n_valid). Both products run on the
- * int8 K/V codes as stored; q (scaled per query and head) is split into three exact 8-bit parts and the
- * probabilities times v_scale (scaled per KV head) into four, so every int32 sum is exact.
- * out [n_q][n_q_heads][head_dim]; sm_scale multiplies q . k. Requires pos0 >= 0, head_dim == 128
- * (QSA_ERR_UNSUPPORTED otherwise) and scratch_bytes >= qsa_prompt_scratch_bytes (QSA_ERR_SCRATCH). */
+ * positions pos0 .. pos0 + n_q - 1 over the pool's cells c <= pos (and c < n_valid). With head_dim 128 and int8 V
+ * both products run on the int8 K/V codes as stored; q (scaled per query and head) is split into three exact 8-bit
+ * parts and the probabilities times v_scale (scaled per KV head) into four, so every int32 sum is exact. Every other
+ * shape the decode calls take (head_dim 64 or 256, K8V4 pools at head_dim 128 or 256) gives the same attention
+ * through the chunk attention kernel in dense mode and the merge, 64 queries at a time (much slower: each query
+ * reads its own cells). out [n_q][n_q_heads][head_dim]; sm_scale multiplies q . k. Requires pos0 >= 0 and
+ * pos0 + n_q - 1 <= INT32_MAX (QSA_ERR_RANGE), a supported head_dim and V format (QSA_ERR_UNSUPPORTED: head_dim 192,
+ * K8V4 at head_dim 64) and scratch_bytes >= qsa_prompt_scratch_bytes (QSA_ERR_SCRATCH). */
 qsa_status qsa_prompt_attn(const float *q, int32_t n_q, int32_t pos0, const qsa_pool *pool, qsa_dims dims,
                            float sm_scale, float *out, void *scratch, size_t scratch_bytes, qsa_stream_t stream);
 

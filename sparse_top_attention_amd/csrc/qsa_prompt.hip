@@ -26,6 +26,8 @@
 // with m_ref set DELTA above the new max so that later small increases need no fold.
 #include "qsa_internal.h"
 
+#include <stdint.h>
+
 #include <type_traits>
 
 namespace qsa {
@@ -491,14 +493,85 @@ PromptScratch prompt_layout(int32_t n_q, int64_t n_cells, const qsa_dims &d)
     return s;
 }
 
+// ------------------------------------------------------------------------------------- other head dims, K8V4
+// The matrix-core kernel above covers head_dim 128 with int8 V. Every other shape the decode kernels support (head_dim
+// 64 or 256, K8V4 pools) takes the chunk attention kernel in dense mode -- query i as a row at position pos0 + i over
+// blocks of its visible cells, split in up to FB_MAX_CHUNKS chunks -- and the log-sum-exp merge, FB_BATCH queries at
+// a time so that the partials stay small. Same result (softmax attention over the visible cells), on the VALU or the
+// fp16 matrix cores instead of the int8 digit products, and every query reads its own cells, so it is much slower.
+constexpr int32_t FB_BATCH = 64, FB_MAX_CHUNKS = 32;
+
+struct DenseLayout {
+    size_t pos, m, l, e, o, total;
+    int32_t batch, chunks;   // queries per batch, chunk slots per row
+};
+
+DenseLayout dense_layout(int32_t n_q, int64_t n_cells, const qsa_dims &d)
+{
+    auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    DenseLayout s{};
+    s.batch = n_q < FB_BATCH ? n_q : FB_BATCH;
+    const int64_t n_blocks = (n_cells + QSA_BLOCK - 1) / QSA_BLOCK;
+    s.chunks = (int32_t)(n_blocks < 1 ? 1 : (n_blocks < FB_MAX_CHUNKS ? n_blocks : FB_MAX_CHUNKS));
+    const size_t rh = (size_t)s.batch * d.n_q_heads * s.chunks;
+    size_t off = 0;
+    s.pos = off; off += al((size_t)n_q * sizeof(int32_t));
+    s.m = off; off += al(rh * sizeof(float));
+    s.l = off; off += al(rh * sizeof(float));
+    s.e = off; off += al(rh);
+    s.o = off; off += al(rh * d.head_dim * sizeof(float));
+    s.total = off;
+    return s;
+}
+
+__global__ __launch_bounds__(256) void prompt_pos_kernel(int32_t *__restrict__ pos, int32_t n_q, int32_t pos0)
+{
+    const int32_t i = (int32_t)(blockIdx.x * 256 + threadIdx.x);
+    if (i < n_q) pos[i] = pos0 + i;
+}
+
+// Validated by qsa_prompt_attn (dims, pool, pointers, n_q > 0, positions in range).
+qsa_status prompt_dense(const float *q, int32_t n_q, int32_t pos0, const qsa_pool *pool, const qsa_dims &dims,
+                        float sm_scale, float *out, void *scratch, size_t scratch_bytes, hipStream_t s)
+{
+    const int64_t last = (int64_t)pos0 + n_q;
+    const DenseLayout lay = dense_layout(n_q, last, dims);
+    if (!scratch) return QSA_ERR_NULL;
+    if (scratch_bytes < lay.total) return QSA_ERR_SCRATCH;
+    // chunks over the blocks holding the cells the call can see: balanced runs of blocks, at most lay.chunks of them
+    const int64_t n_cells = last < pool->n_valid ? last : pool->n_valid;
+    const int32_t n_blocks = (int32_t)((n_cells + QSA_BLOCK - 1) / QSA_BLOCK);
+    const int32_t want = n_blocks < 1 ? 1 : (n_blocks < lay.chunks ? n_blocks : lay.chunks);
+    const int32_t bpc = n_blocks < 1 ? 1 : (n_blocks + want - 1) / want;
+    const int32_t n_chunks = n_blocks < 1 ? 1 : (n_blocks + bpc - 1) / bpc;
+    char *base = static_cast<char *>(scratch);
+    int32_t *pos = reinterpret_cast<int32_t *>(base + lay.pos);
+    qsa_partials parts{reinterpret_cast<float *>(base + lay.m), reinterpret_cast<float *>(base + lay.l),
+                       reinterpret_cast<float *>(base + lay.o), reinterpret_cast<uint8_t *>(base + lay.e), lay.chunks};
+    prompt_pos_kernel<<<dim3((uint32_t)((n_q + 255) / 256)), 256, 0, s>>>(pos, n_q, pos0);
+    qsa_status st = launch_status();
+    const int64_t row = (int64_t)dims.n_q_heads * dims.head_dim;
+    for (int32_t b0 = 0; b0 < n_q && st == QSA_OK; b0 += lay.batch) {
+        const int32_t nb = n_q - b0 < lay.batch ? n_q - b0 : lay.batch;
+        st = qsa_attn_chunk(q + b0 * row, pos + b0, nb, pool, 1, nullptr, dims, nullptr, nullptr, 0, bpc, n_chunks,
+                            sm_scale, &parts, s);
+        if (st == QSA_OK) st = qsa_attn_merge(&parts, nb, dims, n_chunks, nullptr, out + b0 * row, nullptr, s);
+    }
+    return st;
+}
+
 }  // namespace qsa
 
 using namespace qsa;
 
 extern "C" size_t qsa_prompt_scratch_bytes(int32_t n_q, int32_t pos0, qsa_dims dims)
 {
-    if (n_q <= 0 || pos0 < 0 || check_dims(dims) != QSA_OK || dims.head_dim != PD) return 0;
-    return prompt_layout(n_q, (int64_t)pos0 + n_q, dims).total;
+    if (n_q <= 0 || pos0 < 0 || check_dims(dims) != QSA_OK) return 0;
+    const int64_t last = (int64_t)pos0 + n_q;
+    const size_t dense = dense_layout(n_q, last, dims).total;
+    if (dims.head_dim != PD) return dense;
+    const size_t mfma = prompt_layout(n_q, last, dims).total;   // int8 V; a K8V4 pool takes the dense path
+    return mfma > dense ? mfma : dense;
 }
 
 extern "C" qsa_status qsa_prompt_attn(const float *q, int32_t n_q, int32_t pos0, const qsa_pool *pool, qsa_dims dims,
@@ -509,9 +582,14 @@ extern "C" qsa_status qsa_prompt_attn(const float *q, int32_t n_q, int32_t pos0,
     if (st != QSA_OK) return st;
     if ((st = check_pool(pool, true)) != QSA_OK) return st;
     if (!q || !out) return QSA_ERR_NULL;
-    if (n_q < 0 || pos0 < 0) return QSA_ERR_RANGE;
-    if (dims.head_dim != PD || v_bits_of(*pool) != 8) return QSA_ERR_UNSUPPORTED;
+    if (n_q < 0 || pos0 < 0 || (int64_t)pos0 + n_q - 1 > INT32_MAX) return QSA_ERR_RANGE;
+    if (!common_v_bits(pool, 1, dims.head_dim)) return QSA_ERR_UNSUPPORTED;   // K8V4 needs head_dim >= 128
     if (n_q == 0) return QSA_OK;
+    if (!scratch) return QSA_ERR_NULL;
+    // one requirement for both paths: the size qsa_prompt_scratch_bytes reports, whatever the pool's V format
+    if (scratch_bytes < qsa_prompt_scratch_bytes(n_q, pos0, dims)) return QSA_ERR_SCRATCH;
+    if (dims.head_dim != PD || v_bits_of(*pool) != 8)
+        return prompt_dense(q, n_q, pos0, pool, dims, sm_scale, out, scratch, scratch_bytes, (hipStream_t)stream);
     const int64_t last = (int64_t)pos0 + n_q;
     const int32_t n_cells = (int32_t)(last < pool->n_valid ? last : pool->n_valid);
     const PromptScratch lay = prompt_layout(n_q, n_cells, dims);

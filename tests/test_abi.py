@@ -169,12 +169,24 @@ def test_prompt_scratch_sizing_and_checks():
     assert n >= L.qsa_prompt_scratch_bytes(2048, 0, GOOD) + 4 * 30720 * 2 * 4   # scaled v_scale per seen cell
     assert L.qsa_prompt_scratch_bytes(0, 0, GOOD) == 0
     assert L.qsa_prompt_scratch_bytes(16, -1, GOOD) == 0
-    assert L.qsa_prompt_scratch_bytes(16, 0, D(24, 4, 64, 64)) == 0   # head_dim 64 has no prompt kernel
+    # head_dims without the int8 matrix-core kernel take the dense chunk path: its partials for one 64-query batch
+    d64, d256 = D(24, 4, 64, 64), D(24, 4, 256, 64)
+    assert L.qsa_prompt_scratch_bytes(16, 0, d64) >= 16 * 24 * 1 * (64 * 4 + 9)
+    assert L.qsa_prompt_scratch_bytes(100, 4000, d256) >= 64 * 24 * 32 * (256 * 4 + 9)
+    assert L.qsa_prompt_scratch_bytes(16, 0, D(24, 4, 192, 64)) == 0
     p = _pool()
     assert L.qsa_prompt_attn(1, 16, 0, ctypes.byref(p), GOOD, 1.0, 1, None, 0, None) == -1       # no scratch
     need = L.qsa_prompt_scratch_bytes(16, 0, GOOD)
     assert L.qsa_prompt_attn(1, 16, 0, ctypes.byref(p), GOOD, 1.0, 1, 1, need - 1, None) == -4
-    assert L.qsa_prompt_attn(1, 16, 0, ctypes.byref(p), D(24, 4, 64, 64), 1.0, 1, 1, need, None) == -3
+    # the dense path checks its own scratch need, and a K8V4 pool at head_dim 128 takes it too
+    need64 = L.qsa_prompt_scratch_bytes(16, 0, d64)
+    p64 = _pool()
+    assert L.qsa_prompt_attn(1, 16, 0, ctypes.byref(p64), d64, 1.0, 1, 1, need64 - 1, None) == -4
+    p4 = _pool(v_bits=4)
+    assert L.qsa_prompt_attn(1, 16, 0, ctypes.byref(p4), GOOD, 1.0, 1, 1, 0, None) == -4
+    assert L.qsa_prompt_attn(1, 16, 0, ctypes.byref(p4), d64, 1.0, 1, 1, need, None) == -3     # K8V4 at head_dim 64
+    assert L.qsa_prompt_attn(1, 16, 0, ctypes.byref(p), D(24, 4, 192, 64), 1.0, 1, 1, need, None) == -3
+    assert L.qsa_prompt_attn(1, 2, 2**31 - 1, ctypes.byref(p), GOOD, 1.0, 1, 1, need, None) == -5  # positions past int32
     assert L.qsa_prompt_attn(1, 0, 0, ctypes.byref(p), GOOD, 1.0, 1, None, 0, None) == 0
 
 
@@ -236,8 +248,8 @@ def test_kv_append_validation():
 
 
 def test_v_bits_validation():
-    """V formats: 0/8 int8, 4 K8V4; anything else, mixed formats in one call, K8V4 at head_dim 64 and in the prompt
-    call are unsupported."""
+    """V formats: 0/8 int8, 4 K8V4; anything else, mixed formats in one call and K8V4 at head_dim 64 (in the decode
+    calls and in the prompt call) are unsupported."""
     L = qsa.lib_handle()
     parts = _parts(8)
 
@@ -247,7 +259,7 @@ def test_v_bits_validation():
     assert chunk((qsa._Pool * 2)(_pool(v_bits=8), _pool(v_bits=4)), 2) == -3
     assert chunk((qsa._Pool * 1)(_pool(v_bits=4)), 1, D(4, 4, 64, 64)) == -3
     p4 = _pool(v_bits=4)
-    assert L.qsa_prompt_attn(1, 16, 0, ctypes.byref(p4), GOOD, 1.0, 1, 1, 1 << 30, None) == -3
+    assert L.qsa_prompt_attn(1, 16, 0, ctypes.byref(p4), D(4, 4, 64, 64), 1.0, 1, 1, 1 << 30, None) == -3
     assert L.qsa_kv_append((qsa._Pool * 1)(_pool(v_bits=4)), 1, None, D(4, 4, 64, 64), 1, 1, 1, 4, None) == -3
 
 

@@ -42,6 +42,25 @@ def test_prompt_small(n_kv, G, n_q, pos0, n_valid, cap):
     assert rel_err_rows(got, ref).max() <= TOL
 
 
+@pytest.mark.parametrize("d,v_bits,n_kv,G,n_q,pos0,n_valid,cap", [
+    (64, 8, 2, 6, 130, 300, 400, 420),        # three 64-query batches, queries past n_valid
+    (256, 8, 2, 3, 70, 1000, 1049, 1100),     # head_dim 256, a ragged last block
+    (128, 4, 4, 6, 65, 500, 640, 700),        # K8V4 at head_dim 128 (6 heads per KV head)
+    (256, 4, 1, 8, 40, 0, 2100, 2100),        # K8V4 at 256, the first query sees one cell
+])
+def test_prompt_other_shapes_match_oracle(d, v_bits, n_kv, G, n_q, pos0, n_valid, cap):
+    """Shapes without the int8 matrix-core kernel (head_dim 64 or 256, K8V4 pools) take the dense chunk path: the
+    same causal attention, checked against the FP64 oracle on every row."""
+    pool = synth.random_pool(360 + d + v_bits, n_kv, cap, n_valid, d, v_bits=v_bits)
+    q = synth.random_q(361 + d, n_q, n_kv * G, d)
+    dims = qsa.Dims(n_kv * G, n_kv, d)
+    got = run_prompt(q, pos0, to_device(pool), dims, sm_scale=0.9)
+    pos = (pos0 + np.arange(n_q)).astype(np.int32)
+    ref, _ = oracle.attn(q, pos, pool, n_kv, sm_scale=0.9)
+    assert np.all(np.isfinite(got))
+    assert rel_err_rows(got, ref).max() <= TOL
+
+
 def test_prompt_sm_scale_and_zero_query():
     pool = synth.random_pool(311, 2, 300, 260, 128)
     q = synth.random_q(312, 20, 12, 128)
