@@ -44,6 +44,8 @@ def parse():
     ap.add_argument("--no-prompt", action="store_true", help="skip the prompt-chunk measurement")
     ap.add_argument("--no-other", action="store_true", help="skip the batch-window and drafter measurements")
     ap.add_argument("--prompt-steps", type=int, default=20)
+    ap.add_argument("--v-bits", type=int, default=8, choices=[8, 4],
+                    help="V format of the prompt chunk's pool with --workload prompt_chunk (4 = K8V4)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of known size (to scale HBM byte counters)")
     ap.add_argument("--copies", type=int, default=64, help="pool copies the steps rotate over")
@@ -137,13 +139,15 @@ def main():
             print(json.dumps(line), flush=True)
         return
     if args.workload == "prompt_chunk":
-        res = bench_prompt(args, args.steps if args.steps != 1280 else args.prompt_steps, main_line=True)
+        res = bench_prompt(args, args.steps if args.steps != 1280 else args.prompt_steps, main_line=True,
+                           v_bits=args.v_bits)
     else:
         res = bench_decode(args)
         if args.workload == "verify_window" and not args.no_other:
             res["other_decode_workloads"] = bench_other_decode()
         if not args.no_prompt:
             res["prompt_chunk"] = bench_prompt(args, args.prompt_steps, main_line=False)
+            res["prompt_chunk_k8v4"] = bench_prompt(args, args.prompt_steps, main_line=False, v_bits=4, cpu=False)
     print(json.dumps(res))
 
 
@@ -647,27 +651,29 @@ def prompt_ops(w):
     return {"useful": pairs * w.head_dim * 4, "planes": pairs * w.head_dim * 12, "issued": issued}, vis
 
 
-def bench_prompt(args, steps, main_line):
+def bench_prompt(args, steps, main_line, v_bits=8, cpu=True):
     """The 2,048-query prompt chunk at the end of a 32,768-cell context: one qsa_prompt_attn call per step, replayed
-    from a HIP graph over pool copies (K/V and q are resident in HBM)."""
+    from a HIP graph over pool copies (K/V and q are resident in HBM). v_bits 4 times a K8V4 pool of the same
+    shape (same q and K draws, 4-bit V codes)."""
     import torch
 
     import sparse_top_attention_amd as qsa
     import synth
 
     dev = torch.device("cuda:0")
-    w = synth.workload("prompt_chunk", poison=False)
+    w = synth.workload("prompt_chunk", poison=False, v_bits=v_bits)
     pool_np = w.pools[0]
     dims = qsa.Dims(w.n_q_heads, w.n_kv_heads, w.head_dim)
     n_q = w.q.shape[0]
+    tkey = "prompt_attn_prompt_chunk" + ("" if v_bits == 8 else "_k8v4")
 
     def t(a):
         return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
     n_copies = 8
-    base = qsa.Pool(t(pool_np.k), t(pool_np.ks), t(pool_np.v), t(pool_np.vs), pool_np.n_valid)
+    base = qsa.Pool(t(pool_np.k), t(pool_np.ks), t(pool_np.v), t(pool_np.vs), pool_np.n_valid, v_bits=v_bits)
     copies = [base] + [qsa.Pool(base.k.clone(), base.k_scale.clone(), base.v.clone(), base.v_scale.clone(),
-                                base.n_valid) for _ in range(n_copies - 1)]
+                                base.n_valid, v_bits=v_bits) for _ in range(n_copies - 1)]
     qs = [t(w.q)] + [None] * (n_copies - 1)
     for c in range(1, n_copies):
         qs[c] = qs[0].clone()
@@ -708,13 +714,13 @@ def bench_prompt(args, steps, main_line):
 
     res = {
         "workload": "prompt_chunk", "queries": n_q, "pos0": w.pos0, "n_valid": pool_np.n_valid,
-        "q_heads": w.n_q_heads, "kv_heads": w.n_kv_heads, "head_dim": w.head_dim,
+        "q_heads": w.n_q_heads, "kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "v_bits": v_bits,
         "ms_per_call": round(ms, 4), "calls_timed": n_calls,
         "roofline": {"bound": "mfma", "kernel": "qsa_prompt_attn (q split + attention + chunk merge)",
                      "achieved": round(tops, 1), "peak": INT8_PEAK_TOPS, "unit": "TOPS",
                      "frac": round(tops / INT8_PEAK_TOPS, 4), "ops_per_launch": int(ops),
                      "ops": "useful: 4 x head_dim per visible (query, q head, cell) pair (q.k and p.v)",
-                     "traffic": measured_traffic("prompt_attn_prompt_chunk")},
+                     "traffic": measured_traffic(tkey)},
         "digit_plane_ops": {"ops_per_call": int(opc["planes"]), "frac_of_int8_peak": frac(opc["planes"]),
                             "about": "the useful products on three 8-bit digit planes each (the pages' 24-bit "
                                      "split): 3x the useful ops"},
@@ -730,9 +736,9 @@ def bench_prompt(args, steps, main_line):
             "dtype": "i8", "data": "synthetic",
             "config": {"workload": "prompt_chunk", "queries": n_q, "q_heads": w.n_q_heads,
                        "kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "n_valid": pool_np.n_valid,
-                       "pos0": w.pos0, "pool_copies": n_copies},
+                       "pos0": w.pos0, "v_bits": v_bits, "pool_copies": n_copies},
             "roofline": res["roofline"], "cpu_baseline": None}
-    if not args.no_cpu_baseline:
+    if cpu and not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline_prompt(w, ops, vis, args.cpu_seconds)
     del copies, qs, scratch
     torch.cuda.empty_cache()

@@ -169,10 +169,10 @@ qsa_status qsa_attn_merge(const qsa_partials *in, int32_t n_rows, qsa_dims dims,
 size_t qsa_prompt_scratch_bytes(int32_t n_q, int32_t pos0, qsa_dims dims);
 
 /* Prompt-chunk attention on int8 matrix cores ([1367] "What it does"): dense causal attention for n_q queries at
- * positions pos0 .. pos0 + n_q - 1 over the pool's cells c <= pos (and c < n_valid). With head_dim 128 and int8 V
- * both products run on the int8 K/V codes as stored; q (scaled per query and head) is split into three exact 8-bit
- * parts and the probabilities times v_scale (scaled per KV head) into four, so every int32 sum is exact. Every other
- * shape the decode calls take (head_dim 64 or 256, K8V4 pools at head_dim 128 or 256) gives the same attention
+ * positions pos0 .. pos0 + n_q - 1 over the pool's cells c <= pos (and c < n_valid). With head_dim 128 both
+ * products run on the int8 K/V codes as stored (K8V4 pools: the 4-bit V codes widened to int8 in LDS); q (scaled per
+ * query and head) is split into three exact 8-bit parts and the probabilities times v_scale (scaled per KV head)
+ * into four, so every int32 sum is exact. Head_dim 64 and 256 (int8, and K8V4 at 256) give the same attention
  * through the chunk attention kernel in dense mode and the merge, 64 queries at a time (much slower: each query
  * reads its own cells). out [n_q][n_q_heads][head_dim]; sm_scale multiplies q . k. Requires pos0 >= 0 and
  * pos0 + n_q - 1 <= INT32_MAX (QSA_ERR_RANGE), a supported head_dim and V format (QSA_ERR_UNSUPPORTED: head_dim 192,

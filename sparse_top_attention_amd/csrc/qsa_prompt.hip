@@ -24,6 +24,9 @@
 // The PV int32 sums are accumulated across tiles while the reference max m_ref of a row does not move; when a tile's
 // row max exceeds m_ref, the wave folds the int32 sums into fp32 (rescaled by 2^(m_old - m_new)) and restarts them,
 // with m_ref set DELTA above the new max so that later small increases need no fold.
+//
+// K8V4 pools (4-bit V codes, two per byte) take the same kernel: the packed V tile is copied into LDS and widened to
+// int8 codes there (exact), after which every product and split is the one of an int8 pool.
 #include "qsa_internal.h"
 
 #include <stdint.h>
@@ -64,6 +67,7 @@ __device__ __forceinline__ uint32_t bperm(uint32_t s0, uint32_t s1, uint32_t sel
 // s_waitcnt immediates (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
 constexpr int WAIT_VM0_LGKM0 = 0x0070;   // all vector memory and LDS operations done
 constexpr int WAIT_VM5_LGKM0 = 0x0075;   // all but the 5 newest vector memory operations done, LDS done
+constexpr int WAIT_VM4_LGKM0 = 0x0074;   // all but the 4 newest
 
 // ---------------------------------------------------------------------------------------------- q digits
 // One wave per (query, q head): qd[g][r][plane][d] int8 with r = query * G + head-in-group, plane 0/1/2 = h/l/m,
@@ -165,6 +169,34 @@ struct __align__(16) PromptTile {
     float vs[PT * 2];      // [cell][grp], scaled to w
 };
 
+// K8V4 pools: wave w stages the packed 4-bit V codes of the tile's cells 16w .. 16w + 15 (1,024 bytes, lane l holds
+// cell 16w + l/4, dims 32 (l & 3) .. + 31) at the start of its own 2,048-byte share of the V slot, and once its copies
+// have landed expands them in place into the int8 layout of the slot: two 16-byte chunks of the cell's row per lane.
+// Every byte a wave reads lies in the rows it writes, and a wave's reads complete before its writes, so the expansion
+// needs no barrier of its own; the step's barrier publishes it.
+__device__ __forceinline__ uint32_t s4_lo(uint32_t u)   // signed low nibbles of the 4 bytes -> 4 int8
+{
+    return (((u & 0x0F0F0F0Fu) ^ 0x08080808u) + 0x78787878u) ^ 0x80808080u;
+}
+__device__ __forceinline__ void expand_v4(int8_t *tv, int wave, int lane)
+{
+    const int cell = 16 * wave + (lane >> 2), pos = lane & 3;
+    const v4i pk = *reinterpret_cast<const v4i *>(tv + 2048 * wave + 16 * lane);
+    uint32_t o[8];
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+        const uint32_t lo = s4_lo((uint32_t)pk[k]), hi = s4_lo((uint32_t)pk[k] >> 4);   // dims 8k + 2j, 8k + 2j + 1
+        o[2 * k] = bperm(hi, lo, 0x05010400u);
+        o[2 * k + 1] = bperm(hi, lo, 0x07030602u);
+    }
+    int8_t *row = tv + cell * PD;
+    *reinterpret_cast<v4i *>(row + 16 * ((2 * pos) ^ swz_v(cell))) =
+        v4i{(int32_t)o[0], (int32_t)o[1], (int32_t)o[2], (int32_t)o[3]};
+    *reinterpret_cast<v4i *>(row + 16 * ((2 * pos + 1) ^ swz_v(cell))) =
+        v4i{(int32_t)o[4], (int32_t)o[5], (int32_t)o[6], (int32_t)o[7]};
+}
+
+template <int VB>
 __global__ __launch_bounds__(256, 2) void prompt_attn_kernel(const PromptArgs a)
 {
     __shared__ PromptTile tile[NBUF];
@@ -234,10 +266,15 @@ __global__ __launch_bounds__(256, 2) void prompt_attn_kernel(const PromptArgs a)
     };
     float lsum = 0.f, mref = -INFINITY;
 
-    // ---- tile staging, straight from HBM into LDS: per 64-cell tile, 8 KB of K codes, 8 KB of V codes and 512 B of
-    // each scale; wave w issues 16-byte slots [128 w, 128 w + 128) of K and of V and one 64-float half of a scale array
+    // ---- tile staging, straight from HBM into LDS: per 64-cell tile, 8 KB of K codes, 8 KB of V codes (4 KB packed
+    // for K8V4) and 512 B of each scale; wave w issues 16-byte slots [128 w, 128 w + 128) of K and of V (slots
+    // [64 w, 64 w + 64) of packed V) and one 64-float half of a scale array
+    constexpr int VROW = VB == 8 ? PD : PD / 2;   // V bytes per cell
+    constexpr int NCOPY = VB == 8 ? 5 : 4;        // copies each wave issues per tile
+    constexpr int WAIT_TILE = VB == 8 ? WAIT_VM5_LGKM0 : WAIT_VM4_LGKM0;   // all but the newest tile's copies done
+    static_assert((WAIT_TILE & 15) == NCOPY, "the tile wait counts one tile's copies");
     const int8_t *kg = P.k + (int64_t)g * P.capacity * PD;
-    const int8_t *vg = P.v + (int64_t)g * P.capacity * PD;
+    const int8_t *vg = P.v + (int64_t)g * P.capacity * VROW;
     const float *ksg = P.ks + (int64_t)g * P.capacity * 2;
     const float *vsg = a.w + (int64_t)g * a.w_cells * 2;
     // The tile's base address is wave-uniform (scalar registers); a lane's byte offset within a full tile is the
@@ -251,12 +288,12 @@ __global__ __launch_bounds__(256, 2) void prompt_attn_kernel(const PromptArgs a)
         voff[h] = cell * PD + 16 * (pos ^ swz_v(cell));
     }
     const int se = 64 * (wave & 1) + lane;   // float se of the tile's [cell][grp] scales
-    // (each wave issues 5 copies per tile)
+    // (each wave issues NCOPY copies per tile)
     auto stage = [&](int32_t t, int buf) {
         const int32_t cb = t * PT;
         PromptTile &T = tile[buf];
         const int8_t *kt = kg + (int64_t)cb * PD;
-        const int8_t *vt = vg + (int64_t)cb * PD;
+        const int8_t *vt = vg + (int64_t)cb * VROW;
         const float *st = (wave < 2 ? ksg : vsg) + (int64_t)cb * 2;
         float *sdst = (wave < 2 ? T.ks : T.vs) + 64 * (wave & 1);
         const int32_t nfull = c_last - cb;   // cells past nfull re-read cell nfull
@@ -264,8 +301,9 @@ __global__ __launch_bounds__(256, 2) void prompt_attn_kernel(const PromptArgs a)
 #pragma unroll
             for (int h = 0; h < 2; h++) {
                 copy_lds16(kt, koff[h], lds_addr(T.k + 1024 * (2 * wave + h)));
-                copy_lds16(vt, voff[h], lds_addr(T.v + 1024 * (2 * wave + h)));
+                if constexpr (VB == 8) copy_lds16(vt, voff[h], lds_addr(T.v + 1024 * (2 * wave + h)));
             }
+            if constexpr (VB == 4) copy_lds16(vt, 1024 * wave + 16 * lane, lds_addr(T.v + 2048 * wave));
             copy_lds4(st, 4 * se, lds_addr(sdst));
         } else {
 #pragma unroll
@@ -273,9 +311,19 @@ __global__ __launch_bounds__(256, 2) void prompt_attn_kernel(const PromptArgs a)
                 const int slot = 128 * wave + 64 * h + lane;
                 const int cell = slot >> 3, pos = slot & 7, c = min(cell, nfull);
                 copy_lds16(kt, c * PD + 16 * (pos ^ swz_k(cell)), lds_addr(T.k + 1024 * (2 * wave + h)));
-                copy_lds16(vt, c * PD + 16 * (pos ^ swz_v(cell)), lds_addr(T.v + 1024 * (2 * wave + h)));
+                if constexpr (VB == 8)
+                    copy_lds16(vt, c * PD + 16 * (pos ^ swz_v(cell)), lds_addr(T.v + 1024 * (2 * wave + h)));
             }
+            if constexpr (VB == 4)
+                copy_lds16(vt, min(16 * wave + (lane >> 2), nfull) * VROW + 16 * (lane & 3), lds_addr(T.v + 2048 * wave));
             copy_lds4(st, 4 * (2 * min(se >> 1, nfull) + (se & 1)), lds_addr(sdst));
+        }
+    };
+    // K8V4: expand this wave's share of a landed packed tile (the compiler barrier keeps its LDS reads after the wait)
+    auto expand = [&](int32_t t) {
+        if constexpr (VB == 4) {
+            asm volatile("" ::: "memory");
+            expand_v4(tile[(t - t0) % NBUF].v, wave, lane);
         }
     };
 
@@ -283,8 +331,9 @@ __global__ __launch_bounds__(256, 2) void prompt_attn_kernel(const PromptArgs a)
     // issued at the start of step t - 2, so they have two steps to land.
     if (t0 < t1) stage(t0, 0);
     if (t0 + 1 < t1) stage(t0 + 1, 1);
-    if (t0 + 1 < t1) __builtin_amdgcn_s_waitcnt(WAIT_VM5_LGKM0);   // tile t0 has landed
+    if (t0 + 1 < t1) __builtin_amdgcn_s_waitcnt(WAIT_TILE);   // tile t0 has landed
     else __builtin_amdgcn_s_waitcnt(WAIT_VM0_LGKM0);
+    if (t0 < t1) expand(t0);
     __syncthreads();
 
     // Tiles before t_mask end at or before the wave's smallest limit and need no causal mask; the loop is split so
@@ -414,8 +463,9 @@ __global__ __launch_bounds__(256, 2) void prompt_attn_kernel(const PromptArgs a)
 
         __builtin_amdgcn_s_setprio(0);
         // this wave's copies of tile t + 1 have landed (those of tile t + 2 may still be in flight)
-        if (t + 2 < t1) __builtin_amdgcn_s_waitcnt(WAIT_VM5_LGKM0);
+        if (t + 2 < t1) __builtin_amdgcn_s_waitcnt(WAIT_TILE);
         else __builtin_amdgcn_s_waitcnt(WAIT_VM0_LGKM0);
+        if (t + 1 < t1) expand(t + 1);
         __syncthreads();
     };
     int32_t t = t0;
@@ -568,10 +618,8 @@ extern "C" size_t qsa_prompt_scratch_bytes(int32_t n_q, int32_t pos0, qsa_dims d
 {
     if (n_q <= 0 || pos0 < 0 || check_dims(dims) != QSA_OK) return 0;
     const int64_t last = (int64_t)pos0 + n_q;
-    const size_t dense = dense_layout(n_q, last, dims).total;
-    if (dims.head_dim != PD) return dense;
-    const size_t mfma = prompt_layout(n_q, last, dims).total;   // int8 V; a K8V4 pool takes the dense path
-    return mfma > dense ? mfma : dense;
+    // head_dim 128 runs the matrix-core kernel (int8 or K8V4 pools alike), the other head dims the dense chunk path
+    return dims.head_dim == PD ? prompt_layout(n_q, last, dims).total : dense_layout(n_q, last, dims).total;
 }
 
 extern "C" qsa_status qsa_prompt_attn(const float *q, int32_t n_q, int32_t pos0, const qsa_pool *pool, qsa_dims dims,
@@ -586,9 +634,9 @@ extern "C" qsa_status qsa_prompt_attn(const float *q, int32_t n_q, int32_t pos0,
     if (!common_v_bits(pool, 1, dims.head_dim)) return QSA_ERR_UNSUPPORTED;   // K8V4 needs head_dim >= 128
     if (n_q == 0) return QSA_OK;
     if (!scratch) return QSA_ERR_NULL;
-    // one requirement for both paths: the size qsa_prompt_scratch_bytes reports, whatever the pool's V format
+    // the size qsa_prompt_scratch_bytes reports, whatever the pool's V format
     if (scratch_bytes < qsa_prompt_scratch_bytes(n_q, pos0, dims)) return QSA_ERR_SCRATCH;
-    if (dims.head_dim != PD || v_bits_of(*pool) != 8)
+    if (dims.head_dim != PD)
         return prompt_dense(q, n_q, pos0, pool, dims, sm_scale, out, scratch, scratch_bytes, (hipStream_t)stream);
     const int64_t last = (int64_t)pos0 + n_q;
     const int32_t n_cells = (int32_t)(last < pool->n_valid ? last : pool->n_valid);
@@ -625,7 +673,8 @@ extern "C" qsa_status qsa_prompt_attn(const float *q, int32_t n_q, int32_t pos0,
         a.o_out = reinterpret_cast<float *>(base + lay.o);
     }
     dim3 grid((uint32_t)((R + PROWS - 1) / PROWS), S, dims.n_kv_heads);
-    prompt_attn_kernel<<<grid, 256, 0, s>>>(a);
+    if (v_bits_of(*pool) == 8) prompt_attn_kernel<8><<<grid, 256, 0, s>>>(a);
+    else prompt_attn_kernel<4><<<grid, 256, 0, s>>>(a);
     if ((st = launch_status()) != QSA_OK) return st;
     if (S > 1) return merge_launch(a.m_out, a.l_out, a.o_out, a.e_out, S, S, nullptr, n_q, dims.n_q_heads, PD, out,
                                    nullptr, s);

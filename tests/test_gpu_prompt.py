@@ -1,5 +1,6 @@
 """Parity of the int8-MFMA prompt-chunk attention against the FP64 oracle (dense causal attention), through the
-C ABI. Bar: max relative error 1e-5 per (query, head) row. Pools carry poison past n_valid."""
+C ABI, for int8 and K8V4 pools. Bar: max relative error 1e-5 per (query, head) row. Pools carry poison past
+n_valid."""
 import numpy as np
 import pytest
 import torch
@@ -23,6 +24,7 @@ def run_prompt(q, pos0, p_dev, dims, sm_scale=1.0):
     return out.cpu().numpy()
 
 
+@pytest.mark.parametrize("v_bits", [8, 4], ids=["int8", "k8v4"])
 @pytest.mark.parametrize("n_kv,G,n_q,pos0,n_valid,cap", [
     (4, 6, 70, 300, 400, 420),       # 24/4 heads, ragged tile tails, several workgroups
     (2, 6, 11, 0, 700, 700),         # the first query sees one cell
@@ -31,8 +33,9 @@ def run_prompt(q, pos0, p_dev, dims, sm_scale=1.0):
     (2, 2, 33, 64, 97, 128),
     (2, 8, 50, 1000, 1049, 1100),
 ])
-def test_prompt_small(n_kv, G, n_q, pos0, n_valid, cap):
-    pool = synth.random_pool(300 + n_q, n_kv, cap, n_valid, 128)
+def test_prompt_small(n_kv, G, n_q, pos0, n_valid, cap, v_bits):
+    """head_dim 128 on the matrix-core kernel; a K8V4 pool's 4-bit V codes are widened to int8 in LDS."""
+    pool = synth.random_pool(300 + n_q + v_bits, n_kv, cap, n_valid, 128, v_bits=v_bits)
     q = synth.random_q(301 + n_q, n_q, n_kv * G, 128)
     dims = qsa.Dims(n_kv * G, n_kv, 128)
     got = run_prompt(q, pos0, to_device(pool), dims)
@@ -45,12 +48,11 @@ def test_prompt_small(n_kv, G, n_q, pos0, n_valid, cap):
 @pytest.mark.parametrize("d,v_bits,n_kv,G,n_q,pos0,n_valid,cap", [
     (64, 8, 2, 6, 130, 300, 400, 420),        # three 64-query batches, queries past n_valid
     (256, 8, 2, 3, 70, 1000, 1049, 1100),     # head_dim 256, a ragged last block
-    (128, 4, 4, 6, 65, 500, 640, 700),        # K8V4 at head_dim 128 (6 heads per KV head)
     (256, 4, 1, 8, 40, 0, 2100, 2100),        # K8V4 at 256, the first query sees one cell
 ])
 def test_prompt_other_shapes_match_oracle(d, v_bits, n_kv, G, n_q, pos0, n_valid, cap):
-    """Shapes without the int8 matrix-core kernel (head_dim 64 or 256, K8V4 pools) take the dense chunk path: the
-    same causal attention, checked against the FP64 oracle on every row."""
+    """Head dims without the int8 matrix-core kernel (64 and 256) take the dense chunk path: the same causal
+    attention, checked against the FP64 oracle on every row."""
     pool = synth.random_pool(360 + d + v_bits, n_kv, cap, n_valid, d, v_bits=v_bits)
     q = synth.random_q(361 + d, n_q, n_kv * G, d)
     dims = qsa.Dims(n_kv * G, n_kv, d)
@@ -108,9 +110,10 @@ def test_prompt_forced_fold_past_1024_tiles():
         assert rel_err_rows(got[i, h][None], ref[None]).max() <= TOL, (i, h)
 
 
-def test_prompt_chunk_full_size_sampled():
+@pytest.mark.parametrize("v_bits", [8, 4], ids=["int8", "k8v4"])
+def test_prompt_chunk_full_size_sampled(v_bits):
     """The 2,048-query prompt chunk at the end of a 32,768-cell context, checked on sampled rows."""
-    w = synth.workload("prompt_chunk")
+    w = synth.workload("prompt_chunk", v_bits=v_bits)
     pool = w.pools[0]
     dims = qsa.Dims(w.n_q_heads, w.n_kv_heads, w.head_dim)
     got = run_prompt(w.q, w.pos0, to_device(pool), dims)
@@ -123,7 +126,7 @@ def test_prompt_chunk_full_size_sampled():
         ref, _ = oracle.attn_one(w.q, w.pos, i, h, pool, w.n_kv_heads)
         errs.append(rel_err_rows(got[i, h][None], ref[None]).max())
         assert errs[-1] <= TOL, (i, h)
-    print(f"prompt_chunk sampled rows: max rel err {max(errs):.3e} over {len(picks)} rows")
+    print(f"prompt_chunk (v_bits {v_bits}) sampled rows: max rel err {max(errs):.3e} over {len(picks)} rows")
 
 
 def test_prompt_last_row_equals_dense_decode():
