@@ -70,16 +70,19 @@ constexpr int WAIT_VM5_LGKM0 = 0x0075;   // all but the 5 newest vector memory o
 constexpr int WAIT_VM4_LGKM0 = 0x0074;   // all but the 4 newest
 
 // ---------------------------------------------------------------------------------------------- q digits
-// One wave per (query, q head): qd[g][r][plane][d] int8 with r = query * G + head-in-group, plane 0/1/2 = h/l/m,
-// and qs[g][r] = max|q| / (127 * 65536) * sm_scale * log2(e) so that q . k * sm_scale * log2(e) = qs * (X . k).
-__global__ __launch_bounds__(64) void prompt_qsplit_kernel(const float *__restrict__ q, int32_t n_qh, int32_t G,
-                                                           int32_t R, float qscale, int8_t *__restrict__ qd,
-                                                           float *__restrict__ qs)
+// One wave per (query, q head), four per workgroup: qd[g][r][plane][d] int8 with r = query * G + head-in-group,
+// plane 0/1/2 = h/l/m, and qs[g][r] = max|q| / (127 * 65536) * sm_scale * log2(e) so that
+// q . k * sm_scale * log2(e) = qs * (X . k).
+__global__ __launch_bounds__(256) void prompt_qsplit_kernel(const float *__restrict__ q, int32_t n_qh, int32_t G,
+                                                            int32_t R, int64_t n_rows, float qscale,
+                                                            int8_t *__restrict__ qd, float *__restrict__ qs)
 {
-    const int lane = threadIdx.x;
-    const int32_t qi = blockIdx.x / n_qh, h = blockIdx.x % n_qh;
+    const int lane = threadIdx.x % 64;
+    const int64_t row = (int64_t)blockIdx.x * 4 + threadIdx.x / 64;   // = query * n_qh + head
+    if (row >= n_rows) return;                                          // whole waves leave together
+    const int32_t qi = (int32_t)(row / n_qh), h = (int32_t)(row % n_qh);
     const int32_t g = h / G, r = qi * G + h % G;
-    const float2 x = reinterpret_cast<const float2 *>(q + (int64_t)blockIdx.x * PD)[lane];
+    const float2 x = reinterpret_cast<const float2 *>(q + row * PD)[lane];
     const float amax = group_max<64>(fmaxf(fabsf(x.x), fabsf(x.y)));
     const float s = amax > 0.f ? QMAX / amax : 0.f;
     const int32_t X[2] = {(int32_t)rintf(x.x * s), (int32_t)rintf(x.y * s)};
@@ -128,24 +131,11 @@ __device__ __forceinline__ float head_vs(const float *__restrict__ VSp, int32_t 
     return VS > 0.f ? VS : 1.f;
 }
 
-// w[g][c][grp] = v_scale * 127 * 2^24 / VS[g] for the n_cells cells the call sees.
-__global__ __launch_bounds__(256) void prompt_vscale_kernel(const float *__restrict__ vs, int32_t cap, int32_t n_cells,
-                                                            const float *__restrict__ VSp, float *__restrict__ w)
-{
-    const int32_t g = blockIdx.y;
-    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (e >= 2 * (int64_t)n_cells) return;
-    const float sc = PMAX / head_vs(VSp, g);
-    w[(int64_t)g * n_cells * 2 + e] = vs[(int64_t)g * cap * 2 + e] * sc;
-}
-
 // ------------------------------------------------------------------------------------------- main kernel
 struct PromptArgs {
     const int8_t *qd;
     const float *qs;
     const float *VSp;  // [n_kv][VS_SLICES] partial maxima of v_scale
-    const float *w;    // [n_kv][w_cells][2] scaled v_scale
-    int32_t w_cells;
     PoolArg pool;
     float *m_out;
     float *l_out;
@@ -166,7 +156,7 @@ struct __align__(16) PromptTile {
     int8_t k[PT * PD];     // [cell][128], 16-byte chunk p of row c holds chunk p ^ swz_k(c)
     int8_t v[PT * PD];     // [cell][128], 16-byte chunk p of row c holds chunk p ^ swz_v(c)
     float ks[PT * 2];      // [cell][grp]
-    float vs[PT * 2];      // [cell][grp], scaled to w
+    float vs[PT * 2];      // [cell][grp], scaled in LDS to w = v_scale * 127 * 2^24 / VS[g]
 };
 
 // K8V4 pools: wave w stages the packed 4-bit V codes of the tile's cells 16w .. 16w + 15 (1,024 bytes, lane l holds
@@ -236,7 +226,9 @@ __global__ __launch_bounds__(256, 2) void prompt_attn_kernel(const PromptArgs a)
 
     // logit scale of the row; a floor keeps -inf * crow = -inf for all-zero q rows (whose logits are all 0)
     const float crow = fmaxf(row_ok ? a.qs[(int64_t)g * a.R + r] : 0.f, 1e-30f);
-    const float sw = head_vs(a.VSp, g) / PMAX;  // value of one unit of the p * w digits
+    const float VS = head_vs(a.VSp, g);
+    const float sw = VS / PMAX;     // value of one unit of the p * w digits
+    const float vsc = PMAX / VS;    // w = v_scale * vsc
 
     v4i acc[4][8];   // PV int32 sums per digit plane (weights 2^24, 2^16, 2^8, 1)
 #pragma unroll
@@ -276,7 +268,7 @@ __global__ __launch_bounds__(256, 2) void prompt_attn_kernel(const PromptArgs a)
     const int8_t *kg = P.k + (int64_t)g * P.capacity * PD;
     const int8_t *vg = P.v + (int64_t)g * P.capacity * VROW;
     const float *ksg = P.ks + (int64_t)g * P.capacity * 2;
-    const float *vsg = a.w + (int64_t)g * a.w_cells * 2;
+    const float *vsg = P.vs + (int64_t)g * P.capacity * 2;
     // The tile's base address is wave-uniform (scalar registers); a lane's byte offset within a full tile is the
     // same for every tile, and only a tile that runs past the last cell clamps its cells.
     uint32_t koff[2], voff[2];
@@ -319,21 +311,22 @@ __global__ __launch_bounds__(256, 2) void prompt_attn_kernel(const PromptArgs a)
             copy_lds4(st, 4 * (2 * min(se >> 1, nfull) + (se & 1)), lds_addr(sdst));
         }
     };
-    // K8V4: expand this wave's share of a landed packed tile (the compiler barrier keeps its LDS reads after the wait)
-    auto expand = [&](int32_t t) {
-        if constexpr (VB == 4) {
-            asm volatile("" ::: "memory");
-            expand_v4(tile[(t - t0) % NBUF].v, wave, lane);
-        }
+    // Once this wave's copies of tile t have landed (the compiler barrier keeps the LDS reads after the wait): the
+    // waves that copied the v_scale halves turn them into w, and for K8V4 every wave widens its share of the V codes.
+    auto finish = [&](int32_t t) {
+        PromptTile &T = tile[(t - t0) % NBUF];
+        asm volatile("" ::: "memory");
+        if (wave >= 2) T.vs[se] *= vsc;
+        if constexpr (VB == 4) expand_v4(T.v, wave, lane);
     };
 
-    // Tiles are triple-buffered and prefetched two ahead: tile t lives in buffer (t - t0) % 3, and its copies are
-    // issued at the start of step t - 2, so they have two steps to land.
+    // Tiles are triple-buffered and prefetched two ahead: tile t lives in buffer (t - t0) % 3, its copies are issued
+    // at the start of step t - 2, and each wave waits for its own in the middle of step t - 1 and finishes its share.
     if (t0 < t1) stage(t0, 0);
     if (t0 + 1 < t1) stage(t0 + 1, 1);
     if (t0 + 1 < t1) __builtin_amdgcn_s_waitcnt(WAIT_TILE);   // tile t0 has landed
     else __builtin_amdgcn_s_waitcnt(WAIT_VM0_LGKM0);
-    if (t0 < t1) expand(t0);
+    if (t0 < t1) finish(t0);
     __syncthreads();
 
     // Tiles before t_mask end at or before the wave's smallest limit and need no causal mask; the loop is split so
@@ -408,6 +401,14 @@ __global__ __launch_bounds__(256, 2) void prompt_attn_kernel(const PromptArgs a)
         }
         const float mexp = mref == -INFINITY ? 0.f : mref;
 
+        // ---- tile t + 1, whose copies were issued a step ago, is finished here so that the exponentials and
+        // splits below hide the LDS round trips (its buffer is not read before the step's closing barrier)
+        if (t + 1 < t1) {
+            if (t + 2 < t1) __builtin_amdgcn_s_waitcnt(WAIT_TILE);
+            else __builtin_amdgcn_s_waitcnt(WAIT_VM0_LGKM0);
+            finish(t + 1);
+        }
+
         // ---- p = 2^(t - m_ref); the digits of p * w, per scale group, are the B operands of O^T += V^T . P^T,
         // run over the group's four 16-dim blocks. V^T rows come from two transposing reads per block.
         float p[4][4];
@@ -462,10 +463,6 @@ __global__ __launch_bounds__(256, 2) void prompt_attn_kernel(const PromptArgs a)
         }
 
         __builtin_amdgcn_s_setprio(0);
-        // this wave's copies of tile t + 1 have landed (those of tile t + 2 may still be in flight)
-        if (t + 2 < t1) __builtin_amdgcn_s_waitcnt(WAIT_TILE);
-        else __builtin_amdgcn_s_waitcnt(WAIT_VM0_LGKM0);
-        if (t + 1 < t1) expand(t + 1);
         __syncthreads();
     };
     int32_t t = t0;
@@ -497,7 +494,57 @@ __global__ __launch_bounds__(256, 2) void prompt_attn_kernel(const PromptArgs a)
     }
 }
 
-// Cell chunks per row block: enough workgroups to fill the chip in whole rounds of two per CU.
+// ------------------------------------------------------------------------------------------- chunk merge
+// The S <= MAX_S cell chunks of each (query, q head) row folded as the decode merge folds them: M over the non-empty
+// chunks, weights e^(m_j - M) added in chunk order, empty chunks skipped by select (their o may hold anything), a row
+// with none gets zeros. 32 lanes per row with four dims each, 8 rows per 256-thread workgroup, every load of a row
+// issued before the first use: the partials are streamed once, with no cross-lane work.
+constexpr int MAX_S = 4;
+
+__global__ __launch_bounds__(256) void prompt_merge_kernel(const float *__restrict__ m, const float *__restrict__ l,
+                                                           const uint8_t *__restrict__ em, const float *__restrict__ o,
+                                                           int32_t S, int64_t rows, float *__restrict__ out)
+{
+    const int64_t row = (int64_t)blockIdx.x * 8 + threadIdx.x / 32;
+    if (row >= rows) return;
+    const int dl = threadIdx.x % 32;
+    float4 ov[MAX_S];
+    float mv[MAX_S], lv[MAX_S];
+    bool live[MAX_S];
+#pragma unroll
+    for (int j = 0; j < MAX_S; j++) {
+        if (j < S) {
+            const int64_t e = row * S + j;
+            ov[j] = *reinterpret_cast<const float4 *>(o + e * PD + 4 * dl);
+            mv[j] = m[e];
+            lv[j] = l[e];
+            live[j] = em[e] == 0;
+        } else {
+            ov[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+            mv[j] = lv[j] = 0.f;
+            live[j] = false;
+        }
+    }
+    float M = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < MAX_S; j++) M = live[j] ? fmaxf(M, mv[j]) : M;
+    float L = 0.f;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int j = 0; j < MAX_S; j++) {
+        if (live[j]) {
+            const float w = expf(mv[j] - M);
+            L = fmaf(w, lv[j], L);
+            acc = make_float4(fmaf(w, ov[j].x, acc.x), fmaf(w, ov[j].y, acc.y), fmaf(w, ov[j].z, acc.z),
+                              fmaf(w, ov[j].w, acc.w));
+        }
+    }
+    const bool none = M == -INFINITY;
+    *reinterpret_cast<float4 *>(out + row * PD + 4 * dl) =
+        none ? make_float4(0.f, 0.f, 0.f, 0.f) : make_float4(acc.x / L, acc.y / L, acc.z / L, acc.w / L);
+}
+
+// Cell chunks per row block: enough workgroups to fill the chip in whole rounds of two per CU (at most MAX_S).
 int prompt_chunks(int32_t n_q, const qsa_dims &d)
 {
     const int64_t R = (int64_t)n_q * (d.n_q_heads / d.n_kv_heads);
@@ -506,7 +553,7 @@ int prompt_chunks(int32_t n_q, const qsa_dims &d)
     const int64_t slots = 2 * NCU;
     int best = 1;
     double best_eff = 0.0;
-    for (int S = 1; S <= 4; S++) {
+    for (int S = 1; S <= MAX_S; S++) {
         const int64_t n = wg * S;
         const double eff = (double)n / (double)(((n + slots - 1) / slots) * slots);
         if (eff > best_eff + 0.05) {
@@ -518,11 +565,10 @@ int prompt_chunks(int32_t n_q, const qsa_dims &d)
 }
 
 struct PromptScratch {
-    size_t qd, qs, vs, w, m, l, o, e, total;
+    size_t qd, qs, vs, m, l, o, e, total;
 };
 
-// n_cells: pool cells the call sees (scaled v_scale is kept for each of them).
-PromptScratch prompt_layout(int32_t n_q, int64_t n_cells, const qsa_dims &d)
+PromptScratch prompt_layout(int32_t n_q, const qsa_dims &d)
 {
     auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
     const size_t rows = (size_t)n_q * d.n_q_heads;
@@ -532,7 +578,6 @@ PromptScratch prompt_layout(int32_t n_q, int64_t n_cells, const qsa_dims &d)
     s.qd = off; off += al(rows * 3 * PD);
     s.qs = off; off += al(rows * sizeof(float));
     s.vs = off; off += al((size_t)d.n_kv_heads * VS_SLICES * sizeof(float));
-    s.w = off; off += al((size_t)d.n_kv_heads * (size_t)n_cells * 2 * sizeof(float));
     if (S > 1) {
         s.m = off; off += al(rows * S * sizeof(float));
         s.l = off; off += al(rows * S * sizeof(float));
@@ -543,12 +588,13 @@ PromptScratch prompt_layout(int32_t n_q, int64_t n_cells, const qsa_dims &d)
     return s;
 }
 
-// ------------------------------------------------------------------------------------- other head dims, K8V4
-// The matrix-core kernel above covers head_dim 128 with int8 V. Every other shape the decode kernels support (head_dim
-// 64 or 256, K8V4 pools) takes the chunk attention kernel in dense mode -- query i as a row at position pos0 + i over
-// blocks of its visible cells, split in up to FB_MAX_CHUNKS chunks -- and the log-sum-exp merge, FB_BATCH queries at
-// a time so that the partials stay small. Same result (softmax attention over the visible cells), on the VALU or the
-// fp16 matrix cores instead of the int8 digit products, and every query reads its own cells, so it is much slower.
+// ------------------------------------------------------------------------------------------- other head dims
+// The matrix-core kernel above covers head_dim 128 (int8 and K8V4 pools). The other head dims the decode kernels
+// support (64 and 256, K8V4 at 256) take the chunk attention kernel in dense mode -- query i as a row at position
+// pos0 + i over blocks of its visible cells, split in up to FB_MAX_CHUNKS chunks -- and the log-sum-exp merge,
+// FB_BATCH queries at a time so that the partials stay small. Same result (softmax attention over the visible cells),
+// on the VALU or the fp16 matrix cores instead of the int8 digit products, and every query reads its own cells, so it
+// is much slower.
 constexpr int32_t FB_BATCH = 64, FB_MAX_CHUNKS = 32;
 
 struct DenseLayout {
@@ -619,7 +665,7 @@ extern "C" size_t qsa_prompt_scratch_bytes(int32_t n_q, int32_t pos0, qsa_dims d
     if (n_q <= 0 || pos0 < 0 || check_dims(dims) != QSA_OK) return 0;
     const int64_t last = (int64_t)pos0 + n_q;
     // head_dim 128 runs the matrix-core kernel (int8 or K8V4 pools alike), the other head dims the dense chunk path
-    return dims.head_dim == PD ? prompt_layout(n_q, last, dims).total : dense_layout(n_q, last, dims).total;
+    return dims.head_dim == PD ? prompt_layout(n_q, dims).total : dense_layout(n_q, last, dims).total;
 }
 
 extern "C" qsa_status qsa_prompt_attn(const float *q, int32_t n_q, int32_t pos0, const qsa_pool *pool, qsa_dims dims,
@@ -640,7 +686,7 @@ extern "C" qsa_status qsa_prompt_attn(const float *q, int32_t n_q, int32_t pos0,
         return prompt_dense(q, n_q, pos0, pool, dims, sm_scale, out, scratch, scratch_bytes, (hipStream_t)stream);
     const int64_t last = (int64_t)pos0 + n_q;
     const int32_t n_cells = (int32_t)(last < pool->n_valid ? last : pool->n_valid);
-    const PromptScratch lay = prompt_layout(n_q, n_cells, dims);
+    const PromptScratch lay = prompt_layout(n_q, dims);
     if (!scratch) return QSA_ERR_NULL;
     if (scratch_bytes < lay.total) return QSA_ERR_SCRATCH;
     const int32_t G = dims.n_q_heads / dims.n_kv_heads;
@@ -653,16 +699,13 @@ extern "C" qsa_status qsa_prompt_attn(const float *q, int32_t n_q, int32_t pos0,
     int8_t *qd = reinterpret_cast<int8_t *>(base + lay.qd);
     float *qs = reinterpret_cast<float *>(base + lay.qs);
     float *VSp = reinterpret_cast<float *>(base + lay.vs);
-    prompt_qsplit_kernel<<<dim3((uint32_t)n_q * dims.n_q_heads), 64, 0, s>>>(q, dims.n_q_heads, G, (int32_t)R,
+    const int64_t n_rows = (int64_t)n_q * dims.n_q_heads;
+    prompt_qsplit_kernel<<<dim3((uint32_t)((n_rows + 3) / 4)), 256, 0, s>>>(q, dims.n_q_heads, G, (int32_t)R, n_rows,
                                                                              sm_scale * PLOG2E, qd, qs);
-    float *w = reinterpret_cast<float *>(base + lay.w);
     prompt_vsmax_kernel<<<dim3(dims.n_kv_heads, VS_SLICES), 256, 0, s>>>(pool->v_scale, pool->capacity, n_cells, VSp);
-    if (n_cells > 0)
-        prompt_vscale_kernel<<<dim3((uint32_t)((2 * (int64_t)n_cells + 255) / 256), dims.n_kv_heads), 256, 0, s>>>(
-            pool->v_scale, pool->capacity, n_cells, VSp, w);
 
     PromptArgs a{};
-    a.qd = qd; a.qs = qs; a.VSp = VSp; a.w = w; a.w_cells = n_cells;
+    a.qd = qd; a.qs = qs; a.VSp = VSp;
     a.pool = PoolArg{pool->k, pool->k_scale, pool->v, pool->v_scale, pool->capacity, pool->n_valid};
     a.out = out;
     a.n_q = n_q; a.pos0 = pos0; a.n_qh = dims.n_q_heads; a.G = G; a.R = (int32_t)R; a.S = S;
@@ -676,7 +719,11 @@ extern "C" qsa_status qsa_prompt_attn(const float *q, int32_t n_q, int32_t pos0,
     if (v_bits_of(*pool) == 8) prompt_attn_kernel<8><<<grid, 256, 0, s>>>(a);
     else prompt_attn_kernel<4><<<grid, 256, 0, s>>>(a);
     if ((st = launch_status()) != QSA_OK) return st;
-    if (S > 1) return merge_launch(a.m_out, a.l_out, a.o_out, a.e_out, S, S, nullptr, n_q, dims.n_q_heads, PD, out,
-                                   nullptr, s);
+    if (S > 1) {
+        const int64_t rows = (int64_t)n_q * dims.n_q_heads;
+        prompt_merge_kernel<<<dim3((uint32_t)((rows + 7) / 8)), 256, 0, s>>>(a.m_out, a.l_out, a.e_out, a.o_out, S,
+                                                                             rows, out);
+        return launch_status();
+    }
     return QSA_OK;
 }

@@ -166,7 +166,8 @@ def test_prompt_scratch_sizing_and_checks():
     L = qsa.lib_handle()
     n = L.qsa_prompt_scratch_bytes(2048, 30720, GOOD)
     assert n >= 2048 * 24 * (3 * 128 + 4)          # q digits and row scales at least
-    assert n >= L.qsa_prompt_scratch_bytes(2048, 0, GOOD) + 4 * 30720 * 2 * 4   # scaled v_scale per seen cell
+    assert n >= 2048 * 24 * 2 * (128 * 4 + 9)      # and two cell chunks' (m, l, empty, o) partials per row
+    assert n == L.qsa_prompt_scratch_bytes(2048, 0, GOOD)   # nothing per pool cell (v_scale is scaled in LDS)
     assert L.qsa_prompt_scratch_bytes(0, 0, GOOD) == 0
     assert L.qsa_prompt_scratch_bytes(16, -1, GOOD) == 0
     # head_dims without the int8 matrix-core kernel take the dense chunk path: its partials for one 64-query batch
@@ -178,7 +179,7 @@ def test_prompt_scratch_sizing_and_checks():
     assert L.qsa_prompt_attn(1, 16, 0, ctypes.byref(p), GOOD, 1.0, 1, None, 0, None) == -1       # no scratch
     need = L.qsa_prompt_scratch_bytes(16, 0, GOOD)
     assert L.qsa_prompt_attn(1, 16, 0, ctypes.byref(p), GOOD, 1.0, 1, 1, need - 1, None) == -4
-    # the dense path checks its own scratch need, and a K8V4 pool at head_dim 128 takes it too
+    # the dense path checks its own scratch need; a K8V4 pool at head_dim 128 needs the matrix-core kernel's
     need64 = L.qsa_prompt_scratch_bytes(16, 0, d64)
     p64 = _pool()
     assert L.qsa_prompt_attn(1, 16, 0, ctypes.byref(p64), d64, 1.0, 1, 1, need64 - 1, None) == -4
