@@ -311,12 +311,16 @@ __global__ __launch_bounds__(256, 2) void prompt_attn_kernel(const PromptArgs a)
             copy_lds4(st, 4 * (2 * min(se >> 1, nfull) + (se & 1)), lds_addr(sdst));
         }
     };
-    // Once this wave's copies of tile t have landed (the compiler barrier keeps the LDS reads after the wait): the
+    // Once this wave's copies of a tile have landed (the compiler barrier keeps the LDS reads after the wait): the
     // waves that copied the v_scale halves turn them into w, and for K8V4 every wave widens its share of the V codes.
-    auto finish = [&](int32_t t) {
-        PromptTile &T = tile[(t - t0) % NBUF];
+    // No branch (the K-scale waves rewrite theirs times 1), so the step's scheduler can interleave it with the
+    // exponentials that follow.
+    const float sfac = wave >= 2 ? vsc : 1.f;
+    auto finish = [&](int buf) {
+        PromptTile &T = tile[buf];
         asm volatile("" ::: "memory");
-        if (wave >= 2) T.vs[se] *= vsc;
+        float *sc = (wave < 2 ? T.ks : T.vs) + se;
+        *sc = *sc * sfac;
         if constexpr (VB == 4) expand_v4(T.v, wave, lane);
     };
 
@@ -326,16 +330,23 @@ __global__ __launch_bounds__(256, 2) void prompt_attn_kernel(const PromptArgs a)
     if (t0 + 1 < t1) stage(t0 + 1, 1);
     if (t0 + 1 < t1) __builtin_amdgcn_s_waitcnt(WAIT_TILE);   // tile t0 has landed
     else __builtin_amdgcn_s_waitcnt(WAIT_VM0_LGKM0);
-    if (t0 < t1) finish(t0);
+    if (t0 < t1) finish(0);
     __syncthreads();
 
     // Tiles before t_mask end at or before the wave's smallest limit and need no causal mask; the loop is split so
     // the mask compares only run on the last tiles. Every iteration has one barrier, so the waves stay matched.
     const int32_t t_mask = wave_lim < PT - 1 ? 0 : (wave_lim - (PT - 1)) / PT + 1;
-    auto step = [&](int32_t t, auto masked_tag) {
+    // BUF_TAG is tile t's buffer when known at compile time (the unrolled loop), or -1: constant buffer indexes turn
+    // every LDS address of the step into a loop-invariant register plus an immediate offset.
+    auto step = [&](int32_t t, auto masked_tag, auto buf_tag) {
         constexpr bool masked = decltype(masked_tag)::value;
-        const int buf = (t - t0) % NBUF;
-        if (t + 2 < t1) stage(t + 2, (t + 2 - t0) % NBUF);   // the buffer tile t - 1 used
+        constexpr int BUF = decltype(buf_tag)::value;
+        const int buf = BUF >= 0 ? BUF : (t - t0) % NBUF;
+        const int buf1 = BUF >= 0 ? (BUF + 1) % NBUF : (buf + 1 == NBUF ? 0 : buf + 1);
+        const int buf2 = BUF >= 0 ? (BUF + 2) % NBUF : (buf1 + 1 == NBUF ? 0 : buf1 + 1);
+        // tile t + 2 into the buffer tile t - 1 used; past the last tile the last one is copied again into a buffer
+        // nobody reads any more, so that every step waits and finishes the same way, without a branch
+        stage(min(t + 2, t1 - 1), buf2);
         const PromptTile &T = tile[buf];
         const int32_t cb = t * PT;
 
@@ -403,11 +414,8 @@ __global__ __launch_bounds__(256, 2) void prompt_attn_kernel(const PromptArgs a)
 
         // ---- tile t + 1, whose copies were issued a step ago, is finished here so that the exponentials and
         // splits below hide the LDS round trips (its buffer is not read before the step's closing barrier)
-        if (t + 1 < t1) {
-            if (t + 2 < t1) __builtin_amdgcn_s_waitcnt(WAIT_TILE);
-            else __builtin_amdgcn_s_waitcnt(WAIT_VM0_LGKM0);
-            finish(t + 1);
-        }
+        __builtin_amdgcn_s_waitcnt(WAIT_TILE);
+        finish(buf1);
 
         // ---- p = 2^(t - m_ref); the digits of p * w, per scale group, are the B operands of O^T += V^T . P^T,
         // run over the group's four 16-dim blocks. V^T rows come from two transposing reads per block.
@@ -465,9 +473,18 @@ __global__ __launch_bounds__(256, 2) void prompt_attn_kernel(const PromptArgs a)
         __builtin_amdgcn_s_setprio(0);
         __syncthreads();
     };
+    using runtime_buf = std::integral_constant<int, -1>;
     int32_t t = t0;
-    for (; t < min(t_mask, t1); t++) step(t, std::false_type{});
-    for (; t < t1; t++) step(t, std::true_type{});
+    const int32_t t_plain = min(t_mask, t1);
+    static_assert(NBUF == 3, "the plain loop is unrolled once per buffer");
+    for (; t + NBUF <= t_plain; t += NBUF) {   // (t - t0) % NBUF == 0 here
+        step(t, std::false_type{}, std::integral_constant<int, 0>{});
+        step(t + 1, std::false_type{}, std::integral_constant<int, 1>{});
+        step(t + 2, std::false_type{}, std::integral_constant<int, 2>{});
+    }
+    for (; t < t_plain; t++) step(t, std::false_type{}, runtime_buf{});
+    for (; t < t1; t++) step(t, std::true_type{}, runtime_buf{});
+    __builtin_amdgcn_s_waitcnt(WAIT_VM0_LGKM0);   // the repeated copies of the last steps have landed
 
     // ---- final fold and output
     lsum = sum16(lsum);
