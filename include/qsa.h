@@ -176,7 +176,8 @@ size_t qsa_prompt_scratch_bytes(int32_t n_q, int32_t pos0, qsa_dims dims);
  * through the chunk attention kernel in dense mode and the merge, 64 queries at a time (much slower: each query
  * reads its own cells). out [n_q][n_q_heads][head_dim]; sm_scale multiplies q . k. Requires pos0 >= 0 and
  * pos0 + n_q - 1 <= INT32_MAX (QSA_ERR_RANGE), a supported head_dim and V format (QSA_ERR_UNSUPPORTED: head_dim 192,
- * K8V4 at head_dim 64) and scratch_bytes >= qsa_prompt_scratch_bytes (QSA_ERR_SCRATCH). */
+ * K8V4 at head_dim 64), n_q * n_q_heads <= INT32_MAX (QSA_ERR_UNSUPPORTED) and
+ * scratch_bytes >= qsa_prompt_scratch_bytes (QSA_ERR_SCRATCH). */
 qsa_status qsa_prompt_attn(const float *q, int32_t n_q, int32_t pos0, const qsa_pool *pool, qsa_dims dims,
                            float sm_scale, float *out, void *scratch, size_t scratch_bytes, qsa_stream_t stream);
 

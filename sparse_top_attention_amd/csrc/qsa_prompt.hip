@@ -680,6 +680,7 @@ using namespace qsa;
 extern "C" size_t qsa_prompt_scratch_bytes(int32_t n_q, int32_t pos0, qsa_dims dims)
 {
     if (n_q <= 0 || pos0 < 0 || check_dims(dims) != QSA_OK) return 0;
+    if ((int64_t)n_q * dims.n_q_heads > INT32_MAX) return 0;
     const int64_t last = (int64_t)pos0 + n_q;
     // head_dim 128 runs the matrix-core kernel (int8 or K8V4 pools alike), the other head dims the dense chunk path
     return dims.head_dim == PD ? prompt_layout(n_q, dims).total : dense_layout(n_q, last, dims).total;
@@ -695,6 +696,7 @@ extern "C" qsa_status qsa_prompt_attn(const float *q, int32_t n_q, int32_t pos0,
     if (!q || !out) return QSA_ERR_NULL;
     if (n_q < 0 || pos0 < 0 || (int64_t)pos0 + n_q - 1 > INT32_MAX) return QSA_ERR_RANGE;
     if (!common_v_bits(pool, 1, dims.head_dim)) return QSA_ERR_UNSUPPORTED;   // K8V4 needs head_dim >= 128
+    if ((int64_t)n_q * dims.n_q_heads > INT32_MAX) return QSA_ERR_UNSUPPORTED;   // (query, head) rows index grids
     if (n_q == 0) return QSA_OK;
     if (!scratch) return QSA_ERR_NULL;
     // the size qsa_prompt_scratch_bytes reports, whatever the pool's V format

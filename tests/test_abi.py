@@ -170,6 +170,7 @@ def test_prompt_scratch_sizing_and_checks():
     assert n == L.qsa_prompt_scratch_bytes(2048, 0, GOOD)   # nothing per pool cell (v_scale is scaled in LDS)
     assert L.qsa_prompt_scratch_bytes(0, 0, GOOD) == 0
     assert L.qsa_prompt_scratch_bytes(16, -1, GOOD) == 0
+    assert L.qsa_prompt_scratch_bytes(2**27, 0, GOOD) == 0     # more (query, head) rows than an int32 holds
     # head_dims without the int8 matrix-core kernel take the dense chunk path: its partials for one 64-query batch
     d64, d256 = D(24, 4, 64, 64), D(24, 4, 256, 64)
     assert L.qsa_prompt_scratch_bytes(16, 0, d64) >= 16 * 24 * 1 * (64 * 4 + 9)
@@ -188,6 +189,7 @@ def test_prompt_scratch_sizing_and_checks():
     assert L.qsa_prompt_attn(1, 16, 0, ctypes.byref(p4), d64, 1.0, 1, 1, need, None) == -3     # K8V4 at head_dim 64
     assert L.qsa_prompt_attn(1, 16, 0, ctypes.byref(p), D(24, 4, 192, 64), 1.0, 1, 1, need, None) == -3
     assert L.qsa_prompt_attn(1, 2, 2**31 - 1, ctypes.byref(p), GOOD, 1.0, 1, 1, need, None) == -5  # positions past int32
+    assert L.qsa_prompt_attn(1, 2**27, 0, ctypes.byref(p), GOOD, 1.0, 1, 1, need, None) == -3  # 3.2e9 (query, head) rows
     assert L.qsa_prompt_attn(1, 0, 0, ctypes.byref(p), GOOD, 1.0, 1, None, 0, None) == 0
 
 
