@@ -24,7 +24,8 @@
  *   - Values that live in device memory (positions, ids, counts, pool indices) cannot be checked on the host;
  *     the kernels treat out-of-range values as "no cell" and never read outside the pool (documented per call).
  *   - Supported shapes: head_dim in {64, 128, 256}; block_cells == 64; n_q_heads a multiple of n_kv_heads with
- *     at most 8 q heads per KV head. Anything else returns QSA_ERR_UNSUPPORTED.
+ *     at most 8 q heads per KV head; at most 65,535 KV heads (a launch grid dimension). Anything else returns
+ *     QSA_ERR_UNSUPPORTED.
  *
  * Layouts (row-major):
  *   K and V codes   int8  [n_kv_heads][capacity][head_dim]
@@ -159,8 +160,8 @@ qsa_status qsa_attn_chunk(const float *q, const int32_t *pos, int32_t n_rows, co
  * reaches are folded). For each row i and q head h, over chunks j < n_active[i] (n_active NULL = n_chunks;
  * values are clamped to [0, n_chunks]) that are not marked empty: M = max m_j, L = sum e^(m_j - M) l_j,
  * out[i][h][:] = sum e^(m_j - M) o_j / L, lse[i][h] = M + ln L (lse may be NULL). A row with no such chunk gets
- * out = 0 and lse = -inf. out is [n_rows][n_q_heads][head_dim]. Requires 1 <= n_chunks (QSA_ERR_RANGE) and
- * n_chunks <= in->max_chunks (QSA_ERR_SCRATCH). */
+ * out = 0 and lse = -inf. out is [n_rows][n_q_heads][head_dim]. Requires 1 <= n_chunks (QSA_ERR_RANGE),
+ * n_chunks <= in->max_chunks (QSA_ERR_SCRATCH) and n_rows * n_q_heads <= INT32_MAX (QSA_ERR_UNSUPPORTED). */
 qsa_status qsa_attn_merge(const qsa_partials *in, int32_t n_rows, qsa_dims dims, int32_t n_chunks,
                           const int32_t *n_active, float *out, float *lse, qsa_stream_t stream);
 

@@ -649,6 +649,7 @@ extern "C" qsa_status qsa_attn_merge(const qsa_partials *in, int32_t n_rows, qsa
     if (n_rows < 0) return QSA_ERR_SHAPE;
     if (n_chunks < 1) return QSA_ERR_RANGE;   // the merge kernel reads chunk n_chunks - 1 as its clamp target
     if (n_chunks > in->max_chunks) return QSA_ERR_SCRATCH;
+    if ((int64_t)n_rows * dims.n_q_heads > INT32_MAX) return QSA_ERR_UNSUPPORTED;   // one workgroup per (row, head)
     if (n_rows == 0) return QSA_OK;
     return merge_launch(in->m, in->l, in->o, in->empty, in->max_chunks, n_chunks, n_active, n_rows, dims.n_q_heads,
                         dims.head_dim, out, lse, (hipStream_t)stream);

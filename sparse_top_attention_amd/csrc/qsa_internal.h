@@ -22,6 +22,7 @@ inline bool dims_supported(const qsa_dims &d)
     if (d.head_dim != 64 && d.head_dim != 128 && d.head_dim != 256) return false;
     if (d.n_kv_heads <= 0 || d.n_q_heads <= 0 || d.n_q_heads % d.n_kv_heads != 0) return false;
     if (d.n_q_heads / d.n_kv_heads > 8) return false;
+    if (d.n_kv_heads > 65535) return false;   // KV heads index a launch grid's y dimension
     return true;
 }
 

@@ -67,6 +67,7 @@ GOOD = D(24, 4, 128, 64)
     (D(24, 5, 128, 64), -2),   # q heads not a multiple of KV heads
     (D(40, 4, 128, 64), -3),   # more than 8 q heads per KV head
     (D(0, 4, 128, 64), -2),
+    (D(65536, 65536, 128, 64), -3),   # KV heads past a launch grid dimension
 ])
 def test_dims_validation(dims, expect):
     L = qsa.lib_handle()
@@ -152,6 +153,8 @@ def test_merge_validation():
     assert L.qsa_attn_merge(ctypes.byref(parts), 4, GOOD, 0, None, 1, None, None) == -5
     assert L.qsa_attn_merge(ctypes.byref(parts), 0, GOOD, 0, None, 1, None, None) == -5
     assert L.qsa_attn_merge(ctypes.byref(parts), 4, GOOD, -1, None, 1, None, None) == -5
+    # one workgroup per (row, q head): more than INT32_MAX of them is refused, not launched on a wrapped grid
+    assert L.qsa_attn_merge(ctypes.byref(parts), 2**27, GOOD, 8, None, 1, None, None) == -3
 
 
 def test_prompt_validation():
