@@ -21,6 +21,7 @@
  *   - Arguments are validated first. On any error the call returns a negative qsa_status and has launched
  *     nothing -- the convention of [1888] "What changed", where the split launcher returns false with nothing
  *     launched when the case is unsupported or the partials would not fit the caller's scratch.
+ *   - sm_scale (the calls that take one) may be any finite value; inf or NaN returns QSA_ERR_RANGE.
  *   - Values that live in device memory (positions, ids, counts, pool indices) cannot be checked on the host;
  *     the kernels treat out-of-range values as "no cell" and never read outside the pool (documented per call).
  *   - Supported shapes: head_dim in {64, 128, 256}; block_cells == 64; n_q_heads a multiple of n_kv_heads with

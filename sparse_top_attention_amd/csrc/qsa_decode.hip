@@ -590,7 +590,7 @@ extern "C" qsa_status qsa_attn_chunk(const float *q, const int32_t *pos, int32_t
     } else if (blocks_per_chunk <= 0) {
         return QSA_ERR_RANGE;
     }
-    if (n_chunks <= 0) return QSA_ERR_RANGE;
+    if (n_chunks <= 0 || !scale_ok(sm_scale)) return QSA_ERR_RANGE;
     if (n_chunks > out->max_chunks) return QSA_ERR_SCRATCH;
     if (n_rows == 0) return QSA_OK;
     if (n_rows > 65535) return QSA_ERR_UNSUPPORTED;
@@ -734,12 +734,12 @@ namespace {
 // Host-side checks of qsa_decode_layer's arguments (everything but the scratch buffer); fills sa and vb.
 qsa_status layer_setup(const float *q, const int32_t *pos, int32_t n_rows, const qsa_pool *pools, int32_t n_pools,
                        const int32_t *row_pool, const qsa_dims &dims, int32_t n_blocks, int32_t k, int32_t n_chunks,
-                       const float *out, SelectArgs &sa, int &vb)
+                       float sm_scale, const float *out, SelectArgs &sa, int &vb)
 {
     qsa_status st = select_setup(q, pos, n_rows, pools, n_pools, row_pool, dims, n_blocks, k, sa);
     if (st != QSA_OK) return st;
     if (!out) return QSA_ERR_NULL;
-    if (n_chunks < 1) return QSA_ERR_RANGE;
+    if (n_chunks < 1 || !scale_ok(sm_scale)) return QSA_ERR_RANGE;
     vb = common_v_bits(pools, n_pools, dims.head_dim);
     if (!vb) return QSA_ERR_UNSUPPORTED;
     return QSA_OK;
@@ -798,7 +798,8 @@ extern "C" qsa_status qsa_decode_layer(const float *q, const int32_t *pos, int32
 {
     SelectArgs sa;
     int vb = 0;
-    qsa_status st = layer_setup(q, pos, n_rows, pools, n_pools, row_pool, dims, n_blocks, k, n_chunks, out, sa, vb);
+    qsa_status st =
+        layer_setup(q, pos, n_rows, pools, n_pools, row_pool, dims, n_blocks, k, n_chunks, sm_scale, out, sa, vb);
     if (st != QSA_OK) return st;
     if (n_rows == 0) return QSA_OK;
     if (!scratch) return QSA_ERR_NULL;
@@ -842,7 +843,8 @@ extern "C" qsa_status qsa_decode_layer_noalloc(const float *q, const int32_t *po
 {
     SelectArgs sa;
     int vb = 0;
-    qsa_status st = layer_setup(q, pos, n_rows, pools, n_pools, row_pool, dims, n_blocks, k, n_chunks, out, sa, vb);
+    qsa_status st =
+        layer_setup(q, pos, n_rows, pools, n_pools, row_pool, dims, n_blocks, k, n_chunks, sm_scale, out, sa, vb);
     if (st != QSA_OK) return st;
     if (n_rows == 0) return QSA_OK;
     if (layer_layout(n_rows, dims, n_blocks, k, n_chunks).total > (size_t)QSA_NOALLOC_SCRATCH_BYTES)

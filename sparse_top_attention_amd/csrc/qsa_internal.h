@@ -44,6 +44,9 @@ inline qsa_status check_pool(const qsa_pool *p, bool need_v)
     return QSA_OK;
 }
 
+// A softmax scale the kernels can use (any finite value, negative and zero included).
+inline bool scale_ok(float s) { return __builtin_isfinite(s); }
+
 // V bits of a pool (0 means 8).
 inline int v_bits_of(const qsa_pool &p) { return p.v_bits == 4 ? 4 : 8; }
 

@@ -71,8 +71,9 @@ constexpr int WAIT_VM4_LGKM0 = 0x0074;   // all but the 4 newest
 
 // ---------------------------------------------------------------------------------------------- q digits
 // One wave per (query, q head), four per workgroup: qd[g][r][plane][d] int8 with r = query * G + head-in-group,
-// plane 0/1/2 = h/l/m, and qs[g][r] = max|q| / (127 * 65536) * sm_scale * log2(e) so that
-// q . k * sm_scale * log2(e) = qs * (X . k).
+// plane 0/1/2 = h/l/m, and qs[g][r] = max|q| / (127 * 65536) * |sm_scale| * log2(e) so that
+// q . k * sm_scale * log2(e) = qs * (X . k): the digits are those of sign(sm_scale) * q, so the logit scale of a row
+// is never negative (the attention kernel floors it at a tiny positive value).
 __global__ __launch_bounds__(256) void prompt_qsplit_kernel(const float *__restrict__ q, int32_t n_qh, int32_t G,
                                                             int32_t R, int64_t n_rows, float qscale,
                                                             int8_t *__restrict__ qd, float *__restrict__ qs)
@@ -84,7 +85,7 @@ __global__ __launch_bounds__(256) void prompt_qsplit_kernel(const float *__restr
     const int32_t g = h / G, r = qi * G + h % G;
     const float2 x = reinterpret_cast<const float2 *>(q + row * PD)[lane];
     const float amax = group_max<64>(fmaxf(fabsf(x.x), fabsf(x.y)));
-    const float s = amax > 0.f ? QMAX / amax : 0.f;
+    const float s = amax > 0.f ? copysignf(QMAX / amax, qscale) : 0.f;
     const int32_t X[2] = {(int32_t)rintf(x.x * s), (int32_t)rintf(x.y * s)};
     int32_t dg[3][2];
 #pragma unroll
@@ -102,7 +103,7 @@ __global__ __launch_bounds__(256) void prompt_qsplit_kernel(const float *__restr
         const uint16_t pair = (uint16_t)((dg[p][0] & 255) | ((dg[p][1] & 255) << 8));
         reinterpret_cast<uint16_t *>(dst + p * PD)[lane] = pair;
     }
-    if (lane == 0) qs[(int64_t)g * R + r] = amax > 0.f ? amax / QMAX * qscale : 0.f;
+    if (lane == 0) qs[(int64_t)g * R + r] = amax > 0.f ? amax / QMAX * fabsf(qscale) : 0.f;
 }
 
 // ------------------------------------------------------------------------------------------ V-scale bound
@@ -694,7 +695,7 @@ extern "C" qsa_status qsa_prompt_attn(const float *q, int32_t n_q, int32_t pos0,
     if (st != QSA_OK) return st;
     if ((st = check_pool(pool, true)) != QSA_OK) return st;
     if (!q || !out) return QSA_ERR_NULL;
-    if (n_q < 0 || pos0 < 0 || (int64_t)pos0 + n_q - 1 > INT32_MAX) return QSA_ERR_RANGE;
+    if (n_q < 0 || pos0 < 0 || (int64_t)pos0 + n_q - 1 > INT32_MAX || !scale_ok(sm_scale)) return QSA_ERR_RANGE;
     if (!common_v_bits(pool, 1, dims.head_dim)) return QSA_ERR_UNSUPPORTED;   // K8V4 needs head_dim >= 128
     if ((int64_t)n_q * dims.n_q_heads > INT32_MAX) return QSA_ERR_UNSUPPORTED;   // (query, head) rows index grids
     if (n_q == 0) return QSA_OK;

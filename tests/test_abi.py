@@ -126,6 +126,8 @@ def test_chunk_validation():
                                 a["ids"], a["counts"], a["k"], a["bpc"], a["n_chunks"], a["sm"], a["out"],
                                 a["stream"])
     assert call(n_chunks=9) == -4                        # partials too small
+    for bad in (float("inf"), float("-inf"), float("nan")):   # any finite scale is taken, negative included
+        assert call(sm=bad) == -5
     assert call(n_chunks=0) == -5
     assert call(k=0) == -5
     assert call(counts=None) == -1
@@ -162,6 +164,7 @@ def test_prompt_validation():
     p = _pool()
     assert L.qsa_prompt_attn(None, 16, 0, ctypes.byref(p), GOOD, 1.0, 1, None, 0, None) == -1
     assert L.qsa_prompt_attn(1, 16, -1, ctypes.byref(p), GOOD, 1.0, 1, None, 0, None) == -5
+    assert L.qsa_prompt_attn(1, 16, 0, ctypes.byref(p), GOOD, float("inf"), 1, None, 0, None) == -5
     assert L.qsa_prompt_attn(1, 16, 0, ctypes.byref(p), D(24, 4, 96, 64), 1.0, 1, None, 0, None) == -3
 
 
@@ -223,6 +226,8 @@ def test_decode_layer_validation():
     assert call(k=17) == -5                                # k > n_blocks
     assert call(nb=17) == -5                               # wider than ceil(cap / 64)
     assert call(S=0) == -5
+    assert call(sm=float("nan")) == -5
+    assert call(sm=float("inf")) == -5
     assert call(n_pools=9) == -3
     assert call(dims=D(24, 4, 96, 64)) == -3
     noidx = (qsa._Pool * 2)(_pool(), _pool(index=None))
@@ -359,5 +364,7 @@ def test_noalloc_layer_refuses_oversized_scratch_before_any_hip_call():
                                       None) == -5
     assert L.qsa_decode_layer_noalloc(1, 1, 64, pools, 1, None, GOOD, 1024, 64, 4, 1.0, None, None, None, None, None,
                                       None) == -1
+    assert L.qsa_decode_layer_noalloc(1, 1, 64, pools, 1, None, GOOD, 1024, 64, 4, float("nan"), 1, None, None, None,
+                                      None, None) == -5
     assert L.qsa_decode_layer_noalloc(1, 1, 0, pools, 1, None, GOOD, 1024, 64, 4, 1.0, 1, None, None, None, None,
                                       None) == 0

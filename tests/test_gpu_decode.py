@@ -401,3 +401,20 @@ def test_dense_partials_one_and_two_waves_per_chunk(n_chunks, rows):
     lse_r = rm[full] + np.log(rl[full])
     assert np.abs(lse_g - lse_r).max() <= TOL
     assert rel_err_rows(go[full] / gl[full][:, None], ro[full] / rl[full][:, None]).max() <= TOL
+
+
+@pytest.mark.parametrize("G,v_bits", [(6, 8), (2, 8), (6, 4)], ids=["mfma-int8", "valu-int8", "mfma-k8v4"])
+@pytest.mark.parametrize("scale", [-0.7, 0.0, 3.0])
+def test_dense_chunks_any_finite_scale(G, v_bits, scale):
+    """sm_scale may be any finite value: a negative one flips which cells dominate, zero gives uniform weights over
+    the visible cells, a large one sharpens the softmax. Dense chunks and the merge against the oracle."""
+    w = small_workload(71 + G + v_bits, n_kv=2, G=G, cap=900, n_valid=830, rows=3, v_bits=v_bits)
+    dims = dims_of(w)
+    n_chunks = 4
+    part = qsa.Partials.empty_like_shape(3, dims.n_q_heads, n_chunks, dims.head_dim)
+    qsa.qsa_attn_chunk(dev(w.q), dev(w.pos), [to_device(w.pools[0])], dims, part, n_chunks, scale, blocks_per_chunk=4)
+    out = torch.empty(3, dims.n_q_heads, dims.head_dim, dtype=torch.float32, device="cuda")
+    qsa.qsa_attn_merge(part, dims, n_chunks, out)
+    torch.cuda.synchronize()
+    ref, _ = oracle.attn(w.q, w.pos, w.pools[0], w.n_kv_heads, sm_scale=scale)
+    assert rel_err_rows(out.cpu().numpy(), ref).max() <= TOL

@@ -63,6 +63,24 @@ def test_prompt_other_shapes_match_oracle(d, v_bits, n_kv, G, n_q, pos0, n_valid
     assert rel_err_rows(got, ref).max() <= TOL
 
 
+@pytest.mark.parametrize("v_bits", [8, 4], ids=["int8", "k8v4"])
+def test_prompt_edge_cases(v_bits):
+    """A pool with no valid cell (every row sees nothing: zeros), a single query, and a negative scale."""
+    dims = qsa.Dims(12, 2, 128)
+    empty = synth.random_pool(351, 2, 256, 0, 128, v_bits=v_bits)
+    q = synth.random_q(352, 40, 12, 128)
+    got = run_prompt(q, 100, to_device(empty), dims)
+    assert np.all(got == 0.0)
+    pool = synth.random_pool(353, 2, 900, 700, 128, v_bits=v_bits)
+    p = to_device(pool)
+    for n_q, pos0, scale in [(1, 0, 1.0), (1, 699, 1.0), (1, 5000, 0.8), (70, 600, -0.6)]:
+        q = synth.random_q(354 + n_q + pos0, n_q, 12, 128)
+        got = run_prompt(q, pos0, p, dims, sm_scale=scale)
+        pos = (pos0 + np.arange(n_q)).astype(np.int32)
+        ref, _ = oracle.attn(q, pos, pool, 2, sm_scale=scale)
+        assert rel_err_rows(got, ref).max() <= TOL, (n_q, pos0, scale)
+
+
 def test_prompt_sm_scale_and_zero_query():
     pool = synth.random_pool(311, 2, 300, 260, 128)
     q = synth.random_q(312, 20, 12, 128)
@@ -90,14 +108,15 @@ def test_prompt_single_chunk_path():
             assert rel_err_rows(got[i, h][None], ref[None]).max() <= TOL, (i, h)
 
 
-def test_prompt_forced_fold_past_1024_tiles():
+@pytest.mark.parametrize("v_bits", [8, 4], ids=["int8", "k8v4"])
+def test_prompt_forced_fold_past_1024_tiles(v_bits):
     """One cell chunk longer than 1,024 tiles of 64 cells: the PV int32 sums are folded into fp32 every 1,024
     tiles whether or not the row max moved (8 KV heads x 4,096 queries fill the chip without splitting the cells,
     and pos0 = 66,000 gives every workgroup at least 1,032 tiles). Checked on sampled rows."""
     n_kv, G, n_q, pos0 = 8, 1, 4096, 66000
     n_valid = pos0 + n_q
     dims = qsa.Dims(n_kv * G, n_kv, 128)
-    pool = synth.random_pool(341, n_kv, n_valid + 40, n_valid, 128)
+    pool = synth.random_pool(341, n_kv, n_valid + 40, n_valid, 128, v_bits=v_bits)
     q = synth.random_q(342, n_q, n_kv * G, 128)
     got = run_prompt(q, pos0, to_device(pool), dims)
     assert np.all(np.isfinite(got))
