@@ -1,8 +1,9 @@
 """Python binding of libqsa (QSA attention over an int8 KV cache, MI355X / gfx950).
 
 Argument marshalling only: every function checks dtypes, devices, contiguity and sizes of torch tensors (the sizes
-against the dims, row counts, k, n_blocks and max_chunks the C side will index them by), passes their device pointers and the current HIP stream to the C ABI declared in include/qsa.h, and raises QSAError on a
-non-zero status. No torch operator runs on the compute path; PyTorch supplies device memory and streams.
+against the dims, row counts, k, n_blocks and max_chunks the C side will index them by), passes their device
+pointers and the current HIP stream to the C ABI declared in include/qsa.h, and raises QSAError on a non-zero
+status. No torch operator runs on the compute path; PyTorch supplies device memory and streams.
 
 The library is the in-tree ``libqsa.so``; importing this package raises if it has not been built (there is no
 fallback implementation).

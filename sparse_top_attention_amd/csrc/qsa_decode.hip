@@ -1,7 +1,8 @@
 // Decode-path kernels of libqsa for gfx950: block index, block scores, the log-sum-exp merge and the append path,
 // and the host side of every decode call (the split-K chunk attention kernels live in qsa_chunk.h and are
-// instantiated per head dim and V width in qsa_chunk_d*.hip). The kernels stream int8 codes / fp32 rows from HBM with 16-byte coalesced loads; per cell the
-// work is a few hundred FMAs against 272 bytes, so HBM and the fp32 VALU are the ceilings. With 4 or more q heads
+// instantiated per head dim and V width in qsa_chunk_d*.hip). The kernels stream int8 codes / fp32 rows from HBM
+// with 16-byte coalesced loads; per cell the work is a few hundred FMAs against 272 bytes, so HBM and the fp32 VALU
+// are the ceilings. With 4 or more q heads
 // per KV head at d = 128 the chunk kernel runs both of its products on the matrix cores (fp16 MFMA with exact K and V
 // codes and two-term splits of q and p * v_scale), on the VALU otherwise.
 //

@@ -4,7 +4,7 @@
 // bytes, so every int32 sum is exact and only the recombination is fp32:
 //   q    : one scale per (query, head) maps max |q| to 127 * 2^16; X = rint(q * scale) = 2^16 h + 2^8 l + m.
 //   p*vs : p = 2^(t - m_ref) <= 1 and w = vs * 127 * 2^24 / VS[g] (VS[g] = max v_scale over the cells the call
-//          sees, w precomputed per cell and group), X = p * w rounded to an integer = 2^24 d3 + 2^16 d2 + 2^8 d1 + d0.
+//          sees, w made per tile in LDS), X = p * w rounded to an integer = 2^24 d3 + 2^16 d2 + 2^8 d1 + d0.
 //          Four bytes (31 bits) rather than three because one scale covers a whole row: most cells sit far below
 //          the row maximum, and with 24 bits their rounding alone reached 1e-5 relative at a 32K context.
 //
@@ -16,7 +16,7 @@
 // cells 16G .. 16G + 15 (G = l / 16) of its row -- exactly the k-slots lane l must supply as the B operand of the
 // PV product, and the cells the lane's V^T operand holds. P never leaves registers.
 //
-// Tiles go from HBM straight into LDS (global_load_lds, no staging registers), double-buffered; bank swizzles are
+// Tiles go from HBM straight into LDS (global_load_lds, no staging registers), triple-buffered; bank swizzles are
 // applied by choosing which 16-byte chunk each lane fetches. V stays [cell][dim] in LDS; ds_read_b64_tr_b8 (within
 // each 16-lane group, lane j receives byte i of the 8 bytes addressed by lane 2i + (j >= 8), at byte j mod 8) turns
 // two reads per 16-dim block into the V^T operand.
