@@ -74,12 +74,12 @@ constexpr int WAIT_VM4_LGKM0 = 0x0074;   // all but the 4 newest
 // plane 0/1/2 = h/l/m, and qs[g][r] = max|q| / (127 * 65536) * |sm_scale| * log2(e) so that
 // q . k * sm_scale * log2(e) = qs * (X . k): the digits are those of sign(sm_scale) * q, so the logit scale of a row
 // is never negative (the attention kernel floors it at a tiny positive value).
-__global__ __launch_bounds__(256) void prompt_qsplit_kernel(const float *__restrict__ q, int32_t n_qh, int32_t G,
-                                                            int32_t R, int64_t n_rows, float qscale,
-                                                            int8_t *__restrict__ qd, float *__restrict__ qs)
+__device__ __forceinline__ void prompt_qsplit(const float *__restrict__ q, int32_t n_qh, int32_t G, int32_t R,
+                                              int64_t n_rows, float qscale, int8_t *__restrict__ qd,
+                                              float *__restrict__ qs, uint32_t wg)
 {
     const int lane = threadIdx.x % 64;
-    const int64_t row = (int64_t)blockIdx.x * 4 + threadIdx.x / 64;   // = query * n_qh + head
+    const int64_t row = (int64_t)wg * 4 + threadIdx.x / 64;   // = query * n_qh + head
     if (row >= n_rows) return;                                          // whole waves leave together
     const int32_t qi = (int32_t)(row / n_qh), h = (int32_t)(row % n_qh);
     const int32_t g = h / G, r = qi * G + h % G;
@@ -109,11 +109,10 @@ __global__ __launch_bounds__(256) void prompt_qsplit_kernel(const float *__restr
 // ------------------------------------------------------------------------------------------ V-scale bound
 // Partial maxima of v_scale (both 64-dim groups) over the cells any query of the call can see: each workgroup
 // reduces one of VS_SLICES slices of KV head g's cells; the attention kernel folds the slices.
-__global__ __launch_bounds__(256) void prompt_vsmax_kernel(const float *__restrict__ vs, int32_t cap, int32_t n_cells,
-                                                           float *__restrict__ VSp)
+__device__ __forceinline__ void prompt_vsmax(const float *__restrict__ vs, int32_t cap, int32_t n_cells,
+                                             float *__restrict__ VSp, int32_t g, int32_t sl)
 {
     __shared__ float red[4];
-    const int32_t g = blockIdx.x, sl = blockIdx.y;
     const int32_t per = (n_cells + VS_SLICES - 1) / VS_SLICES;
     const int32_t e0 = 2 * min(n_cells, sl * per), e1 = 2 * min(n_cells, (sl + 1) * per);
     float m = 0.f;
@@ -124,11 +123,27 @@ __global__ __launch_bounds__(256) void prompt_vsmax_kernel(const float *__restri
     if (threadIdx.x == 0) VSp[g * VS_SLICES + sl] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
 }
 
-__device__ __forceinline__ float head_vs(const float *__restrict__ VSp, int32_t g)
+// Both preparation steps in one launch (they are independent): workgroups [0, nqb) split q, the next
+// n_kv * VS_SLICES reduce the v_scale slices.
+__global__ __launch_bounds__(256) void prompt_prep_kernel(const float *__restrict__ q, int32_t n_qh, int32_t G,
+                                                          int32_t R, int64_t n_rows, float qscale,
+                                                          int8_t *__restrict__ qd, float *__restrict__ qs, uint32_t nqb,
+                                                          const float *__restrict__ vs, int32_t cap, int32_t n_cells,
+                                                          float *__restrict__ VSp)
 {
-    float VS = 0.f;
-#pragma unroll 4
-    for (int k = 0; k < VS_SLICES; k++) VS = fmaxf(VS, VSp[g * VS_SLICES + k]);
+    if (blockIdx.x < nqb) {
+        prompt_qsplit(q, n_qh, G, R, n_rows, qscale, qd, qs, blockIdx.x);
+    } else {
+        const uint32_t e = blockIdx.x - nqb;
+        prompt_vsmax(vs, cap, n_cells, VSp, (int32_t)(e / VS_SLICES), (int32_t)(e % VS_SLICES));
+    }
+}
+
+// VS[g] from its VS_SLICES partial maxima, one per lane (lanes past them hold 0): a wave max.
+__device__ __forceinline__ float head_vs(float part)
+{
+    static_assert(VS_SLICES <= 64, "one slice per lane");
+    const float VS = group_max<64>(part);
     return VS > 0.f ? VS : 1.f;
 }
 
@@ -215,21 +230,25 @@ __global__ __launch_bounds__(256, 2) void prompt_attn_kernel(const PromptArgs a)
     const int32_t t0 = (int32_t)(((int64_t)n_tiles * j) / a.S), t1 = (int32_t)(((int64_t)n_tiles * (j + 1)) / a.S);
     const int32_t c_last = c_end - 1;
 
-    // q digits of the workgroup's rows (B operands of S^T) into LDS; rows past R are zero
-    for (int e = tid; e < PROWS * (3 * PD / 16); e += 256) {
-        const int rr = e / (3 * PD / 16), k16 = e % (3 * PD / 16);
-        const int32_t rg = row0 + rr;
-        int4 v = make_int4(0, 0, 0, 0);
-        if (rg < a.R) v = *reinterpret_cast<const int4 *>(a.qd + ((int64_t)g * a.R + rg) * 3 * PD + 16 * k16);
-        *reinterpret_cast<int4 *>(sq + rr * QROW + 16 * k16) = v;
+    // Prologue loads, all issued at once (they land while the first tiles' copies are issued): the q digits of the
+    // workgroup's rows (B operands of S^T, stored to LDS below; rows past R are zero), the row's logit scale and one
+    // partial maximum of v_scale per lane.
+    constexpr int QV = PROWS * (3 * PD / 16) / 256;   // 16-byte q-digit loads per thread
+    static_assert(QV * 256 == PROWS * (3 * PD / 16), "whole loads per thread");
+    // (every load is unconditional, from a clamped index, so none waits behind a branch)
+    int4 qv[QV];
+#pragma unroll
+    for (int u = 0; u < QV; u++) {
+        const int e = tid + 256 * u, rr = e / (3 * PD / 16), k16 = e % (3 * PD / 16);
+        const int32_t rg = min(row0 + rr, a.R - 1);
+        qv[u] = *reinterpret_cast<const int4 *>(a.qd + ((int64_t)g * a.R + rg) * 3 * PD + 16 * k16);
     }
+    const float qs_ld = a.qs[(int64_t)g * a.R + min(r, a.R - 1)];
+    const float vs_ld = a.VSp[g * VS_SLICES + lane % VS_SLICES];
     const int8_t *qrow_lds = sq + (16 * wave + n16) * QROW + 16 * G4;
-
-    // logit scale of the row; a floor keeps -inf * crow = -inf for all-zero q rows (whose logits are all 0)
-    const float crow = fmaxf(row_ok ? a.qs[(int64_t)g * a.R + r] : 0.f, 1e-30f);
-    const float VS = head_vs(a.VSp, g);
-    const float sw = VS / PMAX;     // value of one unit of the p * w digits
-    const float vsc = PMAX / VS;    // w = v_scale * vsc
+    // set in the prologue below: the row's logit scale (a floor keeps -inf * crow = -inf for all-zero q rows, whose
+    // logits are all 0), the value of one unit of the p * w digits, and w = v_scale * vsc
+    float crow = 0.f, sw = 0.f, vsc = 0.f;
 
     v4i acc[4][8];   // PV int32 sums per digit plane (weights 2^24, 2^16, 2^8, 1)
 #pragma unroll
@@ -308,7 +327,8 @@ __global__ __launch_bounds__(256, 2) void prompt_attn_kernel(const PromptArgs a)
                     copy_lds16(vt, c * PD + 16 * (pos ^ swz_v(cell)), lds_addr(T.v + 1024 * (2 * wave + h)));
             }
             if constexpr (VB == 4)
-                copy_lds16(vt, min(16 * wave + (lane >> 2), nfull) * VROW + 16 * (lane & 3), lds_addr(T.v + 2048 * wave));
+                copy_lds16(vt, min(16 * wave + (lane >> 2), nfull) * VROW + 16 * (lane & 3),
+                           lds_addr(T.v + 2048 * wave));
             copy_lds4(st, 4 * (2 * min(se >> 1, nfull) + (se & 1)), lds_addr(sdst));
         }
     };
@@ -316,12 +336,11 @@ __global__ __launch_bounds__(256, 2) void prompt_attn_kernel(const PromptArgs a)
     // waves that copied the v_scale halves turn them into w, and for K8V4 every wave widens its share of the V codes.
     // No branch (the K-scale waves rewrite theirs times 1), so the step's scheduler can interleave it with the
     // exponentials that follow.
-    const float sfac = wave >= 2 ? vsc : 1.f;
     auto finish = [&](int buf) {
         PromptTile &T = tile[buf];
         asm volatile("" ::: "memory");
         float *sc = (wave < 2 ? T.ks : T.vs) + se;
-        *sc = *sc * sfac;
+        *sc = *sc * (wave >= 2 ? vsc : 1.f);
         if constexpr (VB == 4) expand_v4(T.v, wave, lane);
     };
 
@@ -329,6 +348,17 @@ __global__ __launch_bounds__(256, 2) void prompt_attn_kernel(const PromptArgs a)
     // at the start of step t - 2, and each wave waits for its own in the middle of step t - 1 and finishes its share.
     if (t0 < t1) stage(t0, 0);
     if (t0 + 1 < t1) stage(t0 + 1, 1);
+#pragma unroll
+    for (int u = 0; u < QV; u++) {   // (the q loads are older than the copies: they land first)
+        const int e = tid + 256 * u, rr = e / (3 * PD / 16), k16 = e % (3 * PD / 16);
+        *reinterpret_cast<int4 *>(sq + rr * QROW + 16 * k16) = row0 + rr < a.R ? qv[u] : make_int4(0, 0, 0, 0);
+    }
+    crow = fmaxf(row_ok ? qs_ld : 0.f, 1e-30f);
+    {
+        const float VS = head_vs(lane < VS_SLICES ? vs_ld : 0.f);
+        sw = VS / PMAX;
+        vsc = PMAX / VS;
+    }
     if (t0 + 1 < t1) __builtin_amdgcn_s_waitcnt(WAIT_TILE);   // tile t0 has landed
     else __builtin_amdgcn_s_waitcnt(WAIT_VM0_LGKM0);
     if (t0 < t1) finish(0);
@@ -513,12 +543,13 @@ __global__ __launch_bounds__(256, 2) void prompt_attn_kernel(const PromptArgs a)
 }
 
 // ------------------------------------------------------------------------------------------- chunk merge
-// The S <= MAX_S cell chunks of each (query, q head) row folded as the decode merge folds them: M over the non-empty
-// chunks, weights e^(m_j - M) added in chunk order, empty chunks skipped by select (their o may hold anything), a row
-// with none gets zeros. 32 lanes per row with four dims each, 8 rows per 256-thread workgroup, every load of a row
-// issued before the first use: the partials are streamed once, with no cross-lane work.
-constexpr int MAX_S = 4;
+// The S cell chunks of each (query, q head) row folded as the decode merge folds them: M over the non-empty chunks,
+// weights e^(m_j - M) added in chunk order, empty chunks skipped by select (their o may hold anything), a row with
+// none gets zeros. 32 lanes per row with four dims each, 8 rows per 256-thread workgroup, no cross-lane work. Up to
+// NS = 4 chunks every load of a row is issued before the first use; more chunks (small calls) take a loop.
+constexpr int MAX_S = 32;   // cell chunks per row block at most
 
+template <int NS>
 __global__ __launch_bounds__(256) void prompt_merge_kernel(const float *__restrict__ m, const float *__restrict__ l,
                                                            const uint8_t *__restrict__ em, const float *__restrict__ o,
                                                            int32_t S, int64_t rows, float *__restrict__ out)
@@ -526,11 +557,48 @@ __global__ __launch_bounds__(256) void prompt_merge_kernel(const float *__restri
     const int64_t row = (int64_t)blockIdx.x * 8 + threadIdx.x / 32;
     if (row >= rows) return;
     const int dl = threadIdx.x % 32;
-    float4 ov[MAX_S];
-    float mv[MAX_S], lv[MAX_S];
-    bool live[MAX_S];
+    if constexpr (NS == 0) {
+        // lane dl of the row holds chunk dl's (m, l, empty) (S <= MAX_S = 32 lanes): M and the weights in one round
+        // of loads and a 32-lane max; the o rows are then loaded eight chunks at a time, every load unconditional
+        // (an empty chunk's row is read but skipped by select)
+        static_assert(MAX_S <= 32, "one chunk per lane of the row's 32");
+        const bool in = dl < S;
+        const int64_t e0 = row * S;
+        const float mj = in ? m[e0 + dl] : -INFINITY;
+        const float lj = in ? l[e0 + dl] : 0.f;
+        const bool live = in && em[e0 + dl] == 0;
+        const float M = max16(group_max<16>(live ? mj : -INFINITY));   // over the row's 32 lanes
+        const float w = live ? expf(mj - M) : 0.f;
+        const float L = sum16(group_sum<16>(live ? w * lj : 0.f));
+        const int base = threadIdx.x & 32;   // the row's first lane in the wave
+        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int32_t j0 = 0; j0 < S; j0 += 8) {
+            float4 ov[8];
 #pragma unroll
-    for (int j = 0; j < MAX_S; j++) {
+            for (int u = 0; u < 8; u++) {
+                const int32_t jj = j0 + u < S ? j0 + u : S - 1;
+                ov[u] = *reinterpret_cast<const float4 *>(o + (e0 + jj) * PD + 4 * dl);
+            }
+#pragma unroll
+            for (int u = 0; u < 8; u++) {
+                const int src = base + ((j0 + u) & 31);
+                const float wu = __int_as_float(__builtin_amdgcn_ds_bpermute(4 * src, __float_as_int(w)));
+                const bool lu = j0 + u < S && wu > 0.f;
+                acc = lu ? make_float4(fmaf(wu, ov[u].x, acc.x), fmaf(wu, ov[u].y, acc.y), fmaf(wu, ov[u].z, acc.z),
+                                       fmaf(wu, ov[u].w, acc.w))
+                         : acc;
+            }
+        }
+        *reinterpret_cast<float4 *>(out + row * PD + 4 * dl) = M == -INFINITY
+            ? make_float4(0.f, 0.f, 0.f, 0.f) : make_float4(acc.x / L, acc.y / L, acc.z / L, acc.w / L);
+        return;
+    }
+    constexpr int N = NS > 0 ? NS : 1;
+    float4 ov[N];
+    float mv[N], lv[N];
+    bool live[N];
+#pragma unroll
+    for (int j = 0; j < N; j++) {
         if (j < S) {
             const int64_t e = row * S + j;
             ov[j] = *reinterpret_cast<const float4 *>(o + e * PD + 4 * dl);
@@ -545,11 +613,11 @@ __global__ __launch_bounds__(256) void prompt_merge_kernel(const float *__restri
     }
     float M = -INFINITY;
 #pragma unroll
-    for (int j = 0; j < MAX_S; j++) M = live[j] ? fmaxf(M, mv[j]) : M;
+    for (int j = 0; j < N; j++) M = live[j] ? fmaxf(M, mv[j]) : M;
     float L = 0.f;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-    for (int j = 0; j < MAX_S; j++) {
+    for (int j = 0; j < N; j++) {
         if (live[j]) {
             const float w = expf(mv[j] - M);
             L = fmaf(w, lv[j], L);
@@ -562,20 +630,24 @@ __global__ __launch_bounds__(256) void prompt_merge_kernel(const float *__restri
         none ? make_float4(0.f, 0.f, 0.f, 0.f) : make_float4(acc.x / L, acc.y / L, acc.z / L, acc.w / L);
 }
 
-// Cell chunks per row block: enough workgroups to fill the chip in whole rounds of two per CU (at most MAX_S).
-int prompt_chunks(int32_t n_q, const qsa_dims &d)
+// Cell chunks per row block (at most MAX_S): the S that minimises rounds of workgroups (two per CU) times the tiles a
+// workgroup walks, plus two tiles' worth of start-up and store per workgroup, the smaller S on a tie. `last` (pos0 +
+// n_q) stands for the cells the call sees, so the choice and the scratch size depend on the arguments alone. The
+// 2,048-query chunk at a 32K context gets 2 (three full rounds); a handful of queries gets up to 32, so its few
+// row blocks still spread over the chip.
+int prompt_chunks(int32_t n_q, int64_t last, const qsa_dims &d)
 {
     const int64_t R = (int64_t)n_q * (d.n_q_heads / d.n_kv_heads);
     const int64_t wg = d.n_kv_heads * ((R + PROWS - 1) / PROWS);
     if (wg <= 0) return 1;
-    const int64_t slots = 2 * NCU;
+    const int64_t slots = 2 * NCU, tiles = (last + PT - 1) / PT;
     int best = 1;
-    double best_eff = 0.0;
+    int64_t best_cost = INT64_MAX;
     for (int S = 1; S <= MAX_S; S++) {
-        const int64_t n = wg * S;
-        const double eff = (double)n / (double)(((n + slots - 1) / slots) * slots);
-        if (eff > best_eff + 0.05) {
-            best_eff = eff;
+        const int64_t rounds = (wg * S + slots - 1) / slots;
+        const int64_t cost = rounds * ((tiles + S - 1) / S + 2);
+        if (cost < best_cost) {
+            best_cost = cost;
             best = S;
         }
     }
@@ -586,11 +658,11 @@ struct PromptScratch {
     size_t qd, qs, vs, m, l, o, e, total;
 };
 
-PromptScratch prompt_layout(int32_t n_q, const qsa_dims &d)
+PromptScratch prompt_layout(int32_t n_q, int64_t last, const qsa_dims &d)
 {
     auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
     const size_t rows = (size_t)n_q * d.n_q_heads;
-    const int S = prompt_chunks(n_q, d);
+    const int S = prompt_chunks(n_q, last, d);
     PromptScratch s{};
     size_t off = 0;
     s.qd = off; off += al(rows * 3 * PD);
@@ -684,7 +756,7 @@ extern "C" size_t qsa_prompt_scratch_bytes(int32_t n_q, int32_t pos0, qsa_dims d
     if ((int64_t)n_q * dims.n_q_heads > INT32_MAX) return 0;
     const int64_t last = (int64_t)pos0 + n_q;
     // head_dim 128 runs the matrix-core kernel (int8 or K8V4 pools alike), the other head dims the dense chunk path
-    return dims.head_dim == PD ? prompt_layout(n_q, dims).total : dense_layout(n_q, last, dims).total;
+    return dims.head_dim == PD ? prompt_layout(n_q, last, dims).total : dense_layout(n_q, last, dims).total;
 }
 
 extern "C" qsa_status qsa_prompt_attn(const float *q, int32_t n_q, int32_t pos0, const qsa_pool *pool, qsa_dims dims,
@@ -706,13 +778,11 @@ extern "C" qsa_status qsa_prompt_attn(const float *q, int32_t n_q, int32_t pos0,
         return prompt_dense(q, n_q, pos0, pool, dims, sm_scale, out, scratch, scratch_bytes, (hipStream_t)stream);
     const int64_t last = (int64_t)pos0 + n_q;
     const int32_t n_cells = (int32_t)(last < pool->n_valid ? last : pool->n_valid);
-    const PromptScratch lay = prompt_layout(n_q, dims);
-    if (!scratch) return QSA_ERR_NULL;
-    if (scratch_bytes < lay.total) return QSA_ERR_SCRATCH;
+    const PromptScratch lay = prompt_layout(n_q, last, dims);
     const int32_t G = dims.n_q_heads / dims.n_kv_heads;
     const int64_t R = (int64_t)n_q * G;
     if (R > (int64_t)1 << 30) return QSA_ERR_UNSUPPORTED;
-    const int S = prompt_chunks(n_q, dims);
+    const int S = prompt_chunks(n_q, last, dims);
     char *base = static_cast<char *>(scratch);
     hipStream_t s = (hipStream_t)stream;
 
@@ -720,9 +790,10 @@ extern "C" qsa_status qsa_prompt_attn(const float *q, int32_t n_q, int32_t pos0,
     float *qs = reinterpret_cast<float *>(base + lay.qs);
     float *VSp = reinterpret_cast<float *>(base + lay.vs);
     const int64_t n_rows = (int64_t)n_q * dims.n_q_heads;
-    prompt_qsplit_kernel<<<dim3((uint32_t)((n_rows + 3) / 4)), 256, 0, s>>>(q, dims.n_q_heads, G, (int32_t)R, n_rows,
-                                                                             sm_scale * PLOG2E, qd, qs);
-    prompt_vsmax_kernel<<<dim3(dims.n_kv_heads, VS_SLICES), 256, 0, s>>>(pool->v_scale, pool->capacity, n_cells, VSp);
+    const uint32_t nqb = (uint32_t)((n_rows + 3) / 4);
+    prompt_prep_kernel<<<dim3(nqb + (uint32_t)dims.n_kv_heads * VS_SLICES), 256, 0, s>>>(
+        q, dims.n_q_heads, G, (int32_t)R, n_rows, sm_scale * PLOG2E, qd, qs, nqb, pool->v_scale, pool->capacity,
+        n_cells, VSp);
 
     PromptArgs a{};
     a.qd = qd; a.qs = qs; a.VSp = VSp;
@@ -741,8 +812,9 @@ extern "C" qsa_status qsa_prompt_attn(const float *q, int32_t n_q, int32_t pos0,
     if ((st = launch_status()) != QSA_OK) return st;
     if (S > 1) {
         const int64_t rows = (int64_t)n_q * dims.n_q_heads;
-        prompt_merge_kernel<<<dim3((uint32_t)((rows + 7) / 8)), 256, 0, s>>>(a.m_out, a.l_out, a.e_out, a.o_out, S,
-                                                                             rows, out);
+        const dim3 mgrid((uint32_t)((rows + 7) / 8));
+        if (S <= 4) prompt_merge_kernel<4><<<mgrid, 256, 0, s>>>(a.m_out, a.l_out, a.e_out, a.o_out, S, rows, out);
+        else prompt_merge_kernel<0><<<mgrid, 256, 0, s>>>(a.m_out, a.l_out, a.e_out, a.o_out, S, rows, out);
         return launch_status();
     }
     return QSA_OK;

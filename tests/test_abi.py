@@ -173,7 +173,8 @@ def test_prompt_scratch_sizing_and_checks():
     n = L.qsa_prompt_scratch_bytes(2048, 30720, GOOD)
     assert n >= 2048 * 24 * (3 * 128 + 4)          # q digits and row scales at least
     assert n >= 2048 * 24 * 2 * (128 * 4 + 9)      # and two cell chunks' (m, l, empty, o) partials per row
-    assert n == L.qsa_prompt_scratch_bytes(2048, 0, GOOD)   # nothing per pool cell (v_scale is scaled in LDS)
+    # a handful of queries is split into many more cell chunks, so its few row blocks spread over the chip
+    assert L.qsa_prompt_scratch_bytes(16, 4096, GOOD) >= 16 * 24 * 16 * (128 * 4 + 9)
     assert L.qsa_prompt_scratch_bytes(0, 0, GOOD) == 0
     assert L.qsa_prompt_scratch_bytes(16, -1, GOOD) == 0
     assert L.qsa_prompt_scratch_bytes(2**27, 0, GOOD) == 0     # more (query, head) rows than an int32 holds
