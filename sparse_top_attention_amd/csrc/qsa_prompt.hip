@@ -429,7 +429,10 @@ __global__ __launch_bounds__(256, 2) void prompt_attn_kernel(const PromptArgs a)
         const bool force = ((t - t0) % FOLD_EVERY) == FOLD_EVERY - 1;   // wave-uniform
         if (__any(need) || force) {
             const float mnew = need ? rm + PDELTA : mref;
-            if ((need || force) && row_ok) {   // both sums are relative to the old reference
+            // a row whose reference is still -inf has summed nothing (every p was 0): it only takes the reference
+            const bool fold_row = (need || force) && row_ok;
+            const bool store = fold_row && mref != -INFINITY;
+            if (store) {   // both sums are relative to the old reference
                 const float alpha = need ? __builtin_amdgcn_exp2f(mref - mnew) : 1.f;
                 float4 o[8];
                 fold(alpha, o);
@@ -437,9 +440,10 @@ __global__ __launch_bounds__(256, 2) void prompt_attn_kernel(const PromptArgs a)
                 for (int db = 0; db < 8; db++) *reinterpret_cast<float4 *>(orow + 16 * db) = o[db];
                 have_o = true;
                 lsum *= alpha;
-                mref = mnew;
             }
-            __builtin_amdgcn_s_waitcnt(WAIT_VM0_LGKM0);   // the fold's stores are not left behind the tile copies
+            if (fold_row) mref = mnew;
+            // the fold's stores are not left behind the tile copies
+            if (__any(store)) __builtin_amdgcn_s_waitcnt(WAIT_VM0_LGKM0);
         }
         const float mexp = mref == -INFINITY ? 0.f : mref;
 
