@@ -81,6 +81,24 @@ def test_prompt_edge_cases(v_bits):
         assert rel_err_rows(got, ref).max() <= TOL, (n_q, pos0, scale)
 
 
+@pytest.mark.parametrize("v_bits", [8, 4], ids=["int8", "k8v4"])
+def test_prompt_rising_logits_fold_many_times(v_bits):
+    """Key scales ramping 12x along the context make each row's max keep rising, so the int32 sums are folded into
+    the stored output again and again (5 to 10 times per row: each time the max passes the reference), with
+    rescales between folds. The logits stay within about +-80 (log2 units), where fp32 logits still meet the bar."""
+    n_kv, G, n_q, pos0, n_valid = 2, 6, 64, 1500, 1564
+    pool = synth.random_pool(361 + v_bits, n_kv, n_valid, n_valid, 128, v_bits=v_bits)
+    ramp = np.linspace(1.0, 12.0, n_valid, dtype=np.float32)[None, :, None]
+    pool.ks[:] = pool.ks * ramp
+    q = synth.random_q(362, n_q, n_kv * G, 128)
+    dims = qsa.Dims(n_kv * G, n_kv, 128)
+    got = run_prompt(q, pos0, to_device(pool), dims)
+    pos = (pos0 + np.arange(n_q)).astype(np.int32)
+    ref, _ = oracle.attn(q, pos, pool, n_kv)
+    assert np.all(np.isfinite(got))
+    assert rel_err_rows(got, ref).max() <= TOL
+
+
 def test_prompt_sm_scale_and_zero_query():
     pool = synth.random_pool(311, 2, 300, 260, 128)
     q = synth.random_q(312, 20, 12, 128)
