@@ -123,20 +123,18 @@ __device__ __forceinline__ void prompt_vsmax(const float *__restrict__ vs, int32
     if (threadIdx.x == 0) VSp[g * VS_SLICES + sl] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
 }
 
-// Both preparation steps in one launch (they are independent): workgroups [0, nqb) split q, the next
-// n_kv * VS_SLICES reduce the v_scale slices.
+// Both preparation steps in one launch (they are independent): the first nvb = n_kv * VS_SLICES workgroups reduce
+// the v_scale slices (dispatched first, so they run beside the q split rather than after it), the rest split q.
 __global__ __launch_bounds__(256) void prompt_prep_kernel(const float *__restrict__ q, int32_t n_qh, int32_t G,
                                                           int32_t R, int64_t n_rows, float qscale,
-                                                          int8_t *__restrict__ qd, float *__restrict__ qs, uint32_t nqb,
+                                                          int8_t *__restrict__ qd, float *__restrict__ qs, uint32_t nvb,
                                                           const float *__restrict__ vs, int32_t cap, int32_t n_cells,
                                                           float *__restrict__ VSp)
 {
-    if (blockIdx.x < nqb) {
-        prompt_qsplit(q, n_qh, G, R, n_rows, qscale, qd, qs, blockIdx.x);
-    } else {
-        const uint32_t e = blockIdx.x - nqb;
-        prompt_vsmax(vs, cap, n_cells, VSp, (int32_t)(e / VS_SLICES), (int32_t)(e % VS_SLICES));
-    }
+    if (blockIdx.x < nvb)
+        prompt_vsmax(vs, cap, n_cells, VSp, (int32_t)(blockIdx.x / VS_SLICES), (int32_t)(blockIdx.x % VS_SLICES));
+    else
+        prompt_qsplit(q, n_qh, G, R, n_rows, qscale, qd, qs, blockIdx.x - nvb);
 }
 
 // VS[g] from its VS_SLICES partial maxima, one per lane (lanes past them hold 0): a wave max.
@@ -794,9 +792,9 @@ extern "C" qsa_status qsa_prompt_attn(const float *q, int32_t n_q, int32_t pos0,
     float *qs = reinterpret_cast<float *>(base + lay.qs);
     float *VSp = reinterpret_cast<float *>(base + lay.vs);
     const int64_t n_rows = (int64_t)n_q * dims.n_q_heads;
-    const uint32_t nqb = (uint32_t)((n_rows + 3) / 4);
-    prompt_prep_kernel<<<dim3(nqb + (uint32_t)dims.n_kv_heads * VS_SLICES), 256, 0, s>>>(
-        q, dims.n_q_heads, G, (int32_t)R, n_rows, sm_scale * PLOG2E, qd, qs, nqb, pool->v_scale, pool->capacity,
+    const uint32_t nvb = (uint32_t)dims.n_kv_heads * VS_SLICES;
+    prompt_prep_kernel<<<dim3(nvb + (uint32_t)((n_rows + 3) / 4)), 256, 0, s>>>(
+        q, dims.n_q_heads, G, (int32_t)R, n_rows, sm_scale * PLOG2E, qd, qs, nvb, pool->v_scale, pool->capacity,
         n_cells, VSp);
 
     PromptArgs a{};
