@@ -50,6 +50,8 @@ def parse():
                     help="only run a plain device copy of known size (to scale HBM byte counters)")
     ap.add_argument("--copies", type=int, default=64, help="pool copies the steps rotate over")
     ap.add_argument("--chunks", type=int, default=0, help="split count (0 = the library default for the shape)")
+    ap.add_argument("--pages-shapes", action="store_true",
+                    help="time the shapes of the pages' own kernel tables and print them beside the pages' figures")
     ap.add_argument("--scale", action="store_true",
                     help="only measure the chunk kernel on 1, 2, 4 and 8 verify-window slots in one launch")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -138,6 +140,10 @@ def main():
         for line in bench_scale():
             print(json.dumps(line), flush=True)
         return
+    if args.pages_shapes:
+        for line in bench_pages_shapes(args):
+            print(json.dumps(line), flush=True)
+        return
     if args.workload == "prompt_chunk":
         res = bench_prompt(args, args.steps if args.steps != 1280 else args.prompt_steps, main_line=True,
                            v_bits=args.v_bits)
@@ -145,6 +151,7 @@ def main():
         res = bench_decode(args)
         if args.workload == "verify_window" and not args.no_other:
             res["other_decode_workloads"] = bench_other_decode()
+            res["pages_shapes"] = bench_pages_shapes(args)
         if not args.no_prompt:
             res["prompt_chunk"] = bench_prompt(args, args.prompt_steps, main_line=False)
             res["prompt_chunk_k8v4"] = bench_prompt(args, args.prompt_steps, main_line=False, v_bits=4, cpu=False)
@@ -615,6 +622,125 @@ def bench_scale(slot_counts=(1, 2, 4, 8), chunk_counts=(4, 16)):
     return out
 
 
+# The pages' own kernel tables, as context beside this library's time on the same shapes (other hardware, other
+# engines; not targets): "#2806 sycl: decode QSA selection and attention in fewer, shorter launches", Summary
+# (kernel table: one Arc Pro B70, 24 q heads, int8 K/V, 200,000-cell capacity, graph replay, us at 1K / 16K / 64K of
+# context, the optimised column), and "#1367 prompt attention: STRATA_PROMPT_ATTN_IMMA=1 - the int8-KV kernel on
+# INT8 tensor cores", Measured (per launch on an RTX 5090, the int8 kernel's column).
+PAGES_LAYER_US = {(1, 1024): 62.3, (1, 16384): 107.9, (1, 65536): 156.2,
+                  (2, 1024): 78.3, (2, 16384): 138.2, (2, 65536): 205.0}   # (rows per slot, context): us per layer
+PAGES_DRAFTER_US = {1024: 41.0, 16384: 157.2, 65536: 335.9}                # one row, 32K window: us per call
+PAGES_PROMPT_MS = {(32768, 2048): 1.55, (1500, 1500): 0.40, (2100, 256): 0.26}   # (context, queries): ms per launch
+
+
+def _graph_avg_us(stream, fn, n, reps=10):
+    """Mean us per call of fn(0) .. fn(n - 1), captured once in a HIP graph on `stream` and replayed reps times."""
+    import torch
+    with torch.cuda.stream(stream):
+        for c in range(n):
+            fn(c)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for c in range(n):
+            fn(c)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        g.replay()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            g.replay()
+        b.record(stream)
+        torch.cuda.synchronize()
+    return a.elapsed_time(b) * 1e3 / (reps * n)
+
+
+def bench_pages_shapes(args, copies=16):
+    """This library on the shapes of the pages' kernel tables (readings where the pages leave a size open: 4 KV
+    heads, head_dim 128, top-64 blocks (all 16 at 1K, where the pages select every cell), 32 chunks per row (16 at
+    1K); the drafter's 32K window holds min(context,
+    32,768) valid cells in 512 chunks of 64 with an active-only merge; the prompt's queries are the last rows of
+    their context). One JSON line per shape with the pages' figure and hardware beside it."""
+    import torch
+
+    import sparse_top_attention_amd as qsa
+    import synth
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.Stream()
+
+    def t(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    def dev_pool(pn, dims, with_index):
+        p = qsa.Pool(t(pn.k), t(pn.ks), t(pn.v), t(pn.vs), pn.n_valid)
+        if with_index:
+            p.index = torch.zeros(dims.n_kv_heads, -(-pn.capacity // BLOCK), dims.head_dim, dtype=torch.float32,
+                                  device=dev)
+            qsa.qsa_block_index(p, dims, 0, pn.n_valid, p.index)
+        return p
+
+    def clone(p):
+        return qsa.Pool(p.k.clone(), p.k_scale.clone(), p.v.clone(), p.v_scale.clone(), p.n_valid,
+                        None if p.index is None else p.index.clone())
+
+    lines = []
+    for rows in (1, 2):
+        for ctx in (1024, 16384, 65536):
+            w = synth.workload("batch_window", poison=False, rows=rows, n_valid=ctx, topk=min(64, -(-ctx // BLOCK)))
+            dims = qsa.Dims(w.n_q_heads, w.n_kv_heads, w.head_dim)
+            base = [dev_pool(pn, dims, True) for pn in w.pools]
+            sets = [base] + [[clone(p) for p in base] for _ in range(copies - 1)]
+            n_rows, nb, S = w.q.shape[0], -(-ctx // BLOCK), 16 if ctx <= 1024 else 32
+            q, pos, rp = t(w.q), t(w.pos), t(w.row_pool)
+            ids = torch.empty(n_rows, w.n_kv_heads, w.topk, dtype=torch.int32, device=dev)
+            counts = torch.empty(n_rows, w.n_kv_heads, dtype=torch.int32, device=dev)
+            out = torch.empty(n_rows, w.n_q_heads, w.head_dim, dtype=torch.float32, device=dev)
+            lse = torch.empty(n_rows, w.n_q_heads, dtype=torch.float32, device=dev)
+            scratch = torch.empty(qsa.qsa_decode_layer_scratch_bytes(n_rows, dims, nb, w.topk, S), dtype=torch.uint8,
+                                  device=dev)
+
+            def layer(c):
+                qsa.qsa_decode_layer(q, pos, sets[c], dims, nb, w.topk, S, out, lse, sm_scale=w.sm_scale,
+                                     row_pool=rp, ids=ids, counts=counts, scratch=scratch)
+            us = _graph_avg_us(stream, layer, copies)
+            lines.append({"shape": f"selection + attention per layer, 2 slots x {rows} row(s), {ctx} valid cells",
+                          "us": round(us, 2), "pages_us": PAGES_LAYER_US[(rows, ctx)], "pages_hw": "Arc Pro B70",
+                          "q_heads": w.n_q_heads, "kv_heads": w.n_kv_heads, "topk": w.topk, "chunks": S})
+            del sets, base
+            torch.cuda.empty_cache()
+    for ctx in (1024, 16384, 65536):
+        n_valid = min(ctx, 32768)
+        w = synth.workload("drafter", poison=False, n_valid=n_valid, n_active=-(-n_valid // BLOCK))
+        dims = qsa.Dims(w.n_q_heads, w.n_kv_heads, w.head_dim)
+        base = dev_pool(w.pools[0], dims, False)
+        pools = [base] + [clone(base) for _ in range(copies - 1)]
+        q, pos = t(w.q), t(w.pos)
+        part = qsa.Partials.empty_like_shape(1, w.n_q_heads, w.n_chunks, w.head_dim, device=dev)
+        out = torch.empty(1, w.n_q_heads, w.head_dim, dtype=torch.float32, device=dev)
+        lse = torch.empty(1, w.n_q_heads, dtype=torch.float32, device=dev)
+        n_active = t(np.array([w.n_active], np.int32))
+
+        def drafter(c):
+            qsa.qsa_attn_chunk(q, pos, [pools[c]], dims, part, w.n_chunks, w.sm_scale,
+                               blocks_per_chunk=w.blocks_per_chunk)
+            qsa.qsa_attn_merge(part, dims, w.n_chunks, out, lse, n_active=n_active)
+        us = _graph_avg_us(stream, drafter, copies)
+        lines.append({"shape": f"drafter call, one row, 32K window, {ctx} of context ({n_valid} valid cells, "
+                               f"{w.n_active} active chunks)", "us": round(us, 2), "pages_us": PAGES_DRAFTER_US[ctx],
+                      "pages_hw": "Arc Pro B70"})
+        del pools, base
+        torch.cuda.empty_cache()
+    for (ctx, n_q), ms in PAGES_PROMPT_MS.items():
+        r = bench_prompt(args, 16, main_line=False, cpu=False, shape=dict(n_valid=ctx, cap=ctx, rows=n_q))
+        lines.append({"shape": f"prompt chunk, {n_q} queries at the end of a {ctx}-cell context",
+                      "ms": r["ms_per_call"], "pages_ms": ms, "pages_hw": "RTX 5090",
+                      "useful_int8_frac": r["roofline"]["frac"]})
+    return lines
+
+
 def copy_calibration(nbytes=1 << 28, reps=4):
     """A plain device-to-device copy of nbytes, reps times: a profiler's byte counters for these dispatches, divided
     by nbytes read and nbytes written, give the factor that turns counter readings into bytes."""
@@ -651,17 +777,17 @@ def prompt_ops(w):
     return {"useful": pairs * w.head_dim * 4, "planes": pairs * w.head_dim * 12, "issued": issued}, vis
 
 
-def bench_prompt(args, steps, main_line, v_bits=8, cpu=True):
+def bench_prompt(args, steps, main_line, v_bits=8, cpu=True, shape=None):
     """The 2,048-query prompt chunk at the end of a 32,768-cell context: one qsa_prompt_attn call per step, replayed
     from a HIP graph over pool copies (K/V and q are resident in HBM). v_bits 4 times a K8V4 pool of the same
-    shape (same q and K draws, 4-bit V codes)."""
+    shape (same q and K draws, 4-bit V codes); `shape` overrides the workload's sizes (n_valid, cap, rows)."""
     import torch
 
     import sparse_top_attention_amd as qsa
     import synth
 
     dev = torch.device("cuda:0")
-    w = synth.workload("prompt_chunk", poison=False, v_bits=v_bits)
+    w = synth.workload("prompt_chunk", poison=False, v_bits=v_bits, **(shape or {}))
     pool_np = w.pools[0]
     dims = qsa.Dims(w.n_q_heads, w.n_kv_heads, w.head_dim)
     n_q = w.q.shape[0]
