@@ -407,6 +407,9 @@ __device__ __forceinline__ void attn_chunk_body(const ChunkArgs &a)
                 load_lds16(vp + (c * RB + 16 * (pch ^ mswz(cell))), lds_addr(svw + 1024 * q));
             }
             __builtin_amdgcn_sched_barrier(0);   // every copy is in flight before the logits start
+            // the piece's matrix-core section runs at raised wave priority (its MFMAs issue ahead of the other waves'
+            // VALU work on the SIMD)
+            __builtin_amdgcn_s_setprio(1);
             if (!qready) {
                 make_qb();
                 qready = true;
@@ -533,6 +536,7 @@ __device__ __forceinline__ void attn_chunk_body(const ChunkArgs &a)
                     oacc[t1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo[t1 / (NTL / NG)], bv1, oacc[t1], 0, 0, 0);
                 }
             }
+            __builtin_amdgcn_s_setprio(0);
         } else {
             // ---- loads: K slices and scales into registers, the V piece into LDS
             int4 kw[STEPS];
