@@ -223,7 +223,8 @@ __global__ __launch_bounds__(256, 2) void prompt_attn_kernel(const PromptArgs a)
 
     // cells the workgroup's last row can see, cut into S chunks of whole tiles
     const int32_t rlast = min(row0 + PROWS - 1, a.R - 1);
-    const int32_t c_end = min(P.n_valid, a.pos0 + rlast / a.G + 1);
+    // (64-bit: the last query may sit at position INT32_MAX)
+    const int32_t c_end = (int32_t)min((int64_t)P.n_valid, (int64_t)a.pos0 + rlast / a.G + 1);
     const int32_t n_tiles = c_end > 0 ? (c_end + PT - 1) / PT : 0;
     const int32_t t0 = (int32_t)(((int64_t)n_tiles * j) / a.S), t1 = (int32_t)(((int64_t)n_tiles * (j + 1)) / a.S);
     const int32_t c_last = c_end - 1;

@@ -73,7 +73,8 @@ def test_prompt_edge_cases(v_bits):
     assert np.all(got == 0.0)
     pool = synth.random_pool(353, 2, 900, 700, 128, v_bits=v_bits)
     p = to_device(pool)
-    for n_q, pos0, scale in [(1, 0, 1.0), (1, 699, 1.0), (1, 5000, 0.8), (70, 600, -0.6)]:
+    for n_q, pos0, scale in [(1, 0, 1.0), (1, 699, 1.0), (1, 5000, 0.8), (70, 600, -0.6),
+                             (3, 2**31 - 3, 1.0)]:   # the last query at position INT32_MAX sees every valid cell
         q = synth.random_q(354 + n_q + pos0, n_q, 12, 128)
         got = run_prompt(q, pos0, p, dims, sm_scale=scale)
         pos = (pos0 + np.arange(n_q)).astype(np.int32)
