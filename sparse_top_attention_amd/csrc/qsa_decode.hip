@@ -29,13 +29,13 @@ __device__ __forceinline__ void block_mean(const int8_t *__restrict__ k, const f
 {
     constexpr int LPC = D / 16, CPS = 64 / LPC, STEPS = QSA_BLOCK / CPS, NG = D / QSA_GROUP;
     const int lane = threadIdx.x % 64, r = lane / LPC, s = lane % LPC, grp = (16 * s) / QSA_GROUP;
-    const int32_t c0 = b * QSA_BLOCK;
+    const int64_t c0 = (int64_t)b * QSA_BLOCK;   // 64-bit: a capacity near INT32_MAX
     float acc[16];
 #pragma unroll
     for (int e = 0; e < 16; e++) acc[e] = 0.f;
 #pragma unroll
     for (int st = 0; st < STEPS; st++) {
-        const int32_t c = c0 + st * CPS + r;
+        const int64_t c = c0 + st * CPS + r;
         if (c < n_valid) {
             const int64_t cell = (int64_t)g * cap + c;
             const int4 w = *reinterpret_cast<const int4 *>(k + cell * D + 16 * s);
@@ -48,8 +48,8 @@ __device__ __forceinline__ void block_mean(const int8_t *__restrict__ k, const f
     }
 #pragma unroll
     for (int e = 0; e < 16; e++) acc[e] = strided_sum<LPC>(acc[e]);
-    int32_t nb = n_valid - c0;
-    nb = nb < 0 ? 0 : (nb > QSA_BLOCK ? QSA_BLOCK : nb);
+    const int64_t left = n_valid - c0;
+    const int32_t nb = left < 0 ? 0 : (left > QSA_BLOCK ? QSA_BLOCK : (int32_t)left);
     const float inv = nb > 0 ? 1.0f / (float)nb : 0.f;
     if (r == 0) {
         float4 *dst = reinterpret_cast<float4 *>(index + ((int64_t)g * blk_stride + b) * D + 16 * s);
@@ -139,7 +139,7 @@ __global__ __launch_bounds__(64) void append_index_kernel(const AppendArgs a)
     PoolArg P;
     int32_t c;
     if (!append_row(a, i, P, c) || !P.index) return;
-    block_mean<D>(P.k, P.ks, P.capacity, P.n_valid, g, c / QSA_BLOCK, (P.capacity + QSA_BLOCK - 1) / QSA_BLOCK,
+    block_mean<D>(P.k, P.ks, P.capacity, P.n_valid, g, c / QSA_BLOCK, ceil_div(P.capacity, QSA_BLOCK),
                   const_cast<float *>(P.index));
 }
 
@@ -249,7 +249,7 @@ __global__ __launch_bounds__(64) void select_scores_kernel(const SelectArgs a)
     }
     const bool bad = rp < 0 || rp >= a.n_pools;
     const PoolArg P = a.pools[bad ? 0 : rp];
-    const int32_t stride = (P.capacity + QSA_BLOCK - 1) / QSA_BLOCK;
+    const int32_t stride = ceil_div(P.capacity, QSA_BLOCK);
     const int32_t n_live = bad ? 0 : min(a.width, (int32_t)(((int64_t)P.n_valid + QSA_BLOCK - 1) / QSA_BLOCK));
     float rv[NSTEP][8];
 #pragma unroll

@@ -60,7 +60,8 @@ inline int common_v_bits(const qsa_pool *pools, int32_t n_pools, int32_t head_di
     return vb;
 }
 
-inline int32_t ceil_div(int32_t a, int32_t b) { return (a + b - 1) / b; }
+// ceil(a / b) for a >= 0, b > 0, in 64 bits so that counts near INT32_MAX do not wrap.
+__host__ __device__ inline int32_t ceil_div(int32_t a, int32_t b) { return (int32_t)(((int64_t)a + b - 1) / b); }
 
 inline qsa_status launch_status()
 {

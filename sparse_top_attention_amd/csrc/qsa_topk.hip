@@ -64,11 +64,11 @@ __global__ __launch_bounds__(64 * NW) void select_kernel(const SelectArgs a)
         if (pool_ok && pidx != 0) P = a.pools[pidx];
     }
     const int32_t n_valid = pool_ok ? P.n_valid : 0;
-    const int32_t stride = (P.capacity + QSA_BLOCK - 1) / QSA_BLOCK;
+    const int32_t stride = ceil_div(P.capacity, QSA_BLOCK);
 
     const int rb = lane / LPB, s = lane % LPB;
     const float *idx_g = P.index + (int64_t)g * stride * D + 8 * s;
-    const int32_t n_live = min(a.width, (int32_t)((n_valid + QSA_BLOCK - 1) / QSA_BLOCK));
+    const int32_t n_live = min(a.width, ceil_div(n_valid, QSA_BLOCK));
     // batches of NST steps of SB blocks each. Loads are unconditional (a dead block reads block 0 and is zeroed
     // afterwards) so a whole batch is in flight before the first wait.
     constexpr int NST = 16;
