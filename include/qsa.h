@@ -113,7 +113,8 @@ qsa_status qsa_block_index(const qsa_pool *pool, qsa_dims dims, int32_t cell_beg
  * every pool with a non-NULL index, the index row of each block that received a cell is recomputed as
  * qsa_block_index does (after all rows are written, so rows may share a block). The pools' n_valid must already
  * count the new cells: a row whose cell is outside [0, n_valid) or whose device-side row_pool value is out of
- * range writes nothing. Two launches. */
+ * range writes nothing. Rows must name distinct (pool, cell) pairs: two rows naming the same one race and may
+ * leave a mix of both encodings. Two launches. */
 qsa_status qsa_kv_append(const qsa_pool *pools, int32_t n_pools, const int32_t *row_pool, qsa_dims dims,
                          const float *k_new, const float *v_new, const int32_t *cells, int32_t n_rows,
                          qsa_stream_t stream);
