@@ -24,7 +24,7 @@
  *   - sm_scale (the calls that take one) may be any finite value; inf or NaN returns QSA_ERR_RANGE.
  *   - Values that live in device memory (positions, ids, counts, pool indices) cannot be checked on the host;
  *     the kernels treat out-of-range values as "no cell" and never read outside the pool (documented per call).
- *   - Supported shapes: head_dim in {64, 128, 256}; block_cells == 64; n_q_heads a multiple of n_kv_heads with
+ *   - Supported shapes: head_dim in {64, 128, 192, 256}; block_cells == 64; n_q_heads a multiple of n_kv_heads with
  *     at most 8 q heads per KV head; at most 65,535 KV heads (a launch grid dimension). Anything else returns
  *     QSA_ERR_UNSUPPORTED.
  *
@@ -60,7 +60,7 @@ typedef void *qsa_stream_t; /* hipStream_t */
 typedef struct {
     int32_t n_q_heads;
     int32_t n_kv_heads;
-    int32_t head_dim;    /* 64, 128 or 256 */
+    int32_t head_dim;    /* 64, 128, 192 or 256 */
     int32_t block_cells; /* must be 64 */
 } qsa_dims;
 
@@ -69,8 +69,8 @@ typedef struct {
  * int8 (#1888, "What changed": formats left alone; #2075, "Bit for bit": parity cases per KV format) without its
  * layout -- V codes are signed 4-bit integers (-7..7), two per byte (dim 2j in the low nibble, 2j + 1 in the high
  * one), v is [n_kv_heads][capacity][head_dim / 2] bytes, and v_scale is as for int8. K8V4 is supported by the decode
- * calls and the prompt call at head_dim 128 and 256 (QSA_ERR_UNSUPPORTED otherwise); the pools of one call must share
- * a format. */
+ * calls and the prompt call at head_dim 128, 192 and 256 (QSA_ERR_UNSUPPORTED at 64); the pools of one call must
+ * share a format. */
 typedef struct {
     const int8_t *k;
     const float *k_scale;
@@ -175,11 +175,11 @@ size_t qsa_prompt_scratch_bytes(int32_t n_q, int32_t pos0, qsa_dims dims);
  * positions pos0 .. pos0 + n_q - 1 over the pool's cells c <= pos (and c < n_valid). With head_dim 128 both
  * products run on the int8 K/V codes as stored (K8V4 pools: the 4-bit V codes widened to int8 in LDS); q (scaled per
  * query and head) is split into three exact 8-bit parts and the probabilities times v_scale (scaled per KV head)
- * into four, so every int32 sum is exact. Head_dim 64 and 256 (int8, and K8V4 at 256) give the same attention
- * through the chunk attention kernel in dense mode and the merge, 64 queries at a time (much slower: each query
- * reads its own cells). out [n_q][n_q_heads][head_dim]; sm_scale multiplies q . k. Requires pos0 >= 0 and
- * pos0 + n_q - 1 <= INT32_MAX (QSA_ERR_RANGE), a supported head_dim and V format (QSA_ERR_UNSUPPORTED: head_dim 192,
- * K8V4 at head_dim 64), n_q * n_q_heads <= INT32_MAX (QSA_ERR_UNSUPPORTED) and
+ * into four, so every int32 sum is exact. Head_dim 64, 192 and 256 (int8, and K8V4 at 192 and 256) give the same
+ * attention through the chunk attention kernel in dense mode and the merge, 64 queries at a time (much slower: each
+ * query reads its own cells). out [n_q][n_q_heads][head_dim]; sm_scale multiplies q . k. Requires pos0 >= 0 and
+ * pos0 + n_q - 1 <= INT32_MAX (QSA_ERR_RANGE), a supported head_dim and V format (QSA_ERR_UNSUPPORTED: K8V4 at
+ * head_dim 64), n_q * n_q_heads <= INT32_MAX (QSA_ERR_UNSUPPORTED) and
  * scratch_bytes >= qsa_prompt_scratch_bytes (QSA_ERR_SCRATCH). */
 qsa_status qsa_prompt_attn(const float *q, int32_t n_q, int32_t pos0, const qsa_pool *pool, qsa_dims dims,
                            float sm_scale, float *out, void *scratch, size_t scratch_bytes, qsa_stream_t stream);

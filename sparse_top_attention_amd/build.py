@@ -11,7 +11,8 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libqsa.so")
 SOURCES = ["qsa_decode.hip", "qsa_topk.hip", "qsa_prompt.hip", "qsa_chunk_d64_v8.hip", "qsa_chunk_d128_v8.hip",
-           "qsa_chunk_d128_v4.hip", "qsa_chunk_d256_v8.hip", "qsa_chunk_d256_v4.hip"]
+           "qsa_chunk_d128_v4.hip", "qsa_chunk_d192_v8.hip", "qsa_chunk_d192_v4.hip", "qsa_chunk_d256_v8.hip",
+           "qsa_chunk_d256_v4.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # Packed-FP32 VALU ops are switched off on purpose (-packed-fp32-ops): the kernels use scalar fp32 FMAs only.

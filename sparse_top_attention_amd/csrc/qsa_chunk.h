@@ -162,20 +162,25 @@ template <int D, int G, int VB, int WPC, bool FZ>
 __device__ __forceinline__ void attn_chunk_body(const ChunkArgs &a)
 {
     static_assert(VB == 8 || (VB == 4 && D >= 128), "K8V4 needs head_dim >= 128");
+    // DL: the lane layout's dims (head_dim 192 runs on 256's; its lanes past dim 191 hold zeros and store nothing)
+    constexpr int DL = lane_dims<D>();
     constexpr int PC = D <= 128 ? 32 : 16;           // cells per piece
-    constexpr int LPC = D / 16, CPS = 64 / LPC, STEPS = PC / CPS, NG = D / QSA_GROUP;
-    constexpr int DPL = D / 64;                      // output dims per lane
-    constexpr int RB = D * VB / 8;                   // V bytes per cell row
+    constexpr int LPC = DL / 16, CPS = 64 / LPC, STEPS = PC / CPS, NG = DL / QSA_GROUP;
+    constexpr int NGM = D / QSA_GROUP;               // scale groups stored per cell
+    constexpr int DPL = DL / 64;                     // output dims per lane
+    constexpr int RB = D * VB / 8;                   // V bytes per cell row in the pool
+    constexpr int RBL = DL * VB / 8;                 // V bytes per cell row in LDS
     constexpr int NPB = 8 / VB;                      // V codes per byte
     constexpr int NT = DPL / NPB;                    // transposing reads per lane per 8 cells
     constexpr int DPC = 16 * NPB;                    // dims per 16-byte chunk
     constexpr int CPG = QSA_GROUP / DPC;             // 16-byte chunks per scale group
     constexpr int SUBS = 4 / NG;                     // 16-lane subgroups per scale group in the p . v layout
-    constexpr int CHUNKS = RB / 16;                  // 16-byte chunks per V row
+    constexpr int CHUNKS = RBL / 16;                 // 16-byte chunks per V row in LDS
+    constexpr int MCH = RB / 16;                     // the pool row's chunks (the rest of an LDS row is not read)
     constexpr int SWZ = (CHUNKS < 8 ? CHUNKS : 8) - 1;
-    constexpr int VCH = PC * RB / 1024;              // 1 KB global -> LDS copies per piece
+    constexpr int VCH = PC * RBL / 1024;             // 1 KB global -> LDS copies per piece
     constexpr int GP = (G + 3) & ~3;                 // p * v_scale row padded to float4s
-    static_assert(CPG == SUBS * NT && VCH * 1024 == PC * RB, "p . v lane layout");
+    static_assert(CPG == SUBS * NT && VCH * 1024 == PC * RBL, "p . v lane layout");
     // Both products on the matrix cores (int8 K and V, d = 128, 4 or more heads; MPV): the logits of the piece's 32
     // cells as S[cell][head] = K q^T per 64-dim scale group, and per 16-dim output tile O[head][dim] +=
     // P[head][cell] V[cell][dim], all with v_mfma_f32_16x16x32_f16 (heads padded to 16 rows). K and V codes are exact
@@ -183,11 +188,11 @@ __device__ __forceinline__ void attn_chunk_body(const ChunkArgs &a)
     // keep them in fp16's range, both terms accumulating into the same fp32 tile.
     constexpr bool MPV = D == 128 && G >= 4;
     constexpr int NTL = D / 16;                      // 16-dim output tiles (MPV)
-    static_assert(!MPV || (NG == 2 && PC == 32), "MFMA form: d = 128, 32-cell pieces");
+    static_assert(!MPV || (NG == 2 && PC == 32 && DL == D), "MFMA form: d = 128, 32-cell pieces");
     // MFMA form: output tile t's lane jl holds dim 16 t + jl (int8 V); with 4-bit V a transposing read of 16-byte
     // chunk c gives dims 32 c + 2 jl (low nibbles, tile 2 c) and 32 c + 2 jl + 1 (high nibbles, tile 2 c + 1)
     auto tile_dim = [](int t, int l) { return VB == 8 ? 16 * t + l : 32 * (t >> 1) + 2 * l + (t & 1); };
-    __shared__ __align__(16) int8_t sv[CW][PC * RB]; // the wave's V piece: [cell][RB], chunk c of row r at c ^ swizzle(r)
+    __shared__ __align__(16) int8_t sv[CW][PC * RBL];   // the wave's V piece: [cell][RBL], chunk c of row r at c ^ swizzle(r)
     // p * v_scale rows [cell][group][head] of the VALU p . v (the MFMA form keeps p in registers)
     __shared__ __align__(16) float sp[CW][MPV ? 4 : PC * NG * GP];
     __shared__ float sm[CW][G], sl[CW][G];
@@ -198,7 +203,10 @@ __device__ __forceinline__ void attn_chunk_body(const ChunkArgs &a)
     __shared__ __align__(16) float sq[G * D];        // the G q rows of (row i, KV head g)
     const int tid = threadIdx.x, lane = tid % 64;
     const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
-    const int r = lane / LPC, s = lane % LPC, grp_s = s / (LPC / NG);
+    const int r = lane / LPC, s = lane % LPC;
+    const bool s_in = DL == D || 16 * s < D;         // the lane's slice holds dims of the row
+    const int s_ld = s_in ? s : 0;                   // the slice it loads (padding slices load slice 0, unused)
+    const int grp_s = s_ld / (LPC / NG);
     const int G4 = lane >> 4, jl = lane & 15;
     const int grp_v = G4 / SUBS, sub_v = G4 % SUBS;  // the p . v lane's scale group and subgroup
     // wave -> (chunk j of the workgroup's CW / wpc chunks, sub-wave sub of the chunk's wpc waves)
@@ -273,10 +281,10 @@ __device__ __forceinline__ void attn_chunk_body(const ChunkArgs &a)
     float qv[G][16];
 #pragma unroll
     for (int h = 0; h < G; h++) {
-        const float4 *src = reinterpret_cast<const float4 *>(sq + h * D + 16 * s);
+        const float4 *src = reinterpret_cast<const float4 *>(sq + h * D + 16 * s_ld);
 #pragma unroll
         for (int jj = 0; jj < 4; jj++) {
-            const float4 u = src[jj];
+            const float4 u = s_in ? src[jj] : make_float4(0.f, 0.f, 0.f, 0.f);
             qv[h][4 * jj + 0] = u.x;
             qv[h][4 * jj + 1] = u.y;
             qv[h][4 * jj + 2] = u.z;
@@ -358,10 +366,10 @@ __device__ __forceinline__ void attn_chunk_body(const ChunkArgs &a)
     for (int t = 0; t < NTL; t++) oacc[t] = f4v{0.f, 0.f, 0.f, 0.f};
     int32_t srun = 1000;
 
-    const int8_t *kbase = P.k + (int64_t)g * P.capacity * D + 16 * s;
+    const int8_t *kbase = P.k + (int64_t)g * P.capacity * D + 16 * s_ld;
     const int8_t *vbase = P.v + (int64_t)g * P.capacity * RB;
-    const float *ksbase = P.ks + (int64_t)g * P.capacity * NG + grp_s;
-    const float *vsbase = P.vs + (int64_t)g * P.capacity * NG;
+    const float *ksbase = P.ks + (int64_t)g * P.capacity * NGM + grp_s;
+    const float *vsbase = P.vs + (int64_t)g * P.capacity * NGM;
     const int8_t *kmu = P.k + (int64_t)g * P.capacity * D;   // MFMA form: K and key scales of KV head g
     const float *ksm = P.ks + (int64_t)g * P.capacity * NG;
     int8_t *svw = sv[wave];
@@ -545,9 +553,11 @@ __device__ __forceinline__ void attn_chunk_body(const ChunkArgs &a)
             for (int st = 0; st < STEPS; st++) {
                 const int32_t c = min(cb + st * CPS + r, limit);
                 kw[st] = *reinterpret_cast<const int4 *>(kbase + (int64_t)c * D);
-                ksc[st] = ksbase[(int64_t)c * NG] * a.qscale;   // sm_scale * log2(e) rides on the key scale
-                const float *vsrc = vsbase + (int64_t)c * NG;   // all NG group scales of the cell, one load
-                if constexpr (NG == 4) {
+                ksc[st] = ksbase[(int64_t)c * NGM] * a.qscale;  // sm_scale * log2(e) rides on the key scale
+                const float *vsrc = vsbase + (int64_t)c * NGM;  // all group scales of the cell, one load
+                if constexpr (NGM == 3) {
+                    vsc[st][0] = vsrc[0]; vsc[st][1] = vsrc[1]; vsc[st][2] = vsrc[2]; vsc[st][3] = 0.f;
+                } else if constexpr (NG == 4) {
                     const float4 u = *reinterpret_cast<const float4 *>(vsrc);
                     vsc[st][0] = u.x; vsc[st][1] = u.y; vsc[st][2] = u.z; vsc[st][3] = u.w;
                 } else if constexpr (NG == 2) {
@@ -561,7 +571,8 @@ __device__ __forceinline__ void attn_chunk_body(const ChunkArgs &a)
             for (int q = 0; q < VCH; q++) {
                 const int slot = 64 * q + lane, cell = slot / CHUNKS, pch = slot % CHUNKS;
                 const int32_t c = min(cb + cell, limit);
-                load_lds16(vbase + (int64_t)c * RB + 16 * (pch ^ (cell & SWZ)), lds_addr(svw + 1024 * q));
+                const int mc = pch ^ (cell & SWZ);      // the pool chunk this LDS position holds
+                load_lds16(vbase + (int64_t)c * RB + 16 * (RB == RBL || mc < MCH ? mc : 0), lds_addr(svw + 1024 * q));
             }
             __builtin_amdgcn_sched_barrier(0);   // every copy is in flight before the logits start
 
@@ -647,7 +658,7 @@ __device__ __forceinline__ void attn_chunk_body(const ChunkArgs &a)
                     const int lc = CPG * grp_v + sub_v + SUBS * t;   // logical 16-byte chunk of the lane's dims
                     const int cell = 8 * co + i8;
                     dst[t] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-                        (QSA_LDS v2i *)(svw + cell * RB + 16 * (lc ^ (cell & SWZ)) + 8 * hh));
+                        (QSA_LDS v2i *)(svw + cell * RBL + 16 * (lc ^ (cell & SWZ)) + 8 * hh));
                 }
             };
             float4 ring[PWD][GR];
@@ -708,6 +719,7 @@ __device__ __forceinline__ void attn_chunk_body(const ChunkArgs &a)
 #pragma unroll
                 for (int n = 0; n < NPB; n++) {
                     const int d = DPC * (CPG * grp_v + sub_v + SUBS * t) + NPB * jl + n;
+                    if (DL != D && d >= D) continue;
 #pragma unroll
                     for (int h = 0; h < G; h++)
                         a.o_out[(row0 + (int64_t)h * a.max_chunks) * D + d] = o[h][NPB * t + n];
@@ -753,6 +765,7 @@ __device__ __forceinline__ void attn_chunk_body(const ChunkArgs &a)
 #pragma unroll
             for (int n = 0; n < NPB; n++) {
                 const int d = DPC * (CPG * grp_v + sub_v + SUBS * t) + NPB * jl + n;
+                if (DL != D && d >= D) continue;
 #pragma unroll
                 for (int h = 0; h < G; h++) so[wave][h][d] = o[h][NPB * t + n];
             }
@@ -849,6 +862,8 @@ __global__ __launch_bounds__(64 * CW) void attn_chunk_select_kernel(const ChunkA
 void launch_chunk_64_8(int G, int wpc, dim3 grid, hipStream_t s, const ChunkArgs &a);
 void launch_chunk_128_8(int G, int wpc, dim3 grid, hipStream_t s, const ChunkArgs &a);
 void launch_chunk_128_4(int G, int wpc, dim3 grid, hipStream_t s, const ChunkArgs &a);
+void launch_chunk_192_8(int G, int wpc, dim3 grid, hipStream_t s, const ChunkArgs &a);
+void launch_chunk_192_4(int G, int wpc, dim3 grid, hipStream_t s, const ChunkArgs &a);
 void launch_chunk_256_8(int G, int wpc, dim3 grid, hipStream_t s, const ChunkArgs &a);
 void launch_chunk_256_4(int G, int wpc, dim3 grid, hipStream_t s, const ChunkArgs &a);
 

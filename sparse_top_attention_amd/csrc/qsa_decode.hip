@@ -27,8 +27,9 @@ __device__ __forceinline__ void block_mean(const int8_t *__restrict__ k, const f
                                            int32_t n_valid, int32_t g, int32_t b, int32_t blk_stride,
                                            float *__restrict__ index)
 {
-    constexpr int LPC = D / 16, CPS = 64 / LPC, STEPS = QSA_BLOCK / CPS, NG = D / QSA_GROUP;
+    constexpr int DL = lane_dims<D>(), LPC = DL / 16, CPS = 64 / LPC, STEPS = QSA_BLOCK / CPS, NG = D / QSA_GROUP;
     const int lane = threadIdx.x % 64, r = lane / LPC, s = lane % LPC, grp = (16 * s) / QSA_GROUP;
+    const bool sl = DL == D || 16 * s < D;        // the lane's slice holds dims of the row
     const int64_t c0 = (int64_t)b * QSA_BLOCK;   // 64-bit: a capacity near INT32_MAX
     float acc[16];
 #pragma unroll
@@ -36,7 +37,7 @@ __device__ __forceinline__ void block_mean(const int8_t *__restrict__ k, const f
 #pragma unroll
     for (int st = 0; st < STEPS; st++) {
         const int64_t c = c0 + st * CPS + r;
-        if (c < n_valid) {
+        if (c < n_valid && sl) {
             const int64_t cell = (int64_t)g * cap + c;
             const int4 w = *reinterpret_cast<const int4 *>(k + cell * D + 16 * s);
             const float sc = ks[cell * NG + grp];
@@ -51,7 +52,7 @@ __device__ __forceinline__ void block_mean(const int8_t *__restrict__ k, const f
     const int64_t left = n_valid - c0;
     const int32_t nb = left < 0 ? 0 : (left > QSA_BLOCK ? QSA_BLOCK : (int32_t)left);
     const float inv = nb > 0 ? 1.0f / (float)nb : 0.f;
-    if (r == 0) {
+    if (r == 0 && sl) {
         float4 *dst = reinterpret_cast<float4 *>(index + ((int64_t)g * blk_stride + b) * D + 16 * s);
 #pragma unroll
         for (int j = 0; j < 4; j++)
@@ -153,8 +154,10 @@ __global__ __launch_bounds__(64) void block_scores_kernel(const float *__restric
                                                           int32_t n_valid, int32_t n_blocks,
                                                           float *__restrict__ scores)
 {
-    constexpr int LPB = D / 8, BPS = 64 / LPB, NSTEP = 4;
-    const int lane = threadIdx.x, rb = lane / LPB, s = lane % LPB;
+    constexpr int DL = lane_dims<D>(), LPB = DL / 8, BPS = 64 / LPB, NSTEP = 4;
+    const int lane = threadIdx.x, rb = lane / LPB, s0 = lane % LPB;
+    const bool sl = DL == D || 8 * s0 < D;   // the lane's 8 dims are dims of the row (else it adds zeros)
+    const int s = sl ? s0 : 0;
     const int32_t g = blockIdx.y;
     const int32_t bw = blockIdx.x * (BPS * NSTEP);
     float rv[NSTEP][8];
@@ -165,7 +168,7 @@ __global__ __launch_bounds__(64) void block_scores_kernel(const float *__restric
     for (int st = 0; st < NSTEP; st++) {
         const int32_t b = bw + st * BPS + rb;
         bidx[st] = b;
-        const bool live = b < n_live;
+        const bool live = b < n_live && sl;
         const float4 *src =
             reinterpret_cast<const float4 *>(index + ((int64_t)g * blk_stride + (live ? b : 0)) * D + 8 * s);
         const float4 u = src[0], w = src[1];
@@ -193,7 +196,7 @@ __global__ __launch_bounds__(64) void block_scores_kernel(const float *__restric
                 }
 #pragma unroll
                 for (int h = 0; h < 8; h++) {
-                    if (h < G) {
+                    if (h < G && sl) {
                         qt[rr][0] += u[h].x; qt[rr][1] += u[h].y; qt[rr][2] += u[h].z; qt[rr][3] += u[h].w;
                         qt[rr][4] += w[h].x; qt[rr][5] += w[h].y; qt[rr][6] += w[h].z; qt[rr][7] += w[h].w;
                     }
@@ -213,7 +216,7 @@ __global__ __launch_bounds__(64) void block_scores_kernel(const float *__restric
                 dot = group_sum<LPB>(dot);
                 const int32_t b = bidx[st];
                 const int64_t first = (int64_t)b * QSA_BLOCK;
-                if (s == 0 && b < n_blocks)
+                if (s0 == 0 && b < n_blocks)
                     scores[((int64_t)i * n_kv + g) * n_blocks + b] = (first <= p && first < n_valid) ? dot : -INFINITY;
             }
         }
@@ -232,8 +235,10 @@ __global__ __launch_bounds__(64) void select_scores_kernel(const SelectArgs a)
     // one wave per (tile of BPS * NSTEP blocks, KV head g, row i): the row's words and q rows, then the tile's index
     // rows of the row's pool (the block-score arithmetic: 8-dim fmaf chains per lane, a DPP sum over the block's
     // lanes); blocks past the pool's valid cells, and every block of a row whose pool index is out of range, are -inf
-    constexpr int LPB = D / 8, BPS = 64 / LPB, NSTEP = SCORE_STEPS;
-    const int lane = threadIdx.x, rb = lane / LPB, s = lane % LPB;
+    constexpr int DL = lane_dims<D>(), LPB = DL / 8, BPS = 64 / LPB, NSTEP = SCORE_STEPS;
+    const int lane = threadIdx.x, rb = lane / LPB, s0 = lane % LPB;
+    const bool sl = DL == D || 8 * s0 < D;   // the lane's 8 dims are dims of the row (else it adds zeros)
+    const int s = sl ? s0 : 0;
     const int32_t g = blockIdx.y, i = blockIdx.z;
     const int32_t bw = blockIdx.x * (BPS * NSTEP);
     const int32_t rp = a.row_pool ? a.row_pool[i] : 0;
@@ -255,7 +260,7 @@ __global__ __launch_bounds__(64) void select_scores_kernel(const SelectArgs a)
 #pragma unroll
     for (int st = 0; st < NSTEP; st++) {
         const int32_t b = bw + st * BPS + rb;
-        const bool live = b < n_live;
+        const bool live = b < n_live && sl;
         const float4 *src =
             reinterpret_cast<const float4 *>(P.index + ((int64_t)g * stride + (live ? b : 0)) * D + 8 * s);
         const float4 x = src[0], y = src[1];
@@ -269,7 +274,7 @@ __global__ __launch_bounds__(64) void select_scores_kernel(const SelectArgs a)
     for (int e = 0; e < 8; e++) qt[e] = 0.f;
 #pragma unroll
     for (int h = 0; h < 8; h++) {
-        if (h < a.G) {
+        if (h < a.G && sl) {
             qt[0] += u[h].x; qt[1] += u[h].y; qt[2] += u[h].z; qt[3] += u[h].w;
             qt[4] += w[h].x; qt[5] += w[h].y; qt[6] += w[h].z; qt[7] += w[h].w;
         }
@@ -282,7 +287,7 @@ __global__ __launch_bounds__(64) void select_scores_kernel(const SelectArgs a)
         dot = group_sum<LPB>(dot);
         const int32_t b = bw + st * BPS + rb;
         const int64_t first = (int64_t)b * QSA_BLOCK;
-        if (s == 0 && b < a.width)
+        if (s0 == 0 && b < a.width)
             a.scores[((int64_t)i * a.n_kv + g) * a.width + b] = (b < n_live && first <= p) ? dot : -INFINITY;
     }
 }
@@ -460,6 +465,7 @@ extern "C" qsa_status qsa_block_index(const qsa_pool *pool, qsa_dims dims, int32
     switch (dims.head_dim) {
     case 64: block_index_kernel<64><<<grid, 64, 0, s>>>(pool->k, pool->k_scale, pool->capacity, pool->n_valid, b0, stride, index); break;
     case 128: block_index_kernel<128><<<grid, 64, 0, s>>>(pool->k, pool->k_scale, pool->capacity, pool->n_valid, b0, stride, index); break;
+    case 192: block_index_kernel<192><<<grid, 64, 0, s>>>(pool->k, pool->k_scale, pool->capacity, pool->n_valid, b0, stride, index); break;
     default: block_index_kernel<256><<<grid, 64, 0, s>>>(pool->k, pool->k_scale, pool->capacity, pool->n_valid, b0, stride, index); break;
     }
     return launch_status();
@@ -492,12 +498,15 @@ extern "C" qsa_status qsa_kv_append(const qsa_pool *pools, int32_t n_pools, cons
     case 64: append_encode_kernel<64, 8><<<grid, 64, 0, s>>>(a); break;
     case 128: append_encode_kernel<128, 8><<<grid, 64, 0, s>>>(a); break;
     case -128: append_encode_kernel<128, 4><<<grid, 64, 0, s>>>(a); break;
+    case 192: append_encode_kernel<192, 8><<<grid, 64, 0, s>>>(a); break;
+    case -192: append_encode_kernel<192, 4><<<grid, 64, 0, s>>>(a); break;
     case -256: append_encode_kernel<256, 4><<<grid, 64, 0, s>>>(a); break;
     default: append_encode_kernel<256, 8><<<grid, 64, 0, s>>>(a); break;
     }
     switch (dims.head_dim) {
     case 64: append_index_kernel<64><<<grid, 64, 0, s>>>(a); break;
     case 128: append_index_kernel<128><<<grid, 64, 0, s>>>(a); break;
+    case 192: append_index_kernel<192><<<grid, 64, 0, s>>>(a); break;
     default: append_index_kernel<256><<<grid, 64, 0, s>>>(a); break;
     }
     return launch_status();
@@ -506,11 +515,12 @@ extern "C" qsa_status qsa_kv_append(const qsa_pool *pools, int32_t n_pools, cons
 qsa_status qsa::select_scores_launch(const SelectArgs &a, int32_t n_rows, int32_t n_kv, int32_t head_dim,
                                      hipStream_t s)
 {
-    const int32_t per_wave = (64 / (head_dim / 8)) * SCORE_STEPS;
+    const int32_t per_wave = (64 / (lane_dims(head_dim) / 8)) * SCORE_STEPS;
     dim3 grid(ceil_div(a.width, per_wave), n_kv, n_rows);
     switch (head_dim) {
     case 64: select_scores_kernel<64><<<grid, 64, 0, s>>>(a); break;
     case 128: select_scores_kernel<128><<<grid, 64, 0, s>>>(a); break;
+    case 192: select_scores_kernel<192><<<grid, 64, 0, s>>>(a); break;
     default: select_scores_kernel<256><<<grid, 64, 0, s>>>(a); break;
     }
     return launch_status();
@@ -528,13 +538,14 @@ extern "C" qsa_status qsa_block_scores(const float *q, const int32_t *pos, int32
     if (n_blocks > stride) return QSA_ERR_RANGE;
     if (n_rows == 0 || n_blocks == 0) return QSA_OK;
     const int32_t G = dims.n_q_heads / dims.n_kv_heads;
-    const int32_t per_wave = (64 / (dims.head_dim / 8)) * 4;
+    const int32_t per_wave = (64 / (lane_dims(dims.head_dim) / 8)) * 4;
     dim3 grid(ceil_div(n_blocks, per_wave), dims.n_kv_heads);
     hipStream_t s = (hipStream_t)stream;
 #define QSA_SCORES(DD) block_scores_kernel<DD><<<grid, 64, 0, s>>>(q, pos, n_rows, dims.n_q_heads, dims.n_kv_heads, G, pool->index, stride, pool->n_valid, n_blocks, scores)
     switch (dims.head_dim) {
     case 64: QSA_SCORES(64); break;
     case 128: QSA_SCORES(128); break;
+    case 192: QSA_SCORES(192); break;
     default: QSA_SCORES(256); break;
     }
 #undef QSA_SCORES
@@ -559,12 +570,14 @@ void launch_chunk_d(int D, int vb, int G, int wpc, dim3 grid, hipStream_t s, con
 {
     if (vb == 4) {
         if (D == 128) launch_chunk_128_4(G, wpc, grid, s, a);
+        else if (D == 192) launch_chunk_192_4(G, wpc, grid, s, a);
         else launch_chunk_256_4(G, wpc, grid, s, a);
         return;
     }
     switch (D) {
     case 64: launch_chunk_64_8(G, wpc, grid, s, a); break;
     case 128: launch_chunk_128_8(G, wpc, grid, s, a); break;
+    case 192: launch_chunk_192_8(G, wpc, grid, s, a); break;
     default: launch_chunk_256_8(G, wpc, grid, s, a); break;
     }
 }
@@ -634,6 +647,7 @@ qsa_status qsa::merge_launch(const float *m, const float *l, const float *o, con
     switch (head_dim) {
     case 64: QSA_MERGE(64); break;
     case 128: QSA_MERGE(128); break;
+    case 192: QSA_MERGE(192); break;
     default: QSA_MERGE(256); break;
     }
 #undef QSA_MERGE

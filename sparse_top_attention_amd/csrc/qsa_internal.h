@@ -15,11 +15,18 @@
 
 namespace qsa {
 
+// The lane layouts cut a cell's dims into 16-dim slices (8-dim slices for the index rows) and reduce across a cell's
+// slices with power-of-two cross-lane steps. head_dim 192 (12 slices) therefore runs on the layouts of 256: the lanes
+// of slices past dim 191 load nothing of the row and add exact zeros.
+template <int D>
+constexpr int lane_dims() { return D == 192 ? 256 : D; }
+inline int lane_dims(int d) { return d == 192 ? 256 : d; }
+
 // ------------------------------------------------------------------------------------------------ host side
 inline bool dims_supported(const qsa_dims &d)
 {
     if (d.block_cells != QSA_BLOCK) return false;
-    if (d.head_dim != 64 && d.head_dim != 128 && d.head_dim != 256) return false;
+    if (d.head_dim != 64 && d.head_dim != 128 && d.head_dim != 192 && d.head_dim != 256) return false;
     if (d.n_kv_heads <= 0 || d.n_q_heads <= 0 || d.n_q_heads % d.n_kv_heads != 0) return false;
     if (d.n_q_heads / d.n_kv_heads > 8) return false;
     if (d.n_kv_heads > 65535) return false;   // KV heads index a launch grid's y dimension

@@ -36,7 +36,7 @@ __global__ __launch_bounds__(64 * NW) void topk_kernel(const float *__restrict__
 template <int D, int KPT, int NW>
 __global__ __launch_bounds__(64 * NW) void select_kernel(const SelectArgs a)
 {
-    constexpr int LPB = D / 8, BPS = 64 / LPB;       // lanes per block, blocks per wave step
+    constexpr int DL = lane_dims<D>(), LPB = DL / 8, BPS = 64 / LPB;   // lanes per block, blocks per wave step
     constexpr int T = 64 * NW, SB = NW * BPS;         // threads, blocks per workgroup step
     static_assert(T >= D, "one thread per dim sums q");
     __shared__ float sqs[D];
@@ -66,7 +66,9 @@ __global__ __launch_bounds__(64 * NW) void select_kernel(const SelectArgs a)
     const int32_t n_valid = pool_ok ? P.n_valid : 0;
     const int32_t stride = ceil_div(P.capacity, QSA_BLOCK);
 
-    const int rb = lane / LPB, s = lane % LPB;
+    const int rb = lane / LPB, s0 = lane % LPB;
+    const bool sl = DL == D || 8 * s0 < D;   // the lane's 8 dims are dims of the row (else it adds zeros)
+    const int s = sl ? s0 : 0;
     const float *idx_g = P.index + (int64_t)g * stride * D + 8 * s;
     const int32_t n_live = min(a.width, ceil_div(n_valid, QSA_BLOCK));
     // batches of NST steps of SB blocks each. Loads are unconditional (a dead block reads block 0 and is zeroed
@@ -104,7 +106,7 @@ __global__ __launch_bounds__(64 * NW) void select_kernel(const SelectArgs a)
     __syncthreads();
     float qt[8];
 #pragma unroll
-    for (int e = 0; e < 8; e++) qt[e] = sqs[8 * s + e];
+    for (int e = 0; e < 8; e++) qt[e] = sl ? sqs[8 * s + e] : 0.f;
     // one batch of index rows in registers at a time: each step's registers take the next batch's rows as soon as
     // its score is done
 #pragma unroll 1
@@ -113,12 +115,12 @@ __global__ __launch_bounds__(64 * NW) void select_kernel(const SelectArgs a)
 #pragma unroll
         for (int st = 0; st < NST; st++) {
             const int32_t b = base + st * SB + wave * BPS + rb;
-            const bool live = b < n_live;
+            const bool live = b < n_live && sl;
             float dot = 0.f;
 #pragma unroll
             for (int e = 0; e < 8; e++) dot = fmaf(qt[e], live ? rv[st][e] : 0.f, dot);
             dot = group_sum<LPB>(dot);
-            if (s == 0 && b < T * KPT) {
+            if (s0 == 0 && b < T * KPT) {
                 const int64_t first = (int64_t)b * QSA_BLOCK;
                 const float sc = (b < a.width && first <= p && first < n_valid) ? dot : -INFINITY;
                 ssc[b] = sc;
@@ -181,6 +183,7 @@ qsa_status qsa::select_launch(const SelectArgs &a, int32_t n_rows, int32_t n_kv,
     switch (head_dim) {
     case 64: QSA_SEL_D(64); break;
     case 128: QSA_SEL_D(128); break;
+    case 192: QSA_SEL_D(192); break;
     default: QSA_SEL_D(256); break;
     }
 #undef QSA_SEL_D

@@ -62,7 +62,7 @@ GOOD = D(24, 4, 128, 64)
 
 @pytest.mark.parametrize("dims,expect", [
     (D(24, 4, 96, 64), -3),    # head_dim not supported
-    (D(24, 4, 192, 64), -3),   # 64-dim groups, but 12 lanes per cell: not supported
+    (D(24, 4, 320, 64), -3),   # 64-dim groups, but past 256
     (D(24, 4, 128, 32), -3),   # block size not 64
     (D(24, 5, 128, 64), -2),   # q heads not a multiple of KV heads
     (D(40, 4, 128, 64), -3),   # more than 8 q heads per KV head
@@ -182,7 +182,8 @@ def test_prompt_scratch_sizing_and_checks():
     d64, d256 = D(24, 4, 64, 64), D(24, 4, 256, 64)
     assert L.qsa_prompt_scratch_bytes(16, 0, d64) >= 16 * 24 * 1 * (64 * 4 + 9)
     assert L.qsa_prompt_scratch_bytes(100, 4000, d256) >= 64 * 24 * 32 * (256 * 4 + 9)
-    assert L.qsa_prompt_scratch_bytes(16, 0, D(24, 4, 192, 64)) == 0
+    d192 = D(24, 4, 192, 64)
+    assert L.qsa_prompt_scratch_bytes(16, 0, d192) >= 16 * 24 * 1 * (192 * 4 + 9)
     p = _pool()
     assert L.qsa_prompt_attn(1, 16, 0, ctypes.byref(p), GOOD, 1.0, 1, None, 0, None) == -1       # no scratch
     need = L.qsa_prompt_scratch_bytes(16, 0, GOOD)
@@ -194,7 +195,8 @@ def test_prompt_scratch_sizing_and_checks():
     p4 = _pool(v_bits=4)
     assert L.qsa_prompt_attn(1, 16, 0, ctypes.byref(p4), GOOD, 1.0, 1, 1, 0, None) == -4
     assert L.qsa_prompt_attn(1, 16, 0, ctypes.byref(p4), d64, 1.0, 1, 1, need, None) == -3     # K8V4 at head_dim 64
-    assert L.qsa_prompt_attn(1, 16, 0, ctypes.byref(p), D(24, 4, 192, 64), 1.0, 1, 1, need, None) == -3
+    need192 = L.qsa_prompt_scratch_bytes(16, 0, d192)
+    assert L.qsa_prompt_attn(1, 16, 0, ctypes.byref(p), d192, 1.0, 1, 1, need192 - 1, None) == -4
     assert L.qsa_prompt_attn(1, 2, 2**31 - 1, ctypes.byref(p), GOOD, 1.0, 1, 1, need, None) == -5  # positions past int32
     assert L.qsa_prompt_attn(1, 2**27, 0, ctypes.byref(p), GOOD, 1.0, 1, 1, need, None) == -3  # 3.2e9 (query, head) rows
     assert L.qsa_prompt_attn(1, 0, 0, ctypes.byref(p), GOOD, 1.0, 1, None, 0, None) == 0

@@ -29,7 +29,7 @@ def _host(p):
             p.index.cpu().numpy())
 
 
-@pytest.mark.parametrize("d,many", [(64, False), (128, False), (256, False), (64, True), (128, True)])
+@pytest.mark.parametrize("d,many", [(64, False), (128, False), (192, False), (256, False), (64, True), (128, True)])
 def test_append_matches_oracle_bitwise(d, many):
     """6 or 12 new rows (12 rows: six more cells in the same two blocks) against the oracle's encoder, bit for bit."""
     n_kv, cap, n_old = 2, 700, 600

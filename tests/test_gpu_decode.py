@@ -31,7 +31,8 @@ def small_workload(seed, n_kv=2, G=3, d=128, cap=1400, n_valid=1290, rows=3, top
 
 
 # ------------------------------------------------------------------------------------------------ index
-@pytest.mark.parametrize("d,n_valid,cap", [(128, 1290, 1400), (64, 64, 64), (256, 700, 1000), (128, 16384, 200_000)])
+@pytest.mark.parametrize("d,n_valid,cap", [(128, 1290, 1400), (64, 64, 64), (256, 700, 1000), (192, 1000, 1100),
+                                           (128, 16384, 200_000)])
 def test_block_index(d, n_valid, cap):
     pool = synth.random_pool(7, 2, cap, n_valid, d)
     dims = qsa.Dims(6, 2, d)
@@ -62,7 +63,7 @@ def test_block_index_partial_range_touches_only_its_blocks():
 
 
 # ----------------------------------------------------------------------------------------------- scores
-@pytest.mark.parametrize("d,G,rows", [(128, 6, 4), (64, 1, 1), (256, 8, 3), (128, 5, 9)])
+@pytest.mark.parametrize("d,G,rows", [(128, 6, 4), (64, 1, 1), (256, 8, 3), (128, 5, 9), (192, 3, 5)])
 def test_block_scores(d, G, rows):
     n_kv, n_valid, cap = 2, 3000, 4096
     pool = synth.random_pool(11, n_kv, cap, n_valid, d)
@@ -151,7 +152,7 @@ def test_chunk_partials_short_selection_and_bad_ids():
 
 
 @pytest.mark.parametrize("d,G", [(64, 1), (64, 4), (64, 6), (64, 8), (128, 1), (128, 2), (128, 5), (128, 8),
-                                 (256, 1), (256, 3), (256, 6), (256, 8)])
+                                 (192, 1), (192, 4), (192, 6), (192, 8), (256, 1), (256, 3), (256, 6), (256, 8)])
 def test_decode_head_dims_and_group_sizes(d, G):
     w = small_workload(31 + d + G, n_kv=2, G=G, d=d, cap=2100, n_valid=2010, rows=2, topk=9)
     dims = dims_of(w)

@@ -50,9 +50,9 @@ def test_rejected_calls_write_nothing(setup):
     D, Hq, Hkv = dims.head_dim, dims.n_q_heads, dims.n_kv_heads
     q, pos = dev(w.q), dev(w.pos)
     nb = -(-w.pools[0].n_valid // BLOCK)
-    bad_dims = qsa._Dims(Hq, Hkv, 192, 64)
+    bad_dims = qsa._Dims(Hq, Hkv, 320, 64)
 
-    # block index: cell range past the capacity (QSA_ERR_RANGE); head_dim 192 (QSA_ERR_UNSUPPORTED)
+    # block index: cell range past the capacity (QSA_ERR_RANGE); head_dim 320 (QSA_ERR_UNSUPPORTED)
     index = _canary(*p.index.shape)
     assert L.qsa_block_index(ctypes.byref(pc), dims.c(), 0, p.capacity + 1, _ptr(index), s) == -5
     assert L.qsa_block_index(ctypes.byref(pc), bad_dims, 0, 64, _ptr(index), s) == -3
@@ -100,7 +100,7 @@ def test_rejected_calls_write_nothing(setup):
                               _ptr(lse), None, None, None, _ptr(scratch), need, s) == -5
     _unchanged(out, lse, scratch)
 
-    # prompt: scratch one byte short (QSA_ERR_SCRATCH); head_dim 192 (QSA_ERR_UNSUPPORTED)
+    # prompt: scratch one byte short (QSA_ERR_SCRATCH); head_dim 320 (QSA_ERR_UNSUPPORTED)
     pq = dev(synth.random_q(9, 8, Hq, D))
     pout = _canary(8, Hq, D)
     pneed = L.qsa_prompt_scratch_bytes(8, 100, dims.c())

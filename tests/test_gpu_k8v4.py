@@ -18,7 +18,7 @@ pytestmark = pytest.mark.gpu
 TOL = 1e-5
 
 
-@pytest.mark.parametrize("d,G,S", [(128, 6, 5), (128, 1, 3), (256, 3, 4), (256, 8, 7), (128, 8, 12)])
+@pytest.mark.parametrize("d,G,S", [(128, 6, 5), (128, 1, 3), (256, 3, 4), (256, 8, 7), (128, 8, 12), (192, 6, 4)])
 def test_k8v4_chunk_partials(d, G, S):
     w = small_workload(2000 + d + G, n_kv=2, G=G, d=d, cap=1500, n_valid=1421, rows=3, topk=9, v_bits=4)
     dims = dims_of(w)
@@ -29,7 +29,8 @@ def test_k8v4_chunk_partials(d, G, S):
     _partials_vs_oracle(w, to_device(pool), dims, S, ids.reshape(3, 2, -1), counts.reshape(3, 2))
 
 
-@pytest.mark.parametrize("d,G,rows,topk,S", [(128, 6, 4, 7, 3), (256, 4, 3, 9, 5), (128, 2, 2, 20, 16)])
+@pytest.mark.parametrize("d,G,rows,topk,S", [(128, 6, 4, 7, 3), (256, 4, 3, 9, 5), (128, 2, 2, 20, 16),
+                                             (192, 5, 3, 9, 4)])
 def test_k8v4_layer_equals_separate_calls_and_oracle(d, G, rows, topk, S):
     w = small_workload(2100 + d + G, n_kv=2, G=G, d=d, cap=2100, n_valid=2010, rows=rows, topk=topk, v_bits=4)
     dims = dims_of(w)
@@ -92,7 +93,7 @@ def test_k8v4_mixed_formats_rejected():
                            blocks_per_chunk=2)
 
 
-@pytest.mark.parametrize("d", [128, 256])
+@pytest.mark.parametrize("d", [128, 192, 256])
 def test_k8v4_append_matches_oracle_bitwise(d):
     n_kv, cap, n_old = 2, 700, 600
     pool = synth.random_pool(2300 + d, n_kv, cap, n_old, d, poison=False, v_bits=4)

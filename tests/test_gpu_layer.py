@@ -35,7 +35,7 @@ def run_layer(w, pdevs, dims, n_chunks, row_pool=None, nb=None, scratch=None, q=
 
 
 @pytest.mark.parametrize("d,G,rows,topk,S", [(128, 6, 4, 7, 3), (64, 1, 2, 5, 8), (256, 8, 3, 9, 2),
-                                             (128, 5, 5, 12, 5), (128, 3, 2, 4, 9)])
+                                             (128, 5, 5, 12, 5), (128, 3, 2, 4, 9), (192, 6, 3, 8, 3)])
 def test_layer_equals_separate_calls_and_oracle(d, G, rows, topk, S):
     w = small_workload(500 + d + G, n_kv=2, G=G, d=d, cap=2100, n_valid=2010, rows=rows, topk=topk)
     dims = dims_of(w)
@@ -175,7 +175,7 @@ def test_layer_first_position_sees_one_block():
     _check_end_to_end(w, got)
 
 
-@pytest.mark.parametrize("d,G,width_extra", [(128, 6, 0), (64, 2, 1), (256, 4, 0)])
+@pytest.mark.parametrize("d,G,width_extra", [(128, 6, 0), (64, 2, 1), (256, 4, 0), (192, 3, 1)])
 def test_select_equals_separate_calls(d, G, width_extra):
     """qsa_decode_select gives the bits of qsa_block_scores + qsa_topk, with or without a score output, and on
     score rows wider than the valid blocks (extra columns are -inf)."""

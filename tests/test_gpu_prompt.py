@@ -49,9 +49,11 @@ def test_prompt_small(n_kv, G, n_q, pos0, n_valid, cap, v_bits):
     (64, 8, 2, 6, 130, 300, 400, 420),        # three 64-query batches, queries past n_valid
     (256, 8, 2, 3, 70, 1000, 1049, 1100),     # head_dim 256, a ragged last block
     (256, 4, 1, 8, 40, 0, 2100, 2100),        # K8V4 at 256, the first query sees one cell
+    (192, 8, 2, 6, 90, 700, 760, 800),        # head_dim 192 (lanes of the 256 layout), two batches
+    (192, 4, 1, 3, 20, 1200, 1290, 1300),     # K8V4 at 192
 ])
 def test_prompt_other_shapes_match_oracle(d, v_bits, n_kv, G, n_q, pos0, n_valid, cap):
-    """Head dims without the int8 matrix-core kernel (64 and 256) take the dense chunk path: the same causal
+    """Head dims without the int8 matrix-core kernel (64, 192 and 256) take the dense chunk path: the same causal
     attention, checked against the FP64 oracle on every row."""
     pool = synth.random_pool(360 + d + v_bits, n_kv, cap, n_valid, d, v_bits=v_bits)
     q = synth.random_q(361 + d, n_q, n_kv * G, d)
