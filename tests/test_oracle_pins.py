@@ -36,6 +36,7 @@ def small_case(seed, n_kv=2, G=3, d=64, cap=300, n_valid=290, rows=3, poison=Tru
     (64, 290, [289, 288, 200]),      # ragged last block, a query inside a block
     (128, 256, [255, 63, 64]),       # exact blocks, queries at a block's last and a block's first cell
     (64, 70, [0, 5, 69]),            # query at cell 0 sees one cell
+    (192, 150, [149, 64, 100]),      # three scale groups per cell
 ])
 def test_dense_equals_textbook(d, n_valid, positions):
     pool, q, _ = small_case(11, d=d, cap=n_valid + 17, n_valid=n_valid, rows=len(positions))
@@ -409,7 +410,7 @@ def k8v4_case(seed, d=128, cap=400, n_valid=330, rows=3):
     return pool, q, pos
 
 
-@pytest.mark.parametrize("d", [128, 256])
+@pytest.mark.parametrize("d", [128, 192, 256])
 def test_k8v4_dense_and_selected_equal_textbook(d):
     """4-bit V unpacked by numpy in the brute-force path; poison (code -8, NaN scales) past n_valid stays unread."""
     pool, q, pos = k8v4_case(950 + d, d=d)
