@@ -10,7 +10,8 @@
 // 16 dims (one 16-byte load of int8 codes), so a wave covers 64 / (D/16) cells per step; lane = cell_slot * LPC +
 // slice. A slice never straddles a 64-dim scale group. The index kernel finishes its per-cell sums with a DPP sum
 // over the LPC lanes of the cell; the chunk kernel finishes its G per-cell dot products with a reduce-scatter over
-// those lanes, so that each (cell, head) logit ends in one lane.
+// those lanes, so that each (cell, head) logit ends in one lane. Head dim 192 uses the lane layouts of 256, its lanes
+// past dim 191 idle (lane_dims).
 #include "qsa_chunk.h"
 #include "qsa_internal.h"
 #include "qsa_radix.h"
