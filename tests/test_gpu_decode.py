@@ -137,8 +137,9 @@ def test_chunk_partials(S):
     _partials_vs_oracle(w, to_device(pool), dims, S, ids, counts)
 
 
-def test_chunk_partials_short_selection_and_bad_ids():
-    w = small_workload(23, rows=3)
+@pytest.mark.parametrize("d", [128, 192])
+def test_chunk_partials_short_selection_and_bad_ids(d):
+    w = small_workload(23, rows=3, d=d)
     dims = dims_of(w)
     ids = np.array([[[0, 5, 19, -1, -1, -1, -1], [20, 3, 7, 8, 9, 1, 2]],      # row 0: 3 of 7 valid
                     [[-1] * 7, [4, 1 << 30, -7, 6, 100000, 2, 19]],           # row 1: none; junk ids skipped
@@ -404,12 +405,13 @@ def test_dense_partials_one_and_two_waves_per_chunk(n_chunks, rows):
     assert rel_err_rows(go[full] / gl[full][:, None], ro[full] / rl[full][:, None]).max() <= TOL
 
 
-@pytest.mark.parametrize("G,v_bits", [(6, 8), (2, 8), (6, 4)], ids=["mfma-int8", "valu-int8", "mfma-k8v4"])
+@pytest.mark.parametrize("G,v_bits,d", [(6, 8, 128), (2, 8, 128), (6, 4, 128), (6, 8, 192)],
+                         ids=["mfma-int8", "valu-int8", "mfma-k8v4", "valu-int8-d192"])
 @pytest.mark.parametrize("scale", [-0.7, 0.0, 3.0])
-def test_dense_chunks_any_finite_scale(G, v_bits, scale):
+def test_dense_chunks_any_finite_scale(G, v_bits, d, scale):
     """sm_scale may be any finite value: a negative one flips which cells dominate, zero gives uniform weights over
     the visible cells, a large one sharpens the softmax. Dense chunks and the merge against the oracle."""
-    w = small_workload(71 + G + v_bits, n_kv=2, G=G, cap=900, n_valid=830, rows=3, v_bits=v_bits)
+    w = small_workload(71 + G + v_bits, n_kv=2, G=G, d=d, cap=900, n_valid=830, rows=3, v_bits=v_bits)
     dims = dims_of(w)
     n_chunks = 4
     part = qsa.Partials.empty_like_shape(3, dims.n_q_heads, n_chunks, dims.head_dim)
